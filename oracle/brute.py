@@ -1,0 +1,61 @@
+"""Pure-Python brute force for tiny paged-attention inputs (no numpy math).
+
+TEST INFRASTRUCTURE: used only by the tests, to check the C oracle on tiny
+inputs with an independent implementation (scalar loops, math.exp).
+
+Follows the definition on the "vLLM engineering deep-dive" page, section 3.1:
+look up the physical block of each logical token through the block table,
+score it against the query, softmax the scores, weight the values.  The
+element positions follow the "cache structure" page's key layout
+[blocks][heads][hs/x][B][x] and value layout [blocks][heads][hs][B].
+"""
+from __future__ import annotations
+
+import math
+import struct
+
+
+def _as_float(bits_or_value, is_bf16: bool) -> float:
+    if is_bf16:
+        return struct.unpack("<f", struct.pack("<I", int(bits_or_value) << 16))[0]
+    return float(bits_or_value)
+
+
+def attention(q, k_flat, v_flat, tables, lens, scale, Hq, Hkv, hs, B, is_bf16):
+    """q: nested list [S][Hq][hs]; k_flat/v_flat: flat lists of pool elements;
+    tables: nested list [S][M]; returns nested list [S][Hq][hs] of floats."""
+    x = 8 if is_bf16 else 4
+    G = Hq // Hkv
+    out = []
+    for s in range(len(lens)):
+        L = int(lens[s])
+        rows = []
+        for h in range(Hq):
+            kvh = h // G
+            if L == 0:
+                rows.append([0.0] * hs)
+                continue
+            scores = []
+            places = []
+            for t in range(L):
+                blk = int(tables[s][t // B])
+                j = t % B
+                places.append((blk, j))
+                acc = 0.0
+                for d in range(hs):
+                    kpos = (((blk * Hkv + kvh) * (hs // x) + d // x) * B + j) * x + d % x
+                    acc += _as_float(q[s][h][d], is_bf16) * _as_float(k_flat[kpos], is_bf16)
+                scores.append(acc * scale)
+            m = max(scores)
+            w = [math.exp(sc - m) for sc in scores]
+            z = sum(w)
+            o = []
+            for d in range(hs):
+                acc = 0.0
+                for (blk, j), wt in zip(places, w):
+                    vpos = ((blk * Hkv + kvh) * hs + d) * B + j
+                    acc += wt * _as_float(v_flat[vpos], is_bf16)
+                o.append(acc / z)
+            rows.append(o)
+        out.append(rows)
+    return out
