@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark for the paged KV-cache library on one MI355X.
+
+A step is one pass of the whole decode hot path over one batch: slot
+mapping of the new tokens, KV append, paged decode attention (context
+partitions plus their log-sum-exp merge).  Inputs are synthetic and
+resident in HBM before timing starts.
+
+Default workload: the MHA decode layer (64 sequences, 32/32 heads, head size
+128, block size 16, lengths uniform on [128, 2048], a pool of 8192 blocks
+with shuffled IDs, bf16).  `--config N` selects another decode
+configuration.
+
+Prints one JSON line.  `value` is KV-read GB/s of the whole step (KV bytes
+the attention must read / step time); `roofline` is the attention call
+timed with HIP events on its own stream; `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--partition-tokens", type=int, default=None,
+                    help="context partition length (default: the configuration's, else the library's choice)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--traffic", type=str, default=None,
+                    help="JSON file with measured HBM bytes per attention launch (from rocprofv3 counters)")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the benchmark, run 20 device-to-device copies of MIB MiB (counter calibration)")
+    return ap.parse_args()
+
+
+def device_inputs(w, torch):
+    def t(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+    return dict(q=t(w.q), kc=t(w.k_cache), vc=t(w.v_cache), bt=t(w.block_tables), sl=t(w.seq_lens),
+                nk=t(w.new_k), nv=t(w.new_v))
+
+
+def calib_copy(mib: int) -> None:
+    import torch
+
+    n = mib * (1 << 20)
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(20):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes": n, "launches": 20}))
+
+
+def cpu_baseline(w, target_s: float) -> dict:
+    """Time the CPU oracle (fp64, as it stands) on the workload's attention:
+    whole passes over every (sequence, query head), repeated until about
+    target_s seconds of wall time have passed."""
+    import oracle
+
+    slots = oracle.decode_slot_mapping(w.block_tables, w.seq_lens, w.B)
+    kp, vp = w.k_cache.copy(), w.v_cache.copy()
+    oracle.kv_append(w.new_k, w.new_v, slots, kp, vp)
+    passes = 0
+    used = oracle.max_threads()
+    t0 = time.perf_counter()
+    while True:
+        _, used = oracle.paged_attention(w.q, kp, vp, w.block_tables, w.seq_lens, w.scale, return_threads=True)
+        passes += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    el = time.perf_counter() - t0
+    bytes_read = passes * w.kv_read_bytes()
+    return {"value": round(bytes_read / el / 1e9, 4), "unit": "GB/s", "cores": int(used), "kind": "oracle",
+            "sample": f"{passes} full passes of the workload's attention (all {w.S} sequences x {w.Hq} query "
+                      f"heads), fp64 C oracle with OpenMP, {el:.1f} s wall on {used} threads; "
+                      f"same KV-byte accounting as value"}
+
+
+def main() -> int:
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no multi-GPU path",
+              file=sys.stderr)
+        return 2
+    import torch
+
+    if args.calib_copy:
+        calib_copy(args.calib_copy)
+        return 0
+
+    import paged_kv_cache_35_amd as pkv
+    import pkv_inputs as pi
+
+    pkv.library()
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    w = pi.make_workload(args.config, mode="timing")
+    log(f"generated config {args.config} ({w.description}) in {time.perf_counter() - t0:.1f} s")
+    P = w.partition_tokens if args.partition_tokens is None else args.partition_tokens
+    d = device_inputs(w, torch)
+    ws = pkv.alloc_workspace(d["q"], d["kc"], d["vc"], d["bt"], P)
+    out = torch.empty_like(d["q"])
+    slots = torch.empty(w.S, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    P_used = pkv.decode_partition_tokens(w.S, w.Hq, w.Hkv, w.hs, w.M, w.B, P)
+
+    def step(ev=None):
+        pkv.decode_slot_mapping(d["bt"], d["sl"], w.B, out=slots, stream=stream)
+        pkv.kv_cache_append(d["nk"], d["nv"], slots, d["kc"], d["vc"], stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        pkv.paged_decode_attention(d["q"], d["kc"], d["vc"], d["bt"], d["sl"], w.scale, out=out, workspace=ws,
+                                   partition_tokens=P, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    # timed region: K whole steps between two events
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+
+    # the attention call alone, bracketed by events on the same stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, attention median {np.median(attn_ms) * 1e3:.1f} us")
+
+    kv_bytes = w.kv_read_bytes()
+    attn_avg_s = float(attn_ms.mean()) / 1e3
+    achieved = kv_bytes / attn_avg_s / 1e9
+    traffic = None
+    if args.traffic and os.path.exists(args.traffic):
+        with open(args.traffic) as f:
+            traffic = json.load(f).get("bytes_per_launch")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                "kernel": "paged_decode_attention (partition kernel + log-sum-exp merge kernel)",
+                "algorithmic_bytes_per_launch": kv_bytes,
+                "launch_us": {"mean": round(attn_avg_s * 1e6, 2), "median": round(float(np.median(attn_ms)) * 1e3, 2),
+                              "p10": round(float(np.percentile(attn_ms, 10)) * 1e3, 2),
+                              "p90": round(float(np.percentile(attn_ms, 90)) * 1e3, 2)}}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle sample")
+        cpu = cpu_baseline(pi.make_workload(args.config, mode="timing"), args.cpu_seconds)
+    value = kv_bytes / (ms_step / 1e3) / 1e9
+    rec = {
+        "metric": "paged decode attention KV-read GB/s (% of HBM peak) + decode tokens/s, 1 GPU",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.dtype == "f32" else "bf16",
+        "data": "synthetic (seeded N(0,1) q/K/V, shuffled block IDs; no dataset)",
+        "config": {"workload": w.description, "config": args.config, "seed": w.seed, "num_seqs": w.S,
+                   "q_heads": w.Hq, "kv_heads": w.Hkv, "head_size": w.hs, "block_size": w.B,
+                   "pool_blocks": w.num_blocks, "sum_seq_len": int(w.seq_lens.sum()),
+                   "partition_tokens": P_used, "kv_bytes_per_step": kv_bytes},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "decode_tokens_per_s": round(w.S / (ms_step / 1e3), 1),
+        "attention_calls_per_s": round(1.0 / attn_avg_s, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

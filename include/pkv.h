@@ -1,0 +1,199 @@
+/*
+ * pkv.h — C ABI of the paged KV-cache decode library for AMD MI355X (gfx950).
+ *
+ * Two operations make up one decode step of PagedAttention:
+ *   1. kv_cache_append: store each sequence's new key/value vectors in the
+ *      slot the block allocator gave them (slot = block_id * B + offset);
+ *   2. paged_decode_attention: for every sequence and query head, walk the
+ *      sequence's block table to the physical blocks that hold its keys and
+ *      values and compute softmax(scale * q K^T) V over its seq_len tokens.
+ * pkv_decode_slot_mapping computes the slots of a decode step's new tokens
+ * from the block tables and lengths.
+ *
+ * Sources: the pages on PagedAttention —
+ *   "PagedAttention 详解：缓存的存储结构" (kefan.life): sections "Block Table",
+ *     "软件地址翻译" (software address translation, the K/V layouts and the
+ *     block_tables / seq_lens inputs), "一个具体的例子" (worked example) and
+ *     "写入新 K/V" (slot_mapping and its split in the cache-write kernel);
+ *   "vLLM 核心工程深度剖析" (ybb.press), section 3.1 (kernel signature: out,
+ *     q, k_cache, v_cache, block_tables, context_lens, max blocks per
+ *     sequence, scaling) and section 3.2;
+ *   "PagedAttention是什麼？" (yololab.net), section on the kernel (grid over
+ *     sequence, head and partition; partition reduction for long contexts).
+ *
+ * ---------------------------------------------------------------------------
+ * Data layout (device memory, all buffers owned by the caller)
+ * ---------------------------------------------------------------------------
+ * Element type T is fp32 (PKV_F32) or bfloat16 (PKV_BF16, 16-bit patterns).
+ * x = 16 / sizeof(T) elements form one 16-byte chunk (4 for fp32, 8 for bf16).
+ *
+ *   key pool    [num_blocks][num_kv_heads][head_size / x][block_size][x]
+ *   value pool  [num_blocks][num_kv_heads][head_size][block_size]
+ *
+ * so element d of token slot t of KV head h in block b sits at
+ *   key:   ((b*Hkv + h)*(hs/x) + d/x)*(B*x) + t*x + d%x
+ *   value: ((b*Hkv + h)*hs + d)*B + t
+ * Each (block, KV head) tile is B*hs contiguous elements in both pools.
+ *
+ *   q, out        [num_seqs][num_q_heads][head_size], element type T
+ *   k, v (append) [num_tokens][num_kv_heads][head_size], element type T
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]
+ *   seq_lens      int32 [num_seqs]
+ *   slot_mapping  int64 [num_tokens]
+ *
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).
+ * Token t of sequence s lives in block block_tables[s][t / B], slot t % B.
+ * Table entries at index >= ceil(seq_len / B) and slots >= seq_len in the
+ * last block are never read; they may hold anything, NaN included.
+ * All q/out/k/v/pool pointers must be 16-byte aligned.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions
+ * ---------------------------------------------------------------------------
+ * - Every call is asynchronous on `stream` (a hipStream_t, passed as void*;
+ *   NULL is the default stream).  Nothing is read back to the host, so
+ *   seq_lens and block_tables stay on the device.
+ * - The library allocates no device memory; the caller sizes the attention
+ *   workspace with pkv_decode_workspace_bytes.
+ * - Arguments that can be checked on the host are checked before any launch;
+ *   a failed check returns an error status and launches nothing.
+ * - Device-side contract (not checked on the host): block IDs of used table
+ *   entries lie in [0, num_blocks); 0 <= seq_len <= max_blocks_per_seq * B;
+ *   slots of one append call are distinct.  A kernel that meets an
+ *   out-of-range block ID or slot skips that block or token instead of
+ *   touching memory outside the pools, and a seq_len above
+ *   max_blocks_per_seq * B is treated as that maximum.
+ * - Results are deterministic: the reduction order depends only on the
+ *   logical token order, so relabelling physical blocks or sharing blocks
+ *   between tables gives bit-identical outputs.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define PKV_API __attribute__((visibility("default")))
+#else
+#define PKV_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PKV_OK = 0,
+    PKV_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misaligned pointer */
+    PKV_ERR_UNSUPPORTED = -2,  /* a shape or type this build has no kernel for */
+    PKV_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required */
+    PKV_ERR_HIP = -4           /* a HIP launch failed; see pkv_last_hip_error */
+} pkv_status;
+
+typedef enum {
+    PKV_F32 = 0,
+    PKV_BF16 = 1
+} pkv_dtype;
+
+/* Describes both pools (key and value share it). */
+typedef struct {
+    int32_t num_blocks;    /* physical blocks in each pool                     */
+    int32_t num_kv_heads;  /* Hkv                                              */
+    int32_t block_size;    /* B: token slots per block; 16 or 32               */
+    int32_t head_size;     /* hs: 64 or 128                                    */
+    int32_t dtype;         /* pkv_dtype of the pools, q, out, k and v          */
+} pkv_cache_desc;
+
+/* Layout contract version; changes whenever the pool layout above changes. */
+PKV_API int32_t pkv_layout_version(void);
+
+/* Human-readable name of a status code (static storage). */
+PKV_API const char* pkv_status_string(int32_t status);
+
+/* Name of the HIP error behind the last PKV_ERR_HIP on this host thread. */
+PKV_API const char* pkv_last_hip_error(void);
+
+/*
+ * Slot mapping of a decode step ("writing new K/V" section: slot =
+ * block_tables[s][pos / B] * B + pos % B).  The new token of sequence s is
+ * the last one, pos = seq_lens[s] - 1; sequences with seq_len <= 0, or whose
+ * position falls outside the table row, get slot -1 (the append skips it).
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
+ *   seq_lens      device int32 [num_seqs]
+ *   slot_mapping  device int64 [num_seqs], written
+ * Errors: PKV_ERR_INVALID_ARG for null pointers or non-positive sizes.
+ */
+PKV_API pkv_status pkv_decode_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens,
+                                   int32_t num_seqs, int32_t max_blocks_per_seq,
+                                   int32_t block_size, int64_t* slot_mapping, void* stream);
+
+/*
+ * KV append ("writing new K/V" section: the cache-write kernel splits each
+ * slot into block_id = slot / B and offset = slot % B and stores the token's
+ * key and value there).  Bit-exact copy, no type conversion: k, v and the
+ * pools share cache->dtype.
+ *   k, v          device T [num_tokens][num_kv_heads][head_size]
+ *   slot_mapping  device int64 [num_tokens]; slot < 0 means skip the token
+ *   k_cache, v_cache  device pools (layout above), written in place
+ * num_tokens == 0 is a no-op.  Errors: PKV_ERR_INVALID_ARG (null pointer,
+ * negative count, misaligned pointer, bad descriptor), PKV_ERR_UNSUPPORTED
+ * (dtype, head_size or block_size without a kernel), PKV_ERR_HIP.
+ */
+PKV_API pkv_status kv_cache_append(const void* k, const void* v, const int64_t* slot_mapping,
+                           int32_t num_tokens, const pkv_cache_desc* cache,
+                           void* k_cache, void* v_cache, void* stream);
+
+/*
+ * Context-partition length, in tokens, that paged_decode_attention will use
+ * for these sizes.  partition_tokens > 0 requests that length (it must be a
+ * multiple of block_size and at most 64 * block_size); 0 lets the library
+ * choose.  Returns 0 for invalid sizes.
+ */
+PKV_API int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_size, int32_t max_blocks_per_seq,
+                                    int32_t block_size, int32_t partition_tokens);
+
+/*
+ * Bytes of device workspace paged_decode_attention needs for these sizes
+ * (fp32 partial results per (sequence, query head, partition)).  Zero when
+ * one partition covers max_blocks_per_seq * block_size tokens.
+ */
+PKV_API size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_size, int32_t max_blocks_per_seq,
+                                  int32_t block_size, int32_t partition_tokens);
+
+/*
+ * Paged decode attention (signature of the "vLLM engineering deep-dive"
+ * page, section 3.1; partitioned long-context variant of the yololab page's
+ * kernel section).  For each sequence s and query head h, with
+ * kvh = h / (num_q_heads / num_kv_heads) and L = seq_lens[s]:
+ *   out[s][h] = sum_t softmax_t(scale * q[s][h] . K[t]) * V[t],  t < L,
+ * where K[t] and V[t] are slot t % B of block block_tables[s][t / B], KV
+ * head kvh.  Accumulation is fp32; a bf16 output is rounded to nearest
+ * even; L == 0 gives a zero output.
+ *   q             device T [num_seqs][num_q_heads][head_size]
+ *   k_cache, v_cache  device pools (layout above)
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
+ *   seq_lens      device int32 [num_seqs]
+ *   out           device T [num_seqs][num_q_heads][head_size], written
+ *   workspace     device scratch of workspace_bytes >= pkv_decode_workspace_bytes(...)
+ *                 (may be NULL when that size is 0); contents are overwritten
+ *   partition_tokens  0 = library's choice, else as in pkv_decode_partition_tokens
+ * Calls that share a workspace must be ordered on one stream.
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (head_size not 64/128,
+ * block_size not 16/32, num_q_heads / num_kv_heads not in 1..16 or not an
+ * integer), PKV_ERR_WORKSPACE, PKV_ERR_HIP.
+ */
+PKV_API pkv_status paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* seq_lens,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                  const pkv_cache_desc* cache, float scale, void* out,
+                                  void* workspace, size_t workspace_bytes,
+                                  int32_t partition_tokens, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

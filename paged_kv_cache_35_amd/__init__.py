@@ -1,0 +1,209 @@
+"""Paged KV-cache decode attention for AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of libpkv.so (include/pkv.h): it checks
+tensor shapes, dtypes and devices, turns tensors into device pointers and
+passes torch's current HIP stream.  Every step of the decode path runs in
+the library's HIP kernels; there is no Python or CPU fallback, and using the
+binding without the built library raises.
+
+Pool layouts (x = 16 / element size):
+    k_cache [num_blocks, Hkv, head_size // x, block_size, x]
+    v_cache [num_blocks, Hkv, head_size, block_size]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpkv.so")
+
+PKV_OK = 0
+PKV_F32 = 0
+PKV_BF16 = 1
+
+_DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, func: str, status: int, lib):
+        name = lib.pkv_status_string(status).decode()
+        extra = ""
+        if name == "PKV_ERR_HIP":
+            extra = " (" + lib.pkv_last_hip_error().decode() + ")"
+        super().__init__(f"{func} failed: {name}{extra}")
+        self.status = status
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("head_size", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def library():
+    """The loaded libpkv.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -m paged_kv_cache_35_amd.build "
+                               "or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+        L.pkv_layout_version.restype = i32
+        L.pkv_layout_version.argtypes = []
+        L.pkv_status_string.restype = ctypes.c_char_p
+        L.pkv_status_string.argtypes = [i32]
+        L.pkv_last_hip_error.restype = ctypes.c_char_p
+        L.pkv_last_hip_error.argtypes = []
+        L.pkv_decode_slot_mapping.restype = i32
+        L.pkv_decode_slot_mapping.argtypes = [P, P, i32, i32, i32, P, P]
+        L.kv_cache_append.restype = i32
+        L.kv_cache_append.argtypes = [P, P, P, i32, ctypes.POINTER(CacheDesc), P, P, P]
+        L.pkv_decode_partition_tokens.restype = i32
+        L.pkv_decode_partition_tokens.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.pkv_decode_workspace_bytes.restype = sz
+        L.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+        L.paged_decode_attention.restype = i32
+        L.paged_decode_attention.argtypes = [P, P, P, P, P, i32, i32, i32, ctypes.POINTER(CacheDesc), f32, P, P, sz,
+                                             i32, P]
+        _lib = L
+    return _lib
+
+
+def _check(func: str, status: int) -> None:
+    if status != PKV_OK:
+        raise PkvError(func, status, library())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor) -> CacheDesc:
+    """Descriptor of a key/value pool pair in the documented layouts."""
+    if k_cache.dtype != v_cache.dtype or k_cache.dtype not in _DTYPES:
+        raise ValueError("k_cache and v_cache must share dtype float32 or bfloat16")
+    if v_cache.dim() != 4 or k_cache.dim() != 5:
+        raise ValueError("k_cache must be [nb, Hkv, hs/x, B, x] and v_cache [nb, Hkv, hs, B]")
+    nb, hkv, hs, B = v_cache.shape
+    x = 16 // k_cache.element_size()
+    if tuple(k_cache.shape) != (nb, hkv, hs // x, B, x) or hs % x:
+        raise ValueError(f"k_cache shape {tuple(k_cache.shape)} does not match v_cache {tuple(v_cache.shape)}")
+    return CacheDesc(nb, hkv, B, hs, _DTYPES[k_cache.dtype])
+
+
+def layout_version() -> int:
+    return int(library().pkv_layout_version())
+
+
+def decode_slot_mapping(block_tables: torch.Tensor, seq_lens: torch.Tensor, block_size: int,
+                        out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """int64 [S]: slot of each sequence's newest token (position L-1); -1 when L <= 0."""
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_tables and seq_lens must be int32")
+    S, M = block_tables.shape
+    if out is None:
+        out = torch.empty(S, dtype=torch.int64, device=block_tables.device)
+    _check("pkv_decode_slot_mapping", library().pkv_decode_slot_mapping(
+        _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), S, M, block_size,
+        _dev(out, "out"), _stream(stream)))
+    return out
+
+
+def kv_cache_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                    v_cache: torch.Tensor, stream=None) -> None:
+    """Write k[i], v[i] ([T, Hkv, hs]) into slot slot_mapping[i] of the pools (in place)."""
+    desc = cache_desc(k_cache, v_cache)
+    T = k.shape[0]
+    if k.shape != v.shape or tuple(k.shape[1:]) != (desc.num_kv_heads, desc.head_size):
+        raise ValueError("k and v must be [T, Hkv, head_size]")
+    if k.dtype != k_cache.dtype or v.dtype != k_cache.dtype:
+        raise ValueError("k, v and the pools must share a dtype")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be int64 [T]")
+    if T == 0:
+        return
+    _check("kv_cache_append", library().kv_cache_append(
+        _dev(k, "k"), _dev(v, "v"), _dev(slot_mapping, "slot_mapping"), T, ctypes.byref(desc),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _stream(stream)))
+
+
+def decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq, block_size,
+                            partition_tokens=0) -> int:
+    return int(library().pkv_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, head_size,
+                                                     max_blocks_per_seq, block_size, partition_tokens))
+
+
+def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq, block_size,
+                           partition_tokens=0) -> int:
+    return int(library().pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size,
+                                                    max_blocks_per_seq, block_size, partition_tokens))
+
+
+def alloc_workspace(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                    partition_tokens: int = 0) -> Optional[torch.Tensor]:
+    desc = cache_desc(k_cache, v_cache)
+    S, Hq, _ = q.shape
+    n = decode_workspace_bytes(S, Hq, desc.num_kv_heads, desc.head_size, block_tables.shape[1], desc.block_size,
+                               partition_tokens)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                           block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           partition_tokens: int = 0, stream=None) -> torch.Tensor:
+    """out[s, h] = softmax(scale * q[s, h] K^T) V over the L = seq_lens[s]
+    tokens of sequence s, K/V found through block_tables."""
+    desc = cache_desc(k_cache, v_cache)
+    if q.dtype != k_cache.dtype:
+        raise ValueError("q must have the pools' dtype")
+    S, Hq, hs = q.shape
+    if hs != desc.head_size:
+        raise ValueError("q head size does not match the pools")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_tables and seq_lens must be int32")
+    if block_tables.shape[0] != S or seq_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, M] and seq_lens [S]")
+    M = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if workspace is None:
+        workspace = alloc_workspace(q, k_cache, v_cache, block_tables, partition_tokens)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("paged_decode_attention", library().paged_decode_attention(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
+        _dev(seq_lens, "seq_lens"), S, Hq, M, ctypes.byref(desc), float(scale), _dev(out, "out"), ws_ptr, ws_bytes,
+        int(partition_tokens), _stream(stream)))
+    return out
+
+
+def decode_step(q, k_cache, v_cache, block_tables, seq_lens, new_k, new_v, scale, out=None, workspace=None,
+                slot_mapping=None, partition_tokens=0, stream=None) -> torch.Tensor:
+    """One decode step: slot mapping of the new tokens, append, attention."""
+    desc = cache_desc(k_cache, v_cache)
+    slot_mapping = decode_slot_mapping(block_tables, seq_lens, desc.block_size, out=slot_mapping, stream=stream)
+    kv_cache_append(new_k, new_v, slot_mapping, k_cache, v_cache, stream=stream)
+    return paged_decode_attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out=out,
+                                  workspace=workspace, partition_tokens=partition_tokens, stream=stream)

@@ -1,0 +1,204 @@
+// C-ABI entry points: host-side validation, workspace sizing, partition
+// choice and dispatch to the kernels.  The contract is documented in
+// include/pkv.h.
+#include <string.h>
+
+#include "../../include/pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+pkv_status hip_status(hipError_t e)
+{
+    if (e == hipSuccess)
+        return PKV_OK;
+    g_last_hip_error = e;
+    return PKV_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : 2; }
+
+// Validates a pool descriptor; returns PKV_OK or the status to report.
+pkv_status check_cache(const pkv_cache_desc* c)
+{
+    if (!c)
+        return PKV_ERR_INVALID_ARG;
+    if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->block_size <= 0 || c->head_size <= 0)
+        return PKV_ERR_INVALID_ARG;
+    if (c->dtype != PKV_F32 && c->dtype != PKV_BF16)
+        return PKV_ERR_UNSUPPORTED;
+    if (c->head_size != 64 && c->head_size != 128)
+        return PKV_ERR_UNSUPPORTED;
+    if (c->block_size != 16 && c->block_size != 32)
+        return PKV_ERR_UNSUPPORTED;
+    return PKV_OK;
+}
+
+// Library choice of the context-partition length: 512 tokens (32 blocks at
+// B = 16, 16 at B = 32), or one partition when the table is shorter.
+int32_t resolve_partition_tokens(int32_t max_blocks_per_seq, int32_t block_size, int32_t requested)
+{
+    if (requested < 0 || max_blocks_per_seq <= 0 || block_size <= 0)
+        return 0;
+    if (requested > 0) {
+        if (requested % block_size != 0 || requested / block_size > 64)
+            return 0;
+        return requested;
+    }
+    const int64_t whole = (int64_t)max_blocks_per_seq * block_size;
+    const int32_t dflt = 512;
+    return (int32_t)(whole < dflt ? whole : dflt);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pkv_layout_version(void) { return 1; }
+
+const char* pkv_status_string(int32_t status)
+{
+    switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_INVALID_ARG: return "PKV_ERR_INVALID_ARG";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    default: return "PKV_UNKNOWN_STATUS";
+    }
+}
+
+const char* pkv_last_hip_error(void) { return hipGetErrorName(g_last_hip_error); }
+
+pkv_status pkv_decode_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                                   int32_t max_blocks_per_seq, int32_t block_size, int64_t* slot_mapping,
+                                   void* stream)
+{
+    if (num_seqs < 0 || max_blocks_per_seq <= 0 || block_size <= 0)
+        return PKV_ERR_INVALID_ARG;
+    if (num_seqs == 0)
+        return PKV_OK;
+    if (!block_tables || !seq_lens || !slot_mapping)
+        return PKV_ERR_INVALID_ARG;
+    return hip_status(pkv::launch_slot_mapping(block_tables, seq_lens, num_seqs, max_blocks_per_seq, block_size,
+                                               slot_mapping, (hipStream_t)stream));
+}
+
+pkv_status kv_cache_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                           const pkv_cache_desc* cache, void* k_cache, void* v_cache, void* stream)
+{
+    if (num_tokens < 0)
+        return PKV_ERR_INVALID_ARG;
+    pkv_status st = check_cache(cache);
+    if (st != PKV_OK)
+        return st;
+    if (!k_cache || !v_cache || !aligned16(k_cache) || !aligned16(v_cache))
+        return PKV_ERR_INVALID_ARG;
+    if (num_tokens == 0)
+        return PKV_OK;
+    if (!k || !v || !slot_mapping || !aligned16(k) || !aligned16(v))
+        return PKV_ERR_INVALID_ARG;
+    pkv::AppendArgs a;
+    a.k = k;
+    a.v = v;
+    a.slot_mapping = slot_mapping;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.num_tokens = num_tokens;
+    a.num_kv_heads = cache->num_kv_heads;
+    a.head_size = cache->head_size;
+    a.block_size = cache->block_size;
+    a.num_blocks = cache->num_blocks;
+    a.elem_bytes = elem_bytes(cache->dtype);
+    return hip_status(pkv::launch_append(a, (hipStream_t)stream));
+}
+
+int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_size, int32_t max_blocks_per_seq, int32_t block_size,
+                                    int32_t partition_tokens)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_size <= 0)
+        return 0;
+    return resolve_partition_tokens(max_blocks_per_seq, block_size, partition_tokens);
+}
+
+size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_size,
+                                  int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_tokens)
+{
+    const int32_t P = pkv_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, head_size,
+                                                  max_blocks_per_seq, block_size, partition_tokens);
+    if (P <= 0)
+        return 0;
+    const int64_t pb = P / block_size;
+    const int64_t parts = (max_blocks_per_seq + pb - 1) / pb;
+    if (parts <= 1)
+        return 0;
+    return (size_t)num_seqs * num_q_heads * parts * ((size_t)head_size + 2) * sizeof(float);
+}
+
+pkv_status paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                                  float scale, void* out, void* workspace, size_t workspace_bytes,
+                                  int32_t partition_tokens, void* stream)
+{
+    if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
+        return PKV_ERR_INVALID_ARG;
+    pkv_status st = check_cache(cache);
+    if (st != PKV_OK)
+        return st;
+    const int32_t Hkv = cache->num_kv_heads;
+    if (num_q_heads % Hkv != 0)
+        return PKV_ERR_INVALID_ARG;
+    const int32_t G = num_q_heads / Hkv;
+    if (G > 16)
+        return PKV_ERR_UNSUPPORTED;
+    if ((int64_t)max_blocks_per_seq * cache->block_size > INT32_MAX)
+        return PKV_ERR_INVALID_ARG;
+    if (num_seqs == 0)
+        return PKV_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out)
+        return PKV_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return PKV_ERR_INVALID_ARG;
+    const int32_t P = resolve_partition_tokens(max_blocks_per_seq, cache->block_size, partition_tokens);
+    if (P <= 0)
+        return PKV_ERR_INVALID_ARG;
+    const int32_t pb = P / cache->block_size;
+    const int32_t parts = (max_blocks_per_seq + pb - 1) / pb;
+    if (num_seqs > 65535 || parts > 65535)
+        return PKV_ERR_UNSUPPORTED;
+    const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, Hkv, cache->head_size,
+                                                   max_blocks_per_seq, cache->block_size, partition_tokens);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+        return PKV_ERR_WORKSPACE;
+
+    pkv::DecodeArgs a;
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.out = out;
+    const size_t units = (size_t)num_seqs * num_q_heads * parts;
+    a.ws_o = need > 0 ? (float*)workspace : nullptr;
+    a.ws_ml = need > 0 ? (float*)workspace + units * cache->head_size : nullptr;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = Hkv;
+    a.head_size = cache->head_size;
+    a.block_size = cache->block_size;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.num_blocks = cache->num_blocks;
+    a.dtype = cache->dtype;
+    a.partition_blocks = pb;
+    a.max_parts = parts;
+    a.scale = scale;
+    return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,57 @@
+// Internal launch interface between the C-ABI entry points (api.hip) and
+// the kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+// Problem description shared by the decode launchers; every field has been
+// validated on the host before a launcher sees it.
+struct DecodeArgs {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* block_tables;
+    const int32_t* seq_lens;
+    void* out;
+    float* ws_o;    // [S][Hq][max_parts][hs] fp32, or null when max_parts == 1
+    float* ws_ml;   // [S][Hq][max_parts][2]  fp32 (running max in log2 units, sum)
+    int32_t num_seqs;
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_size;
+    int32_t block_size;
+    int32_t max_blocks_per_seq;
+    int32_t num_blocks;
+    int32_t dtype;            // pkv_dtype
+    int32_t partition_blocks; // blocks per context partition (<= 64)
+    int32_t max_parts;        // ceil(max_blocks_per_seq / partition_blocks)
+    float scale;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+struct AppendArgs {
+    const void* k;
+    const void* v;
+    const int64_t* slot_mapping;
+    void* k_cache;
+    void* v_cache;
+    int32_t num_tokens;
+    int32_t num_kv_heads;
+    int32_t head_size;
+    int32_t block_size;
+    int32_t num_blocks;
+    int32_t elem_bytes;  // 2 or 4
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+
+hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                               int32_t max_blocks_per_seq, int32_t block_size, int64_t* slot_mapping,
+                               hipStream_t stream);
+
+}  // namespace pkv

@@ -1,0 +1,132 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_35_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, -1, -2, -3
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"PKV_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pkv.LIB_PATH):
+        pytest.fail("libpkv.so is not built (run __graft_entry__.build())")
+    return pkv.library()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("paged_decode_attention", "kv_cache_append", "pkv_decode_slot_mapping",
+              "pkv_decode_workspace_bytes", "pkv_decode_partition_tokens", "pkv_status_string",
+              "pkv_layout_version", "pkv_last_hip_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(pkv.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), f"{name} declared in pkv.h but not exported"
+
+
+def test_status_strings_and_layout(lib):
+    assert lib.pkv_status_string(OK) == b"PKV_OK"
+    assert lib.pkv_status_string(WORKSPACE) == b"PKV_ERR_WORKSPACE"
+    assert lib.pkv_layout_version() == 1
+
+
+def desc(nb=32, hkv=8, B=16, hs=64, dtype=0):
+    return pkv.CacheDesc(nb, hkv, B, hs, dtype)
+
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
+
+
+def attn(lib, *, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, S=4, Hq=8, M=4, d=None, out=FAKE, ws=None,
+         ws_bytes=0, P=0):
+    d = d or desc()
+    return lib.paged_decode_attention(q, kc, vc, bt, sl, S, Hq, M, ctypes.byref(d), 0.125, out, ws, ws_bytes, P,
+                                      None)
+
+
+def test_attention_rejects_bad_arguments(lib):
+    assert attn(lib, q=None) == INVALID
+    assert attn(lib, out=None) == INVALID
+    assert attn(lib, Hq=12) == INVALID                      # Hq % Hkv != 0
+    assert attn(lib, Hq=8 * 32, d=desc(hkv=8)) == UNSUPPORTED  # group of 32 query heads
+    assert attn(lib, d=desc(hs=96)) == UNSUPPORTED
+    assert attn(lib, d=desc(B=8)) == UNSUPPORTED
+    assert attn(lib, d=desc(dtype=7)) == UNSUPPORTED
+    assert attn(lib, d=desc(nb=0)) == INVALID
+    assert attn(lib, M=0) == INVALID
+    assert attn(lib, S=-1) == INVALID
+    assert attn(lib, q=ctypes.c_void_p(0x10008)) == INVALID   # misaligned
+    assert attn(lib, P=24) == INVALID                        # not a multiple of B
+    assert attn(lib, P=16 * 65) == INVALID                   # more than 64 blocks per partition
+    assert attn(lib, M=0x7FFFFFFF) == INVALID                # M * B overflows
+    # a long table needs a workspace
+    assert attn(lib, M=4096) == WORKSPACE
+    need = lib.pkv_decode_workspace_bytes(4, 8, 8, 64, 4096, 16, 0)
+    assert attn(lib, M=4096, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
+    # nothing to do: valid no-op without touching the GPU
+    assert attn(lib, S=0) == OK
+
+
+def test_workspace_and_partition_sizes(lib):
+    # one partition covers a short table: no workspace
+    assert lib.pkv_decode_partition_tokens(4, 8, 8, 64, 4, 16, 0) == 64
+    assert lib.pkv_decode_workspace_bytes(4, 8, 8, 64, 4, 16, 0) == 0
+    # 512-token partitions by default; 128 blocks of 16 -> 4 partitions
+    assert lib.pkv_decode_partition_tokens(64, 32, 32, 128, 128, 16, 0) == 512
+    assert lib.pkv_decode_workspace_bytes(64, 32, 32, 128, 128, 16, 0) == 64 * 32 * 4 * 130 * 4
+    # explicit partition length
+    assert lib.pkv_decode_partition_tokens(8, 64, 8, 128, 4096, 32, 512) == 512
+    assert lib.pkv_decode_workspace_bytes(8, 64, 8, 128, 4096, 32, 512) == 8 * 64 * 256 * 130 * 4
+    assert lib.pkv_decode_partition_tokens(8, 64, 8, 128, 4096, 32, 48) == 0
+
+
+def test_append_rejects_bad_arguments(lib):
+    d = desc()
+    f = lib.kv_cache_append
+    assert f(FAKE, FAKE, FAKE, 4, None, FAKE, FAKE, None) == INVALID
+    assert f(None, FAKE, FAKE, 4, ctypes.byref(d), FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, None, 4, ctypes.byref(d), FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, -1, ctypes.byref(d), FAKE, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, 4, ctypes.byref(d), None, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, 4, ctypes.byref(desc(hs=80)), FAKE, FAKE, None) == UNSUPPORTED
+    assert f(ctypes.c_void_p(0x10004), FAKE, FAKE, 4, ctypes.byref(d), FAKE, FAKE, None) == INVALID
+    assert f(None, None, None, 0, ctypes.byref(d), FAKE, FAKE, None) == OK
+
+
+def test_slot_mapping_rejects_bad_arguments(lib):
+    f = lib.pkv_decode_slot_mapping
+    assert f(None, FAKE, 4, 4, 16, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, 4, 0, 16, FAKE, None) == INVALID
+    assert f(FAKE, FAKE, 4, 4, 0, FAKE, None) == INVALID
+    assert f(None, None, 0, 4, 16, None, None) == OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    q = torch.zeros(2, 4, 64)
+    kc = torch.zeros(8, 4, 16, 16, 4)
+    vc = torch.zeros(8, 4, 64, 16)
+    bt = torch.zeros(2, 2, dtype=torch.int32)
+    sl = torch.ones(2, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        pkv.paged_decode_attention(q, kc, vc, bt, sl, 0.125, out=torch.zeros_like(q), workspace=None)
+    with pytest.raises(ValueError):
+        pkv.cache_desc(kc, vc[:, :, :32])
