@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--partition-tokens", type=int, default=None,
                     help="context partition length (default: the configuration's, else the library's choice)")
+    ap.add_argument("--contiguous", action="store_true",
+                    help="diagnostic: each sequence's blocks adjacent in the pool (paged vs contiguous storage)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--traffic", type=str, default=None,
@@ -120,7 +122,7 @@ def main() -> int:
     pkv.library()
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
-    w = pi.make_workload(args.config, mode="timing")
+    w = pi.make_workload(args.config, mode="timing", contiguous=args.contiguous)
     log(f"generated config {args.config} ({w.description}) in {time.perf_counter() - t0:.1f} s")
     P = w.partition_tokens if args.partition_tokens is None else args.partition_tokens
     d = device_inputs(w, torch)
@@ -197,7 +199,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32" if w.dtype == "f32" else "bf16",
         "data": "synthetic (seeded N(0,1) q/K/V, shuffled block IDs; no dataset)",
-        "config": {"workload": w.description, "config": args.config, "seed": w.seed, "num_seqs": w.S,
+        "config": {"workload": w.description + (" [contiguous block order]" if args.contiguous else ""),
+                   "config": args.config, "seed": w.seed, "num_seqs": w.S,
                    "q_heads": w.Hq, "kv_heads": w.Hkv, "head_size": w.hs, "block_size": w.B,
                    "pool_blocks": w.num_blocks, "sum_seq_len": int(w.seq_lens.sum()),
                    "partition_tokens": P_used, "kv_bytes_per_step": kv_bytes},

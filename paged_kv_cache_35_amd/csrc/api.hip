@@ -133,11 +133,13 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
                                                   max_blocks_per_seq, block_size, partition_tokens);
     if (P <= 0)
         return 0;
-    const int64_t pb = P / block_size;
-    const int64_t parts = (max_blocks_per_seq + pb - 1) / pb;
-    if (parts <= 1)
+    // one fp32 partial (o[hs], m, l) per (sequence, query head, chunk of
+    // kDecodeWaves partitions); none when one chunk covers the table
+    const int64_t cb = (int64_t)(P / block_size) * pkv::kDecodeWaves;
+    const int64_t chunks = (max_blocks_per_seq + cb - 1) / cb;
+    if (chunks <= 1)
         return 0;
-    return (size_t)num_seqs * num_q_heads * parts * ((size_t)head_size + 2) * sizeof(float);
+    return (size_t)num_seqs * num_q_heads * chunks * ((size_t)head_size + 2) * sizeof(float);
 }
 
 pkv_status paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
@@ -169,7 +171,7 @@ pkv_status paged_decode_attention(const void* q, const void* k_cache, const void
     if (P <= 0)
         return PKV_ERR_INVALID_ARG;
     const int32_t pb = P / cache->block_size;
-    const int32_t parts = (max_blocks_per_seq + pb - 1) / pb;
+    const int32_t parts = (max_blocks_per_seq + pb * pkv::kDecodeWaves - 1) / (pb * pkv::kDecodeWaves);
     if (num_seqs > 65535 || parts > 65535)
         return PKV_ERR_UNSUPPORTED;
     const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, Hkv, cache->head_size,

@@ -36,6 +36,8 @@
 //    zeroed by selection, so stale or NaN pool contents never reach a sum.
 #include <math.h>
 
+#include <type_traits>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -43,6 +45,7 @@ namespace pkv {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: probabilities stay <= 256
@@ -86,43 +89,99 @@ struct Ops<float> {
     };
 };
 
-template <typename T, int HS, int BS>
+// Operand registers of one 16-token sub-tile (a block of B = 32 holds two).
+template <typename T, int HS>
 struct TileRegs {
-    static constexpr int MT = BS / 16;
-    typename Ops<T>::template KReg<HS> k[MT];
-    typename Ops<T>::template VReg<HS> v[MT];
+    typename Ops<T>::template KReg<HS> k;
+    typename Ops<T>::template VReg<HS> v;
 };
+
+// bf16 blocks of 32 tokens are handled as one 32-token unit: two key
+// M-tiles and a value operand of 8 tokens per lane (v_mfma_f32_16x16x32_bf16
+// with the tokens as the reduction dimension).  Each value load then covers
+// a whole 64-byte [hs][32] row segment: 1 KiB contiguous per wave load.
+template <int HS>
+struct WideRegs {
+    Ops<__bf16>::KReg<HS> k[2];
+    bf16x8 v[HS / 16];
+};
+
+// Key row c of M-tile mp of a 32-token unit holds token
+// 8*(c/4) + 4*mp + c%4, so that the score layout of the two M-tiles gives
+// lane group r the tokens 8r .. 8r+7 (the value MFMA's reduction order).
+__device__ __forceinline__ int wide_token(int mp, int c) { return 8 * (c >> 2) + 4 * mp + (c & 3); }
 
 __device__ __forceinline__ float to_float(__bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_float(float x) { return x; }
 __device__ __forceinline__ void store_elem(__bf16* p, float x) { *p = (__bf16)x; }
 __device__ __forceinline__ void store_elem(float* p, float x) { *p = x; }
 
-// Issue the loads of one (block, KV head) tile.  `tile_k`/`tile_v` point at
-// the tile's first element; lane = 16*r + c.
+// K/V tiles are read exactly once per call: streaming (non-temporal) loads
+// keep them from displacing reusable lines (queries, tables, partials).
+#ifndef PKV_STREAMING_LOADS
+#define PKV_STREAMING_LOADS 1
+#endif
+
+#ifndef PKV_STREAMING_V
+#define PKV_STREAMING_V PKV_STREAMING_LOADS
+#endif
+
+template <typename V>
+__device__ __forceinline__ V load_stream(const V* p)
+{
+#if PKV_STREAMING_LOADS
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+template <typename V>
+__device__ __forceinline__ V load_stream_v(const V* p)
+{
+#if PKV_STREAMING_V
+    return __builtin_nontemporal_load(p);
+#else
+    return *p;
+#endif
+}
+
+// Issue the loads of 16-token sub-tile m of one (block, KV head) tile.
+// `tile_k`/`tile_v` point at the tile's first element; lane = 16*r + c.
 template <typename T, int HS, int BS>
-__device__ __forceinline__ void load_tile(TileRegs<T, HS, BS>& t, const T* __restrict__ tile_k,
-                                          const T* __restrict__ tile_v, int r, int c)
+__device__ __forceinline__ void load_tile(TileRegs<T, HS>& t, const T* __restrict__ tile_k,
+                                          const T* __restrict__ tile_v, int m, int r, int c)
+{
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < HS / 32; ++i)  // chunk 4i + r of token 16m + c
+            t.k.v[i] = load_stream((const bf16x8*)(tile_k + ((4 * i + r) * BS + 16 * m + c) * 8));
+    } else {
+#pragma unroll
+        for (int i = 0; i < HS / 16; ++i)
+            t.k.v[i] = load_stream((const f32x4*)(tile_k + ((4 * i + r) * BS + 16 * m + c) * 4));
+    }
+#pragma unroll
+    for (int i = 0; i < HS / 16; ++i) {  // head dim 16i + c, tokens 16m + 4r .. +3
+        if constexpr (sizeof(T) == 2)
+            t.v.v[i] = load_stream_v((const bf16x4*)(tile_v + (16 * i + c) * BS + 16 * m + 4 * r));
+        else
+            t.v.v[i] = load_stream_v((const f32x4*)(tile_v + (16 * i + c) * BS + 16 * m + 4 * r));
+    }
+}
+
+template <int HS>
+__device__ __forceinline__ void load_wide(WideRegs<HS>& t, const __bf16* __restrict__ tile_k,
+                                          const __bf16* __restrict__ tile_v, int r, int c)
 {
 #pragma unroll
-    for (int mt = 0; mt < BS / 16; ++mt) {
-        if constexpr (sizeof(T) == 2) {
+    for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
-            for (int i = 0; i < HS / 32; ++i)  // chunk 4i + r of token 16mt + c
-                t.k[mt].v[i] = *(const bf16x8*)(tile_k + ((4 * i + r) * BS + 16 * mt + c) * 8);
-        } else {
+        for (int i = 0; i < HS / 32; ++i)
+            t.k[mp].v[i] = load_stream((const bf16x8*)(tile_k + ((4 * i + r) * 32 + wide_token(mp, c)) * 8));
 #pragma unroll
-            for (int i = 0; i < HS / 16; ++i)
-                t.k[mt].v[i] = *(const f32x4*)(tile_k + ((4 * i + r) * BS + 16 * mt + c) * 4);
-        }
-#pragma unroll
-        for (int i = 0; i < HS / 16; ++i) {  // head dim 16i + c, tokens 16mt + 4r .. +3
-            if constexpr (sizeof(T) == 2)
-                t.v[mt].v[i] = *(const bf16x4*)(tile_v + (16 * i + c) * BS + 16 * mt + 4 * r);
-            else
-                t.v[mt].v[i] = *(const f32x4*)(tile_v + (16 * i + c) * BS + 16 * mt + 4 * r);
-        }
-    }
+    for (int i = 0; i < HS / 16; ++i)  // head dim 16i + c, tokens 8r .. 8r+7
+        t.v[i] = load_stream((const bf16x8*)(tile_v + (16 * i + c) * 32 + 8 * r));
 }
 
 // Scores S^T for one 16-token sub-tile: element j of the result is token
@@ -174,34 +233,44 @@ __device__ __forceinline__ void tile_pv(f32x4 (&O)[HS / 16], const float (&p)[4]
     }
 }
 
-template <typename T, int HS, int BS>
-__device__ __forceinline__ void zero_masked_values(TileRegs<T, HS, BS>& t, int tok0, int L, int r)
+// Zero the value operand of tokens at or beyond L (tok0 = the sub-tile's
+// first token), so stale or NaN slots never enter the value sum.
+template <typename T, int HS>
+__device__ __forceinline__ void zero_masked_values(TileRegs<T, HS>& t, int tok0, int L, int r)
 {
 #pragma unroll
-    for (int mt = 0; mt < BS / 16; ++mt)
+    for (int j = 0; j < 4; ++j) {
+        const bool keep = tok0 + 4 * r + j < L;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const bool keep = tok0 + 16 * mt + 4 * r + j < L;
-#pragma unroll
-            for (int i = 0; i < HS / 16; ++i)
-                t.v[mt].v[i][j] = keep ? t.v[mt].v[i][j] : (T)0.f;
-        }
+        for (int i = 0; i < HS / 16; ++i)
+            t.v.v[i][j] = keep ? t.v.v[i][j] : (T)0.f;
+    }
 }
 
+// At least two waves per SIMD: keeps the register allocation (including
+// the MFMA accumulators) within 256 VGPRs so two pipelined waves share a SIMD.
+#ifndef PKV_DECODE_WAVES_PER_EU
+#define PKV_DECODE_WAVES_PER_EU 2
+#endif
+#define PKV_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU)))
+
 template <typename T, int HS, int BS, int NW>
-__global__ __launch_bounds__(NW * 64) void paged_decode_partition_kernel(
+__global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_kernel(
     const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int32_t Hq, int32_t Hkv,
     int32_t M, int32_t num_blocks, int32_t PB, int32_t max_parts, float qscale, T* __restrict__ out,
     float* __restrict__ ws_o, float* __restrict__ ws_ml)
 {
-    constexpr int MT = BS / 16;
-    constexpr int TILE = HS * BS;  // elements per (block, KV head) tile
+    constexpr bool kWide = sizeof(T) == 2 && BS == 32;  // 32-token units (see WideRegs)
+    constexpr int UT = kWide ? 32 : 16;                 // tokens per pipeline unit
+    constexpr int PER = BS / UT;                        // units per block
+    constexpr int TILE = HS * BS;                       // elements per (block, KV head) tile
     const int kvh = blockIdx.x;
     const int s = blockIdx.y;
-    const int part = blockIdx.z;
     const int lane = threadIdx.x & 63;
-    const int w = threadIdx.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, kept scalar
+    const int chunk = blockIdx.z;                                      // NW consecutive partitions
+    const int part = chunk * NW + w;                                   // this wave's partition
     const int r = lane >> 4;
     const int c = lane & 15;
     const int G = Hq / Hkv;
@@ -209,19 +278,22 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_partition_kernel(
     int L = seq_lens[s];
     L = L < 0 ? 0 : (L > M * BS ? M * BS : L);
     if (L == 0) {
-        if (part == 0)
-            for (int idx = threadIdx.x; idx < G * HS; idx += NW * 64)
+        if (chunk == 0 && w == 0)
+            for (int idx = lane; idx < G * HS; idx += 64)
                 store_elem(out + ((int64_t)s * Hq + (int64_t)kvh * G) * HS + idx, 0.f);
         return;
     }
     const int nblk = (L + BS - 1) / BS;
+    if (chunk * NW * PB >= nblk)
+        return;  // the whole work-group is past the end (uniform: before any barrier)
+    const int nchunks = (nblk + NW * PB - 1) / (NW * PB);
     const int b0 = part * PB;
-    if (b0 >= nblk)
-        return;
-    const int nb_part = (nblk - b0 < PB) ? nblk - b0 : PB;
-    const int nparts = (nblk + PB - 1) / PB;
+    // a wave whose partition is past the end has no tiles but still joins
+    // the work-group merge below
+    const int nb_part = b0 >= nblk ? 0 : ((nblk - b0 < PB) ? nblk - b0 : PB);
 
-    // physical block IDs of this partition, one per lane (PB <= 64)
+    // physical block IDs of this partition, one per lane (PB <= 64); the
+    // tile loop broadcasts them with readlane
     const int32_t id_lane = lane < nb_part ? block_tables[(int64_t)s * M + b0 + lane] : 0;
 
     // query operand: head c of this KV head's group (zero for padding rows)
@@ -248,7 +320,9 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_partition_kernel(
 #pragma unroll
     for (int i = 0; i < HS / 16; ++i)
         O[i] = (f32x4)0.f;
-    float m_run = -INFINITY;  // running max for head c, log2 units
+    // running max for head c, log2 units; finite start so that a fully
+    // masked tile gives exp2(-inf - m_run) = 0 rather than NaN
+    float m_run = -1e30f;
     float l_part = 0.f;       // sum of probabilities of this lane's tokens
 
     const int64_t head_off = (int64_t)kvh * TILE;
@@ -263,27 +337,10 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_partition_kernel(
         return ok;
     };
 
-    auto compute = [&](TileRegs<T, HS, BS>& t, int j, bool ok) {
-        if (!ok)
-            return;  // out-of-range block ID: the tile contributes nothing
-        const int tok0 = (b0 + j) * BS;
-        const bool partial = tok0 + BS > L;
-        float sc[MT][4];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const f32x4 S = tile_scores<T, HS>(t.k[mt], qr);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                float v = S[jj] * qscale;
-                if (partial)
-                    v = (tok0 + 16 * mt + 4 * r + jj < L) ? v : -INFINITY;
-                sc[mt][jj] = v;
-                mx = fmaxf(mx, v);
-            }
-        }
-        if (partial)
-            zero_masked_values<T, HS, BS>(t, tok0, L, r);
+    // Online-softmax update shared by both unit shapes: mx is this lane's
+    // maximum over its valid scores (log2 units).  Raises the running maximum
+    // only when mx exceeds it by more than kRescaleSlack.
+    auto update_max = [&](float mx) {
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         if (__ballot(mx > m_run + kRescaleSlack) != 0) {
@@ -301,51 +358,140 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_partition_kernel(
                 for (int jj = 0; jj < 4; ++jj)
                     O[i][jj] *= a_row[jj];
         }
+    };
+
+    // One 16-token sub-tile: scores, online softmax update, value sum.
+    // tok0 is the sub-tile's first token; an out-of-range block ID was
+    // replaced by block 0 and its tokens are all masked (valid below Lt), so
+    // the loaded registers are consumed on every path.
+    auto compute = [&](TileRegs<T, HS>& t, int tok0, bool ok) {
+        const int Lt = ok ? L : tok0;
+        const bool partial = tok0 + 16 > Lt;
+        const f32x4 S = tile_scores<T, HS>(t.k, qr);
+        float sc[4];
+        float mx = -INFINITY;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            float p[4];
+        for (int jj = 0; jj < 4; ++jj) {
+            float v = S[jj] * qscale;
+            if (partial)
+                v = (tok0 + 4 * r + jj < Lt) ? v : -INFINITY;
+            sc[jj] = v;
+            mx = fmaxf(mx, v);
+        }
+        if (partial)
+            zero_masked_values<T, HS>(t, tok0, Lt, r);
+        update_max(mx);
+        float p[4];
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                p[jj] = __builtin_amdgcn_exp2f(sc[mt][jj] - m_run);
-                l_part += p[jj];
+        for (int jj = 0; jj < 4; ++jj) {
+            p[jj] = __builtin_amdgcn_exp2f(sc[jj] - m_run);
+            l_part += p[jj];
+        }
+        tile_pv<T, HS>(O, p, t.v);
+    };
+
+    // One 32-token unit (bf16, B = 32): element jj of M-tile mp's scores is
+    // token 8r + 4mp + jj; value element e of a lane is token 8r + e.
+    auto compute_wide = [&](WideRegs<HS>& t, int tok0, bool ok) {
+        if constexpr (kWide) {
+            const int Lt = ok ? L : tok0;
+            const bool partial = tok0 + 32 > Lt;
+            float sc[8];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mp = 0; mp < 2; ++mp) {
+                const f32x4 S = tile_scores<__bf16, HS>(t.k[mp], qr);
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    float v = S[jj] * qscale;
+                    if (partial)
+                        v = (tok0 + 8 * r + 4 * mp + jj < Lt) ? v : -INFINITY;
+                    sc[4 * mp + jj] = v;
+                    mx = fmaxf(mx, v);
+                }
             }
-            tile_pv<T, HS>(O, p, t.v[mt]);
+            if (partial) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const bool keep = tok0 + 8 * r + e < Lt;
+#pragma unroll
+                    for (int i = 0; i < HS / 16; ++i)
+                        t.v[i][e] = keep ? t.v[i][e] : (__bf16)0.f;
+                }
+            }
+            update_max(mx);
+            bf16x8 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float pe = __builtin_amdgcn_exp2f(sc[e] - m_run);
+                l_part += pe;
+                const __bf16 hb = (__bf16)pe;
+                hi[e] = hb;
+                lo[e] = (__bf16)(pe - (float)hb);
+            }
+#pragma unroll
+            for (int i = 0; i < HS / 16; ++i) {
+                O[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, t.v[i], O[i], 0, 0, 0);
+                O[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, t.v[i], O[i], 0, 0, 0);
+            }
         }
     };
 
-    // software pipeline: the next tile's loads are in flight while the
-    // current tile is computed
-    TileRegs<T, HS, BS> ta, tb;
-    const T* tk;
-    const T* tv;
-    int j = w;
-    bool ok_a = false, ok_b = false;
-    if (j < nb_part) {
-        ok_a = tile_ptr_ok(j, tk, tv);
-        load_tile<T, HS, BS>(ta, tk, tv, r, c);
-    }
-    while (j < nb_part) {
-        if (j + NW < nb_part) {
-            ok_b = tile_ptr_ok(j + NW, tk, tv);
-            load_tile<T, HS, BS>(tb, tk, tv, r, c);
+    // Software pipeline over the partition's units (UT tokens each): unit u
+    // is part m = u % PER of block j = u / PER.  The next unit's
+    // loads are in flight while the current one is computed.  The
+    // steady-state loop always prefetches and the last one or two units are
+    // peeled, so every compute is preceded by exactly one batch of loads and
+    // the memory-counter waits stay precise.
+    using Regs = typename std::conditional<kWide, WideRegs<HS>, TileRegs<T, HS>>::type;
+    const int nunits = nb_part * PER;  // 0 for a wave past the end
+    auto issue = [&](Regs& t, int u) -> bool {
+        const int j = u / PER;
+        const T* tk;
+        const T* tv;
+        const bool ok = tile_ptr_ok(j, tk, tv);
+        if constexpr (kWide)
+            load_wide<HS>(t, tk, tv, r, c);
+        else
+            load_tile<T, HS, BS>(t, tk, tv, u % PER, r, c);
+        return ok;
+    };
+    auto first_token = [&](int u) { return (b0 + u / PER) * BS + UT * (u % PER); };
+    auto run = [&](Regs& t, int u, bool ok) {
+        if constexpr (kWide)
+            compute_wide(t, first_token(u), ok);
+        else
+            compute(t, first_token(u), ok);
+    };
+    if (nunits > 0) {
+        Regs ta, tb;
+        bool ok_a = issue(ta, 0);
+        bool ok_b = false;
+        int u = 0;
+        for (; u + 2 < nunits; u += 2) {
+            ok_b = issue(tb, u + 1);
+            run(ta, u, ok_a);
+            ok_a = issue(ta, u + 2);
+            run(tb, u + 1, ok_b);
         }
-        compute(ta, j, ok_a);
-        j += NW;
-        if (j >= nb_part)
-            break;
-        if (j + NW < nb_part) {
-            ok_a = tile_ptr_ok(j + NW, tk, tv);
-            load_tile<T, HS, BS>(ta, tk, tv, r, c);
+        if (u + 1 < nunits) {
+            ok_b = issue(tb, u + 1);
+            run(ta, u, ok_a);
+            run(tb, u + 1, ok_b);
+        } else {
+            run(ta, u, ok_a);
         }
-        compute(tb, j, ok_b);
-        j += NW;
     }
 
-    // ---- merge the waves' partial states (log-sum-exp) ----
+    // ---- merge the work-group's partitions (log-sum-exp) ----
+    // Each wave stages its partition's normalised G x HS result and the (m, l)
+    // of each head in LDS; the work-group then combines them with weights
+    // l_w * 2^(m_w - M) and writes one block per (sequence, KV head, chunk):
+    // the final output when the sequence has a single chunk, otherwise a
+    // partial for the chunk merge kernel.
     float l_tot = l_part + __shfl_xor(l_part, 16);
     l_tot += __shfl_xor(l_tot, 32);
-
-    __shared__ float sm_o[NW][16][HS];
+    __shared__ __attribute__((aligned(16))) float sm_out[NW][16 * HS];
     __shared__ float sm_m[NW][16];
     __shared__ float sm_l[NW][16];
     if (r == 0) {
@@ -353,38 +499,56 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_partition_kernel(
         sm_l[w][c] = l_tot;
     }
 #pragma unroll
-    for (int i = 0; i < HS / 16; ++i)
+    for (int jj = 0; jj < 4; ++jj) {
+        const int g = 4 * r + jj;
+        const float l_g = __shfl(l_tot, g);
+        const float inv = l_g > 0.f ? 1.f / l_g : 0.f;
+        if (g < G) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-            sm_o[w][4 * r + jj][16 * i + c] = O[i][jj];
+            for (int i = 0; i < HS / 16; ++i)
+                sm_out[w][g * HS + 16 * i + c] = O[i][jj] * inv;
+        }
+    }
     __syncthreads();
 
-    for (int idx = threadIdx.x; idx < G * HS; idx += NW * 64) {
-        const int g = idx / HS;
-        const int d = idx - g * HS;
+    const int64_t hbase = (int64_t)s * Hq + (int64_t)kvh * G;
+    const int64_t blk = ((int64_t)s * Hkv + kvh) * max_parts + chunk;
+    for (int e = threadIdx.x; e < G * HS / 4; e += NW * 64) {  // 4 consecutive elements of head g
+        const int g = (4 * e) / HS;
         float mx = -INFINITY;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww)
             if (sm_l[ww][g] > 0.f)
                 mx = fmaxf(mx, sm_m[ww][g]);
-        float lsum = 0.f, acc = 0.f;
+        float lsum = 0.f;
+        f32x4 acc = (f32x4)0.f;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww)
             if (sm_l[ww][g] > 0.f) {
-                const float f = __builtin_amdgcn_exp2f(sm_m[ww][g] - mx);
-                lsum += sm_l[ww][g] * f;
-                acc += sm_o[ww][g][d] * f;
+                const float f = sm_l[ww][g] * __builtin_amdgcn_exp2f(sm_m[ww][g] - mx);
+                lsum += f;
+                acc += f * *(const f32x4*)(&sm_out[ww][4 * e]);
             }
-        const float o = lsum > 0.f ? acc / lsum : 0.f;
-        const int64_t hrow = (int64_t)s * Hq + (int64_t)kvh * G + g;
-        if (nparts == 1) {
-            store_elem(out + hrow * HS + d, o);
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        acc *= inv;
+        if (nchunks == 1) {
+            T* dst = out + hbase * HS + 4 * e;  // the group's G heads are adjacent rows of out
+            if constexpr (sizeof(T) == 2) {
+                bf16x4 v;
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    v[k] = (__bf16)acc[k];
+                *(bf16x4*)dst = v;
+            } else {
+                *(f32x4*)dst = acc;
+            }
         } else {
-            const int64_t u = hrow * max_parts + part;
-            ws_o[u * HS + d] = o;
-            if (d == 0) {
-                ws_ml[2 * u] = mx;
-                ws_ml[2 * u + 1] = lsum;
+            *(f32x4*)(ws_o + blk * G * HS + 4 * e) = acc;
+            if ((4 * e) % HS == 0) {
+                float2 ml;
+                ml.x = mx;
+                ml.y = lsum;
+                *(float2*)(ws_ml + (blk * G + g) * 2) = ml;
             }
         }
     }
@@ -392,48 +556,120 @@ __global__ __launch_bounds__(NW * 64) void paged_decode_partition_kernel(
 
 // Merge of the context partitions of one (sequence, query head):
 // M = max m_p, w_p = l_p * 2^(m_p - M), out = sum w_p o_p / sum w_p
-// (o_p is already normalised by l_p).  Sequences with one partition were
+// (o_p is already normalised by l_p; partitions whose tiles were all masked
+// carry l_p = 0 and get weight 0).  Sequences with one partition were
 // written by the partition kernel and are skipped here.
-template <typename T, int HS>
-__global__ __launch_bounds__(64) void paged_decode_reduce_kernel(const int32_t* __restrict__ seq_lens, int32_t M,
-                                                                 int32_t BS, int32_t PB, int32_t Hq,
-                                                                 int32_t max_parts, const float* __restrict__ ws_o,
-                                                                 const float* __restrict__ ws_ml,
-                                                                 T* __restrict__ out)
+//
+// A long context has hundreds of partitions per head, so the work is spread
+// over the work-group: the weights are computed once per partition into LDS
+// (in chunks of kMergeChunk partitions), and each thread then accumulates
+// one head dim over a strided subset of partitions with a batch of
+// independent loads in flight; the subsets are combined through LDS.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeChunk = 2048;
+
+__device__ __forceinline__ float block_reduce_max(float v, float* red)
 {
+    for (int o = 32; o > 0; o >>= 1)
+        v = fmaxf(v, __shfl_xor(v, o));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int i = 1; i < kMergeThreads / 64; ++i)
+        r = fmaxf(r, red[i]);
+    return r;
+}
+
+__device__ __forceinline__ float block_reduce_sum(float v, float* red)
+{
+    for (int o = 32; o > 0; o >>= 1)
+        v += __shfl_xor(v, o);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0)
+        red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = red[0];
+    for (int i = 1; i < kMergeThreads / 64; ++i)
+        r += red[i];
+    return r;
+}
+
+template <typename T, int HS>
+__global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
+    const int32_t* __restrict__ seq_lens, int32_t M, int32_t BS, int32_t CB, int32_t Hq, int32_t Hkv,
+    int32_t max_parts, const float* __restrict__ ws_o, const float* __restrict__ ws_ml, T* __restrict__ out)
+{
+    constexpr int R = kMergeThreads / HS;  // partition groups
+    __shared__ float sm_w[kMergeChunk];
+    __shared__ float sm_red[kMergeThreads / 64];
+    __shared__ float sm_acc[R][HS];
     const int h = blockIdx.x;
     const int s = blockIdx.y;
     int L = seq_lens[s];
     L = L < 0 ? 0 : (L > M * BS ? M * BS : L);
     const int nblk = (L + BS - 1) / BS;
-    const int nparts = (nblk + PB - 1) / PB;
+    const int nparts = (nblk + CB - 1) / CB;  // chunks of CB blocks
     if (nparts <= 1)
         return;
-    const int64_t u0 = ((int64_t)s * Hq + h) * max_parts;
+    // chunk p of head h = kvh * G + g: row g of block (s, kvh, p)
+    const int G = Hq / Hkv;
+    const int kvh = h / G;
+    const int g = h - kvh * G;
+    const int64_t u0 = ((int64_t)s * Hkv + kvh) * max_parts;
+    auto row = [&](int p) { return (u0 + p) * G + g; };
+
     float mx = -INFINITY;
-    for (int p = 0; p < nparts; ++p)
-        mx = fmaxf(mx, ws_ml[2 * (u0 + p)]);
-    float wsum = 0.f;
-    float acc[HS / 64];
+    for (int p = threadIdx.x; p < nparts; p += kMergeThreads)
+        if (ws_ml[2 * row(p) + 1] > 0.f)
+            mx = fmaxf(mx, ws_ml[2 * row(p)]);
+    mx = block_reduce_max(mx, sm_red);
+
+    const int d = threadIdx.x % HS;
+    const int grp = threadIdx.x / HS;
+    float acc = 0.f, wpart = 0.f;
+    for (int c0 = 0; c0 < nparts; c0 += kMergeChunk) {
+        const int cn = nparts - c0 < kMergeChunk ? nparts - c0 : kMergeChunk;
+        __syncthreads();  // previous chunk's weights fully consumed
+        for (int i = threadIdx.x; i < cn; i += kMergeThreads) {
+            const float l = ws_ml[2 * row(c0 + i) + 1];
+            const float wgt = l > 0.f ? l * __builtin_amdgcn_exp2f(ws_ml[2 * row(c0 + i)] - mx) : 0.f;
+            sm_w[i] = wgt;
+            wpart += wgt;
+        }
+        __syncthreads();
+        const float* base = ws_o + row(c0) * HS + d;
+        const int64_t pstride = (int64_t)G * HS;  // between consecutive partitions
+        int i = grp;
+        for (; i + 7 * R < cn; i += 8 * R) {
+            float v[8];
 #pragma unroll
-    for (int i = 0; i < HS / 64; ++i)
-        acc[i] = 0.f;
-    for (int p = 0; p < nparts; ++p) {
-        const float f = ws_ml[2 * (u0 + p) + 1] * __builtin_amdgcn_exp2f(ws_ml[2 * (u0 + p)] - mx);
-        wsum += f;
+            for (int k = 0; k < 8; ++k)
+                v[k] = base[(int64_t)(i + k * R) * pstride];
 #pragma unroll
-        for (int i = 0; i < HS / 64; ++i)
-            acc[i] += f * ws_o[(u0 + p) * HS + threadIdx.x + 64 * i];
+            for (int k = 0; k < 8; ++k)
+                acc += sm_w[i + k * R] * v[k];
+        }
+        for (; i < cn; i += R)
+            acc += sm_w[i] * base[(int64_t)i * pstride];
     }
+    const float wsum = block_reduce_sum(wpart, sm_red);
+    sm_acc[grp][d] = acc;
+    __syncthreads();
+    if (threadIdx.x < HS) {
+        float tot = 0.f;
 #pragma unroll
-    for (int i = 0; i < HS / 64; ++i)
-        store_elem(out + ((int64_t)s * Hq + h) * HS + threadIdx.x + 64 * i, acc[i] / wsum);
+        for (int g = 0; g < R; ++g)
+            tot += sm_acc[g][threadIdx.x];
+        store_elem(out + ((int64_t)s * Hq + h) * HS + threadIdx.x, wsum > 0.f ? tot / wsum : 0.f);
+    }
 }
 
 template <typename T, int HS, int BS>
 static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
 {
-    constexpr int NW = 4;
+    constexpr int NW = kDecodeWaves;
     const dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
     hipLaunchKernelGGL((paged_decode_partition_kernel<T, HS, BS, NW>), grid, dim3(NW * 64), 0, stream,
                        (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache, a.block_tables, a.seq_lens,
@@ -441,10 +677,11 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
                        a.max_parts, a.scale * kLog2e, (T*)a.out, a.ws_o, a.ws_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_parts <= 1)
-        return e;
-    hipLaunchKernelGGL((paged_decode_reduce_kernel<T, HS>), dim3(a.num_q_heads, a.num_seqs), dim3(64), 0, stream,
-                       a.seq_lens, a.max_blocks_per_seq, BS, a.partition_blocks, a.num_q_heads, a.max_parts,
-                       a.ws_o, a.ws_ml, (T*)a.out);
+        return e;  // one chunk per sequence: the partition kernel wrote the output
+    hipLaunchKernelGGL((paged_decode_reduce_kernel<T, HS>), dim3(a.num_q_heads, a.num_seqs), dim3(kMergeThreads), 0,
+                       stream,
+                       a.seq_lens, a.max_blocks_per_seq, BS, a.partition_blocks * NW, a.num_q_heads,
+                       a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, (T*)a.out);
     return hipGetLastError();
 }
 

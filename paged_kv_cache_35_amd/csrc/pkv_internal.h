@@ -8,6 +8,14 @@
 
 namespace pkv {
 
+// Waves per work-group of the partition kernel: each wave attends over one
+// context partition and the work-group merges its NW partitions, so one
+// work-group covers a chunk of NW partitions (compile-time tuning knob).
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 4
+#endif
+constexpr int kDecodeWaves = PKV_DECODE_WAVES;
+
 // Problem description shared by the decode launchers; every field has been
 // validated on the host before a launcher sees it.
 struct DecodeArgs {
@@ -17,8 +25,8 @@ struct DecodeArgs {
     const int32_t* block_tables;
     const int32_t* seq_lens;
     void* out;
-    float* ws_o;    // [S][Hq][max_parts][hs] fp32, or null when max_parts == 1
-    float* ws_ml;   // [S][Hq][max_parts][2]  fp32 (running max in log2 units, sum)
+    float* ws_o;    // [S][Hkv][max_parts][G][hs] fp32 chunk partials, null when max_parts == 1
+    float* ws_ml;   // [S][Hkv][max_parts][G][2]  fp32 (running max in log2 units, sum)
     int32_t num_seqs;
     int32_t num_q_heads;
     int32_t num_kv_heads;
@@ -27,8 +35,8 @@ struct DecodeArgs {
     int32_t max_blocks_per_seq;
     int32_t num_blocks;
     int32_t dtype;            // pkv_dtype
-    int32_t partition_blocks; // blocks per context partition (<= 64)
-    int32_t max_parts;        // ceil(max_blocks_per_seq / partition_blocks)
+    int32_t partition_blocks; // blocks per context partition (<= 64), one wave each
+    int32_t max_parts;        // chunks per sequence: ceil(max_blocks_per_seq / (partition_blocks * kDecodeWaves))
     float scale;
 };
 

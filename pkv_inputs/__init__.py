@@ -272,7 +272,7 @@ def make_workload(config: int, mode: str = "parity", *, S: Optional[int] = None,
                   seed: Optional[int] = None, seq_lens: Optional[list] = None,
                   dtype: Optional[str] = None, hs: Optional[int] = None,
                   B: Optional[int] = None, Hq: Optional[int] = None,
-                  Hkv: Optional[int] = None) -> Workload:
+                  Hkv: Optional[int] = None, contiguous: bool = False) -> Workload:
     """Build one decode step's inputs.
 
     mode "parity": slots and blocks that hold no data are NaN (they must never
@@ -301,13 +301,23 @@ def make_workload(config: int, mode: str = "parity", *, S: Optional[int] = None,
 
     # ---- physical block assignment (allocator fixture) ----
     pg = _rng(seed, STREAM_PERM)
-    if config == 1 and seq_lens is None and S == 4:
+    if contiguous:
+        nb_c = {2: 8192}.get(config, 0) if (S == _CFG[config]["S"] and len_hi is None and seq_lens is None) else 0
+        need = sum(nblk) if config != 5 else None
+        if config == 5:
+            prompt = len_hi or 2048
+            shared_n = prompt // Bsz
+            tails = [n - shared_n for n in nblk]
+            need = shared_n + sum(tails)
+        nb = max(nb_c, need if config != 3 else int(math.ceil(1.1 * need)))
+        order = np.arange(nb)
+    elif config == 1 and seq_lens is None and S == 4:
         nb = 32
         rest = np.array([b for b in range(nb) if b not in (7, 3, 12)], dtype=np.int64)
         rest = pg.permutation(rest)
         order = np.concatenate([np.array([7, 3, 12]), rest])
         need = sum(nblk)
-    elif config == 5:
+    elif config == 5 and not contiguous:
         prompt = len_hi or 2048
         if prompt % Bsz:
             raise ValueError("shared prompt must fill whole blocks")

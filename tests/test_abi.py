@@ -88,12 +88,14 @@ def test_workspace_and_partition_sizes(lib):
     # one partition covers a short table: no workspace
     assert lib.pkv_decode_partition_tokens(4, 8, 8, 64, 4, 16, 0) == 64
     assert lib.pkv_decode_workspace_bytes(4, 8, 8, 64, 4, 16, 0) == 0
-    # 512-token partitions by default; 128 blocks of 16 -> 4 partitions
+    # 512-token partitions by default, merged in chunks of 4 per work-group:
+    # 128 blocks of 16 -> 4 partitions -> one chunk, no workspace
     assert lib.pkv_decode_partition_tokens(64, 32, 32, 128, 128, 16, 0) == 512
-    assert lib.pkv_decode_workspace_bytes(64, 32, 32, 128, 128, 16, 0) == 64 * 32 * 4 * 130 * 4
-    # explicit partition length
+    assert lib.pkv_decode_workspace_bytes(64, 32, 32, 128, 128, 16, 0) == 0
+    assert lib.pkv_decode_workspace_bytes(64, 32, 32, 128, 1024, 16, 0) == 64 * 32 * 8 * 130 * 4
+    # explicit partition length: 4096 blocks of 32 in 512-token partitions -> 256 partitions, 64 chunks
     assert lib.pkv_decode_partition_tokens(8, 64, 8, 128, 4096, 32, 512) == 512
-    assert lib.pkv_decode_workspace_bytes(8, 64, 8, 128, 4096, 32, 512) == 8 * 64 * 256 * 130 * 4
+    assert lib.pkv_decode_workspace_bytes(8, 64, 8, 128, 4096, 32, 512) == 8 * 64 * 64 * 130 * 4
     assert lib.pkv_decode_partition_tokens(8, 64, 8, 128, 4096, 32, 48) == 0
 
 
