@@ -2,8 +2,10 @@
 """Decode-step benchmark for the paged KV-cache library on one MI355X.
 
 A step is one pass of the whole decode hot path over one batch: slot
-mapping of the new tokens, KV append, paged decode attention (context
-partitions plus their log-sum-exp merge).  Inputs are synthetic and
+mapping of the new tokens and their KV append (one fused launch), then
+paged decode attention (context partitions, merged by log-sum-exp inside
+each work-group and, for sequences longer than one chunk, by a merge
+kernel).  Inputs are synthetic and
 resident in HBM before timing starts.
 
 Default workload: the MHA decode layer (64 sequences, 32/32 heads, head size
@@ -45,12 +47,17 @@ def parse():
     ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--partition-tokens", type=int, default=None,
                     help="context partition length (default: the configuration's, else the library's choice)")
+    ap.add_argument("--rotate", type=int, default=2,
+                    help="independent copies of the inputs used in turn, so that no step reads what the previous "
+                         "step left in the 256 MB infinity cache")
     ap.add_argument("--contiguous", action="store_true",
                     help="diagnostic: each sequence's blocks adjacent in the pool (paged vs contiguous storage)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--traffic", type=str, default=None,
-                    help="JSON file with measured HBM bytes per attention launch (from rocprofv3 counters)")
+    ap.add_argument("--traffic", type=str,
+                    default=os.path.join(ROOT, "profiles", "traffic_paged_decode_partition_kernel_mha_bf16.txt"),
+                    help="record of measured HBM bytes per attention launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, "
+                         "calibrated); used only when its workload and kernel-source hash match this run")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 20 device-to-device copies of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -77,6 +84,31 @@ def calib_copy(mib: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calib_copy_bytes": n, "launches": 20}))
+
+
+def kernel_sources_sha256(paths) -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(path, config: int, partition_tokens: int, contiguous: bool):
+    """HBM bytes per attention launch from a counter record, or None when the
+    record is missing or was taken on another workload or another version of
+    the kernel sources."""
+    if not path or not os.path.exists(path) or contiguous:
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("config") != config or rec.get("partition_tokens") != partition_tokens:
+        return None
+    if rec.get("kernel_sources_sha256") != kernel_sources_sha256(rec.get("kernel_sources", [])):
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def cpu_baseline(w, target_s: float) -> dict:
@@ -125,16 +157,21 @@ def main() -> int:
     w = pi.make_workload(args.config, mode="timing", contiguous=args.contiguous)
     log(f"generated config {args.config} ({w.description}) in {time.perf_counter() - t0:.1f} s")
     P = w.partition_tokens if args.partition_tokens is None else args.partition_tokens
-    d = device_inputs(w, torch)
-    ws = pkv.alloc_workspace(d["q"], d["kc"], d["vc"], d["bt"], P)
-    out = torch.empty_like(d["q"])
+    copies = [device_inputs(w, torch) for _ in range(max(1, args.rotate))]
+    d0 = copies[0]
+    ws = pkv.alloc_workspace(d0["q"], d0["kc"], d0["vc"], d0["bt"], P)
+    out = torch.empty_like(d0["q"])
     slots = torch.empty(w.S, dtype=torch.int64, device="cuda")
     stream = torch.cuda.current_stream()
     P_used = pkv.decode_partition_tokens(w.S, w.Hq, w.Hkv, w.hs, w.M, w.B, P)
+    turn = [0]
 
     def step(ev=None):
-        pkv.decode_slot_mapping(d["bt"], d["sl"], w.B, out=slots, stream=stream)
-        pkv.kv_cache_append(d["nk"], d["nv"], slots, d["kc"], d["vc"], stream=stream)
+        d = copies[turn[0] % len(copies)]
+        turn[0] += 1
+        # slot of each sequence's new token (from its block table) and the
+        # append of its K/V, one launch; then the attention
+        pkv.decode_append(d["nk"], d["nv"], d["bt"], d["sl"], d["kc"], d["vc"], slot_mapping=slots, stream=stream)
         if ev is not None:
             ev[0].record(stream)
         pkv.paged_decode_attention(d["q"], d["kc"], d["vc"], d["bt"], d["sl"], w.scale, out=out, workspace=ws,
@@ -170,13 +207,12 @@ def main() -> int:
     kv_bytes = w.kv_read_bytes()
     attn_avg_s = float(attn_ms.mean()) / 1e3
     achieved = kv_bytes / attn_avg_s / 1e9
-    traffic = None
-    if args.traffic and os.path.exists(args.traffic):
-        with open(args.traffic) as f:
-            traffic = json.load(f).get("bytes_per_launch")
+    traffic = measured_traffic(args.traffic, args.config, P_used, args.contiguous)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": "paged_decode_attention (partition kernel + log-sum-exp merge kernel)",
+                "kernel": ("paged_decode_partition_kernel (the whole attention call: one chunk per sequence, "
+                           "no merge launch)" if ws is None else
+                           "paged_decode_attention: partition kernel + chunk merge kernel"),
                 "algorithmic_bytes_per_launch": kv_bytes,
                 "launch_us": {"mean": round(attn_avg_s * 1e6, 2), "median": round(float(np.median(attn_ms)) * 1e3, 2),
                               "p10": round(float(np.percentile(attn_ms, 10)) * 1e3, 2),
@@ -200,7 +236,7 @@ def main() -> int:
         "dtype": "f32" if w.dtype == "f32" else "bf16",
         "data": "synthetic (seeded N(0,1) q/K/V, shuffled block IDs; no dataset)",
         "config": {"workload": w.description + (" [contiguous block order]" if args.contiguous else ""),
-                   "config": args.config, "seed": w.seed, "num_seqs": w.S,
+                   "config": args.config, "seed": w.seed, "num_seqs": w.S, "input_copies": len(copies),
                    "q_heads": w.Hq, "kv_heads": w.Hkv, "head_size": w.hs, "block_size": w.B,
                    "pool_blocks": w.num_blocks, "sum_seq_len": int(w.seq_lens.sum()),
                    "partition_tokens": P_used, "kv_bytes_per_step": kv_bytes},

@@ -145,6 +145,23 @@ PKV_API pkv_status kv_cache_append(const void* k, const void* v, const int64_t* 
                            void* k_cache, void* v_cache, void* stream);
 
 /*
+ * Decode-step append in one launch: for each sequence s the new token sits at
+ * position seq_lens[s] - 1, its slot is block_tables[s][pos / B] * B + pos % B
+ * (as in pkv_decode_slot_mapping), and k[s], v[s] are stored there exactly as
+ * kv_cache_append would.  Sequences with seq_len <= 0 or a position outside
+ * their table row are skipped.
+ *   k, v          device T [num_seqs][num_kv_heads][head_size]
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
+ *   seq_lens      device int32 [num_seqs] (lengths including the new token)
+ *   slot_mapping  device int64 [num_seqs] receiving the slots, or NULL
+ * Errors: as kv_cache_append.
+ */
+PKV_API pkv_status pkv_decode_append(const void* k, const void* v, const int32_t* block_tables,
+                                     const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                     const pkv_cache_desc* cache, void* k_cache, void* v_cache,
+                                     int64_t* slot_mapping, void* stream);
+
+/*
  * Context-partition length, in tokens, that paged_decode_attention will use
  * for these sizes.  partition_tokens > 0 requests that length (it must be a
  * multiple of block_size and at most 64 * block_size); 0 lets the library

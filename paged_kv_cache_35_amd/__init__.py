@@ -65,6 +65,8 @@ def library():
         L.pkv_decode_slot_mapping.argtypes = [P, P, i32, i32, i32, P, P]
         L.kv_cache_append.restype = i32
         L.kv_cache_append.argtypes = [P, P, P, i32, ctypes.POINTER(CacheDesc), P, P, P]
+        L.pkv_decode_append.restype = i32
+        L.pkv_decode_append.argtypes = [P, P, P, P, i32, i32, ctypes.POINTER(CacheDesc), P, P, P, P]
         L.pkv_decode_partition_tokens.restype = i32
         L.pkv_decode_partition_tokens.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.pkv_decode_workspace_bytes.restype = sz
@@ -144,6 +146,32 @@ def kv_cache_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _stream(stream)))
 
 
+def decode_append(k: torch.Tensor, v: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                  k_cache: torch.Tensor, v_cache: torch.Tensor, slot_mapping: Optional[torch.Tensor] = None,
+                  stream=None) -> Optional[torch.Tensor]:
+    """One launch: slot of each sequence's newest token from its table, then
+    append k[s], v[s] there.  Writes the slots to slot_mapping if given."""
+    desc = cache_desc(k_cache, v_cache)
+    S = k.shape[0]
+    if k.shape != v.shape or tuple(k.shape[1:]) != (desc.num_kv_heads, desc.head_size):
+        raise ValueError("k and v must be [S, Hkv, head_size]")
+    if k.dtype != k_cache.dtype or v.dtype != k_cache.dtype:
+        raise ValueError("k, v and the pools must share a dtype")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_tables and seq_lens must be int32")
+    if block_tables.shape[0] != S or seq_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, M] and seq_lens [S]")
+    if slot_mapping is not None and (slot_mapping.dtype != torch.int64 or slot_mapping.shape != (S,)):
+        raise ValueError("slot_mapping must be int64 [S]")
+    if S == 0:
+        return slot_mapping
+    _check("pkv_decode_append", library().pkv_decode_append(
+        _dev(k, "k"), _dev(v, "v"), _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), S,
+        block_tables.shape[1], ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(slot_mapping, "slot_mapping") if slot_mapping is not None else None, _stream(stream)))
+    return slot_mapping
+
+
 def decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq, block_size,
                             partition_tokens=0) -> int:
     return int(library().pkv_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, head_size,
@@ -201,9 +229,8 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
 
 def decode_step(q, k_cache, v_cache, block_tables, seq_lens, new_k, new_v, scale, out=None, workspace=None,
                 slot_mapping=None, partition_tokens=0, stream=None) -> torch.Tensor:
-    """One decode step: slot mapping of the new tokens, append, attention."""
-    desc = cache_desc(k_cache, v_cache)
-    slot_mapping = decode_slot_mapping(block_tables, seq_lens, desc.block_size, out=slot_mapping, stream=stream)
-    kv_cache_append(new_k, new_v, slot_mapping, k_cache, v_cache, stream=stream)
+    """One decode step: slot of each new token and its append (one launch),
+    then attention."""
+    decode_append(new_k, new_v, block_tables, seq_lens, k_cache, v_cache, slot_mapping=slot_mapping, stream=stream)
     return paged_decode_attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out=out,
                                   workspace=workspace, partition_tokens=partition_tokens, stream=stream)

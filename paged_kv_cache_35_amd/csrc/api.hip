@@ -88,6 +88,32 @@ pkv_status pkv_decode_slot_mapping(const int32_t* block_tables, const int32_t* s
                                                slot_mapping, (hipStream_t)stream));
 }
 
+namespace {
+
+pkv_status append_common(const void* k, const void* v, int64_t* slot_mapping, const int32_t* block_tables,
+                         const int32_t* seq_lens, int32_t max_blocks_per_seq, int32_t num_tokens,
+                         const pkv_cache_desc* cache, void* k_cache, void* v_cache, void* stream)
+{
+    pkv::AppendArgs a;
+    a.k = k;
+    a.v = v;
+    a.slot_mapping = slot_mapping;
+    a.block_tables = block_tables;
+    a.seq_lens = seq_lens;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.num_tokens = num_tokens;
+    a.num_kv_heads = cache->num_kv_heads;
+    a.head_size = cache->head_size;
+    a.block_size = cache->block_size;
+    a.num_blocks = cache->num_blocks;
+    a.elem_bytes = elem_bytes(cache->dtype);
+    return hip_status(pkv::launch_append(a, (hipStream_t)stream));
+}
+
+}  // namespace
+
 pkv_status kv_cache_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
                            const pkv_cache_desc* cache, void* k_cache, void* v_cache, void* stream)
 {
@@ -102,19 +128,28 @@ pkv_status kv_cache_append(const void* k, const void* v, const int64_t* slot_map
         return PKV_OK;
     if (!k || !v || !slot_mapping || !aligned16(k) || !aligned16(v))
         return PKV_ERR_INVALID_ARG;
-    pkv::AppendArgs a;
-    a.k = k;
-    a.v = v;
-    a.slot_mapping = slot_mapping;
-    a.k_cache = k_cache;
-    a.v_cache = v_cache;
-    a.num_tokens = num_tokens;
-    a.num_kv_heads = cache->num_kv_heads;
-    a.head_size = cache->head_size;
-    a.block_size = cache->block_size;
-    a.num_blocks = cache->num_blocks;
-    a.elem_bytes = elem_bytes(cache->dtype);
-    return hip_status(pkv::launch_append(a, (hipStream_t)stream));
+    // the kernel only reads slot_mapping when no block table is given
+    return append_common(k, v, const_cast<int64_t*>(slot_mapping), nullptr, nullptr, 0, num_tokens, cache, k_cache,
+                         v_cache, stream);
+}
+
+pkv_status pkv_decode_append(const void* k, const void* v, const int32_t* block_tables, const int32_t* seq_lens,
+                             int32_t num_seqs, int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                             void* k_cache, void* v_cache, int64_t* slot_mapping, void* stream)
+{
+    if (num_seqs < 0 || max_blocks_per_seq <= 0)
+        return PKV_ERR_INVALID_ARG;
+    pkv_status st = check_cache(cache);
+    if (st != PKV_OK)
+        return st;
+    if (!k_cache || !v_cache || !aligned16(k_cache) || !aligned16(v_cache))
+        return PKV_ERR_INVALID_ARG;
+    if (num_seqs == 0)
+        return PKV_OK;
+    if (!k || !v || !block_tables || !seq_lens || !aligned16(k) || !aligned16(v))
+        return PKV_ERR_INVALID_ARG;
+    return append_common(k, v, slot_mapping, block_tables, seq_lens, max_blocks_per_seq, num_seqs, cache, k_cache,
+                         v_cache, stream);
 }
 
 int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

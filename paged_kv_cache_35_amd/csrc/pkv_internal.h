@@ -45,7 +45,12 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 struct AppendArgs {
     const void* k;
     const void* v;
-    const int64_t* slot_mapping;
+    // Slots: read from slot_mapping, or (block_tables != null) computed as the
+    // decode slot of each sequence and written to slot_mapping if non-null.
+    int64_t* slot_mapping;
+    const int32_t* block_tables;
+    const int32_t* seq_lens;
+    int32_t max_blocks_per_seq;
     void* k_cache;
     void* v_cache;
     int32_t num_tokens;

@@ -233,3 +233,34 @@ def test_append_skips_negative_slots_and_leaves_the_rest():
     oracle.kv_append(w.new_k, w.new_v, slots, kp, vp)
     assert same_bytes(host_bits(kc), kp)
     assert same_bytes(host_bits(vc), vp)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 4, 5])
+def test_fused_decode_append_bit_exact(cfg):
+    w = pi.make_workload(cfg, **SMALL[cfg])
+    announce(f"fused decode append config {cfg}: lens={list(w.seq_lens)}")
+    kc, vc = dev(w.k_cache), dev(w.v_cache)
+    slots = torch.full((w.S,), -7, dtype=torch.int64, device="cuda")
+    pkv().decode_append(dev(w.new_k), dev(w.new_v), dev(w.block_tables), dev(w.seq_lens), kc, vc, slot_mapping=slots)
+    torch.cuda.synchronize()
+    ref_slots = oracle.decode_slot_mapping(w.block_tables, w.seq_lens, w.B)
+    kp, vp = w.k_cache.copy(), w.v_cache.copy()
+    oracle.kv_append(w.new_k, w.new_v, ref_slots, kp, vp)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    assert same_bytes(host_bits(kc), kp)
+    assert same_bytes(host_bits(vc), vp)
+
+
+def test_fused_decode_append_skips_empty_sequences():
+    lens = [5, 0, 17, 0, 1]
+    w = pi.make_workload(2, seq_lens=lens)
+    announce(f"fused decode append with empty sequences {lens}")
+    kc, vc = dev(w.k_cache), dev(w.v_cache)
+    pkv().decode_append(dev(w.new_k), dev(w.new_v), dev(w.block_tables), dev(w.seq_lens), kc, vc)
+    torch.cuda.synchronize()
+    ref_slots = oracle.decode_slot_mapping(w.block_tables, w.seq_lens, w.B)
+    assert list(ref_slots[[1, 3]]) == [-1, -1]
+    kp, vp = w.k_cache.copy(), w.v_cache.copy()
+    oracle.kv_append(w.new_k, w.new_v, ref_slots, kp, vp)
+    assert same_bytes(host_bits(kc), kp)
+    assert same_bytes(host_bits(vc), vp)
