@@ -209,6 +209,31 @@ PKV_API pkv_status paged_decode_attention(const void* q, const void* k_cache, co
                                   void* workspace, size_t workspace_bytes,
                                   int32_t partition_tokens, void* stream);
 
+/*
+ * One whole decode step in one call: for each sequence s, the new token
+ * new_k[s], new_v[s] is stored in the slot of position seq_lens[s] - 1
+ * (pkv_decode_append), then the attention of paged_decode_attention is
+ * computed over all seq_lens[s] tokens, the new one included.  Two kernels
+ * are launched in order on `stream`; the result, the pools and slot_mapping
+ * are bit-identical to calling those two functions.  Every argument is
+ * validated before anything is launched, so a rejected call changes nothing.
+ * (A single-launch variant, where the wave reading the last block also
+ * stores the new token, was measured slower on MI355X: stores issued while
+ * the pools are being streamed cost more than a separate append launch.)
+ *   new_k, new_v  device T [num_seqs][num_kv_heads][head_size]
+ *   slot_mapping  device int64 [num_seqs] receiving the slots, or NULL
+ *   other arguments as paged_decode_attention (workspace sized by
+ *   pkv_decode_workspace_bytes with the same sizes)
+ * Errors: as paged_decode_attention; new_k / new_v must be non-null and
+ * 16-byte aligned.
+ */
+PKV_API pkv_status paged_decode_step(const void* q, const void* new_k, const void* new_v, void* k_cache,
+                                     void* v_cache, const int32_t* block_tables, const int32_t* seq_lens,
+                                     int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                     const pkv_cache_desc* cache, float scale, void* out,
+                                     int64_t* slot_mapping, void* workspace, size_t workspace_bytes,
+                                     int32_t partition_tokens, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -74,6 +74,9 @@ def library():
         L.paged_decode_attention.restype = i32
         L.paged_decode_attention.argtypes = [P, P, P, P, P, i32, i32, i32, ctypes.POINTER(CacheDesc), f32, P, P, sz,
                                              i32, P]
+        L.paged_decode_step.restype = i32
+        L.paged_decode_step.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, ctypes.POINTER(CacheDesc), f32, P, P, P,
+                                        sz, i32, P]
         _lib = L
     return _lib
 
@@ -227,10 +230,50 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     return out
 
 
+def paged_decode_step(q: torch.Tensor, new_k: torch.Tensor, new_v: torch.Tensor, k_cache: torch.Tensor,
+                      v_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                      out: Optional[torch.Tensor] = None, slot_mapping: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None, partition_tokens: int = 0,
+                      stream=None) -> torch.Tensor:
+    """A whole decode step in one call: store new_k[s], new_v[s]
+    at position seq_lens[s] - 1, then attend over all seq_lens[s] tokens.
+    Bit-identical to decode_append followed by paged_decode_attention."""
+    desc = cache_desc(k_cache, v_cache)
+    if q.dtype != k_cache.dtype:
+        raise ValueError("q must have the pools' dtype")
+    S, Hq, hs = q.shape
+    if hs != desc.head_size:
+        raise ValueError("q head size does not match the pools")
+    if new_k.shape != new_v.shape or tuple(new_k.shape) != (S, desc.num_kv_heads, desc.head_size):
+        raise ValueError("new_k and new_v must be [S, Hkv, head_size]")
+    if new_k.dtype != k_cache.dtype or new_v.dtype != k_cache.dtype:
+        raise ValueError("new_k, new_v and the pools must share a dtype")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_tables and seq_lens must be int32")
+    if block_tables.shape[0] != S or seq_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, M] and seq_lens [S]")
+    if slot_mapping is not None and (slot_mapping.dtype != torch.int64 or slot_mapping.shape != (S,)):
+        raise ValueError("slot_mapping must be int64 [S]")
+    M = block_tables.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if workspace is None:
+        workspace = alloc_workspace(q, k_cache, v_cache, block_tables, partition_tokens)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("paged_decode_step", library().paged_decode_step(
+        _dev(q, "q"), _dev(new_k, "new_k"), _dev(new_v, "new_v"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), S, Hq, M, ctypes.byref(desc), float(scale),
+        _dev(out, "out"), _dev(slot_mapping, "slot_mapping") if slot_mapping is not None else None, ws_ptr, ws_bytes,
+        int(partition_tokens), _stream(stream)))
+    return out
+
+
 def decode_step(q, k_cache, v_cache, block_tables, seq_lens, new_k, new_v, scale, out=None, workspace=None,
                 slot_mapping=None, partition_tokens=0, stream=None) -> torch.Tensor:
-    """One decode step: slot of each new token and its append (one launch),
-    then attention."""
-    decode_append(new_k, new_v, block_tables, seq_lens, k_cache, v_cache, slot_mapping=slot_mapping, stream=stream)
-    return paged_decode_attention(q, k_cache, v_cache, block_tables, seq_lens, scale, out=out,
-                                  workspace=workspace, partition_tokens=partition_tokens, stream=stream)
+    """One decode step: append of the new tokens, then attention (two launches on one stream)."""
+    return paged_decode_step(q, new_k, new_v, k_cache, v_cache, block_tables, seq_lens, scale, out=out,
+                             slot_mapping=slot_mapping, workspace=workspace, partition_tokens=partition_tokens,
+                             stream=stream)

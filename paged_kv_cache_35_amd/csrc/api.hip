@@ -38,8 +38,12 @@ pkv_status check_cache(const pkv_cache_desc* c)
     return PKV_OK;
 }
 
-// Library choice of the context-partition length: 512 tokens (32 blocks at
-// B = 16, 16 at B = 32), or one partition when the table is shorter.
+// Library choice of the context-partition length: PKV_DEFAULT_PARTITION_TOKENS
+// (512: 32 blocks at B = 16, 16 at B = 32), or one partition when the table is
+// shorter.
+#ifndef PKV_DEFAULT_PARTITION_TOKENS
+#define PKV_DEFAULT_PARTITION_TOKENS 512
+#endif
 int32_t resolve_partition_tokens(int32_t max_blocks_per_seq, int32_t block_size, int32_t requested)
 {
     if (requested < 0 || max_blocks_per_seq <= 0 || block_size <= 0)
@@ -50,7 +54,7 @@ int32_t resolve_partition_tokens(int32_t max_blocks_per_seq, int32_t block_size,
         return requested;
     }
     const int64_t whole = (int64_t)max_blocks_per_seq * block_size;
-    const int32_t dflt = 512;
+    const int32_t dflt = PKV_DEFAULT_PARTITION_TOKENS;
     return (int32_t)(whole < dflt ? whole : dflt);
 }
 
@@ -177,12 +181,16 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
     return (size_t)num_seqs * num_q_heads * chunks * ((size_t)head_size + 2) * sizeof(float);
 }
 
-pkv_status paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
-                                  const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
-                                  int32_t num_q_heads, int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
-                                  float scale, void* out, void* workspace, size_t workspace_bytes,
-                                  int32_t partition_tokens, void* stream)
+namespace {
+
+// Validates the attention arguments and fills the launch description; no
+// GPU work.  PKV_OK with *nothing_to_do set when num_seqs == 0.
+pkv_status attention_args(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                          const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                          const pkv_cache_desc* cache, float scale, void* out, void* workspace,
+                          size_t workspace_bytes, int32_t partition_tokens, pkv::DecodeArgs& a, bool& nothing_to_do)
 {
+    nothing_to_do = false;
     if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
         return PKV_ERR_INVALID_ARG;
     pkv_status st = check_cache(cache);
@@ -196,8 +204,10 @@ pkv_status paged_decode_attention(const void* q, const void* k_cache, const void
         return PKV_ERR_UNSUPPORTED;
     if ((int64_t)max_blocks_per_seq * cache->block_size > INT32_MAX)
         return PKV_ERR_INVALID_ARG;
-    if (num_seqs == 0)
+    if (num_seqs == 0) {
+        nothing_to_do = true;
         return PKV_OK;
+    }
     if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out)
         return PKV_ERR_INVALID_ARG;
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
@@ -214,7 +224,6 @@ pkv_status paged_decode_attention(const void* q, const void* k_cache, const void
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
         return PKV_ERR_WORKSPACE;
 
-    pkv::DecodeArgs a;
     a.q = q;
     a.k_cache = k_cache;
     a.v_cache = v_cache;
@@ -234,7 +243,54 @@ pkv_status paged_decode_attention(const void* q, const void* k_cache, const void
     a.dtype = cache->dtype;
     a.partition_blocks = pb;
     a.max_parts = parts;
+    // A requested partition length is honoured literally (each wave owns one
+    // contiguous partition); the library's own choice deals each chunk's
+    // blocks round-robin to the waves, which balances sequences that end
+    // inside a chunk.  Both compute the same attention.
+    a.interleave = partition_tokens == 0 ? 1 : 0;
     a.scale = scale;
+    return PKV_OK;
+}
+
+}  // namespace
+
+pkv_status paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                                  float scale, void* out, void* workspace, size_t workspace_bytes,
+                                  int32_t partition_tokens, void* stream)
+{
+    pkv::DecodeArgs a;
+    bool nothing_to_do;
+    const pkv_status st = attention_args(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                                         max_blocks_per_seq, cache, scale, out, workspace, workspace_bytes,
+                                         partition_tokens, a, nothing_to_do);
+    if (st != PKV_OK || nothing_to_do)
+        return st;
+    return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+}
+
+pkv_status paged_decode_step(const void* q, const void* new_k, const void* new_v, void* k_cache, void* v_cache,
+                             const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                             float scale, void* out, int64_t* slot_mapping, void* workspace,
+                             size_t workspace_bytes, int32_t partition_tokens, void* stream)
+{
+    // every argument is checked before the append, so a rejected call
+    // changes nothing
+    pkv::DecodeArgs a;
+    bool nothing_to_do;
+    pkv_status st = attention_args(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                                   max_blocks_per_seq, cache, scale, out, workspace, workspace_bytes,
+                                   partition_tokens, a, nothing_to_do);
+    if (st != PKV_OK || nothing_to_do)
+        return st;
+    if (!new_k || !new_v || !aligned16(new_k) || !aligned16(new_v))
+        return PKV_ERR_INVALID_ARG;
+    st = append_common(new_k, new_v, slot_mapping, block_tables, seq_lens, max_blocks_per_seq, num_seqs, cache,
+                       k_cache, v_cache, stream);
+    if (st != PKV_OK)
+        return st;
     return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
 }
 

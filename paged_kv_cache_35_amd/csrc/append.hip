@@ -39,6 +39,8 @@ __global__ void decode_slot_mapping_kernel(const int32_t* __restrict__ block_tab
 
 constexpr int kAppendThreads = 256;
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // Token i = blockIdx.x; each thread moves one 16-byte chunk of the token's
 // key and one of its value (chunk ci = blockIdx.y * 256 + threadIdx.x of the
 // Hkv * hs / X chunks).  Key chunk f of KV head h holds head dims
@@ -49,11 +51,18 @@ constexpr int kAppendThreads = 256;
 // (computed from block_tables / seq_lens and also written to slot_mapping);
 // otherwise it is read from slot_mapping.  A negative or out-of-range slot
 // skips the token.
+//
+// The stores cover only part of each 32-byte sector (16 of 32 bytes of a key
+// sector, 2 or 4 bytes of a value row), and the memory system merges them
+// with the old contents.  Writing whole sectors instead (reading the
+// neighbouring bytes first) makes this kernel faster on its own, but the
+// attention launch that follows slows down by more than that gain: a decode
+// step (append, then attention) is fastest with these plain stores.
 template <typename E, bool FROM_TABLE>
 __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
-    const uint4* __restrict__ k, const uint4* __restrict__ v, int64_t* __restrict__ slot_mapping,
+    const u32x4* __restrict__ k, const u32x4* __restrict__ v, int64_t* __restrict__ slot_mapping,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int32_t max_blocks_per_seq,
-    uint4* __restrict__ k_cache, E* __restrict__ v_cache, int32_t num_kv_heads, int32_t head_size,
+    u32x4* __restrict__ k_cache, E* __restrict__ v_cache, int32_t num_kv_heads, int32_t head_size,
     int32_t block_size, int32_t num_blocks)
 {
     constexpr int X = 16 / sizeof(E);
@@ -62,7 +71,7 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     const int32_t nchunks = num_kv_heads * chunks_per_head;
     const int32_t ci = blockIdx.y * kAppendThreads + threadIdx.x;
     const bool active = ci < nchunks;
-    uint4 kval = {0u, 0u, 0u, 0u}, vval = {0u, 0u, 0u, 0u};
+    u32x4 kval = {0u, 0u, 0u, 0u}, vval = {0u, 0u, 0u, 0u};
     if (active) {
         kval = k[(int64_t)i * nchunks + ci];
         vval = v[(int64_t)i * nchunks + ci];
@@ -83,16 +92,17 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
         return;  // out-of-range slot: skipped, never written
     const int32_t h = ci / chunks_per_head;
     const int32_t f = ci - h * chunks_per_head;
-    k_cache[((b * num_kv_heads + h) * chunks_per_head + f) * block_size + off] = kval;
+    // streaming stores: the written lines are not re-read by this kernel
+    __builtin_nontemporal_store(kval, &k_cache[((b * num_kv_heads + h) * chunks_per_head + f) * block_size + off]);
     union {
-        uint4 u;
+        u32x4 u;
         E e[X];
     } val;
     val.u = vval;
     E* vdst = v_cache + ((b * num_kv_heads + h) * head_size + (int64_t)f * X) * block_size + off;
 #pragma unroll
     for (int e = 0; e < X; ++e)
-        vdst[(int64_t)e * block_size] = val.e[e];
+        __builtin_nontemporal_store(val.e[e], &vdst[(int64_t)e * block_size]);
 }
 
 hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
@@ -112,14 +122,14 @@ static hipError_t launch_append_impl(const AppendArgs& a, hipStream_t stream)
     const int32_t nchunks = a.num_kv_heads * a.head_size / (16 / a.elem_bytes);
     const dim3 grid(a.num_tokens, (nchunks + kAppendThreads - 1) / kAppendThreads), block(kAppendThreads);
     if (a.elem_bytes == 2)
-        hipLaunchKernelGGL((kv_append_kernel<uint16_t, FROM_TABLE>), grid, block, 0, stream, (const uint4*)a.k,
-                           (const uint4*)a.v, a.slot_mapping, a.block_tables, a.seq_lens, a.max_blocks_per_seq,
-                           (uint4*)a.k_cache, (uint16_t*)a.v_cache, a.num_kv_heads, a.head_size, a.block_size,
+        hipLaunchKernelGGL((kv_append_kernel<uint16_t, FROM_TABLE>), grid, block, 0, stream, (const u32x4*)a.k,
+                           (const u32x4*)a.v, a.slot_mapping, a.block_tables, a.seq_lens, a.max_blocks_per_seq,
+                           (u32x4*)a.k_cache, (uint16_t*)a.v_cache, a.num_kv_heads, a.head_size, a.block_size,
                            a.num_blocks);
     else
-        hipLaunchKernelGGL((kv_append_kernel<uint32_t, FROM_TABLE>), grid, block, 0, stream, (const uint4*)a.k,
-                           (const uint4*)a.v, a.slot_mapping, a.block_tables, a.seq_lens, a.max_blocks_per_seq,
-                           (uint4*)a.k_cache, (uint32_t*)a.v_cache, a.num_kv_heads, a.head_size, a.block_size,
+        hipLaunchKernelGGL((kv_append_kernel<uint32_t, FROM_TABLE>), grid, block, 0, stream, (const u32x4*)a.k,
+                           (const u32x4*)a.v, a.slot_mapping, a.block_tables, a.seq_lens, a.max_blocks_per_seq,
+                           (u32x4*)a.k_cache, (uint32_t*)a.v_cache, a.num_kv_heads, a.head_size, a.block_size,
                            a.num_blocks);
     return hipGetLastError();
 }

@@ -111,8 +111,6 @@ struct WideRegs {
 // lane group r the tokens 8r .. 8r+7 (the value MFMA's reduction order).
 __device__ __forceinline__ int wide_token(int mp, int c) { return 8 * (c >> 2) + 4 * mp + (c & 3); }
 
-__device__ __forceinline__ float to_float(__bf16 x) { return (float)x; }
-__device__ __forceinline__ float to_float(float x) { return x; }
 __device__ __forceinline__ void store_elem(__bf16* p, float x) { *p = (__bf16)x; }
 __device__ __forceinline__ void store_elem(float* p, float x) { *p = x; }
 
@@ -247,18 +245,17 @@ __device__ __forceinline__ void zero_masked_values(TileRegs<T, HS>& t, int tok0,
     }
 }
 
-// At least two waves per SIMD: keeps the register allocation (including
-// the MFMA accumulators) within 256 VGPRs so two pipelined waves share a SIMD.
-#ifndef PKV_DECODE_WAVES_PER_EU
-#define PKV_DECODE_WAVES_PER_EU 2
-#endif
-#define PKV_OCCUPANCY __attribute__((amdgpu_waves_per_eu(PKV_DECODE_WAVES_PER_EU)))
+// Occupancy targets for bf16: three waves per SIMD with 16-token blocks
+// (<= 168 VGPRs, including the MFMA accumulators), two with 32-token units
+// (<= 256).  The fp32 variants (larger operands) are left unconstrained.
+#define PKV_OCCUPANCY __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (BS == 16 ? 3 : 2) : 1)))
 
 template <typename T, int HS, int BS, int NW>
 __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_kernel(
     const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
-    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int32_t Hq, int32_t Hkv,
-    int32_t M, int32_t num_blocks, int32_t PB, int32_t max_parts, float qscale, T* __restrict__ out,
+    const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ seq_lens, int32_t Hq, int32_t Hkv,
+    int32_t M, int32_t num_blocks, int32_t PB, int32_t max_parts, int32_t interleave, float qscale, T* __restrict__ out,
     float* __restrict__ ws_o, float* __restrict__ ws_ml)
 {
     constexpr bool kWide = sizeof(T) == 2 && BS == 32;  // 32-token units (see WideRegs)
@@ -275,46 +272,61 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     const int c = lane & 15;
     const int G = Hq / Hkv;
 
-    int L = seq_lens[s];
-    L = L < 0 ? 0 : (L > M * BS ? M * BS : L);
+    const int L_in = seq_lens[s];
+    const int L = L_in < 0 ? 0 : (L_in > M * BS ? M * BS : L_in);
     if (L == 0) {
-        if (chunk == 0 && w == 0)
+        if (chunk == 0 && w == 0) {
             for (int idx = lane; idx < G * HS; idx += 64)
                 store_elem(out + ((int64_t)s * Hq + (int64_t)kvh * G) * HS + idx, 0.f);
+        }
         return;
     }
     const int nblk = (L + BS - 1) / BS;
     if (chunk * NW * PB >= nblk)
         return;  // the whole work-group is past the end (uniform: before any barrier)
     const int nchunks = (nblk + NW * PB - 1) / (NW * PB);
-    const int b0 = part * PB;
-    // a wave whose partition is past the end has no tiles but still joins
-    // the work-group merge below
-    const int nb_part = b0 >= nblk ? 0 : ((nblk - b0 < PB) ? nblk - b0 : PB);
+    // This wave's blocks: base, base + stride, ... (nb_w of them, <= PB).
+    // Contiguous mode: partition `part` = PB consecutive blocks.  Interleaved
+    // mode: the chunk's blocks dealt round-robin to the NW waves, which keeps
+    // the waves balanced when a sequence ends inside the chunk.  A wave with
+    // no blocks still joins the work-group merge below.
+    const int cb0 = chunk * NW * PB;
+    const int cnb = (nblk - cb0 < NW * PB) ? nblk - cb0 : NW * PB;
+    int base, stride, nb_w;
+    if (interleave) {
+        base = cb0 + w;
+        stride = NW;
+        nb_w = cnb > w ? (cnb - w + NW - 1) / NW : 0;
+    } else {
+        base = part * PB;
+        stride = 1;
+        nb_w = base >= nblk ? 0 : ((nblk - base < PB) ? nblk - base : PB);
+    }
 
-    // physical block IDs of this partition, one per lane (PB <= 64); the
-    // tile loop broadcasts them with readlane
-    const int32_t id_lane = lane < nb_part ? block_tables[(int64_t)s * M + b0 + lane] : 0;
-
-    // query operand: head c of this KV head's group (zero for padding rows)
+    // query operand: head c of this KV head's group.  Rows c >= G of the
+    // 16-row MFMA tile are padding: they repeat head c % G, and their results
+    // are never stored.  (Loading real rows rather than zeroing them keeps
+    // the query registers free of any use before the tile loop, so the
+    // first tile's loads are issued while the query loads are in flight.)
+    // The query loads are issued before the block-table load for the same
+    // reason.
     typename Ops<T>::template QReg<HS> qr;
     {
-        const bool real = c < G;
-        const T* qh = q + ((int64_t)s * Hq + (int64_t)kvh * G + (real ? c : 0)) * HS;
+        const T* qh = q + ((int64_t)s * Hq + (int64_t)kvh * G + c % G) * HS;
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
-            for (int i = 0; i < HS / 32; ++i) {
-                bf16x8 v = *(const bf16x8*)(qh + 32 * i + 8 * r);
-                qr.v[i] = real ? v : (bf16x8)(__bf16)0.f;
-            }
+            for (int i = 0; i < HS / 32; ++i)
+                qr.v[i] = *(const bf16x8*)(qh + 32 * i + 8 * r);
         } else {
 #pragma unroll
-            for (int i = 0; i < HS / 16; ++i) {
-                f32x4 v = *(const f32x4*)(qh + 16 * i + 4 * r);
-                qr.v[i] = real ? v : (f32x4)0.f;
-            }
+            for (int i = 0; i < HS / 16; ++i)
+                qr.v[i] = *(const f32x4*)(qh + 16 * i + 4 * r);
         }
     }
+
+    // physical block IDs of this wave's blocks, one per lane (nb_w <= 64);
+    // the tile loop broadcasts them with readlane
+    const int32_t id_lane = lane < nb_w ? block_tables[(int64_t)s * M + base + lane * stride] : 0;
 
     f32x4 O[HS / 16];
 #pragma unroll
@@ -328,7 +340,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     const int64_t head_off = (int64_t)kvh * TILE;
     const int64_t block_stride = (int64_t)Hkv * TILE;
 
-    auto tile_ptr_ok = [&](int j, const T*& tk, const T*& tv) -> bool {
+    auto tile_ptr_ok = [&](int j, const T*& tk, const T*& tv) __attribute__((always_inline)) -> bool {
         int32_t id = __builtin_amdgcn_readlane(id_lane, j);
         const bool ok = (uint32_t)id < (uint32_t)num_blocks;
         id = ok ? id : 0;
@@ -340,7 +352,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     // Online-softmax update shared by both unit shapes: mx is this lane's
     // maximum over its valid scores (log2 units).  Raises the running maximum
     // only when mx exceeds it by more than kRescaleSlack.
-    auto update_max = [&](float mx) {
+    auto update_max = [&](float mx) __attribute__((always_inline)) {
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         if (__ballot(mx > m_run + kRescaleSlack) != 0) {
@@ -364,7 +376,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     // tok0 is the sub-tile's first token; an out-of-range block ID was
     // replaced by block 0 and its tokens are all masked (valid below Lt), so
     // the loaded registers are consumed on every path.
-    auto compute = [&](TileRegs<T, HS>& t, int tok0, bool ok) {
+    auto compute = [&](TileRegs<T, HS>& t, int tok0, bool ok) __attribute__((always_inline)) {
         const int Lt = ok ? L : tok0;
         const bool partial = tok0 + 16 > Lt;
         const f32x4 S = tile_scores<T, HS>(t.k, qr);
@@ -392,7 +404,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
 
     // One 32-token unit (bf16, B = 32): element jj of M-tile mp's scores is
     // token 8r + 4mp + jj; value element e of a lane is token 8r + e.
-    auto compute_wide = [&](WideRegs<HS>& t, int tok0, bool ok) {
+    auto compute_wide = [&](WideRegs<HS>& t, int tok0, bool ok) __attribute__((always_inline)) {
         if constexpr (kWide) {
             const int Lt = ok ? L : tok0;
             const bool partial = tok0 + 32 > Lt;
@@ -444,8 +456,8 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     // peeled, so every compute is preceded by exactly one batch of loads and
     // the memory-counter waits stay precise.
     using Regs = typename std::conditional<kWide, WideRegs<HS>, TileRegs<T, HS>>::type;
-    const int nunits = nb_part * PER;  // 0 for a wave past the end
-    auto issue = [&](Regs& t, int u) -> bool {
+    const int nunits = nb_w * PER;  // 0 for a wave past the end
+    auto issue = [&](Regs& t, int u) __attribute__((always_inline)) -> bool {
         const int j = u / PER;
         const T* tk;
         const T* tv;
@@ -456,12 +468,13 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
             load_tile<T, HS, BS>(t, tk, tv, u % PER, r, c);
         return ok;
     };
-    auto first_token = [&](int u) { return (b0 + u / PER) * BS + UT * (u % PER); };
-    auto run = [&](Regs& t, int u, bool ok) {
+    auto first_token = [&](int u) __attribute__((always_inline)) { return (base + (u / PER) * stride) * BS + UT * (u % PER); };
+    auto run = [&](Regs& t, int u, bool ok) __attribute__((always_inline)) {
+        const int tok0 = first_token(u);
         if constexpr (kWide)
-            compute_wide(t, first_token(u), ok);
+            compute_wide(t, tok0, ok);
         else
-            compute(t, first_token(u), ok);
+            compute(t, tok0, ok);
     };
     if (nunits > 0) {
         Regs ta, tb;
@@ -509,7 +522,10 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
                 sm_out[w][g * HS + 16 * i + c] = O[i][jj] * inv;
         }
     }
-    __syncthreads();
+    // LDS-only barrier: the merge exchanges nothing through global memory
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
     const int64_t hbase = (int64_t)s * Hq + (int64_t)kvh * G;
     const int64_t blk = ((int64_t)s * Hkv + kvh) * max_parts + chunk;
@@ -618,7 +634,7 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
     const int kvh = h / G;
     const int g = h - kvh * G;
     const int64_t u0 = ((int64_t)s * Hkv + kvh) * max_parts;
-    auto row = [&](int p) { return (u0 + p) * G + g; };
+    auto row = [&](int p) __attribute__((always_inline)) { return (u0 + p) * G + g; };
 
     float mx = -INFINITY;
     for (int p = threadIdx.x; p < nparts; p += kMergeThreads)
@@ -674,13 +690,12 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
     hipLaunchKernelGGL((paged_decode_partition_kernel<T, HS, BS, NW>), grid, dim3(NW * 64), 0, stream,
                        (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache, a.block_tables, a.seq_lens,
                        a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq, a.num_blocks, a.partition_blocks,
-                       a.max_parts, a.scale * kLog2e, (T*)a.out, a.ws_o, a.ws_ml);
+                       a.max_parts, a.interleave, a.scale * kLog2e, (T*)a.out, a.ws_o, a.ws_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_parts <= 1)
         return e;  // one chunk per sequence: the partition kernel wrote the output
     hipLaunchKernelGGL((paged_decode_reduce_kernel<T, HS>), dim3(a.num_q_heads, a.num_seqs), dim3(kMergeThreads), 0,
-                       stream,
-                       a.seq_lens, a.max_blocks_per_seq, BS, a.partition_blocks * NW, a.num_q_heads,
+                       stream, a.seq_lens, a.max_blocks_per_seq, BS, a.partition_blocks * NW, a.num_q_heads,
                        a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, (T*)a.out);
     return hipGetLastError();
 }

@@ -31,7 +31,7 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("paged_decode_attention", "kv_cache_append", "pkv_decode_slot_mapping",
               "pkv_decode_workspace_bytes", "pkv_decode_partition_tokens", "pkv_status_string",
-              "pkv_layout_version", "pkv_last_hip_error"):
+              "pkv_layout_version", "pkv_last_hip_error", "paged_decode_step", "pkv_decode_append"):
         assert n in names
 
 
@@ -132,3 +132,16 @@ def test_binding_refuses_host_tensors():
         pkv.paged_decode_attention(q, kc, vc, bt, sl, 0.125, out=torch.zeros_like(q), workspace=None)
     with pytest.raises(ValueError):
         pkv.cache_desc(kc, vc[:, :, :32])
+
+
+def test_step_requires_the_new_token(lib):
+    d = desc()
+    f = lib.paged_decode_step
+    assert f(FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 4, ctypes.byref(d), 0.125, FAKE, None, None, 0, 0,
+             None) == INVALID
+    assert f(FAKE, FAKE, ctypes.c_void_p(0x10002), FAKE, FAKE, FAKE, FAKE, 4, 8, 4, ctypes.byref(d), 0.125, FAKE,
+             None, None, 0, 0, None) == INVALID
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 4096, ctypes.byref(d), 0.125, FAKE, None, None, 0, 0,
+             None) == WORKSPACE
+    assert f(None, None, None, FAKE, FAKE, None, None, 0, 8, 4, ctypes.byref(d), 0.125, None, None, None, 0, 0,
+             None) == OK

@@ -236,9 +236,9 @@ def test_append_skips_negative_slots_and_leaves_the_rest():
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 4, 5])
-def test_fused_decode_append_bit_exact(cfg):
+def test_decode_append_bit_exact(cfg):
     w = pi.make_workload(cfg, **SMALL[cfg])
-    announce(f"fused decode append config {cfg}: lens={list(w.seq_lens)}")
+    announce(f"decode append config {cfg}: lens={list(w.seq_lens)}")
     kc, vc = dev(w.k_cache), dev(w.v_cache)
     slots = torch.full((w.S,), -7, dtype=torch.int64, device="cuda")
     pkv().decode_append(dev(w.new_k), dev(w.new_v), dev(w.block_tables), dev(w.seq_lens), kc, vc, slot_mapping=slots)
@@ -251,10 +251,10 @@ def test_fused_decode_append_bit_exact(cfg):
     assert same_bytes(host_bits(vc), vp)
 
 
-def test_fused_decode_append_skips_empty_sequences():
+def test_decode_append_skips_empty_sequences():
     lens = [5, 0, 17, 0, 1]
     w = pi.make_workload(2, seq_lens=lens)
-    announce(f"fused decode append with empty sequences {lens}")
+    announce(f"decode append with empty sequences {lens}")
     kc, vc = dev(w.k_cache), dev(w.v_cache)
     pkv().decode_append(dev(w.new_k), dev(w.new_v), dev(w.block_tables), dev(w.seq_lens), kc, vc)
     torch.cuda.synchronize()
@@ -264,3 +264,71 @@ def test_fused_decode_append_skips_empty_sequences():
     oracle.kv_append(w.new_k, w.new_v, ref_slots, kp, vp)
     assert same_bytes(host_bits(kc), kp)
     assert same_bytes(host_bits(vc), vp)
+
+
+def run_step(w, partition_tokens=None):
+    P = w.partition_tokens if partition_tokens is None else partition_tokens
+    q, kc, vc = dev(w.q), dev(w.k_cache), dev(w.v_cache)
+    bt, sl = dev(w.block_tables), dev(w.seq_lens)
+    slots = torch.full((w.S,), -7, dtype=torch.int64, device="cuda")
+    out = pkv().paged_decode_step(q, dev(w.new_k), dev(w.new_v), kc, vc, bt, sl, w.scale, slot_mapping=slots,
+                                  partition_tokens=P)
+    torch.cuda.synchronize()
+    return out, kc, vc, slots
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+def test_step_matches_oracle(cfg):
+    w = pi.make_workload(cfg, **SMALL[cfg])
+    announce(f"decode step config {cfg}: lens={list(w.seq_lens)}")
+    out, kc, vc, slots = run_step(w)
+    ref_slots, kp, vp, ref = oracle.decode_step(w)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    assert same_bytes(host_bits(kc), kp)
+    assert same_bytes(host_bits(vc), vp)
+    check_attention(w, host_f64(out), ref)
+
+
+@pytest.mark.parametrize("cfg,P", [(1, None), (2, None), (3, None), (3, 256), (4, None), (4, 0), (5, None)])
+def test_step_bit_identical_to_append_then_attention(cfg, P):
+    w = pi.make_workload(cfg, **SMALL[cfg])
+    announce(f"decode step vs separate launches, config {cfg}, P={P}")
+    out, kc, vc, slots = run_step(w, P)
+    r = Run(w, partition_tokens=P)
+    bits = torch.int16 if out.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(out.view(bits), r.out.view(bits))
+    assert torch.equal(kc.view(torch.int16), r.kc.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), r.vc.view(torch.int16))
+    assert torch.equal(slots, r.slots)
+
+
+def test_step_edge_lengths():
+    B = 16
+    lens = [1, B, B + 1, 64 * B, 0, 3, 64 * B - 1, 2 * B]
+    w = pi.make_workload(2, seq_lens=lens)
+    announce(f"decode step edge lengths {lens}")
+    out, kc, vc, slots = run_step(w)
+    ref_slots, kp, vp, ref = oracle.decode_step(w)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    assert same_bytes(host_bits(kc), kp)
+    assert same_bytes(host_bits(vc), vp)
+    got = host_f64(out)
+    assert np.all(got[4] == 0)
+    check_attention(w, got, ref)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_step_full_config(cfg):
+    w = pi.make_workload(cfg)
+    announce(f"decode step, full config {cfg}")
+    out, kc, vc, slots = run_step(w)
+    ref_slots = oracle.decode_slot_mapping(w.block_tables, w.seq_lens, w.B)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    kp, vp = w.k_cache.copy(), w.v_cache.copy()
+    oracle.kv_append(w.new_k, w.new_v, ref_slots, kp, vp)
+    assert same_bytes(host_bits(kc), kp)
+    assert same_bytes(host_bits(vc), vp)
+    units = sample_units(w, 96 if cfg == 4 else 192, 100 + cfg)
+    ref = oracle.paged_attention_units(w.q, kp, vp, w.block_tables, w.seq_lens, w.scale, units)
+    check_attention(w, host_f64(out).reshape(-1, w.hs)[units], ref)
+    assert torch.isfinite(out.float()).all().item()
