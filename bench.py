@@ -1,11 +1,12 @@
 #!/usr/bin/env python3
 """Decode-step benchmark for the paged KV-cache library on one MI355X.
 
-A step is one pass of the whole decode hot path over one batch: slot
-mapping of the new tokens and their KV append (one fused launch), then
-paged decode attention (context partitions, merged by log-sum-exp inside
-each work-group and, for sequences longer than one chunk, by a merge
-kernel).  Inputs are synthetic and
+A step is one pass of the whole decode hot path over one batch, one
+`paged_decode_step` call: slot mapping of the new tokens, their KV append
+and the batch's longest-first schedule (one launch), then paged decode
+attention (context partitions, merged by log-sum-exp inside each
+work-group and, for sequences longer than one chunk, by a merge kernel).
+Inputs are synthetic and
 resident in HBM before timing starts.
 
 Default workload: the MHA decode layer (64 sequences, 32/32 heads, head size
@@ -159,25 +160,35 @@ def main() -> int:
     P = w.partition_tokens if args.partition_tokens is None else args.partition_tokens
     copies = [device_inputs(w, torch) for _ in range(max(1, args.rotate))]
     d0 = copies[0]
+    ws_step = pkv.alloc_step_workspace(d0["q"], d0["kc"], d0["vc"], d0["bt"], P)
     ws = pkv.alloc_workspace(d0["q"], d0["kc"], d0["vc"], d0["bt"], P)
+    sched = pkv.alloc_schedule(d0["bt"])
     out = torch.empty_like(d0["q"])
     slots = torch.empty(w.S, dtype=torch.int64, device="cuda")
     stream = torch.cuda.current_stream()
     P_used = pkv.decode_partition_tokens(w.S, w.Hq, w.Hkv, w.hs, w.M, w.B, P)
     turn = [0]
 
-    def step(ev=None):
+    def step():
+        # one decode step: slot of each sequence's new token (from its block
+        # table), append of its K/V and the longest-first schedule (one
+        # launch), then the attention (plus the chunk merge where needed)
         d = copies[turn[0] % len(copies)]
         turn[0] += 1
-        # slot of each sequence's new token (from its block table) and the
-        # append of its K/V, one launch; then the attention
-        pkv.decode_append(d["nk"], d["nv"], d["bt"], d["sl"], d["kc"], d["vc"], slot_mapping=slots, stream=stream)
-        if ev is not None:
-            ev[0].record(stream)
+        pkv.paged_decode_step(d["q"], d["nk"], d["nv"], d["kc"], d["vc"], d["bt"], d["sl"], w.scale, out=out,
+                              slot_mapping=slots, workspace=ws_step, partition_tokens=P, stream=stream)
+
+    def step_timed(ev):
+        # the same step through the two entry points it is made of, with
+        # events around the attention launch
+        d = copies[turn[0] % len(copies)]
+        turn[0] += 1
+        pkv.decode_append(d["nk"], d["nv"], d["bt"], d["sl"], d["kc"], d["vc"], slot_mapping=slots, schedule=sched,
+                          stream=stream)
+        ev[0].record(stream)
         pkv.paged_decode_attention(d["q"], d["kc"], d["vc"], d["bt"], d["sl"], w.scale, out=out, workspace=ws,
-                                   partition_tokens=P, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+                                   partition_tokens=P, schedule=sched, stream=stream)
+        ev[1].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -199,7 +210,7 @@ def main() -> int:
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for e in evs:
-        step(e)
+        step_timed(e)
     torch.cuda.synchronize()
     attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
     log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, attention median {np.median(attn_ms) * 1e3:.1f} us")

@@ -54,7 +54,9 @@
  *   NULL is the default stream).  Nothing is read back to the host, so
  *   seq_lens and block_tables stay on the device.
  * - The library allocates no device memory; the caller sizes the attention
- *   workspace with pkv_decode_workspace_bytes.
+ *   workspace with pkv_decode_workspace_bytes (attention) or
+ *   pkv_decode_step_workspace_bytes (decode step), and the optional
+ *   schedule buffer with pkv_decode_schedule_bytes.
  * - Arguments that can be checked on the host are checked before any launch;
  *   a failed check returns an error status and launches nothing.
  * - Device-side contract (not checked on the host): block IDs of used table
@@ -145,6 +147,20 @@ PKV_API pkv_status kv_cache_append(const void* k, const void* v, const int64_t* 
                            void* k_cache, void* v_cache, void* stream);
 
 /*
+ * Longest-first schedule of a decode batch: a device buffer that
+ * pkv_decode_append can fill and paged_decode_attention can read.  It lists
+ * the sequences in decreasing number of blocks (ties by index), with their
+ * lengths and block-table rows in that order, so that the attention kernel
+ * starts the longest sequences first and no long one is left running alone
+ * at the end.  This is a scheduling aid of this library, not part of the
+ * method: results are bit-identical with and without it.
+ * Returns its size in bytes for these sizes (int32 order[S], lens[S], each
+ * rounded up to 16 bytes, then tables[S][max_blocks_per_seq]), or 0 when no
+ * schedule is used (num_seqs <= 1 or num_seqs > 4096).
+ */
+PKV_API size_t pkv_decode_schedule_bytes(int32_t num_seqs, int32_t max_blocks_per_seq);
+
+/*
  * Decode-step append in one launch: for each sequence s the new token sits at
  * position seq_lens[s] - 1, its slot is block_tables[s][pos / B] * B + pos % B
  * (as in pkv_decode_slot_mapping), and k[s], v[s] are stored there exactly as
@@ -154,12 +170,19 @@ PKV_API pkv_status kv_cache_append(const void* k, const void* v, const int64_t* 
  *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
  *   seq_lens      device int32 [num_seqs] (lengths including the new token)
  *   slot_mapping  device int64 [num_seqs] receiving the slots, or NULL
- * Errors: as kv_cache_append.
+ *   schedule      device buffer of schedule_bytes >= pkv_decode_schedule_bytes
+ *                 (16-byte aligned) that receives the batch's longest-first
+ *                 schedule, or NULL (ignored when that size is 0)
+ * A sequence's last block must not be shared with another sequence (the
+ * copy-on-write rule: a shared block is copied before it is written).
+ * Errors: as kv_cache_append; PKV_ERR_WORKSPACE for a schedule buffer that is
+ * too small or misaligned.
  */
 PKV_API pkv_status pkv_decode_append(const void* k, const void* v, const int32_t* block_tables,
                                      const int32_t* seq_lens, int32_t num_seqs, int32_t max_blocks_per_seq,
                                      const pkv_cache_desc* cache, void* k_cache, void* v_cache,
-                                     int64_t* slot_mapping, void* stream);
+                                     int64_t* slot_mapping, int32_t* schedule, size_t schedule_bytes,
+                                     void* stream);
 
 /*
  * Context-partition length, in tokens, that paged_decode_attention will use
@@ -197,17 +220,34 @@ PKV_API size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *   workspace     device scratch of workspace_bytes >= pkv_decode_workspace_bytes(...)
  *                 (may be NULL when that size is 0); contents are overwritten
  *   partition_tokens  0 = library's choice, else as in pkv_decode_partition_tokens
+ *   schedule      the longest-first schedule that pkv_decode_append wrote for
+ *                 these same block_tables and seq_lens (schedule_bytes as
+ *                 there), or NULL: then a batch of up to 64 sequences is
+ *                 ranked by the kernel itself and a larger one is attended
+ *                 in batch order.  A schedule that does not match the tables
+ *                 and lengths gives wrong results.
  * Calls that share a workspace must be ordered on one stream.
  * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (head_size not 64/128,
  * block_size not 16/32, num_q_heads / num_kv_heads not in 1..16 or not an
- * integer), PKV_ERR_WORKSPACE, PKV_ERR_HIP.
+ * integer), PKV_ERR_WORKSPACE (workspace or schedule too small or
+ * misaligned), PKV_ERR_HIP.
  */
 PKV_API pkv_status paged_decode_attention(const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* block_tables, const int32_t* seq_lens,
                                   int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                                   const pkv_cache_desc* cache, float scale, void* out,
                                   void* workspace, size_t workspace_bytes,
-                                  int32_t partition_tokens, void* stream);
+                                  int32_t partition_tokens, const int32_t* schedule,
+                                  size_t schedule_bytes, void* stream);
+
+/*
+ * Bytes of device workspace paged_decode_step needs: the attention's
+ * (pkv_decode_workspace_bytes), rounded up to 256, plus the longest-first
+ * schedule (pkv_decode_schedule_bytes).  Zero only when both are zero.
+ */
+PKV_API size_t pkv_decode_step_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                               int32_t head_size, int32_t max_blocks_per_seq,
+                                               int32_t block_size, int32_t partition_tokens);
 
 /*
  * One whole decode step in one call: for each sequence s, the new token
@@ -217,13 +257,17 @@ PKV_API pkv_status paged_decode_attention(const void* q, const void* k_cache, co
  * are launched in order on `stream`; the result, the pools and slot_mapping
  * are bit-identical to calling those two functions.  Every argument is
  * validated before anything is launched, so a rejected call changes nothing.
- * (A single-launch variant, where the wave reading the last block also
- * stores the new token, was measured slower on MI355X: stores issued while
- * the pools are being streamed cost more than a separate append launch.)
+ * The append launch also writes the batch's longest-first schedule into the
+ * workspace, and the attention launch reads it (see
+ * pkv_decode_schedule_bytes).  (A single-launch variant, where the wave
+ * reading the last block also stores the new token, was measured slower on
+ * MI355X: stores issued while the pools are being streamed cost more than a
+ * separate append launch.)
  *   new_k, new_v  device T [num_seqs][num_kv_heads][head_size]
  *   slot_mapping  device int64 [num_seqs] receiving the slots, or NULL
- *   other arguments as paged_decode_attention (workspace sized by
- *   pkv_decode_workspace_bytes with the same sizes)
+ *   workspace     device scratch of workspace_bytes >=
+ *                 pkv_decode_step_workspace_bytes(...), 16-byte aligned
+ *   other arguments as paged_decode_attention
  * Errors: as paged_decode_attention; new_k / new_v must be non-null and
  * 16-byte aligned.
  */

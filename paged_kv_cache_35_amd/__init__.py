@@ -66,14 +66,18 @@ def library():
         L.kv_cache_append.restype = i32
         L.kv_cache_append.argtypes = [P, P, P, i32, ctypes.POINTER(CacheDesc), P, P, P]
         L.pkv_decode_append.restype = i32
-        L.pkv_decode_append.argtypes = [P, P, P, P, i32, i32, ctypes.POINTER(CacheDesc), P, P, P, P]
+        L.pkv_decode_append.argtypes = [P, P, P, P, i32, i32, ctypes.POINTER(CacheDesc), P, P, P, P, sz, P]
+        L.pkv_decode_schedule_bytes.restype = sz
+        L.pkv_decode_schedule_bytes.argtypes = [i32, i32]
+        L.pkv_decode_step_workspace_bytes.restype = sz
+        L.pkv_decode_step_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.pkv_decode_partition_tokens.restype = i32
         L.pkv_decode_partition_tokens.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.pkv_decode_workspace_bytes.restype = sz
         L.pkv_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
         L.paged_decode_attention.restype = i32
         L.paged_decode_attention.argtypes = [P, P, P, P, P, i32, i32, i32, ctypes.POINTER(CacheDesc), f32, P, P, sz,
-                                             i32, P]
+                                             i32, P, sz, P]
         L.paged_decode_step.restype = i32
         L.paged_decode_step.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, ctypes.POINTER(CacheDesc), f32, P, P, P,
                                         sz, i32, P]
@@ -151,9 +155,11 @@ def kv_cache_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor
 
 def decode_append(k: torch.Tensor, v: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
                   k_cache: torch.Tensor, v_cache: torch.Tensor, slot_mapping: Optional[torch.Tensor] = None,
-                  stream=None) -> Optional[torch.Tensor]:
+                  schedule: Optional[torch.Tensor] = None, stream=None) -> Optional[torch.Tensor]:
     """One launch: slot of each sequence's newest token from its table, then
-    append k[s], v[s] there.  Writes the slots to slot_mapping if given."""
+    append k[s], v[s] there.  Writes the slots to slot_mapping if given, and
+    the batch's longest-first schedule to `schedule` (from alloc_schedule) if
+    given."""
     desc = cache_desc(k_cache, v_cache)
     S = k.shape[0]
     if k.shape != v.shape or tuple(k.shape[1:]) != (desc.num_kv_heads, desc.head_size):
@@ -171,7 +177,9 @@ def decode_append(k: torch.Tensor, v: torch.Tensor, block_tables: torch.Tensor, 
     _check("pkv_decode_append", library().pkv_decode_append(
         _dev(k, "k"), _dev(v, "v"), _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), S,
         block_tables.shape[1], ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
-        _dev(slot_mapping, "slot_mapping") if slot_mapping is not None else None, _stream(stream)))
+        _dev(slot_mapping, "slot_mapping") if slot_mapping is not None else None,
+        _dev(schedule, "schedule") if schedule is not None else None,
+        schedule.numel() * schedule.element_size() if schedule is not None else 0, _stream(stream)))
     return slot_mapping
 
 
@@ -198,12 +206,45 @@ def alloc_workspace(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tenso
     return torch.empty(n, dtype=torch.uint8, device=q.device)
 
 
+def schedule_bytes(num_seqs: int, max_blocks_per_seq: int) -> int:
+    return int(library().pkv_decode_schedule_bytes(num_seqs, max_blocks_per_seq))
+
+
+def alloc_schedule(block_tables: torch.Tensor) -> Optional[torch.Tensor]:
+    """Device buffer for the longest-first schedule of a batch with these
+    block tables (None when the batch takes none)."""
+    n = schedule_bytes(block_tables.shape[0], block_tables.shape[1])
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=block_tables.device)
+
+
+def step_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq, block_size,
+                         partition_tokens=0) -> int:
+    return int(library().pkv_decode_step_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size,
+                                                         max_blocks_per_seq, block_size, partition_tokens))
+
+
+def alloc_step_workspace(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         block_tables: torch.Tensor, partition_tokens: int = 0) -> Optional[torch.Tensor]:
+    desc = cache_desc(k_cache, v_cache)
+    S, Hq, _ = q.shape
+    n = step_workspace_bytes(S, Hq, desc.num_kv_heads, desc.head_size, block_tables.shape[1], desc.block_size,
+                             partition_tokens)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
 def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                            block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
                            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                           partition_tokens: int = 0, stream=None) -> torch.Tensor:
+                           partition_tokens: int = 0, schedule: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
     """out[s, h] = softmax(scale * q[s, h] K^T) V over the L = seq_lens[s]
-    tokens of sequence s, K/V found through block_tables."""
+    tokens of sequence s, K/V found through block_tables.  `schedule`: the
+    longest-first schedule decode_append wrote for these tables and lengths
+    (optional; results are the same without it)."""
     desc = cache_desc(k_cache, v_cache)
     if q.dtype != k_cache.dtype:
         raise ValueError("q must have the pools' dtype")
@@ -226,7 +267,8 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     _check("paged_decode_attention", library().paged_decode_attention(
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
         _dev(seq_lens, "seq_lens"), S, Hq, M, ctypes.byref(desc), float(scale), _dev(out, "out"), ws_ptr, ws_bytes,
-        int(partition_tokens), _stream(stream)))
+        int(partition_tokens), _dev(schedule, "schedule") if schedule is not None else None,
+        schedule.numel() * schedule.element_size() if schedule is not None else 0, _stream(stream)))
     return out
 
 
@@ -235,8 +277,10 @@ def paged_decode_step(q: torch.Tensor, new_k: torch.Tensor, new_v: torch.Tensor,
                       out: Optional[torch.Tensor] = None, slot_mapping: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, partition_tokens: int = 0,
                       stream=None) -> torch.Tensor:
-    """A whole decode step in one call: store new_k[s], new_v[s]
-    at position seq_lens[s] - 1, then attend over all seq_lens[s] tokens.
+    """A whole decode step in one call: store new_k[s], new_v[s] at position
+    seq_lens[s] - 1, then attend over all seq_lens[s] tokens.  The append
+    launch also writes the batch's longest-first schedule into the workspace
+    (see alloc_step_workspace) and the attention launch reads it.
     Bit-identical to decode_append followed by paged_decode_attention."""
     desc = cache_desc(k_cache, v_cache)
     if q.dtype != k_cache.dtype:
@@ -260,7 +304,7 @@ def paged_decode_step(q: torch.Tensor, new_k: torch.Tensor, new_v: torch.Tensor,
     if out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must match q")
     if workspace is None:
-        workspace = alloc_workspace(q, k_cache, v_cache, block_tables, partition_tokens)
+        workspace = alloc_step_workspace(q, k_cache, v_cache, block_tables, partition_tokens)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("paged_decode_step", library().paged_decode_step(

@@ -22,6 +22,17 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : 2; }
 
+size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
+
+// Longest-first schedule: int32 order [S], lens [S] (each rounded up to 16
+// bytes), tables [S][M].
+pkv::AppendArgs::Schedule schedule_parts(void* schedule, int32_t num_seqs)
+{
+    char* base = (char*)schedule;
+    const size_t vec = round_up((size_t)num_seqs * 4, 16);
+    return {(int32_t*)base, (int32_t*)(base + vec), (int32_t*)(base + 2 * vec)};
+}
+
 // Validates a pool descriptor; returns PKV_OK or the status to report.
 pkv_status check_cache(const pkv_cache_desc* c)
 {
@@ -96,9 +107,11 @@ namespace {
 
 pkv_status append_common(const void* k, const void* v, int64_t* slot_mapping, const int32_t* block_tables,
                          const int32_t* seq_lens, int32_t max_blocks_per_seq, int32_t num_tokens,
-                         const pkv_cache_desc* cache, void* k_cache, void* v_cache, void* stream)
+                         const pkv_cache_desc* cache, void* k_cache, void* v_cache, void* stream,
+                         pkv::AppendArgs::Schedule sched = {nullptr, nullptr, nullptr})
 {
     pkv::AppendArgs a;
+    a.sched = sched;
     a.k = k;
     a.v = v;
     a.slot_mapping = slot_mapping;
@@ -137,9 +150,17 @@ pkv_status kv_cache_append(const void* k, const void* v, const int64_t* slot_map
                          v_cache, stream);
 }
 
+size_t pkv_decode_schedule_bytes(int32_t num_seqs, int32_t max_blocks_per_seq)
+{
+    if (num_seqs <= 1 || num_seqs > pkv::kScheduleMaxSeqs || max_blocks_per_seq <= 0)
+        return 0;
+    return 2 * round_up((size_t)num_seqs * 4, 16) + (size_t)num_seqs * max_blocks_per_seq * 4;
+}
+
 pkv_status pkv_decode_append(const void* k, const void* v, const int32_t* block_tables, const int32_t* seq_lens,
                              int32_t num_seqs, int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
-                             void* k_cache, void* v_cache, int64_t* slot_mapping, void* stream)
+                             void* k_cache, void* v_cache, int64_t* slot_mapping, int32_t* schedule,
+                             size_t schedule_bytes, void* stream)
 {
     if (num_seqs < 0 || max_blocks_per_seq <= 0)
         return PKV_ERR_INVALID_ARG;
@@ -152,8 +173,15 @@ pkv_status pkv_decode_append(const void* k, const void* v, const int32_t* block_
         return PKV_OK;
     if (!k || !v || !block_tables || !seq_lens || !aligned16(k) || !aligned16(v))
         return PKV_ERR_INVALID_ARG;
+    pkv::AppendArgs::Schedule sched = {nullptr, nullptr, nullptr};
+    const size_t sb = pkv_decode_schedule_bytes(num_seqs, max_blocks_per_seq);
+    if (schedule && sb > 0) {
+        if (schedule_bytes < sb || !aligned16(schedule))
+            return PKV_ERR_WORKSPACE;
+        sched = schedule_parts(schedule, num_seqs);
+    }
     return append_common(k, v, slot_mapping, block_tables, seq_lens, max_blocks_per_seq, num_seqs, cache, k_cache,
-                         v_cache, stream);
+                         v_cache, stream, sched);
 }
 
 int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -179,6 +207,18 @@ size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t
     if (chunks <= 1)
         return 0;
     return (size_t)num_seqs * num_q_heads * chunks * ((size_t)head_size + 2) * sizeof(float);
+}
+
+size_t pkv_decode_step_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_size, int32_t max_blocks_per_seq, int32_t block_size,
+                                       int32_t partition_tokens)
+{
+    const size_t attn = pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size,
+                                                   max_blocks_per_seq, block_size, partition_tokens);
+    if (pkv_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq,
+                                    block_size, partition_tokens) <= 0)
+        return 0;
+    return round_up(attn, 256) + pkv_decode_schedule_bytes(num_seqs, max_blocks_per_seq);
 }
 
 namespace {
@@ -224,6 +264,9 @@ pkv_status attention_args(const void* q, const void* k_cache, const void* v_cach
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
         return PKV_ERR_WORKSPACE;
 
+    a.sched_order = nullptr;
+    a.sched_lens = nullptr;
+    a.sched_tables = nullptr;
     a.q = q;
     a.k_cache = k_cache;
     a.v_cache = v_cache;
@@ -258,7 +301,8 @@ pkv_status paged_decode_attention(const void* q, const void* k_cache, const void
                                   const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
                                   int32_t num_q_heads, int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
                                   float scale, void* out, void* workspace, size_t workspace_bytes,
-                                  int32_t partition_tokens, void* stream)
+                                  int32_t partition_tokens, const int32_t* schedule, size_t schedule_bytes,
+                                  void* stream)
 {
     pkv::DecodeArgs a;
     bool nothing_to_do;
@@ -267,6 +311,15 @@ pkv_status paged_decode_attention(const void* q, const void* k_cache, const void
                                          partition_tokens, a, nothing_to_do);
     if (st != PKV_OK || nothing_to_do)
         return st;
+    const size_t sb = pkv_decode_schedule_bytes(num_seqs, max_blocks_per_seq);
+    if (schedule && sb > 0) {
+        if (schedule_bytes < sb || !aligned16(schedule))
+            return PKV_ERR_WORKSPACE;
+        const pkv::AppendArgs::Schedule p = schedule_parts(const_cast<int32_t*>(schedule), num_seqs);
+        a.sched_order = p.order;
+        a.sched_lens = p.lens;
+        a.sched_tables = p.tables;
+    }
     return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
 }
 
@@ -287,8 +340,25 @@ pkv_status paged_decode_step(const void* q, const void* new_k, const void* new_v
         return st;
     if (!new_k || !new_v || !aligned16(new_k) || !aligned16(new_v))
         return PKV_ERR_INVALID_ARG;
+    const size_t need = pkv_decode_step_workspace_bytes(num_seqs, num_q_heads, cache->num_kv_heads,
+                                                        cache->head_size, max_blocks_per_seq, cache->block_size,
+                                                        partition_tokens);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+        return PKV_ERR_WORKSPACE;
+    // the append launch writes the longest-first schedule after the
+    // attention partials; the attention launch reads it
+    pkv::AppendArgs::Schedule sched = {nullptr, nullptr, nullptr};
+    if (pkv_decode_schedule_bytes(num_seqs, max_blocks_per_seq) > 0) {
+        const size_t attn = pkv_decode_workspace_bytes(num_seqs, num_q_heads, cache->num_kv_heads,
+                                                       cache->head_size, max_blocks_per_seq, cache->block_size,
+                                                       partition_tokens);
+        sched = schedule_parts((char*)workspace + round_up(attn, 256), num_seqs);
+        a.sched_order = sched.order;
+        a.sched_lens = sched.lens;
+        a.sched_tables = sched.tables;
+    }
     st = append_common(new_k, new_v, slot_mapping, block_tables, seq_lens, max_blocks_per_seq, num_seqs, cache,
-                       k_cache, v_cache, stream);
+                       k_cache, v_cache, stream, sched);
     if (st != PKV_OK)
         return st;
     return hip_status(pkv::launch_decode(a, (hipStream_t)stream));

@@ -39,14 +39,84 @@ __global__ void decode_slot_mapping_kernel(const int32_t* __restrict__ block_tab
 
 constexpr int kAppendThreads = 256;
 
+// Longest-first schedule of a decode batch (written by the decode step's
+// append launch, read by its attention launch): sequence i goes to rank
+//   y = #{ j : blocks(j) > blocks(i), or blocks(j) == blocks(i) and j < i },
+// a permutation of 0..S-1 (blocks = ceil(clamped length / B)).  The
+// work-group of sequence i writes order[y] = i, lens[y] = seq_lens[i] and
+// copies its block-table row to tables[y], so that an attention work-group
+// finds its sequence, length and row from y alone, with no dependent load.
+__device__ void write_schedule(int32_t i, int32_t S, const int32_t* __restrict__ seq_lens,
+                               const int32_t* __restrict__ block_tables, int32_t M, int32_t B,
+                               int32_t* __restrict__ order, int32_t* __restrict__ lens,
+                               int32_t* __restrict__ tables)
+{
+    __shared__ int sm_part[kAppendThreads / 64];
+    const int64_t cap = (int64_t)M * B;
+    auto blocks_of = [&](int32_t L) {
+        const int64_t Lc = L < 0 ? 0 : (L > cap ? cap : L);
+        return (Lc + B - 1) / B;
+    };
+    const int32_t Li = seq_lens[i];
+    const int64_t ki = blocks_of(Li);
+    int cnt = 0;
+    for (int j = threadIdx.x; j < S; j += kAppendThreads) {
+        const int64_t kj = blocks_of(seq_lens[j]);
+        cnt += (kj > ki || (kj == ki && j < i)) ? 1 : 0;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        cnt += __shfl_xor(cnt, o);
+    if ((threadIdx.x & 63) == 0)
+        sm_part[threadIdx.x >> 6] = cnt;
+    __syncthreads();
+    int y = 0;
+#pragma unroll
+    for (int k = 0; k < kAppendThreads / 64; ++k)
+        y += sm_part[k];
+    if (threadIdx.x == 0) {
+        order[y] = i;
+        lens[y] = Li;
+    }
+    const int32_t* src = block_tables + (int64_t)i * M;
+    int32_t* dst = tables + (int64_t)y * M;
+    for (int m = threadIdx.x; m < M; m += kAppendThreads)
+        dst[m] = src[m];
+}
+
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Stores 16-byte chunk ci (of the Hkv * hs / X chunks of a token) of the key
+// and value at `slot`: key chunk f of KV head h lands at
+// ((b*Hkv + h)*(hs/X) + f)*B*X + off*X, value head dims f*X .. f*X + X - 1
+// one element each at ((b*Hkv + h)*hs + d)*B + off.
+template <typename E>
+__device__ __forceinline__ void store_token(u32x4 kval, u32x4 vval, int64_t slot, int32_t ci,
+                                            u32x4* __restrict__ k_cache, E* __restrict__ v_cache,
+                                            int32_t num_kv_heads, int32_t head_size, int32_t block_size)
+{
+    constexpr int X = 16 / sizeof(E);
+    const int32_t chunks_per_head = head_size / X;
+    const int64_t b = slot / block_size;
+    const int32_t off = (int32_t)(slot - b * block_size);
+    const int32_t h = ci / chunks_per_head;
+    const int32_t f = ci - h * chunks_per_head;
+    // streaming stores: the written lines are not re-read by this kernel
+    __builtin_nontemporal_store(kval, &k_cache[((b * num_kv_heads + h) * chunks_per_head + f) * block_size + off]);
+    union {
+        u32x4 u;
+        E e[X];
+    } val;
+    val.u = vval;
+    E* vdst = v_cache + ((b * num_kv_heads + h) * head_size + (int64_t)f * X) * block_size + off;
+#pragma unroll
+    for (int e = 0; e < X; ++e)
+        __builtin_nontemporal_store(val.e[e], &vdst[(int64_t)e * block_size]);
+}
 
 // Token i = blockIdx.x; each thread moves one 16-byte chunk of the token's
 // key and one of its value (chunk ci = blockIdx.y * 256 + threadIdx.x of the
-// Hkv * hs / X chunks).  Key chunk f of KV head h holds head dims
-// [f*X, f*X + X) and lands at ((b*Hkv + h)*(hs/X) + f)*B*X + off*X; value
-// head dims are scattered one element each to ((b*Hkv + h)*hs + d)*B + off.
-// The token's data is loaded before the slot is known, so the loads overlap
+// Hkv * hs / X chunks; see store_token).  The token's data is loaded before the slot is known, so the loads overlap
 // the slot lookup.  FROM_TABLE: the slot is the decode slot of sequence i
 // (computed from block_tables / seq_lens and also written to slot_mapping);
 // otherwise it is read from slot_mapping.  A negative or out-of-range slot
@@ -58,17 +128,19 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // neighbouring bytes first) makes this kernel faster on its own, but the
 // attention launch that follows slows down by more than that gain: a decode
 // step (append, then attention) is fastest with these plain stores.
+//
+// With sched.order set (decode step), the first work-group of each sequence
+// also writes its entry of the longest-first schedule (write_schedule).
 template <typename E, bool FROM_TABLE>
 __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     const u32x4* __restrict__ k, const u32x4* __restrict__ v, int64_t* __restrict__ slot_mapping,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int32_t max_blocks_per_seq,
     u32x4* __restrict__ k_cache, E* __restrict__ v_cache, int32_t num_kv_heads, int32_t head_size,
-    int32_t block_size, int32_t num_blocks)
+    int32_t block_size, int32_t num_blocks, AppendArgs::Schedule sched)
 {
     constexpr int X = 16 / sizeof(E);
     const int32_t i = blockIdx.x;
-    const int32_t chunks_per_head = head_size / X;
-    const int32_t nchunks = num_kv_heads * chunks_per_head;
+    const int32_t nchunks = num_kv_heads * (head_size / X);
     const int32_t ci = blockIdx.y * kAppendThreads + threadIdx.x;
     const bool active = ci < nchunks;
     u32x4 kval = {0u, 0u, 0u, 0u}, vval = {0u, 0u, 0u, 0u};
@@ -84,25 +156,11 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     } else {
         slot = slot_mapping[i];
     }
-    if (slot < 0 || !active)
-        return;
-    const int64_t b = slot / block_size;
-    const int32_t off = (int32_t)(slot - b * block_size);
-    if (b >= num_blocks)
-        return;  // out-of-range slot: skipped, never written
-    const int32_t h = ci / chunks_per_head;
-    const int32_t f = ci - h * chunks_per_head;
-    // streaming stores: the written lines are not re-read by this kernel
-    __builtin_nontemporal_store(kval, &k_cache[((b * num_kv_heads + h) * chunks_per_head + f) * block_size + off]);
-    union {
-        u32x4 u;
-        E e[X];
-    } val;
-    val.u = vval;
-    E* vdst = v_cache + ((b * num_kv_heads + h) * head_size + (int64_t)f * X) * block_size + off;
-#pragma unroll
-    for (int e = 0; e < X; ++e)
-        __builtin_nontemporal_store(val.e[e], &vdst[(int64_t)e * block_size]);
+    if (slot >= 0 && active && slot / block_size < num_blocks)  // out-of-range slot: skipped, never written
+        store_token<E>(kval, vval, slot, ci, k_cache, v_cache, num_kv_heads, head_size, block_size);
+    if (FROM_TABLE && sched.order && blockIdx.y == 0)  // (uniform: the whole work-group or none)
+        write_schedule(i, gridDim.x, seq_lens, block_tables, max_blocks_per_seq, block_size, sched.order,
+                       sched.lens, sched.tables);
 }
 
 hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
@@ -125,12 +183,12 @@ static hipError_t launch_append_impl(const AppendArgs& a, hipStream_t stream)
         hipLaunchKernelGGL((kv_append_kernel<uint16_t, FROM_TABLE>), grid, block, 0, stream, (const u32x4*)a.k,
                            (const u32x4*)a.v, a.slot_mapping, a.block_tables, a.seq_lens, a.max_blocks_per_seq,
                            (u32x4*)a.k_cache, (uint16_t*)a.v_cache, a.num_kv_heads, a.head_size, a.block_size,
-                           a.num_blocks);
+                           a.num_blocks, a.sched);
     else
         hipLaunchKernelGGL((kv_append_kernel<uint32_t, FROM_TABLE>), grid, block, 0, stream, (const u32x4*)a.k,
                            (const u32x4*)a.v, a.slot_mapping, a.block_tables, a.seq_lens, a.max_blocks_per_seq,
                            (u32x4*)a.k_cache, (uint32_t*)a.v_cache, a.num_kv_heads, a.head_size, a.block_size,
-                           a.num_blocks);
+                           a.num_blocks, a.sched);
     return hipGetLastError();
 }
 

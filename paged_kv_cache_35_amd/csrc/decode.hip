@@ -255,15 +255,22 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ seq_lens, int32_t Hq, int32_t Hkv,
-    int32_t M, int32_t num_blocks, int32_t PB, int32_t max_parts, int32_t interleave, float qscale, T* __restrict__ out,
+    int32_t M, int32_t num_blocks, int32_t PB, int32_t max_parts, int32_t interleave, int32_t lpt, float qscale,
+    const int32_t* __restrict__ sched_order, const int32_t* __restrict__ sched_lens,
+    const int32_t* __restrict__ sched_tables, T* __restrict__ out,
     float* __restrict__ ws_o, float* __restrict__ ws_ml)
 {
     constexpr bool kWide = sizeof(T) == 2 && BS == 32;  // 32-token units (see WideRegs)
     constexpr int UT = kWide ? 32 : 16;                 // tokens per pipeline unit
     constexpr int PER = BS / UT;                        // units per block
     constexpr int TILE = HS * BS;                       // elements per (block, KV head) tile
+    __shared__ __attribute__((aligned(16))) float sm_out[NW][16 * HS];  // partition results, for the merge
+    __shared__ float sm_m[NW][16];
+    __shared__ float sm_l[NW][16];
+    __shared__ int sm_pick;
+    static_assert(kLptMaxSeqs <= NW * 16 * HS && kLptMaxSeqs <= 256, "the length ranking reuses the merge buffer and keeps the index in 8 bits");
+
     const int kvh = blockIdx.x;
-    const int s = blockIdx.y;
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, kept scalar
     const int chunk = blockIdx.z;                                      // NW consecutive partitions
@@ -272,7 +279,71 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     const int c = lane & 15;
     const int G = Hq / Hkv;
 
-    const int L_in = seq_lens[s];
+    // Longest sequences first.  Work-groups start roughly in blockIdx order,
+    // so a long sequence that happens to sit at the end of the batch would
+    // run alone after everything else has finished.  Instead, blockIdx.y = y
+    // takes the sequence of rank y in decreasing length (ties by index).
+    // Each sequence's result does not depend on which work-group computes it.
+    // - Decode step: its append launch has written the order, and the lengths
+    //   and table rows in that order, so y alone addresses all three.
+    // - Stand-alone call on a small batch (lpt): every work-group ranks the
+    //   batch in LDS (the merge buffer, unused until the merge) by the key
+    //   (blocks << 8) | (255 - index), distinct per sequence, and keeps the
+    //   one of rank y.  Only the first chunk of each sequence
+    //   (blockIdx.z == 0) is placed this way: a work-group of blockIdx.z > 0
+    //   learns that its sequence has no such chunk from one length load.
+    int s = blockIdx.y;
+    if (sched_order) {
+        // schedule given (decode step): rank y's sequence, length and table
+        // row are read below from y alone
+        s = sched_order[blockIdx.y];
+    } else if (lpt && chunk == 0) {
+        const int S = gridDim.y;  // <= kLptMaxSeqs = 256, M < 2^23 (checked on the host)
+        unsigned* sm_key = reinterpret_cast<unsigned*>(&sm_out[0][0]);
+        const int cap = M * BS;
+        for (int i = threadIdx.x; i < S; i += NW * 64) {
+            const int v = seq_lens[i];
+            const int Lc = v < 0 ? 0 : (v > cap ? cap : v);
+            sm_key[i] = ((unsigned)((Lc + BS - 1) / BS) << 8) | (unsigned)(255 - i);
+        }
+        __syncthreads();
+        for (int cand = threadIdx.x; cand < S; cand += NW * 64) {
+            const unsigned key = sm_key[cand];
+            int rank = 0;
+            const uint4* keys4 = reinterpret_cast<const uint4*>(sm_key);
+            for (int j4 = 0; j4 < (S + 3) / 4; ++j4) {  // keys past S are never read: S % 4 handled below
+                const uint4 k4 = keys4[j4];
+                const int j = 4 * j4;
+                rank += (k4.x > key) ? 1 : 0;
+                rank += (j + 1 < S && k4.y > key) ? 1 : 0;
+                rank += (j + 2 < S && k4.z > key) ? 1 : 0;
+                rank += (j + 3 < S && k4.w > key) ? 1 : 0;
+            }
+            if (rank == (int)blockIdx.y)
+                sm_pick = cand;
+        }
+        __syncthreads();
+        s = sm_pick;
+    }
+
+    // This wave's blocks: base, base + stride, ... (nb_w of them, <= PB).
+    // Contiguous mode: partition `part` = PB consecutive blocks.  Interleaved
+    // mode: the chunk's blocks dealt round-robin to the NW waves, which keeps
+    // the waves balanced when a sequence ends inside the chunk.  A wave with
+    // no blocks still joins the work-group merge below.
+    const int cb0 = chunk * NW * PB;
+    const int base = interleave ? cb0 + w : part * PB;
+    const int stride = interleave ? NW : 1;
+    // Physical block IDs of this wave's blocks, one per lane (<= PB <= 64);
+    // the tile loop broadcasts them with readlane.  Loaded for all PB lanes
+    // within the table row, without waiting for the sequence length, so
+    // that this load and the length load are in flight together; entries
+    // past the sequence's blocks are never used.
+    const int tb = base + lane * stride;
+    const int32_t* trow = sched_order ? sched_tables + (int64_t)blockIdx.y * M : block_tables + (int64_t)s * M;
+    const int32_t id_lane = (lane < PB && tb < M) ? trow[tb] : 0;
+
+    const int L_in = sched_order ? sched_lens[blockIdx.y] : seq_lens[s];
     const int L = L_in < 0 ? 0 : (L_in > M * BS ? M * BS : L_in);
     if (L == 0) {
         if (chunk == 0 && w == 0) {
@@ -282,34 +353,18 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
         return;
     }
     const int nblk = (L + BS - 1) / BS;
-    if (chunk * NW * PB >= nblk)
+    if (cb0 >= nblk)
         return;  // the whole work-group is past the end (uniform: before any barrier)
     const int nchunks = (nblk + NW * PB - 1) / (NW * PB);
-    // This wave's blocks: base, base + stride, ... (nb_w of them, <= PB).
-    // Contiguous mode: partition `part` = PB consecutive blocks.  Interleaved
-    // mode: the chunk's blocks dealt round-robin to the NW waves, which keeps
-    // the waves balanced when a sequence ends inside the chunk.  A wave with
-    // no blocks still joins the work-group merge below.
-    const int cb0 = chunk * NW * PB;
     const int cnb = (nblk - cb0 < NW * PB) ? nblk - cb0 : NW * PB;
-    int base, stride, nb_w;
-    if (interleave) {
-        base = cb0 + w;
-        stride = NW;
-        nb_w = cnb > w ? (cnb - w + NW - 1) / NW : 0;
-    } else {
-        base = part * PB;
-        stride = 1;
-        nb_w = base >= nblk ? 0 : ((nblk - base < PB) ? nblk - base : PB);
-    }
+    const int nb_w = interleave ? (cnb > w ? (cnb - w + NW - 1) / NW : 0)
+                                : (base >= nblk ? 0 : ((nblk - base < PB) ? nblk - base : PB));
 
     // query operand: head c of this KV head's group.  Rows c >= G of the
     // 16-row MFMA tile are padding: they repeat head c % G, and their results
     // are never stored.  (Loading real rows rather than zeroing them keeps
     // the query registers free of any use before the tile loop, so the
     // first tile's loads are issued while the query loads are in flight.)
-    // The query loads are issued before the block-table load for the same
-    // reason.
     typename Ops<T>::template QReg<HS> qr;
     {
         const T* qh = q + ((int64_t)s * Hq + (int64_t)kvh * G + c % G) * HS;
@@ -323,10 +378,6 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
                 qr.v[i] = *(const f32x4*)(qh + 16 * i + 4 * r);
         }
     }
-
-    // physical block IDs of this wave's blocks, one per lane (nb_w <= 64);
-    // the tile loop broadcasts them with readlane
-    const int32_t id_lane = lane < nb_w ? block_tables[(int64_t)s * M + base + lane * stride] : 0;
 
     f32x4 O[HS / 16];
 #pragma unroll
@@ -504,9 +555,6 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     // partial for the chunk merge kernel.
     float l_tot = l_part + __shfl_xor(l_part, 16);
     l_tot += __shfl_xor(l_tot, 32);
-    __shared__ __attribute__((aligned(16))) float sm_out[NW][16 * HS];
-    __shared__ float sm_m[NW][16];
-    __shared__ float sm_l[NW][16];
     if (r == 0) {
         sm_m[w][c] = m_run;
         sm_l[w][c] = l_tot;
@@ -690,7 +738,9 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
     hipLaunchKernelGGL((paged_decode_partition_kernel<T, HS, BS, NW>), grid, dim3(NW * 64), 0, stream,
                        (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache, a.block_tables, a.seq_lens,
                        a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq, a.num_blocks, a.partition_blocks,
-                       a.max_parts, a.interleave, a.scale * kLog2e, (T*)a.out, a.ws_o, a.ws_ml);
+                       a.max_parts, a.interleave,
+                       (a.num_seqs <= kLptMaxSeqs && a.max_blocks_per_seq < (1 << 23)) ? 1 : 0, a.scale * kLog2e,
+                       a.sched_order, a.sched_lens, a.sched_tables, (T*)a.out, a.ws_o, a.ws_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_parts <= 1)
         return e;  // one chunk per sequence: the partition kernel wrote the output

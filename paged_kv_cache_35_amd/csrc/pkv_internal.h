@@ -16,6 +16,18 @@ namespace pkv {
 #endif
 constexpr int kDecodeWaves = PKV_DECODE_WAVES;
 
+// A stand-alone attention call on up to this many sequences is scheduled
+// longest first by the attention kernel itself (each work-group ranks all
+// lengths: O(S^2 / threads) work, which outweighs the gain on larger batches).
+#ifndef PKV_LPT_MAX_SEQS
+#define PKV_LPT_MAX_SEQS 64
+#endif
+// The decode step's append launch writes a longest-first schedule for
+// batches of up to this many sequences (each of its work-groups reads all
+// lengths once).
+constexpr int kScheduleMaxSeqs = 4096;
+constexpr int kLptMaxSeqs = PKV_LPT_MAX_SEQS;
+
 // Problem description shared by the decode launchers; every field has been
 // validated on the host before a launcher sees it.
 struct DecodeArgs {
@@ -25,6 +37,12 @@ struct DecodeArgs {
     const int32_t* block_tables;
     const int32_t* seq_lens;
     void* out;
+    // Longest-first schedule written by the decode step's append launch (all
+    // null otherwise): work-group row y attends sequence order[y], whose
+    // length and table row are lens[y] and tables[y].
+    const int32_t* sched_order;
+    const int32_t* sched_lens;
+    const int32_t* sched_tables;
     float* ws_o;    // [S][Hkv][max_parts][G][hs] fp32 chunk partials, null when max_parts == 1
     float* ws_ml;   // [S][Hkv][max_parts][G][2]  fp32 (running max in log2 units, sum)
     int32_t num_seqs;
@@ -60,6 +78,13 @@ struct AppendArgs {
     int32_t block_size;
     int32_t num_blocks;
     int32_t elem_bytes;  // 2 or 4
+    // Decode step only (block_tables != null): when sched.order is non-null,
+    // the launch also writes the longest-first schedule of the batch.
+    struct Schedule {
+        int32_t* order;  // [num_tokens] sequence of rank y
+        int32_t* lens;   // [num_tokens] seq_lens[order[y]]
+        int32_t* tables; // [num_tokens][max_blocks_per_seq] block_tables[order[y]]
+    } sched;
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);

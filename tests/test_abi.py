@@ -31,7 +31,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("paged_decode_attention", "kv_cache_append", "pkv_decode_slot_mapping",
               "pkv_decode_workspace_bytes", "pkv_decode_partition_tokens", "pkv_status_string",
-              "pkv_layout_version", "pkv_last_hip_error", "paged_decode_step", "pkv_decode_append"):
+              "pkv_layout_version", "pkv_last_hip_error", "paged_decode_step", "pkv_decode_append",
+              "pkv_decode_schedule_bytes", "pkv_decode_step_workspace_bytes"):
         assert n in names
 
 
@@ -55,10 +56,10 @@ FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails
 
 
 def attn(lib, *, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, S=4, Hq=8, M=4, d=None, out=FAKE, ws=None,
-         ws_bytes=0, P=0):
+         ws_bytes=0, P=0, sched=None, sched_bytes=0):
     d = d or desc()
     return lib.paged_decode_attention(q, kc, vc, bt, sl, S, Hq, M, ctypes.byref(d), 0.125, out, ws, ws_bytes, P,
-                                      None)
+                                      sched, sched_bytes, None)
 
 
 def test_attention_rejects_bad_arguments(lib):
@@ -80,6 +81,10 @@ def test_attention_rejects_bad_arguments(lib):
     assert attn(lib, M=4096) == WORKSPACE
     need = lib.pkv_decode_workspace_bytes(4, 8, 8, 64, 4096, 16, 0)
     assert attn(lib, M=4096, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
+    # a schedule buffer that is too small or misaligned
+    need = lib.pkv_decode_schedule_bytes(4, 4)
+    assert attn(lib, sched=FAKE, sched_bytes=need - 1) == WORKSPACE
+    assert attn(lib, sched=ctypes.c_void_p(0x10004), sched_bytes=need) == WORKSPACE
     # nothing to do: valid no-op without touching the GPU
     assert attn(lib, S=0) == OK
 
@@ -97,6 +102,21 @@ def test_workspace_and_partition_sizes(lib):
     assert lib.pkv_decode_partition_tokens(8, 64, 8, 128, 4096, 32, 512) == 512
     assert lib.pkv_decode_workspace_bytes(8, 64, 8, 128, 4096, 32, 512) == 8 * 64 * 64 * 130 * 4
     assert lib.pkv_decode_partition_tokens(8, 64, 8, 128, 4096, 32, 48) == 0
+
+
+def test_schedule_and_step_workspace_sizes(lib):
+    # order[S] and lens[S], each rounded up to 16 bytes, then tables[S][M]
+    assert lib.pkv_decode_schedule_bytes(64, 128) == 2 * 256 + 64 * 128 * 4
+    assert lib.pkv_decode_schedule_bytes(5, 3) == 2 * 32 + 5 * 3 * 4
+    assert lib.pkv_decode_schedule_bytes(4096, 8) == 2 * 4096 * 4 + 4096 * 8 * 4
+    # no schedule for a single sequence or above 4096 sequences
+    assert lib.pkv_decode_schedule_bytes(1, 128) == 0
+    assert lib.pkv_decode_schedule_bytes(4097, 8) == 0
+    # step = attention partials rounded up to 256 bytes + schedule
+    assert lib.pkv_decode_step_workspace_bytes(64, 32, 32, 128, 128, 16, 0) == 2 * 256 + 64 * 128 * 4
+    attn = 64 * 32 * 8 * 130 * 4
+    assert lib.pkv_decode_step_workspace_bytes(64, 32, 32, 128, 1024, 16, 0) == attn + 2 * 256 + 64 * 1024 * 4
+    assert lib.pkv_decode_step_workspace_bytes(1, 8, 8, 64, 4, 16, 0) == 0
 
 
 def test_append_rejects_bad_arguments(lib):
@@ -143,5 +163,16 @@ def test_step_requires_the_new_token(lib):
              None, None, 0, 0, None) == INVALID
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 4096, ctypes.byref(d), 0.125, FAKE, None, None, 0, 0,
              None) == WORKSPACE
+    # a batch of 4 takes a schedule, so the step needs a workspace
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 4, ctypes.byref(d), 0.125, FAKE, None, None, 0, 0,
+             None) == WORKSPACE
     assert f(None, None, None, FAKE, FAKE, None, None, 0, 8, 4, ctypes.byref(d), 0.125, None, None, None, 0, 0,
              None) == OK
+
+
+def test_decode_append_rejects_a_small_schedule(lib):
+    d = desc()
+    f = lib.pkv_decode_append
+    need = lib.pkv_decode_schedule_bytes(4, 4)
+    assert f(FAKE, FAKE, FAKE, FAKE, 4, 4, ctypes.byref(d), FAKE, FAKE, None, FAKE, need - 1, None) == WORKSPACE
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, 4, ctypes.byref(d), FAKE, FAKE, None, FAKE, 0, None) == OK

@@ -186,6 +186,82 @@ def test_edge_lengths():
     assert r.slots.cpu().numpy()[7] == -1
 
 
+@pytest.mark.parametrize("S", [64, 65])
+def test_batch_sizes_around_the_in_kernel_ranking_limit(S):
+    # a stand-alone attention call ranks batches of up to 64 sequences itself
+    # and attends larger ones in batch order (lengths up to 2600 tokens:
+    # some sequences span two chunks)
+    w = pi.make_workload(3, S=S, len_lo=1, len_hi=2600)
+    announce(f"batch of {S} sequences, lengths {int(w.seq_lens.min())}..{int(w.seq_lens.max())}")
+    r = Run(w)
+    ref = oracle.decode_step(w)[3]
+    check_attention(w, host_f64(r.out), ref)
+
+
+def test_schedule_does_not_change_results():
+    # the same 64 sequences attended as a batch of 64 (ranked in the kernel),
+    # as the first 64 of a batch of 65 (batch order), and with the schedule
+    # written by the append launch: identical bits
+    w = pi.make_workload(3, S=64, len_lo=1, len_hi=2600)
+    announce("longest-first (in kernel, from the append) vs batch order")
+    r = Run(w)
+    m = pkv()
+    bt = torch.cat([r.bt, r.bt[:1]])
+    sl = torch.cat([r.sl, torch.zeros(1, dtype=torch.int32, device="cuda")])
+    q = torch.cat([r.q, r.q[:1]])
+    out = m.paged_decode_attention(q, r.kc, r.vc, bt, sl, w.scale)
+    sched = m.alloc_schedule(r.bt)
+    kc, vc = dev(w.k_cache), dev(w.v_cache)
+    m.decode_append(r.nk, r.nv, r.bt, r.sl, kc, vc, schedule=sched)
+    out2 = m.paged_decode_attention(r.q, kc, vc, r.bt, r.sl, w.scale, schedule=sched)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:64].view(torch.int16), r.out.view(torch.int16))
+    assert torch.all(out[64].float() == 0)
+    assert torch.equal(out2.view(torch.int16), r.out.view(torch.int16))
+
+
+def expected_schedule(block_tables, seq_lens, B):
+    """Longest-first order by blocks (ties by index), written out on the host."""
+    M = block_tables.shape[1]
+    L = np.clip(seq_lens.astype(np.int64), 0, M * B)
+    blocks = (L + B - 1) // B
+    order = sorted(range(len(L)), key=lambda i: (-int(blocks[i]), i))
+    return np.array(order, np.int32), seq_lens[order].astype(np.int32), block_tables[order].astype(np.int32)
+
+
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_schedule_contents(cfg):
+    w = pi.make_workload(cfg, **SMALL[cfg])
+    S = w.S
+    announce(f"schedule contents config {cfg}: lens={list(w.seq_lens)}")
+    m = pkv()
+    kc, vc = dev(w.k_cache), dev(w.v_cache)
+    bt, sl = dev(w.block_tables), dev(w.seq_lens)
+    sched = m.alloc_schedule(bt)
+    m.decode_append(dev(w.new_k), dev(w.new_v), bt, sl, kc, vc, schedule=sched)
+    torch.cuda.synchronize()
+    raw = sched.cpu().numpy().view(np.int32)
+    vec = -(-S * 4 // 16) * 4  # ints per rounded vector
+    order, lens, tables = expected_schedule(w.block_tables, w.seq_lens, w.B)
+    assert np.array_equal(raw[:S], order)
+    assert np.array_equal(raw[vec:vec + S], lens)
+    assert np.array_equal(raw[2 * vec:2 * vec + S * w.M].reshape(S, w.M), tables)
+
+
+@pytest.mark.parametrize("S", [4096, 4097])
+def test_step_batch_sizes_around_the_schedule_limit(S):
+    # the decode step schedules up to 4096 sequences and attends larger
+    # batches in batch order
+    w = pi.make_workload(2, S=S, len_lo=1, len_hi=40, hs=64, Hq=2, Hkv=2)
+    announce(f"decode step, batch of {S}, lengths 1..40, 2 heads of 64")
+    out, kc, vc, slots = run_step(w)
+    ref_slots, kp, vp, ref = oracle.decode_step(w)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    assert same_bytes(host_bits(kc), kp)
+    assert same_bytes(host_bits(vc), vp)
+    check_attention(w, host_f64(out), ref)
+
+
 @pytest.mark.parametrize("P", [16, 32, 256, 512, 1024])
 def test_partition_length_sweep(P):
     w = pi.make_workload(3, S=5, len_lo=16, len_hi=4000)
