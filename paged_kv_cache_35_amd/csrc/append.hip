@@ -39,6 +39,8 @@ __global__ void decode_slot_mapping_kernel(const int32_t* __restrict__ block_tab
 
 constexpr int kAppendThreads = 256;
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 // Longest-first schedule of a decode batch (written by the decode step's
 // append launch, read by its attention launch): sequence i goes to rank
 //   y = #{ j : blocks(j) > blocks(i), or blocks(j) == blocks(i) and j < i },
@@ -46,9 +48,34 @@ constexpr int kAppendThreads = 256;
 // work-group of sequence i writes order[y] = i, lens[y] = seq_lens[i] and
 // copies its block-table row to tables[y], so that an attention work-group
 // finds its sequence, length and row from y alone, with no dependent load.
-__device__ void write_schedule(int32_t i, int32_t S, const int32_t* __restrict__ seq_lens,
-                               const int32_t* __restrict__ block_tables, int32_t M, int32_t B,
-                               int32_t* __restrict__ order, int32_t* __restrict__ lens,
+//
+// The loads (every length, the row) do not depend on the rank, so they are
+// issued when the work-group starts, together with the token's loads; the
+// first kSchedRegs * 256 lengths and row entries are held in registers and
+// the rest, if any, read in a loop at the end.
+constexpr int kSchedRegs = 4;
+
+struct SchedulePrefetch {
+    int32_t len[kSchedRegs];
+    int32_t row[kSchedRegs];
+};
+
+__device__ __forceinline__ void prefetch_schedule(SchedulePrefetch& p, int32_t i, int32_t S,
+                                                  const int32_t* __restrict__ seq_lens,
+                                                  const int32_t* __restrict__ block_tables, int32_t M)
+{
+    const int32_t* src = block_tables + (int64_t)i * M;
+#pragma unroll
+    for (int t = 0; t < kSchedRegs; ++t) {
+        const int j = threadIdx.x + t * kAppendThreads;
+        p.len[t] = j < S ? seq_lens[j] : 0;
+        p.row[t] = j < M ? src[j] : 0;
+    }
+}
+
+__device__ void write_schedule(const SchedulePrefetch& p, int32_t i, int32_t S,
+                               const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_tables,
+                               int32_t M, int32_t B, int32_t* __restrict__ order, int32_t* __restrict__ lens,
                                int32_t* __restrict__ tables)
 {
     __shared__ int sm_part[kAppendThreads / 64];
@@ -60,7 +87,13 @@ __device__ void write_schedule(int32_t i, int32_t S, const int32_t* __restrict__
     const int32_t Li = seq_lens[i];
     const int64_t ki = blocks_of(Li);
     int cnt = 0;
-    for (int j = threadIdx.x; j < S; j += kAppendThreads) {
+#pragma unroll
+    for (int t = 0; t < kSchedRegs; ++t) {
+        const int j = threadIdx.x + t * kAppendThreads;
+        const int64_t kj = blocks_of(p.len[t]);
+        cnt += (j < S && (kj > ki || (kj == ki && j < i))) ? 1 : 0;
+    }
+    for (int j = threadIdx.x + kSchedRegs * kAppendThreads; j < S; j += kAppendThreads) {
         const int64_t kj = blocks_of(seq_lens[j]);
         cnt += (kj > ki || (kj == ki && j < i)) ? 1 : 0;
     }
@@ -78,13 +111,17 @@ __device__ void write_schedule(int32_t i, int32_t S, const int32_t* __restrict__
         order[y] = i;
         lens[y] = Li;
     }
-    const int32_t* src = block_tables + (int64_t)i * M;
     int32_t* dst = tables + (int64_t)y * M;
-    for (int m = threadIdx.x; m < M; m += kAppendThreads)
+#pragma unroll
+    for (int t = 0; t < kSchedRegs; ++t) {
+        const int m = threadIdx.x + t * kAppendThreads;
+        if (m < M)
+            dst[m] = p.row[t];
+    }
+    const int32_t* src = block_tables + (int64_t)i * M;
+    for (int m = threadIdx.x + kSchedRegs * kAppendThreads; m < M; m += kAppendThreads)
         dst[m] = src[m];
 }
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Stores 16-byte chunk ci (of the Hkv * hs / X chunks of a token) of the key
 // and value at `slot`: key chunk f of KV head h lands at
@@ -143,6 +180,10 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     const int32_t nchunks = num_kv_heads * (head_size / X);
     const int32_t ci = blockIdx.y * kAppendThreads + threadIdx.x;
     const bool active = ci < nchunks;
+    const bool sched_wg = FROM_TABLE && sched.order && blockIdx.y == 0;  // uniform per work-group
+    SchedulePrefetch pre;
+    if (sched_wg)
+        prefetch_schedule(pre, i, gridDim.x, seq_lens, block_tables, max_blocks_per_seq);
     u32x4 kval = {0u, 0u, 0u, 0u}, vval = {0u, 0u, 0u, 0u};
     if (active) {
         kval = k[(int64_t)i * nchunks + ci];
@@ -158,8 +199,8 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     }
     if (slot >= 0 && active && slot / block_size < num_blocks)  // out-of-range slot: skipped, never written
         store_token<E>(kval, vval, slot, ci, k_cache, v_cache, num_kv_heads, head_size, block_size);
-    if (FROM_TABLE && sched.order && blockIdx.y == 0)  // (uniform: the whole work-group or none)
-        write_schedule(i, gridDim.x, seq_lens, block_tables, max_blocks_per_seq, block_size, sched.order,
+    if (sched_wg)
+        write_schedule(pre, i, gridDim.x, seq_lens, block_tables, max_blocks_per_seq, block_size, sched.order,
                        sched.lens, sched.tables);
 }
 

@@ -106,10 +106,37 @@ struct WideRegs {
     bf16x8 v[HS / 16];
 };
 
-// Key row c of M-tile mp of a 32-token unit holds token
-// 8*(c/4) + 4*mp + c%4, so that the score layout of the two M-tiles gives
-// lane group r the tokens 8r .. 8r+7 (the value MFMA's reduction order).
-__device__ __forceinline__ int wide_token(int mp, int c) { return 8 * (c >> 2) + 4 * mp + (c & 3); }
+// Key row c of M-tile mp of a 32-token unit holds token 16*mp + c, so each
+// key load reads 16 consecutive 16-byte chunks (256 contiguous bytes per
+// lane group: whole 128-byte lines for the streaming loads).  The score
+// layout then gives lane group r tokens 4r .. 4r+3 (M-tile 0) and
+// 16+4r .. 16+4r+3 (M-tile 1), while the value MFMA wants tokens
+// 8r .. 8r+7 in lane group r; to_value_order moves the probabilities there.
+//
+// With X_r / Y_r the four values of lane group r from M-tile 0 / 1, lane
+// group r needs (X_{2r}, X_{2r+1}) for r < 2 and (Y_{2r-4}, Y_{2r-3}) for
+// r >= 2.  v_permlane32_swap exchanges lane groups 2,3 of its first operand
+// with groups 0,1 of its second: (X0 X1 Y0 Y1), (X2 X3 Y2 Y3).
+// v_permlane16_swap exchanges odd groups of the first with even groups of
+// the second: (X0 X2 Y0 Y2), (X1 X3 Y1 Y3) -- the first and second four
+// tokens of each lane group.
+//
+// Written as inline assembly because the compiler at hand, given the two
+// swap builtins chained, keeps only the first result of the second swap
+// (the second comes back as a copy of the first).  Both registers are read
+// and written in place; the s_nop 1 before each swap gives the two wait
+// states the swaps need after a vector write of their operands, and the one
+// after covers a read of their results.
+__device__ __forceinline__ void to_value_order(float& x, float& y)
+{
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_permlane32_swap_b32 %0, %1\n\t"
+        "s_nop 1\n\t"
+        "v_permlane16_swap_b32 %0, %1\n\t"
+        "s_nop 1"
+        : "+v"(x), "+v"(y));
+}
 
 __device__ __forceinline__ void store_elem(__bf16* p, float x) { *p = (__bf16)x; }
 __device__ __forceinline__ void store_elem(float* p, float x) { *p = x; }
@@ -176,7 +203,7 @@ __device__ __forceinline__ void load_wide(WideRegs<HS>& t, const __bf16* __restr
     for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
         for (int i = 0; i < HS / 32; ++i)
-            t.k[mp].v[i] = load_stream((const bf16x8*)(tile_k + ((4 * i + r) * 32 + wide_token(mp, c)) * 8));
+            t.k[mp].v[i] = load_stream((const bf16x8*)(tile_k + ((4 * i + r) * 32 + 16 * mp + c) * 8));
 #pragma unroll
     for (int i = 0; i < HS / 16; ++i)  // head dim 16i + c, tokens 8r .. 8r+7
         t.v[i] = load_stream((const bf16x8*)(tile_v + (16 * i + c) * 32 + 8 * r));
@@ -454,7 +481,8 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     };
 
     // One 32-token unit (bf16, B = 32): element jj of M-tile mp's scores is
-    // token 8r + 4mp + jj; value element e of a lane is token 8r + e.
+    // token 16mp + 4r + jj; value element e of a lane is token 8r + e (the
+    // probabilities are moved to that order by to_value_order).
     auto compute_wide = [&](WideRegs<HS>& t, int tok0, bool ok) __attribute__((always_inline)) {
         if constexpr (kWide) {
             const int Lt = ok ? L : tok0;
@@ -468,7 +496,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
                 for (int jj = 0; jj < 4; ++jj) {
                     float v = S[jj] * qscale;
                     if (partial)
-                        v = (tok0 + 8 * r + 4 * mp + jj < Lt) ? v : -INFINITY;
+                        v = (tok0 + 16 * mp + 4 * r + jj < Lt) ? v : -INFINITY;
                     sc[4 * mp + jj] = v;
                     mx = fmaxf(mx, v);
                 }
@@ -483,14 +511,21 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
                 }
             }
             update_max(mx);
+            float pv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pv[e] = __builtin_amdgcn_exp2f(sc[e] - m_run);
+                l_part += pv[e];
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                to_value_order(pv[jj], pv[4 + jj]);  // pv[e] is now token 8r + e
             bf16x8 hi, lo;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float pe = __builtin_amdgcn_exp2f(sc[e] - m_run);
-                l_part += pe;
-                const __bf16 hb = (__bf16)pe;
+                const __bf16 hb = (__bf16)pv[e];
                 hi[e] = hb;
-                lo[e] = (__bf16)(pe - (float)hb);
+                lo[e] = (__bf16)(pv[e] - (float)hb);
             }
 #pragma unroll
             for (int i = 0; i < HS / 16; ++i) {
