@@ -35,6 +35,11 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 
+# counter records (rocprofv3 FETCH_SIZE / WRITE_SIZE of the attention launch) per configuration
+TRAFFIC_RECORDS = {2: "traffic_paged_decode_attention_mha_bf16.txt",
+                   3: "traffic_paged_decode_attention_gqa_bf16.txt",
+                   4: "traffic_paged_decode_attention_long_context_bf16.txt"}
+
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -55,10 +60,10 @@ def parse():
                     help="diagnostic: each sequence's blocks adjacent in the pool (paged vs contiguous storage)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
-    ap.add_argument("--traffic", type=str,
-                    default=os.path.join(ROOT, "profiles", "traffic_paged_decode_partition_kernel_mha_bf16.txt"),
+    ap.add_argument("--traffic", type=str, default=None,
                     help="record of measured HBM bytes per attention launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, "
-                         "calibrated); used only when its workload and kernel-source hash match this run")
+                         "calibrated; default: the configuration's record under profiles/); used only when its "
+                         "workload and kernel-source hash match this run")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 20 device-to-device copies of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -218,12 +223,15 @@ def main() -> int:
     kv_bytes = w.kv_read_bytes()
     attn_avg_s = float(attn_ms.mean()) / 1e3
     achieved = kv_bytes / attn_avg_s / 1e9
-    traffic = measured_traffic(args.traffic, args.config, P_used, args.contiguous)
+    traffic_path = args.traffic or os.path.join(ROOT, "profiles", TRAFFIC_RECORDS.get(args.config, ""))
+    traffic = measured_traffic(traffic_path, args.config, P_used, args.contiguous)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": ("paged_decode_partition_kernel (the whole attention call: one chunk per sequence, "
-                           "no merge launch)" if ws is None else
-                           "paged_decode_attention: partition kernel + chunk merge kernel"),
+                "kernel": ("paged_decode_attention with the step's longest-first schedule: "
+                           "paged_decode_partition_kernel alone (one chunk per sequence, no merge launch)"
+                           if ws is None else
+                           "paged_decode_attention with the step's longest-first schedule: partition kernel + "
+                           "chunk merge kernel"),
                 "algorithmic_bytes_per_launch": kv_bytes,
                 "launch_us": {"mean": round(attn_avg_s * 1e6, 2), "median": round(float(np.median(attn_ms)) * 1e3, 2),
                               "p10": round(float(np.percentile(attn_ms, 10)) * 1e3, 2),
