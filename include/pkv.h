@@ -90,7 +90,8 @@ typedef enum {
     PKV_ERR_INVALID_ARG = -1,  /* null pointer, bad size, misaligned pointer */
     PKV_ERR_UNSUPPORTED = -2,  /* a shape or type this build has no kernel for */
     PKV_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required */
-    PKV_ERR_HIP = -4           /* a HIP launch failed; see pkv_last_hip_error */
+    PKV_ERR_HIP = -4,          /* a HIP launch failed; see pkv_last_hip_error */
+    PKV_ERR_OUT_OF_BLOCKS = -5 /* the block pool has no free block left */
 } pkv_status;
 
 typedef enum {
@@ -277,6 +278,100 @@ PKV_API pkv_status paged_decode_step(const void* q, const void* new_k, const voi
                                      const pkv_cache_desc* cache, float scale, void* out,
                                      int64_t* slot_mapping, void* workspace, size_t workspace_bytes,
                                      int32_t partition_tokens, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Block copy and the host block pool (copy-on-write and fork)
+ * ---------------------------------------------------------------------------
+ */
+
+/*
+ * Block copy ("PagedAttention 笔记" page, copy-on-write section: "copy P8 ->
+ * P11" before the writer's token goes into P11): for each pair
+ * (src, dst) = (pairs[2i], pairs[2i+1]), every element of block src of both
+ * pools (all KV heads, all slots) is copied to block dst, bit for bit.
+ *   pairs      device int32 [num_pairs][2]
+ *   k_cache, v_cache  device pools (layout above)
+ * Device-side contract (not checked on the host): the dst blocks of one call
+ * are distinct and none of them is also a src of the call; a pair with a
+ * block outside [0, num_blocks) is skipped.
+ * Errors: PKV_ERR_INVALID_ARG (null or misaligned pointer, bad descriptor,
+ * num_pairs < 0), PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.
+ */
+PKV_API pkv_status pkv_copy_blocks(const int32_t* pairs, int32_t num_pairs, const pkv_cache_desc* cache,
+                                   void* k_cache, void* v_cache, void* stream);
+
+/*
+ * Host block pool: the bookkeeping of the block allocator of the
+ * "vLLM 核心工程深度剖析" page (section 2.2: a free list used as a stack,
+ * one reference count per block and one block table per sequence; a new
+ * block only when the sequence's last block is full; blocks return to the
+ * free list when their count reaches zero; running out is an error), its
+ * fork (section 4.1: the child shares every block of the parent, one more
+ * reference each) and the copy-on-write rule of the "PagedAttention 笔记"
+ * page (a block referenced by more than one sequence is never written: the
+ * writer takes a new block, the shared block is copied into it with
+ * pkv_copy_blocks, the writer's table entry points at the copy and the
+ * shared block loses a reference).
+ * Host memory only; the pool touches no device memory.  One pool must not be
+ * used from two threads at once.  Sequences are named by caller-chosen
+ * 64-bit ids.
+ */
+typedef struct pkv_block_pool pkv_block_pool;
+
+/* A pool of num_blocks blocks of block_size tokens, all free; the free list
+ * is 0 .. num_blocks-1 and its last entry is handed out first.  NULL for
+ * non-positive sizes or when host memory runs out. */
+PKV_API pkv_block_pool* pkv_pool_create(int32_t num_blocks, int32_t block_size);
+
+/* As pkv_pool_create, with the free list given (count distinct blocks in
+ * [0, num_blocks); the last one is handed out first; blocks not listed are
+ * never handed out).  NULL for an invalid list. */
+PKV_API pkv_block_pool* pkv_pool_create_with_free_list(int32_t num_blocks, int32_t block_size,
+                                                       const int32_t* free_list, int32_t count);
+
+PKV_API void pkv_pool_destroy(pkv_block_pool* pool);
+
+/* A new sequence holding num_tokens tokens: ceil(num_tokens / block_size)
+ * blocks from the free list, in table order.  PKV_ERR_OUT_OF_BLOCKS when the
+ * free list is too short (nothing changes); PKV_ERR_INVALID_ARG for a known
+ * id or a negative count. */
+PKV_API pkv_status pkv_pool_add_sequence(pkv_block_pool* pool, int64_t seq, int64_t num_tokens);
+
+/* Reserves the slot of the next token of each of num_seqs distinct
+ * sequences (position L = the sequence's length, which becomes L + 1) and
+ * returns it in slots[i] = table[L / B] * B + L % B.  A full last block gets
+ * a new block after it; a shared last block is replaced by a new one, and
+ * the pair (shared, new) that pkv_copy_blocks must copy before the token is
+ * written is appended to copies (host int32 [num_seqs][2], *num_copies
+ * pairs).  Everything is checked first: PKV_ERR_OUT_OF_BLOCKS or
+ * PKV_ERR_INVALID_ARG (unknown or repeated id) leave the pool unchanged. */
+PKV_API pkv_status pkv_pool_append_slots(pkv_block_pool* pool, const int64_t* seqs, int32_t num_seqs,
+                                         int64_t* slots, int32_t* copies, int32_t* num_copies);
+
+/* The child (a new id) gets the parent's table and length; every block gains
+ * a reference. */
+PKV_API pkv_status pkv_pool_fork(pkv_block_pool* pool, int64_t parent, int64_t child);
+
+/* Drops one reference on each block of the sequence (in table order) and
+ * returns blocks whose count reaches zero to the end of the free list. */
+PKV_API pkv_status pkv_pool_free(pkv_block_pool* pool, int64_t seq);
+
+/* Queries: free blocks; a block's reference count (-1 if out of range); a
+ * sequence's length (-1 if unknown); a sequence's table (returns its number
+ * of blocks, -1 if unknown, and copies at most capacity entries to out). */
+PKV_API int32_t pkv_pool_num_free(const pkv_block_pool* pool);
+PKV_API int32_t pkv_pool_ref_count(const pkv_block_pool* pool, int32_t block);
+PKV_API int64_t pkv_pool_seq_len(const pkv_block_pool* pool, int64_t seq);
+PKV_API int32_t pkv_pool_block_table(const pkv_block_pool* pool, int64_t seq, int32_t* out, int32_t capacity);
+
+/* Writes the kernel inputs for a batch: block_tables (host int32
+ * [num_seqs][max_blocks_per_seq], padded with pad_block) and seq_lens (host
+ * int32 [num_seqs]).  PKV_ERR_INVALID_ARG for an unknown id or a table longer
+ * than max_blocks_per_seq (nothing is written then). */
+PKV_API pkv_status pkv_pool_export(const pkv_block_pool* pool, const int64_t* seqs, int32_t num_seqs,
+                                   int32_t max_blocks_per_seq, int32_t pad_block, int32_t* block_tables,
+                                   int32_t* seq_lens);
 
 #ifdef __cplusplus
 }

@@ -22,6 +22,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libpkv.so")
 
 PKV_OK = 0
+PKV_ERR_OUT_OF_BLOCKS = -5
 PKV_F32 = 0
 PKV_BF16 = 1
 
@@ -81,6 +82,32 @@ def library():
         L.paged_decode_step.restype = i32
         L.paged_decode_step.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, ctypes.POINTER(CacheDesc), f32, P, P, P,
                                         sz, i32, P]
+        L.pkv_copy_blocks.restype = i32
+        L.pkv_copy_blocks.argtypes = [P, i32, ctypes.POINTER(CacheDesc), P, P, P]
+        L.pkv_pool_create.restype = P
+        L.pkv_pool_create.argtypes = [i32, i32]
+        L.pkv_pool_create_with_free_list.restype = P
+        L.pkv_pool_create_with_free_list.argtypes = [i32, i32, P, i32]
+        L.pkv_pool_destroy.restype = None
+        L.pkv_pool_destroy.argtypes = [P]
+        L.pkv_pool_add_sequence.restype = i32
+        L.pkv_pool_add_sequence.argtypes = [P, i64, i64]
+        L.pkv_pool_append_slots.restype = i32
+        L.pkv_pool_append_slots.argtypes = [P, P, i32, P, P, P]
+        L.pkv_pool_fork.restype = i32
+        L.pkv_pool_fork.argtypes = [P, i64, i64]
+        L.pkv_pool_free.restype = i32
+        L.pkv_pool_free.argtypes = [P, i64]
+        L.pkv_pool_num_free.restype = i32
+        L.pkv_pool_num_free.argtypes = [P]
+        L.pkv_pool_ref_count.restype = i32
+        L.pkv_pool_ref_count.argtypes = [P, i32]
+        L.pkv_pool_seq_len.restype = i64
+        L.pkv_pool_seq_len.argtypes = [P, i64]
+        L.pkv_pool_block_table.restype = i32
+        L.pkv_pool_block_table.argtypes = [P, i64, P, i32]
+        L.pkv_pool_export.restype = i32
+        L.pkv_pool_export.argtypes = [P, P, i32, i32, i32, P, P]
         _lib = L
     return _lib
 
@@ -321,3 +348,107 @@ def decode_step(q, k_cache, v_cache, block_tables, seq_lens, new_k, new_v, scale
     return paged_decode_step(q, new_k, new_v, k_cache, v_cache, block_tables, seq_lens, scale, out=out,
                              slot_mapping=slot_mapping, workspace=workspace, partition_tokens=partition_tokens,
                              stream=stream)
+
+
+def copy_blocks(pairs: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:
+    """Copy whole blocks (every KV head, both pools): pairs is a device int32
+    [n, 2] tensor of (src, dst) block ids; the dst blocks must be distinct
+    and must not be sources of the same call."""
+    desc = cache_desc(k_cache, v_cache)
+    if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int32 [n, 2]")
+    n = pairs.shape[0]
+    if n == 0:
+        return
+    _check("pkv_copy_blocks", library().pkv_copy_blocks(_dev(pairs.contiguous(), "pairs"), n, ctypes.byref(desc),
+                                                        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                                        _stream(stream)))
+
+
+class OutOfBlocks(RuntimeError):
+    """The block pool has no free block left (nothing was changed)."""
+
+
+class BlockPool:
+    """Host block pool of the library (native code): free list, reference
+    counts, block tables, fork and copy-on-write.  Sequence ids are ints."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_list=None):
+        L = library()
+        if free_list is None:
+            h = L.pkv_pool_create(num_blocks, block_size)
+        else:
+            arr = (ctypes.c_int32 * len(free_list))(*free_list)
+            h = L.pkv_pool_create_with_free_list(num_blocks, block_size, ctypes.cast(arr, ctypes.c_void_p),
+                                                 len(free_list))
+        if not h:
+            raise ValueError("invalid pool arguments")
+        self._h = ctypes.c_void_p(h)
+        self._lib = L
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.pkv_pool_destroy(h)
+            self._h = None
+
+    def _st(self, func: str, status: int) -> None:
+        if status == PKV_ERR_OUT_OF_BLOCKS:
+            raise OutOfBlocks(func)
+        _check(func, status)
+
+    def add_sequence(self, seq: int, num_tokens: int) -> None:
+        self._st("pkv_pool_add_sequence", self._lib.pkv_pool_add_sequence(self._h, seq, num_tokens))
+
+    def append_slots(self, seqs):
+        """Reserve the next slot of each sequence.  Returns (slots, copies):
+        a list of slots and a list of (src, dst) block copies to do first."""
+        n = len(seqs)
+        ids = (ctypes.c_int64 * max(n, 1))(*seqs)
+        slots = (ctypes.c_int64 * max(n, 1))()
+        copies = (ctypes.c_int32 * max(2 * n, 1))()
+        nc = ctypes.c_int32(0)
+        self._st("pkv_pool_append_slots", self._lib.pkv_pool_append_slots(
+            self._h, ctypes.cast(ids, ctypes.c_void_p), n, ctypes.cast(slots, ctypes.c_void_p),
+            ctypes.cast(copies, ctypes.c_void_p), ctypes.byref(nc)))
+        return list(slots[:n]), [(copies[2 * i], copies[2 * i + 1]) for i in range(nc.value)]
+
+    def append_slot(self, seq: int):
+        slots, copies = self.append_slots([seq])
+        return slots[0], (copies[0] if copies else None)
+
+    def fork(self, parent: int, child: int) -> None:
+        self._st("pkv_pool_fork", self._lib.pkv_pool_fork(self._h, parent, child))
+
+    def free(self, seq: int) -> None:
+        self._st("pkv_pool_free", self._lib.pkv_pool_free(self._h, seq))
+
+    def num_free(self) -> int:
+        return self._lib.pkv_pool_num_free(self._h)
+
+    def ref_count(self, block: int) -> int:
+        return self._lib.pkv_pool_ref_count(self._h, block)
+
+    def seq_len(self, seq: int) -> int:
+        return self._lib.pkv_pool_seq_len(self._h, seq)
+
+    def table(self, seq: int):
+        n = self._lib.pkv_pool_block_table(self._h, seq, None, 0)
+        if n < 0:
+            raise KeyError(seq)
+        buf = (ctypes.c_int32 * max(n, 1))()
+        self._lib.pkv_pool_block_table(self._h, seq, ctypes.cast(buf, ctypes.c_void_p), n)
+        return list(buf[:n])
+
+    def export(self, seqs, max_blocks_per_seq: int, pad_block: int = 0):
+        """(block_tables int32 [S, M], seq_lens int32 [S]) as host tensors."""
+        n = len(seqs)
+        ids = (ctypes.c_int64 * max(n, 1))(*seqs)
+        bt = torch.empty((n, max_blocks_per_seq), dtype=torch.int32)
+        sl = torch.empty((n,), dtype=torch.int32)
+        _check("pkv_pool_export", self._lib.pkv_pool_export(
+            self._h, ctypes.cast(ids, ctypes.c_void_p), n, max_blocks_per_seq, pad_block, bt.data_ptr(),
+            sl.data_ptr()))
+        return bt, sl

@@ -1,7 +1,8 @@
 """Builds libpkv.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-Each .hip source under csrc/ is compiled to an object file in _build/ and
-the objects are linked into paged_kv_cache_35_amd/libpkv.so.  All device code
+Each source under csrc/ (the .hip kernels and the C ABI, and the host block
+pool in pool.cpp) is compiled to an object file in _build/ and the objects
+are linked into paged_kv_cache_35_amd/libpkv.so.  All device code
 is compiled with packed-fp32 instructions disabled.
 """
 from __future__ import annotations
@@ -18,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "append.hip", "decode.hip"]
+SOURCES = ["api.hip", "append.hip", "decode.hip", "copy.hip", "pool.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

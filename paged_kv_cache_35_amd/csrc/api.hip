@@ -83,6 +83,7 @@ const char* pkv_status_string(int32_t status)
     case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
     case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
     case PKV_ERR_HIP: return "PKV_ERR_HIP";
+    case PKV_ERR_OUT_OF_BLOCKS: return "PKV_ERR_OUT_OF_BLOCKS";
     default: return "PKV_UNKNOWN_STATUS";
     }
 }
@@ -362,6 +363,28 @@ pkv_status paged_decode_step(const void* q, const void* new_k, const void* new_v
     if (st != PKV_OK)
         return st;
     return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+}
+
+pkv_status pkv_copy_blocks(const int32_t* pairs, int32_t num_pairs, const pkv_cache_desc* cache, void* k_cache,
+                           void* v_cache, void* stream)
+{
+    if (num_pairs < 0)
+        return PKV_ERR_INVALID_ARG;
+    const pkv_status st = check_cache(cache);
+    if (st != PKV_OK)
+        return st;
+    if (!k_cache || !v_cache || !aligned16(k_cache) || !aligned16(v_cache))
+        return PKV_ERR_INVALID_ARG;
+    if (num_pairs == 0)
+        return PKV_OK;
+    if (!pairs)
+        return PKV_ERR_INVALID_ARG;
+    if (num_pairs > INT32_MAX / 2)
+        return PKV_ERR_UNSUPPORTED;
+    const int64_t block_bytes =
+        (int64_t)cache->num_kv_heads * cache->block_size * cache->head_size * elem_bytes(cache->dtype);
+    return hip_status(pkv::launch_copy_blocks(pairs, num_pairs, cache->num_blocks, block_bytes, k_cache, v_cache,
+                                              (hipStream_t)stream));
 }
 
 }  // extern "C"

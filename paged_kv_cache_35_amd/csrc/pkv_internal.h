@@ -89,6 +89,10 @@ struct AppendArgs {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 
+// Copies whole blocks (block_bytes per pool) for num_pairs (src, dst) pairs.
+hipError_t launch_copy_blocks(const int32_t* pairs, int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,
+                              void* k_cache, void* v_cache, hipStream_t stream);
+
 hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
                                int32_t max_blocks_per_seq, int32_t block_size, int64_t* slot_mapping,
                                hipStream_t stream);
