@@ -64,6 +64,9 @@ def parse():
                     help="record of measured HBM bytes per attention launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, "
                          "calibrated; default: the configuration's record under profiles/); used only when its "
                          "workload and kernel-source hash match this run")
+    ap.add_argument("--copy-blocks", type=int, default=0, metavar="PAIRS",
+                    help="instead of the decode step, time pkv_copy_blocks (copy-on-write) of PAIRS random block "
+                         "pairs in the configuration's pools and print its own JSON line")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 20 device-to-device copies of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -90,6 +93,51 @@ def calib_copy(mib: int) -> None:
         dst.copy_(src)
     torch.cuda.synchronize()
     print(json.dumps({"calib_copy_bytes": n, "launches": 20}))
+
+
+def bench_copy_blocks(args, w, torch, pkv) -> dict:
+    """pkv_copy_blocks of args.copy_blocks (src, dst) pairs (distinct dsts, none a src) drawn from the pool:
+    algorithmic bytes per launch = pairs x 2 pools x block bytes x 2 (read and write)."""
+    copies = [device_inputs(w, torch) for _ in range(max(1, args.rotate))]
+    n = args.copy_blocks
+    if 2 * n > w.num_blocks:
+        raise SystemExit(f"--copy-blocks {n}: the pool has only {w.num_blocks} blocks")
+    perm = np.random.default_rng(12345).permutation(w.num_blocks)
+    pairs = torch.tensor(np.stack([perm[:n], perm[n:2 * n]], axis=1).astype(np.int32), device="cuda")
+    stream = torch.cuda.current_stream()
+    elem = 4 if w.dtype == "f32" else 2
+    block_bytes = w.Hkv * w.B * w.hs * elem
+    moved = n * 2 * block_bytes * 2
+    turn = [0]
+
+    def once():
+        d = copies[turn[0] % len(copies)]
+        turn[0] += 1
+        pkv.copy_blocks(pairs, d["kc"], d["vc"], stream=stream)
+
+    for _ in range(args.warmup):
+        once()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record(stream)
+        once()
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    t = float(ms.mean()) / 1e3
+    gbps = moved / t / 1e9
+    return {"metric": "block copy GB/s (bytes read + written by pkv_copy_blocks)", "value": round(gbps, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(t * 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32" if w.dtype == "f32" else "bf16", "data": "synthetic",
+            "config": {"workload": f"block copy in the pool of: {w.description}", "pairs": n,
+                       "block_bytes_per_pool": block_bytes},
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "kernel": "copy_blocks_kernel", "algorithmic_bytes_per_launch": moved,
+                         "launch_us": {"mean": round(t * 1e6, 2), "median": round(float(np.median(ms)) * 1e3, 2)}},
+            "cpu_baseline": None}
 
 
 def kernel_sources_sha256(paths) -> str:
@@ -162,6 +210,9 @@ def main() -> int:
     t0 = time.perf_counter()
     w = pi.make_workload(args.config, mode="timing", contiguous=args.contiguous)
     log(f"generated config {args.config} ({w.description}) in {time.perf_counter() - t0:.1f} s")
+    if args.copy_blocks:
+        print(json.dumps(bench_copy_blocks(args, w, torch, pkv)), flush=True)
+        return 0
     P = w.partition_tokens if args.partition_tokens is None else args.partition_tokens
     copies = [device_inputs(w, torch) for _ in range(max(1, args.rotate))]
     d0 = copies[0]
