@@ -22,6 +22,7 @@ _LIB = os.path.join(_HERE, "liborc.so")
 
 ORC_F32 = 0
 ORC_BF16 = 1
+ORC_FP8 = 2
 
 
 def build(force: bool = True) -> str:
@@ -61,6 +62,17 @@ def _bind(path: str):
                                             ctypes.c_int]
     L.orc_max_threads.restype = ctypes.c_int
     L.orc_max_threads.argtypes = []
+    L.orc_fp8_decode.restype = f64
+    L.orc_fp8_decode.argtypes = [ctypes.c_uint8]
+    L.orc_fp8_encode.restype = ctypes.c_uint8
+    L.orc_fp8_encode.argtypes = [ctypes.c_float]
+    L.orc_fp8_quantize.restype = None
+    L.orc_fp8_quantize.argtypes = [P, i64, i32, ctypes.c_float, P]
+    L.orc_kv_append_fp8.restype = None
+    L.orc_kv_append_fp8.argtypes = [P, P, P, i32, i32, i32, i32, i32, ctypes.c_float, ctypes.c_float, P, P]
+    L.orc_paged_attention_units_kv.restype = ctypes.c_int
+    L.orc_paged_attention_units_kv.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f64, f64,
+                                               f64, P, i64, P, ctypes.c_int]
     return L
 
 
@@ -220,3 +232,62 @@ def decode_step(w, threads=0, return_threads=False):
         out, n = r
         return slots, kp, vp, out, n
     return slots, kp, vp, r
+
+
+# ---- FP8 (E4M3) cache elements ---------------------------------------------
+# Reading (the pages fix no format or scale): OCP E4M3 codes, one scale per
+# pool; a value x is stored as the code nearest to fp32(x * inv_scale) (ties to
+# the even mantissa, magnitudes above 448 saturate) and read as value * scale.
+
+def fp8_decode(code: int) -> float:
+    return float(lib().orc_fp8_decode(int(code)))
+
+
+def fp8_encode(v: float) -> int:
+    return int(lib().orc_fp8_encode(float(v)))
+
+
+def fp8_quantize(x: np.ndarray, inv_scale: float) -> np.ndarray:
+    """uint8 codes of fp32 or bf16-bit (uint16) values times inv_scale."""
+    x = np.ascontiguousarray(x)
+    out = np.empty(x.shape, dtype=np.uint8)
+    lib().orc_fp8_quantize(_ptr(x), x.size, _dtype_code(x), float(np.float32(inv_scale)), _ptr(out))
+    return out
+
+
+def kv_append_fp8(k: np.ndarray, v: np.ndarray, slots: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+                  k_inv_scale: float, v_inv_scale: float) -> None:
+    """In place: quantize token i's K/V ([T, Hkv, hs], fp32 or bf16 bits) into
+    slot slots[i] of uint8 pools (key [nb, Hkv, hs/16, B, 16], value
+    [nb, Hkv, hs, B])."""
+    T, Hkv, hs = k.shape
+    B = v_pool.shape[-1]
+    assert k_pool.dtype == v_pool.dtype == np.uint8 and k.dtype == v.dtype
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    s = np.ascontiguousarray(slots, dtype=np.int64)
+    lib().orc_kv_append_fp8(_ptr(k), _ptr(v), _ptr(s), T, Hkv, hs, B, _dtype_code(k),
+                            float(np.float32(k_inv_scale)), float(np.float32(v_inv_scale)), _ptr(k_pool), _ptr(v_pool))
+
+
+def paged_attention_fp8(q, k_pool, v_pool, block_tables, seq_lens, scale, k_scale, v_scale, *, units=None,
+                        threads=0):
+    """fp64 attention over uint8 E4M3 pools read as code value * k_scale /
+    v_scale; q fp32 or bf16 bits.  Every unit ([S, Hq, hs]) or the listed
+    units (rows s * Hq + h)."""
+    q = np.ascontiguousarray(q)
+    S, Hq, hs = q.shape
+    nb, Hkv, _, B, _ = k_pool.shape
+    t = np.ascontiguousarray(block_tables, dtype=np.int32)
+    L = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    if units is None:
+        out = np.empty((S, Hq, hs), dtype=np.float64)
+        uptr, n = None, 0
+    else:
+        u = np.ascontiguousarray(units, dtype=np.int64)
+        out = np.empty((len(u), hs), dtype=np.float64)
+        uptr, n = _ptr(u), len(u)
+    lib().orc_paged_attention_units_kv(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(t), _ptr(L), S, Hq, Hkv, hs, B,
+                                       t.shape[1], _dtype_code(q), ORC_FP8, float(k_scale), float(v_scale),
+                                       float(scale), uptr, n, _ptr(out), int(threads))
+    return out

@@ -34,12 +34,61 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2 };
+
+/* ---- FP8 cache elements ---------------------------------------------------
+ * The pages allow an FP8 cache element (the cache-structure page: x = 16 /
+ * sizeof(cache_t), 16 for FP8) but fix neither the format nor a scale.  The
+ * reading taken here: the E4M3 format of the OCP 8-bit floating-point
+ * specification (sign bit, 4 exponent bits with bias 7, 3 mantissa bits; no
+ * infinities; S.1111.111 is NaN; the exponent field 0 holds the subnormals
+ * m * 2^-9), with one scale per pool: a value x is stored as the code
+ * nearest to x * (1 / scale) (the product rounded to fp32 first) and read
+ * back as code_value * scale. */
+
+/* value of an E4M3 code */
+double orc_fp8_decode(uint8_t c)
+{
+    int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = m * ldexp(1.0, -9);                  /* subnormal: m/8 * 2^(1-7) */
+    else
+        v = (1.0 + m / 8.0) * ldexp(1.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* The E4M3 code nearest to v, found by trying every finite magnitude; a tie
+ * goes to the code with the even mantissa; a magnitude above 448 (the
+ * largest finite value) saturates to 448; NaN gives 0x7F. */
+uint8_t orc_fp8_encode(float v)
+{
+    if (isnan(v))
+        return 0x7F;
+    uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    double a = fabs((double)v);
+    if (a > 448.0)
+        return sign | 0x7E;
+    int best = 0;
+    double best_err = INFINITY;
+    for (int c = 0; c <= 0x7E; ++c) {
+        double err = fabs(orc_fp8_decode((uint8_t)c) - a);
+        if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return sign | (uint8_t)best;
+}
 
 /* ---- element access ------------------------------------------------------ */
 
 static double orc_load(const void* base, size_t idx, int dtype)
 {
+    if (dtype == ORC_FP8)
+        return orc_fp8_decode(((const uint8_t*)base)[idx]);
     if (dtype == ORC_F32)
         return (double)((const float*)base)[idx];
     /* bf16: the 16 stored bits are the upper half of an fp32 pattern */
@@ -132,6 +181,36 @@ void orc_kv_append(const void* k, const void* v, const int64_t* slots, int32_t T
     }
 }
 
+/* FP8 caches: element d of token i's key (value) is stored as
+ * orc_fp8_encode((float)k * k_inv_scale) (the product in fp32); the source
+ * is fp32 or bf16 (src_dtype).  Key layout with x = 16. */
+void orc_kv_append_fp8(const void* k, const void* v, const int64_t* slots, int32_t T,
+                       int32_t Hkv, int32_t hs, int32_t B, int32_t src_dtype,
+                       float k_inv_scale, float v_inv_scale, uint8_t* k_pool, uint8_t* v_pool)
+{
+    for (int32_t i = 0; i < T; ++i) {
+        if (slots[i] < 0)
+            continue;
+        int64_t b, off;
+        orc_slot_split(slots[i], B, &b, &off);
+        for (int32_t h = 0; h < Hkv; ++h)
+            for (int32_t d = 0; d < hs; ++d) {
+                size_t src = ((size_t)i * Hkv + h) * hs + d;
+                float kq = (float)orc_load(k, src, src_dtype) * k_inv_scale;
+                float vq = (float)orc_load(v, src, src_dtype) * v_inv_scale;
+                k_pool[orc_key_index(b, h, off, d, Hkv, B, hs, 16)] = orc_fp8_encode(kq);
+                v_pool[orc_value_index(b, h, off, d, Hkv, B, hs)] = orc_fp8_encode(vq);
+            }
+    }
+}
+
+/* codes of n values (fp32 or bf16) quantized with inv_scale, as in the append */
+void orc_fp8_quantize(const void* src, int64_t n, int32_t src_dtype, float inv_scale, uint8_t* out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_fp8_encode((float)orc_load(src, (size_t)i, src_dtype) * inv_scale);
+}
+
 /* ---- attention ----------------------------------------------------------- */
 
 typedef struct {
@@ -139,6 +218,8 @@ typedef struct {
     const int32_t* block_tables; const int32_t* seq_lens;
     int32_t S, Hq, Hkv, hs, B, M, dtype, x;
     double scale;
+    int32_t kv_dtype;          /* element type of the pools (dtype: of q) */
+    double k_scale, v_scale;   /* pool values are element * scale (1 unless FP8) */
 } orc_problem;
 
 /* Score of logical token t for query head h of sequence s:
@@ -151,7 +232,8 @@ static double orc_score(const orc_problem* p, int32_t s, int32_t h, int32_t kvh,
     double dot = 0.0;
     for (int32_t d = 0; d < p->hs; ++d) {
         double qd = orc_load(p->q, ((size_t)s * p->Hq + h) * p->hs + d, p->dtype);
-        double kd = orc_load(p->k_pool, orc_key_index(block, kvh, slot, d, p->Hkv, p->B, p->hs, p->x), p->dtype);
+        double kd = p->k_scale *
+                    orc_load(p->k_pool, orc_key_index(block, kvh, slot, d, p->Hkv, p->B, p->hs, p->x), p->kv_dtype);
         dot += qd * kd;
     }
     return p->scale * dot;
@@ -160,7 +242,8 @@ static double orc_score(const orc_problem* p, int32_t s, int32_t h, int32_t kvh,
 static double orc_value(const orc_problem* p, int32_t s, int32_t kvh, int64_t t, int32_t d)
 {
     int64_t block = p->block_tables[(size_t)s * p->M + t / p->B];
-    return orc_load(p->v_pool, orc_value_index(block, kvh, t % p->B, d, p->Hkv, p->B, p->hs), p->dtype);
+    return p->v_scale * orc_load(p->v_pool, orc_value_index(block, kvh, t % p->B, d, p->Hkv, p->B, p->hs),
+                                 p->kv_dtype);
 }
 
 /* Softmax attention of one (sequence, query head) over tokens [t0, t1):
@@ -211,14 +294,18 @@ static int orc_run_threads(int threads)
  * row i of `out` receives units[i].  units == NULL selects every unit in
  * order (out is then [S][Hq][hs]).  threads <= 0: OpenMP default.
  * Returns the number of threads used. */
-int orc_paged_attention_units(const void* q, const void* k_pool, const void* v_pool,
-                              const int32_t* block_tables, const int32_t* seq_lens,
-                              int32_t S, int32_t Hq, int32_t Hkv, int32_t hs, int32_t B, int32_t M,
-                              int32_t dtype, double scale, const int64_t* units, int64_t n_units,
-                              double* out, int threads)
+static int32_t orc_x(int32_t dtype) { return dtype == ORC_F32 ? 4 : (dtype == ORC_BF16 ? 8 : 16); }
+
+/* As orc_paged_attention_units, with pools of their own element type
+ * (kv_dtype; FP8 values read as code_value * k_scale / v_scale). */
+int orc_paged_attention_units_kv(const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* block_tables, const int32_t* seq_lens,
+                                 int32_t S, int32_t Hq, int32_t Hkv, int32_t hs, int32_t B, int32_t M,
+                                 int32_t dtype, int32_t kv_dtype, double k_scale, double v_scale,
+                                 double scale, const int64_t* units, int64_t n_units, double* out, int threads)
 {
     orc_problem p = { q, k_pool, v_pool, block_tables, seq_lens, S, Hq, Hkv, hs, B, M, dtype,
-                      16 / (dtype == ORC_F32 ? 4 : 2), scale };
+                      orc_x(kv_dtype), scale, kv_dtype, k_scale, v_scale };
     int64_t maxL = 0;
     for (int32_t s = 0; s < S; ++s)
         if (seq_lens[s] > maxL) maxL = seq_lens[s];
@@ -240,6 +327,16 @@ int orc_paged_attention_units(const void* q, const void* k_pool, const void* v_p
     return nt;
 }
 
+int orc_paged_attention_units(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_tables, const int32_t* seq_lens,
+                              int32_t S, int32_t Hq, int32_t Hkv, int32_t hs, int32_t B, int32_t M,
+                              int32_t dtype, double scale, const int64_t* units, int64_t n_units,
+                              double* out, int threads)
+{
+    return orc_paged_attention_units_kv(q, k_pool, v_pool, block_tables, seq_lens, S, Hq, Hkv, hs, B, M, dtype,
+                                        dtype, 1.0, 1.0, scale, units, n_units, out, threads);
+}
+
 /* out[s][h][d], fp64, every unit. */
 int orc_paged_attention(const void* q, const void* k_pool, const void* v_pool,
                         const int32_t* block_tables, const int32_t* seq_lens,
@@ -259,7 +356,7 @@ int orc_paged_attention_split(const void* q, const void* k_pool, const void* v_p
                               int32_t dtype, double scale, int32_t P, double* out, int threads)
 {
     orc_problem p = { q, k_pool, v_pool, block_tables, seq_lens, S, Hq, Hkv, hs, B, M, dtype,
-                      16 / (dtype == ORC_F32 ? 4 : 2), scale };
+                      orc_x(dtype), scale, dtype, 1.0, 1.0 };
     int64_t maxL = 0;
     for (int32_t s = 0; s < S; ++s)
         if (seq_lens[s] > maxL) maxL = seq_lens[s];

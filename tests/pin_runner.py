@@ -11,6 +11,7 @@ sys.path.insert(0, HERE)
 sys.path.insert(0, os.path.dirname(HERE))
 
 import oracle  # noqa: E402
+import test_oracle_fp8 as F  # noqa: E402
 import test_oracle_pins as T  # noqa: E402
 
 CHECKS = [
@@ -27,6 +28,11 @@ CHECKS = [
     lambda: T.test_partition_merge_equals_direct(48),
     lambda: T.test_append_writes_slots_bit_exactly_and_nothing_else(1, {}),
     T.test_decode_step_reads_the_appended_token,
+    F.test_decode_matches_the_library_for_every_code,
+    F.test_encode_matches_the_library_on_ties_and_grids,
+    F.test_saturation_beyond_the_range,
+    lambda: F.test_fp8_attention_matches_library_sdpa(16, 4),
+    F.test_fp8_append_places_codes_of_each_token,
 ]
 
 

@@ -28,6 +28,12 @@ MUTATIONS = [
     ("no normalisation", "for (int32_t d = 0; d < p->hs; ++d) o[d] /= l;", ""),
     ("merge weight sign", "double w = pl[k] * exp(pm[k] - Mx);", "double w = pl[k] * exp(Mx - pm[k]);"),
     ("slot offset", "int64_t offset_in_block = pos % B;", "int64_t offset_in_block = 0;"),
+    ("fp8 exponent bias", "v = (1.0 + m / 8.0) * ldexp(1.0, e - 7);", "v = (1.0 + m / 8.0) * ldexp(1.0, e - 8);"),
+    ("fp8 subnormal scale", "v = m * ldexp(1.0, -9);", "v = m * ldexp(1.0, -10);"),
+    ("fp8 ties away from even", "(err == best_err && (c & 1) == 0 && (best & 1) == 1)", "(err == best_err)"),
+    ("fp8 overflow to NaN", "if (a > 448.0)\\n        return sign | 0x7E;", "if (a > 448.0)\\n        return sign | 0x7F;"),
+    ("fp8 value scale on keys", "double kd = p->k_scale *", "double kd = p->v_scale *"),
+    ("fp8 key chunk of 8", "k_pool[orc_key_index(b, h, off, d, Hkv, B, hs, 16)]", "k_pool[orc_key_index(b, h, off, d, Hkv, B, hs, 8)]"),
 ]
 
 
@@ -54,6 +60,7 @@ def test_unmutated_source_passes(tmp_path):
 @pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
 def test_mutation_is_caught(tmp_path, name, old, new):
     src = open(SRC).read()
+    old, new = old.replace("\\n", "\n"), new.replace("\\n", "\n")
     assert src.count(old) == 1, f"mutation site for {name!r} not found exactly once"
     r = run_pins(build(src.replace(old, new), str(tmp_path)))
     assert r.returncode != 0, f"planted mistake {name!r} passed every pin"
