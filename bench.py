@@ -64,6 +64,9 @@ def parse():
                     help="record of measured HBM bytes per attention launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, "
                          "calibrated; default: the configuration's record under profiles/); used only when its "
                          "workload and kernel-source hash match this run")
+    ap.add_argument("--kv-dtype", choices=["native", "fp8"], default="native",
+                    help="pool element type: the configuration's own (bf16 or fp32), or FP8 E4M3 codes with one "
+                         "scale per pool (bf16 queries)")
     ap.add_argument("--copy-blocks", type=int, default=0, metavar="PAIRS",
                     help="instead of the decode step, time pkv_copy_blocks (copy-on-write) of PAIRS random block "
                          "pairs in the configuration's pools and print its own JSON line")
@@ -130,7 +133,7 @@ def bench_copy_blocks(args, w, torch, pkv) -> dict:
     return {"metric": "block copy GB/s (bytes read + written by pkv_copy_blocks)", "value": round(gbps, 1),
             "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(t * 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "f32" if w.dtype == "f32" else "bf16", "data": "synthetic",
+            "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 pools, bf16 q/out"}[w.dtype], "data": "synthetic",
             "config": {"workload": f"block copy in the pool of: {w.description}", "pairs": n,
                        "block_bytes_per_pool": block_bytes},
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -173,12 +176,20 @@ def cpu_baseline(w, target_s: float) -> dict:
 
     slots = oracle.decode_slot_mapping(w.block_tables, w.seq_lens, w.B)
     kp, vp = w.k_cache.copy(), w.v_cache.copy()
-    oracle.kv_append(w.new_k, w.new_v, slots, kp, vp)
+    if w.dtype == "fp8":
+        oracle.kv_append_fp8(w.new_k, w.new_v, slots, kp, vp, oracle.fp8_inv_scale(w.k_scale),
+                             oracle.fp8_inv_scale(w.v_scale))
+    else:
+        oracle.kv_append(w.new_k, w.new_v, slots, kp, vp)
     passes = 0
     used = oracle.max_threads()
     t0 = time.perf_counter()
     while True:
-        _, used = oracle.paged_attention(w.q, kp, vp, w.block_tables, w.seq_lens, w.scale, return_threads=True)
+        if w.dtype == "fp8":
+            oracle.paged_attention_fp8(w.q, kp, vp, w.block_tables, w.seq_lens, w.scale, w.k_scale, w.v_scale)
+        else:
+            _, used = oracle.paged_attention(w.q, kp, vp, w.block_tables, w.seq_lens, w.scale,
+                                             return_threads=True)
         passes += 1
         if time.perf_counter() - t0 >= target_s:
             break
@@ -208,7 +219,9 @@ def main() -> int:
     pkv.library()
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
-    w = pi.make_workload(args.config, mode="timing", contiguous=args.contiguous)
+    kvdt = "fp8" if args.kv_dtype == "fp8" else None
+    w = pi.make_workload(args.config, mode="timing", contiguous=args.contiguous, dtype=kvdt)
+    sc = dict(k_scale=w.k_scale, v_scale=w.v_scale)
     log(f"generated config {args.config} ({w.description}) in {time.perf_counter() - t0:.1f} s")
     if args.copy_blocks:
         print(json.dumps(bench_copy_blocks(args, w, torch, pkv)), flush=True)
@@ -232,7 +245,7 @@ def main() -> int:
         d = copies[turn[0] % len(copies)]
         turn[0] += 1
         pkv.paged_decode_step(d["q"], d["nk"], d["nv"], d["kc"], d["vc"], d["bt"], d["sl"], w.scale, out=out,
-                              slot_mapping=slots, workspace=ws_step, partition_tokens=P, stream=stream)
+                              slot_mapping=slots, workspace=ws_step, partition_tokens=P, stream=stream, **sc)
 
     def step_timed(ev):
         # the same step through the two entry points it is made of, with
@@ -240,10 +253,10 @@ def main() -> int:
         d = copies[turn[0] % len(copies)]
         turn[0] += 1
         pkv.decode_append(d["nk"], d["nv"], d["bt"], d["sl"], d["kc"], d["vc"], slot_mapping=slots, schedule=sched,
-                          stream=stream)
+                          stream=stream, **sc)
         ev[0].record(stream)
         pkv.paged_decode_attention(d["q"], d["kc"], d["vc"], d["bt"], d["sl"], w.scale, out=out, workspace=ws,
-                                   partition_tokens=P, schedule=sched, stream=stream)
+                                   partition_tokens=P, schedule=sched, stream=stream, **sc)
         ev[1].record(stream)
 
     for _ in range(args.warmup):
@@ -275,7 +288,7 @@ def main() -> int:
     attn_avg_s = float(attn_ms.mean()) / 1e3
     achieved = kv_bytes / attn_avg_s / 1e9
     traffic_path = args.traffic or os.path.join(ROOT, "profiles", TRAFFIC_RECORDS.get(args.config, ""))
-    traffic = measured_traffic(traffic_path, args.config, P_used, args.contiguous)
+    traffic = None if w.dtype == "fp8" else measured_traffic(traffic_path, args.config, P_used, args.contiguous)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": ("paged_decode_attention with the step's longest-first schedule: "
@@ -290,7 +303,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
-        cpu = cpu_baseline(pi.make_workload(args.config, mode="timing"), args.cpu_seconds)
+        cpu = cpu_baseline(pi.make_workload(args.config, mode="timing", dtype=kvdt), args.cpu_seconds)
     value = kv_bytes / (ms_step / 1e3) / 1e9
     rec = {
         "metric": "paged decode attention KV-read GB/s (% of HBM peak) + decode tokens/s, 1 GPU",
@@ -303,7 +316,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32" if w.dtype == "f32" else "bf16",
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 pools, bf16 q/out"}[w.dtype],
         "data": "synthetic (seeded N(0,1) q/K/V, shuffled block IDs; no dataset)",
         "config": {"workload": w.description + (" [contiguous block order]" if args.contiguous else ""),
                    "config": args.config, "seed": w.seed, "num_seqs": w.S, "input_copies": len(copies),

@@ -24,8 +24,10 @@
  * ---------------------------------------------------------------------------
  * Data layout (device memory, all buffers owned by the caller)
  * ---------------------------------------------------------------------------
- * Element type T is fp32 (PKV_F32) or bfloat16 (PKV_BF16, 16-bit patterns).
- * x = 16 / sizeof(T) elements form one 16-byte chunk (4 for fp32, 8 for bf16).
+ * Pool element type T is fp32 (PKV_F32), bfloat16 (PKV_BF16, 16-bit patterns)
+ * or an FP8 code (PKV_FP8_E4M3, see below).  x = 16 / sizeof(T) elements form
+ * one 16-byte chunk (4 for fp32, 8 for bf16, 16 for FP8: the cache-structure
+ * page's x = 16 / sizeof(cache_t)).
  *
  *   key pool    [num_blocks][num_kv_heads][head_size / x][block_size][x]
  *   value pool  [num_blocks][num_kv_heads][head_size][block_size]
@@ -35,8 +37,8 @@
  *   value: ((b*Hkv + h)*hs + d)*B + t
  * Each (block, KV head) tile is B*hs contiguous elements in both pools.
  *
- *   q, out        [num_seqs][num_q_heads][head_size], element type T
- *   k, v (append) [num_tokens][num_kv_heads][head_size], element type T
+ *   q, out        [num_seqs][num_q_heads][head_size], element type T (bf16 with FP8 pools)
+ *   k, v (append) [num_tokens][num_kv_heads][head_size], element type T (bf16 with FP8 pools)
  *   block_tables  int32 [num_seqs][max_blocks_per_seq]
  *   seq_lens      int32 [num_seqs]
  *   slot_mapping  int64 [num_tokens]
@@ -46,6 +48,14 @@
  * Table entries at index >= ceil(seq_len / B) and slots >= seq_len in the
  * last block are never read; they may hold anything, NaN included.
  * All q/out/k/v/pool pointers must be 16-byte aligned.
+ *
+ * FP8 pools.  The pages allow an FP8 cache element but fix no format or
+ * scale.  Here: the E4M3 codes of the OCP 8-bit floating-point format (sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits, no infinities, 0x7F / 0xFF
+ * NaN, largest finite 448), one scale per pool (cache->k_scale, v_scale).  An
+ * append stores the code nearest to fp32(x * (1 / scale)) (ties to the even
+ * mantissa; magnitudes beyond 448 saturate to 448); attention reads
+ * code_value * scale.
  *
  * ---------------------------------------------------------------------------
  * Conventions
@@ -96,7 +106,8 @@ typedef enum {
 
 typedef enum {
     PKV_F32 = 0,
-    PKV_BF16 = 1
+    PKV_BF16 = 1,
+    PKV_FP8_E4M3 = 2   /* pools only; q, out, k, v are bf16 */
 } pkv_dtype;
 
 /* Describes both pools (key and value share it). */
@@ -105,7 +116,10 @@ typedef struct {
     int32_t num_kv_heads;  /* Hkv                                              */
     int32_t block_size;    /* B: token slots per block; 16 or 32               */
     int32_t head_size;     /* hs: 64 or 128                                    */
-    int32_t dtype;         /* pkv_dtype of the pools, q, out, k and v          */
+    int32_t dtype;         /* pkv_dtype of the pools (and of q, out, k, v,     */
+                           /* which are bf16 when the pools are FP8)           */
+    float k_scale;         /* FP8 pools: key value = code * k_scale (> 0);     */
+    float v_scale;         /* value = code * v_scale.  Ignored otherwise.      */
 } pkv_cache_desc;
 
 /* Layout contract version; changes whenever the pool layout above changes. */

@@ -225,9 +225,15 @@ def decode_step(w, threads=0, return_threads=False):
     slots = decode_slot_mapping(w.block_tables, w.seq_lens, w.B)
     kp = w.k_cache.copy()
     vp = w.v_cache.copy()
-    kv_append(w.new_k, w.new_v, slots, kp, vp)
-    r = paged_attention(w.q, kp, vp, w.block_tables, w.seq_lens, w.scale, threads=threads,
-                        return_threads=return_threads)
+    if w.dtype == "fp8":
+        kv_append_fp8(w.new_k, w.new_v, slots, kp, vp, fp8_inv_scale(w.k_scale), fp8_inv_scale(w.v_scale))
+        out = paged_attention_fp8(w.q, kp, vp, w.block_tables, w.seq_lens, w.scale, w.k_scale, w.v_scale,
+                                  threads=threads)
+        r = (out, max_threads() if threads <= 0 else threads) if return_threads else out
+    else:
+        kv_append(w.new_k, w.new_v, slots, kp, vp)
+        r = paged_attention(w.q, kp, vp, w.block_tables, w.seq_lens, w.scale, threads=threads,
+                            return_threads=return_threads)
     if return_threads:
         out, n = r
         return slots, kp, vp, out, n
@@ -238,6 +244,11 @@ def decode_step(w, threads=0, return_threads=False):
 # Reading (the pages fix no format or scale): OCP E4M3 codes, one scale per
 # pool; a value x is stored as the code nearest to fp32(x * inv_scale) (ties to
 # the even mantissa, magnitudes above 448 saturate) and read as value * scale.
+
+def fp8_inv_scale(scale: float) -> float:
+    """The fp32 reciprocal of a pool scale, as the append multiplies by it."""
+    return float(np.float32(1.0) / np.float32(scale))
+
 
 def fp8_decode(code: int) -> float:
     return float(lib().orc_fp8_decode(int(code)))

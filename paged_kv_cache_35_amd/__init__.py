@@ -25,8 +25,12 @@ PKV_OK = 0
 PKV_ERR_OUT_OF_BLOCKS = -5
 PKV_F32 = 0
 PKV_BF16 = 1
+PKV_FP8_E4M3 = 2
 
-_DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
+# pool element types; FP8 pools hold E4M3 codes (uint8 or float8_e4m3fn tensors)
+_DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16, torch.uint8: PKV_FP8_E4M3}
+if hasattr(torch, "float8_e4m3fn"):
+    _DTYPES[torch.float8_e4m3fn] = PKV_FP8_E4M3
 
 
 class PkvError(RuntimeError):
@@ -41,7 +45,8 @@ class PkvError(RuntimeError):
 
 class CacheDesc(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
-                ("block_size", ctypes.c_int32), ("head_size", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("block_size", ctypes.c_int32), ("head_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
 
 
 _lib = None
@@ -131,17 +136,24 @@ def _dev(t: torch.Tensor, name: str) -> int:
     return t.data_ptr()
 
 
-def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor) -> CacheDesc:
-    """Descriptor of a key/value pool pair in the documented layouts."""
+def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: float = 1.0,
+               v_scale: float = 1.0) -> CacheDesc:
+    """Descriptor of a key/value pool pair in the documented layouts (the
+    scales matter only for FP8 pools: value = code * scale)."""
     if k_cache.dtype != v_cache.dtype or k_cache.dtype not in _DTYPES:
-        raise ValueError("k_cache and v_cache must share dtype float32 or bfloat16")
+        raise ValueError("k_cache and v_cache must share dtype float32, bfloat16 or FP8 (uint8 codes)")
     if v_cache.dim() != 4 or k_cache.dim() != 5:
         raise ValueError("k_cache must be [nb, Hkv, hs/x, B, x] and v_cache [nb, Hkv, hs, B]")
     nb, hkv, hs, B = v_cache.shape
     x = 16 // k_cache.element_size()
     if tuple(k_cache.shape) != (nb, hkv, hs // x, B, x) or hs % x:
         raise ValueError(f"k_cache shape {tuple(k_cache.shape)} does not match v_cache {tuple(v_cache.shape)}")
-    return CacheDesc(nb, hkv, B, hs, _DTYPES[k_cache.dtype])
+    return CacheDesc(nb, hkv, B, hs, _DTYPES[k_cache.dtype], float(k_scale), float(v_scale))
+
+
+def io_dtype(k_cache: torch.Tensor) -> torch.dtype:
+    """Element type of q, out and the appended k, v for these pools."""
+    return torch.bfloat16 if _DTYPES.get(k_cache.dtype) == PKV_FP8_E4M3 else k_cache.dtype
 
 
 def layout_version() -> int:
@@ -163,13 +175,13 @@ def decode_slot_mapping(block_tables: torch.Tensor, seq_lens: torch.Tensor, bloc
 
 
 def kv_cache_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor, k_cache: torch.Tensor,
-                    v_cache: torch.Tensor, stream=None) -> None:
+                    v_cache: torch.Tensor, stream=None, k_scale: float = 1.0, v_scale: float = 1.0) -> None:
     """Write k[i], v[i] ([T, Hkv, hs]) into slot slot_mapping[i] of the pools (in place)."""
-    desc = cache_desc(k_cache, v_cache)
+    desc = cache_desc(k_cache, v_cache, k_scale, v_scale)
     T = k.shape[0]
     if k.shape != v.shape or tuple(k.shape[1:]) != (desc.num_kv_heads, desc.head_size):
         raise ValueError("k and v must be [T, Hkv, head_size]")
-    if k.dtype != k_cache.dtype or v.dtype != k_cache.dtype:
+    if k.dtype != io_dtype(k_cache) or v.dtype != io_dtype(k_cache):
         raise ValueError("k, v and the pools must share a dtype")
     if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
         raise ValueError("slot_mapping must be int64 [T]")
@@ -182,16 +194,17 @@ def kv_cache_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor
 
 def decode_append(k: torch.Tensor, v: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
                   k_cache: torch.Tensor, v_cache: torch.Tensor, slot_mapping: Optional[torch.Tensor] = None,
-                  schedule: Optional[torch.Tensor] = None, stream=None) -> Optional[torch.Tensor]:
+                  schedule: Optional[torch.Tensor] = None, stream=None, k_scale: float = 1.0,
+                  v_scale: float = 1.0) -> Optional[torch.Tensor]:
     """One launch: slot of each sequence's newest token from its table, then
     append k[s], v[s] there.  Writes the slots to slot_mapping if given, and
     the batch's longest-first schedule to `schedule` (from alloc_schedule) if
     given."""
-    desc = cache_desc(k_cache, v_cache)
+    desc = cache_desc(k_cache, v_cache, k_scale, v_scale)
     S = k.shape[0]
     if k.shape != v.shape or tuple(k.shape[1:]) != (desc.num_kv_heads, desc.head_size):
         raise ValueError("k and v must be [S, Hkv, head_size]")
-    if k.dtype != k_cache.dtype or v.dtype != k_cache.dtype:
+    if k.dtype != io_dtype(k_cache) or v.dtype != io_dtype(k_cache):
         raise ValueError("k, v and the pools must share a dtype")
     if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise ValueError("block_tables and seq_lens must be int32")
@@ -267,13 +280,13 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                            block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
                            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                            partition_tokens: int = 0, schedule: Optional[torch.Tensor] = None,
-                           stream=None) -> torch.Tensor:
+                           stream=None, k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
     """out[s, h] = softmax(scale * q[s, h] K^T) V over the L = seq_lens[s]
     tokens of sequence s, K/V found through block_tables.  `schedule`: the
     longest-first schedule decode_append wrote for these tables and lengths
     (optional; results are the same without it)."""
-    desc = cache_desc(k_cache, v_cache)
-    if q.dtype != k_cache.dtype:
+    desc = cache_desc(k_cache, v_cache, k_scale, v_scale)
+    if q.dtype != io_dtype(k_cache):
         raise ValueError("q must have the pools' dtype")
     S, Hq, hs = q.shape
     if hs != desc.head_size:
@@ -303,21 +316,21 @@ def paged_decode_step(q: torch.Tensor, new_k: torch.Tensor, new_v: torch.Tensor,
                       v_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
                       out: Optional[torch.Tensor] = None, slot_mapping: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, partition_tokens: int = 0,
-                      stream=None) -> torch.Tensor:
+                      stream=None, k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
     """A whole decode step in one call: store new_k[s], new_v[s] at position
     seq_lens[s] - 1, then attend over all seq_lens[s] tokens.  The append
     launch also writes the batch's longest-first schedule into the workspace
     (see alloc_step_workspace) and the attention launch reads it.
     Bit-identical to decode_append followed by paged_decode_attention."""
-    desc = cache_desc(k_cache, v_cache)
-    if q.dtype != k_cache.dtype:
+    desc = cache_desc(k_cache, v_cache, k_scale, v_scale)
+    if q.dtype != io_dtype(k_cache):
         raise ValueError("q must have the pools' dtype")
     S, Hq, hs = q.shape
     if hs != desc.head_size:
         raise ValueError("q head size does not match the pools")
     if new_k.shape != new_v.shape or tuple(new_k.shape) != (S, desc.num_kv_heads, desc.head_size):
         raise ValueError("new_k and new_v must be [S, Hkv, head_size]")
-    if new_k.dtype != k_cache.dtype or new_v.dtype != k_cache.dtype:
+    if new_k.dtype != io_dtype(k_cache) or new_v.dtype != io_dtype(k_cache):
         raise ValueError("new_k, new_v and the pools must share a dtype")
     if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise ValueError("block_tables and seq_lens must be int32")
@@ -343,11 +356,11 @@ def paged_decode_step(q: torch.Tensor, new_k: torch.Tensor, new_v: torch.Tensor,
 
 
 def decode_step(q, k_cache, v_cache, block_tables, seq_lens, new_k, new_v, scale, out=None, workspace=None,
-                slot_mapping=None, partition_tokens=0, stream=None) -> torch.Tensor:
+                slot_mapping=None, partition_tokens=0, stream=None, k_scale=1.0, v_scale=1.0) -> torch.Tensor:
     """One decode step: append of the new tokens, then attention (two launches on one stream)."""
     return paged_decode_step(q, new_k, new_v, k_cache, v_cache, block_tables, seq_lens, scale, out=out,
                              slot_mapping=slot_mapping, workspace=workspace, partition_tokens=partition_tokens,
-                             stream=stream)
+                             stream=stream, k_scale=k_scale, v_scale=v_scale)
 
 
 def copy_blocks(pairs: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:

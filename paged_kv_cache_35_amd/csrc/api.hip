@@ -3,6 +3,8 @@
 // include/pkv.h.
 #include <string.h>
 
+#include <cmath>
+
 #include "../../include/pkv.h"
 #include "pkv_internal.h"
 
@@ -20,7 +22,7 @@ pkv_status hip_status(hipError_t e)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : 2; }
+int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : (dtype == PKV_FP8_E4M3 ? 1 : 2); }
 
 size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
 
@@ -40,8 +42,11 @@ pkv_status check_cache(const pkv_cache_desc* c)
         return PKV_ERR_INVALID_ARG;
     if (c->num_blocks <= 0 || c->num_kv_heads <= 0 || c->block_size <= 0 || c->head_size <= 0)
         return PKV_ERR_INVALID_ARG;
-    if (c->dtype != PKV_F32 && c->dtype != PKV_BF16)
+    if (c->dtype != PKV_F32 && c->dtype != PKV_BF16 && c->dtype != PKV_FP8_E4M3)
         return PKV_ERR_UNSUPPORTED;
+    if (c->dtype == PKV_FP8_E4M3 &&
+        !(c->k_scale > 0.f && c->v_scale > 0.f && std::isfinite(c->k_scale) && std::isfinite(c->v_scale)))
+        return PKV_ERR_INVALID_ARG;
     if (c->head_size != 64 && c->head_size != 128)
         return PKV_ERR_UNSUPPORTED;
     if (c->block_size != 16 && c->block_size != 32)
@@ -73,7 +78,7 @@ int32_t resolve_partition_tokens(int32_t max_blocks_per_seq, int32_t block_size,
 
 extern "C" {
 
-int32_t pkv_layout_version(void) { return 1; }
+int32_t pkv_layout_version(void) { return 2; }
 
 const char* pkv_status_string(int32_t status)
 {
@@ -127,6 +132,9 @@ pkv_status append_common(const void* k, const void* v, int64_t* slot_mapping, co
     a.block_size = cache->block_size;
     a.num_blocks = cache->num_blocks;
     a.elem_bytes = elem_bytes(cache->dtype);
+    // FP8: both sides of the append multiply by the fp32 reciprocal of the scale
+    a.k_inv_scale = cache->dtype == PKV_FP8_E4M3 ? 1.0f / cache->k_scale : 1.0f;
+    a.v_inv_scale = cache->dtype == PKV_FP8_E4M3 ? 1.0f / cache->v_scale : 1.0f;
     return hip_status(pkv::launch_append(a, (hipStream_t)stream));
 }
 
@@ -293,6 +301,8 @@ pkv_status attention_args(const void* q, const void* k_cache, const void* v_cach
     // inside a chunk.  Both compute the same attention.
     a.interleave = partition_tokens == 0 ? 1 : 0;
     a.scale = scale;
+    a.k_scale = cache->dtype == PKV_FP8_E4M3 ? cache->k_scale : 1.0f;
+    a.v_scale = cache->dtype == PKV_FP8_E4M3 ? cache->v_scale : 1.0f;
     return PKV_OK;
 }
 

@@ -123,6 +123,32 @@ __device__ void write_schedule(const SchedulePrefetch& p, int32_t i, int32_t S,
         dst[m] = src[m];
 }
 
+// FP8 pools: the E4M3 codes of 16 bf16 values times inv_scale, as one
+// 16-byte chunk.  The product is formed in fp32 and clamped to +-448 (the
+// largest finite E4M3 magnitude), then v_cvt_pk_fp8_f32 rounds it to the
+// nearest code, ties to the even mantissa (checked against the reference
+// encoder on every tie and subnormal; without the clamp the conversion
+// would give NaN from 464 up).
+__device__ __forceinline__ u32x4 quantize16(const u32x4 (&in)[2], float inv_scale)
+{
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {  // output word w: bf16 elements 4w .. 4w+3
+        float f[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const unsigned word = in[w / 2][2 * (w % 2) + e / 2];
+            const unsigned bits = (e & 1) ? (word & 0xFFFF0000u) : (word << 16);
+            const float x = __builtin_bit_cast(float, bits) * inv_scale;
+            f[e] = fminf(fmaxf(x, -448.0f), 448.0f);
+        }
+        int code = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+        code = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], code, true);
+        out[w] = (unsigned)code;
+    }
+    return out;
+}
+
 // Stores 16-byte chunk ci (of the Hkv * hs / X chunks of a token) of the key
 // and value at `slot`: key chunk f of KV head h lands at
 // ((b*Hkv + h)*(hs/X) + f)*B*X + off*X, value head dims f*X .. f*X + X - 1
@@ -173,9 +199,11 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     const u32x4* __restrict__ k, const u32x4* __restrict__ v, int64_t* __restrict__ slot_mapping,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens, int32_t max_blocks_per_seq,
     u32x4* __restrict__ k_cache, E* __restrict__ v_cache, int32_t num_kv_heads, int32_t head_size,
-    int32_t block_size, int32_t num_blocks, AppendArgs::Schedule sched)
+    int32_t block_size, int32_t num_blocks, AppendArgs::Schedule sched, float k_inv_scale, float v_inv_scale)
 {
     constexpr int X = 16 / sizeof(E);
+    constexpr bool Q8 = sizeof(E) == 1;  // FP8 pools: bf16 input, 2 input pieces per pool chunk
+    constexpr int IN = Q8 ? 2 : 1;
     const int32_t i = blockIdx.x;
     const int32_t nchunks = num_kv_heads * (head_size / X);
     const int32_t ci = blockIdx.y * kAppendThreads + threadIdx.x;
@@ -184,10 +212,15 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     SchedulePrefetch pre;
     if (sched_wg)
         prefetch_schedule(pre, i, gridDim.x, seq_lens, block_tables, max_blocks_per_seq);
-    u32x4 kval = {0u, 0u, 0u, 0u}, vval = {0u, 0u, 0u, 0u};
-    if (active) {
-        kval = k[(int64_t)i * nchunks + ci];
-        vval = v[(int64_t)i * nchunks + ci];
+    u32x4 kin[IN], vin[IN];
+#pragma unroll
+    for (int p = 0; p < IN; ++p) {
+        kin[p] = (u32x4){0u, 0u, 0u, 0u};
+        vin[p] = (u32x4){0u, 0u, 0u, 0u};
+        if (active) {
+            kin[p] = k[((int64_t)i * nchunks + ci) * IN + p];
+            vin[p] = v[((int64_t)i * nchunks + ci) * IN + p];
+        }
     }
     int64_t slot;
     if constexpr (FROM_TABLE) {
@@ -197,8 +230,17 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     } else {
         slot = slot_mapping[i];
     }
-    if (slot >= 0 && active && slot / block_size < num_blocks)  // out-of-range slot: skipped, never written
+    if (slot >= 0 && active && slot / block_size < num_blocks) {  // out-of-range slot: skipped, never written
+        u32x4 kval, vval;
+        if constexpr (Q8) {
+            kval = quantize16(kin, k_inv_scale);
+            vval = quantize16(vin, v_inv_scale);
+        } else {
+            kval = kin[0];
+            vval = vin[0];
+        }
         store_token<E>(kval, vval, slot, ci, k_cache, v_cache, num_kv_heads, head_size, block_size);
+    }
     if (sched_wg)
         write_schedule(pre, i, gridDim.x, seq_lens, block_tables, max_blocks_per_seq, block_size, sched.order,
                        sched.lens, sched.tables);
@@ -215,21 +257,26 @@ hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* seq_l
     return hipGetLastError();
 }
 
+template <typename E, bool FROM_TABLE>
+static void launch_append_typed(const AppendArgs& a, dim3 grid, dim3 block, hipStream_t stream)
+{
+    hipLaunchKernelGGL((kv_append_kernel<E, FROM_TABLE>), grid, block, 0, stream, (const u32x4*)a.k,
+                       (const u32x4*)a.v, a.slot_mapping, a.block_tables, a.seq_lens, a.max_blocks_per_seq,
+                       (u32x4*)a.k_cache, (E*)a.v_cache, a.num_kv_heads, a.head_size, a.block_size, a.num_blocks,
+                       a.sched, a.k_inv_scale, a.v_inv_scale);
+}
+
 template <bool FROM_TABLE>
 static hipError_t launch_append_impl(const AppendArgs& a, hipStream_t stream)
 {
     const int32_t nchunks = a.num_kv_heads * a.head_size / (16 / a.elem_bytes);
     const dim3 grid(a.num_tokens, (nchunks + kAppendThreads - 1) / kAppendThreads), block(kAppendThreads);
-    if (a.elem_bytes == 2)
-        hipLaunchKernelGGL((kv_append_kernel<uint16_t, FROM_TABLE>), grid, block, 0, stream, (const u32x4*)a.k,
-                           (const u32x4*)a.v, a.slot_mapping, a.block_tables, a.seq_lens, a.max_blocks_per_seq,
-                           (u32x4*)a.k_cache, (uint16_t*)a.v_cache, a.num_kv_heads, a.head_size, a.block_size,
-                           a.num_blocks, a.sched);
+    if (a.elem_bytes == 1)
+        launch_append_typed<uint8_t, FROM_TABLE>(a, grid, block, stream);
+    else if (a.elem_bytes == 2)
+        launch_append_typed<uint16_t, FROM_TABLE>(a, grid, block, stream);
     else
-        hipLaunchKernelGGL((kv_append_kernel<uint32_t, FROM_TABLE>), grid, block, 0, stream, (const u32x4*)a.k,
-                           (const u32x4*)a.v, a.slot_mapping, a.block_tables, a.seq_lens, a.max_blocks_per_seq,
-                           (u32x4*)a.k_cache, (uint32_t*)a.v_cache, a.num_kv_heads, a.head_size, a.block_size,
-                           a.num_blocks, a.sched);
+        launch_append_typed<uint32_t, FROM_TABLE>(a, grid, block, stream);
     return hipGetLastError();
 }
 

@@ -45,6 +45,7 @@ namespace pkv {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -209,6 +210,73 @@ __device__ __forceinline__ void load_wide(WideRegs<HS>& t, const __bf16* __restr
         t.v[i] = load_stream((const bf16x8*)(tile_v + (16 * i + c) * 32 + 8 * r));
 }
 
+// FP8 (E4M3) caches, bf16 queries: one 16-token sub-tile as raw codes.
+// Keys: chunk 4i + r of token 16m + c, i < HS/64 (16 head dims per 16-byte
+// chunk, key layout [hs/16][B][16]); one wave load is 16 tokens x 4 chunks,
+// 1 KiB contiguous.  The 16 dims of a chunk feed two score MFMAs (dims
+// 8h .. 8h+7 of chunk 4i + r go to MFMA 2i + h), and the query operand is
+// loaded in the same order (see the query load): a dot product does not
+// depend on the order of its terms.  Values: the 4 codes of tokens
+// 16m + 4r .. +3 of head dim 16i + c (one 4-byte load per lane, 256 bytes
+// contiguous per wave load).
+template <int HS>
+struct Fp8Regs {
+    u32x4 k[HS / 64];
+    unsigned v[HS / 16];
+};
+
+template <int HS, int BS>
+__device__ __forceinline__ void load_fp8(Fp8Regs<HS>& t, const uint8_t* __restrict__ tile_k,
+                                         const uint8_t* __restrict__ tile_v, int m, int r, int c)
+{
+#pragma unroll
+    for (int i = 0; i < HS / 64; ++i)
+        t.k[i] = load_stream((const u32x4*)(tile_k + ((4 * i + r) * BS + 16 * m + c) * 16));
+#pragma unroll
+    for (int i = 0; i < HS / 16; ++i)
+        t.v[i] = load_stream_v((const unsigned*)(tile_v + (16 * i + c) * BS + 16 * m + 4 * r));
+}
+
+// Four E4M3 codes (one dword) to four bf16: v_cvt_pk_f32_fp8 gives the exact
+// values in fp32, and an E4M3 value has at most 4 significant bits, so its
+// fp32 pattern's upper half is the same value in bf16.  Element e of the
+// result is code e (byte e of w).
+__device__ __forceinline__ unsigned upper_halves(float x0, float x1)
+{
+    return (__builtin_bit_cast(unsigned, x0) >> 16) | (__builtin_bit_cast(unsigned, x1) & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ void fp8x4_to_bf16(unsigned w, unsigned& lo, unsigned& hi)
+{
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);  // codes 0, 1
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);   // codes 2, 3
+    lo = upper_halves(a[0], a[1]);
+    hi = upper_halves(b[0], b[1]);
+}
+
+template <int HS>
+__device__ __forceinline__ void fp8_to_operands(const Fp8Regs<HS>& raw, TileRegs<__bf16, HS>& t)
+{
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int i = 0; i < HS / 64; ++i)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            unsigned a, b, c, d;
+            fp8x4_to_bf16(raw.k[i][2 * h], a, b);
+            fp8x4_to_bf16(raw.k[i][2 * h + 1], c, d);
+            const u32x4 w = {a, b, c, d};
+            t.k.v[2 * i + h] = __builtin_bit_cast(bf16x8, w);
+        }
+#pragma unroll
+    for (int i = 0; i < HS / 16; ++i) {
+        unsigned a, b;
+        fp8x4_to_bf16(raw.v[i], a, b);
+        const u32x2 w = {a, b};
+        t.v.v[i] = __builtin_bit_cast(bf16x4, w);
+    }
+}
+
 // Scores S^T for one 16-token sub-tile: element j of the result is token
 // 4r + j of the sub-tile, query head c.
 template <typename T, int HS>
@@ -274,20 +342,28 @@ __device__ __forceinline__ void zero_masked_values(TileRegs<T, HS>& t, int tok0,
 
 // Occupancy targets for bf16: three waves per SIMD with 16-token blocks
 // (<= 168 VGPRs, including the MFMA accumulators), two with 32-token units
-// (<= 256).  The fp32 variants (larger operands) are left unconstrained.
-#define PKV_OCCUPANCY __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (BS == 16 ? 3 : 2) : 1)))
+// (<= 256); FP8 pools (smaller raw operands) also three.  The fp32 variants
+// (larger operands) are left unconstrained.
+#define PKV_OCCUPANCY \
+    __attribute__((amdgpu_waves_per_eu(F8 ? 3 : (sizeof(T) == 2 ? (BS == 16 ? 3 : 2) : 1))))
 
-template <typename T, int HS, int BS, int NW>
+// T: element type of q and out (and of the pools unless F8).  F8: the pools
+// hold E4M3 codes (T is bf16); keys are read as code * k_scale (folded into
+// qscale) and values as code * v_scale (oscale, applied to the output).
+template <typename T, int HS, int BS, int NW, bool F8>
 __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_kernel(
-    const T* __restrict__ q, const T* __restrict__ k_cache, const T* __restrict__ v_cache,
+    const T* __restrict__ q, const typename std::conditional<F8, uint8_t, T>::type* __restrict__ k_cache,
+    const typename std::conditional<F8, uint8_t, T>::type* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables,
     const int32_t* __restrict__ seq_lens, int32_t Hq, int32_t Hkv,
     int32_t M, int32_t num_blocks, int32_t PB, int32_t max_parts, int32_t interleave, int32_t lpt, float qscale,
     const int32_t* __restrict__ sched_order, const int32_t* __restrict__ sched_lens,
-    const int32_t* __restrict__ sched_tables, T* __restrict__ out,
+    const int32_t* __restrict__ sched_tables, float oscale, T* __restrict__ out,
     float* __restrict__ ws_o, float* __restrict__ ws_ml)
 {
-    constexpr bool kWide = sizeof(T) == 2 && BS == 32;  // 32-token units (see WideRegs)
+    using C = typename std::conditional<F8, uint8_t, T>::type;  // pool element type
+    static_assert(!F8 || sizeof(T) == 2, "FP8 pools are read with bf16 queries");
+    constexpr bool kWide = sizeof(T) == 2 && BS == 32 && !F8;  // 32-token units (see WideRegs)
     constexpr int UT = kWide ? 32 : 16;                 // tokens per pipeline unit
     constexpr int PER = BS / UT;                        // units per block
     constexpr int TILE = HS * BS;                       // elements per (block, KV head) tile
@@ -395,7 +471,14 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     typename Ops<T>::template QReg<HS> qr;
     {
         const T* qh = q + ((int64_t)s * Hq + (int64_t)kvh * G + c % G) * HS;
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (F8) {
+            // operand 2i + h holds dims (4i + r)*16 + 8h .. +7 (the FP8 key order)
+#pragma unroll
+            for (int i = 0; i < HS / 64; ++i)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    qr.v[2 * i + h] = *(const bf16x8*)(qh + (4 * i + r) * 16 + 8 * h);
+        } else if constexpr (sizeof(T) == 2) {
 #pragma unroll
             for (int i = 0; i < HS / 32; ++i)
                 qr.v[i] = *(const bf16x8*)(qh + 32 * i + 8 * r);
@@ -418,7 +501,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     const int64_t head_off = (int64_t)kvh * TILE;
     const int64_t block_stride = (int64_t)Hkv * TILE;
 
-    auto tile_ptr_ok = [&](int j, const T*& tk, const T*& tv) __attribute__((always_inline)) -> bool {
+    auto tile_ptr_ok = [&](int j, const C*& tk, const C*& tv) __attribute__((always_inline)) -> bool {
         int32_t id = __builtin_amdgcn_readlane(id_lane, j);
         const bool ok = (uint32_t)id < (uint32_t)num_blocks;
         id = ok ? id : 0;
@@ -541,15 +624,18 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     // steady-state loop always prefetches and the last one or two units are
     // peeled, so every compute is preceded by exactly one batch of loads and
     // the memory-counter waits stay precise.
-    using Regs = typename std::conditional<kWide, WideRegs<HS>, TileRegs<T, HS>>::type;
+    using Regs = typename std::conditional<kWide, WideRegs<HS>,
+                                           typename std::conditional<F8, Fp8Regs<HS>, TileRegs<T, HS>>::type>::type;
     const int nunits = nb_w * PER;  // 0 for a wave past the end
     auto issue = [&](Regs& t, int u) __attribute__((always_inline)) -> bool {
         const int j = u / PER;
-        const T* tk;
-        const T* tv;
+        const C* tk;
+        const C* tv;
         const bool ok = tile_ptr_ok(j, tk, tv);
         if constexpr (kWide)
             load_wide<HS>(t, tk, tv, r, c);
+        else if constexpr (F8)
+            load_fp8<HS, BS>(t, tk, tv, u % PER, r, c);
         else
             load_tile<T, HS, BS>(t, tk, tv, u % PER, r, c);
         return ok;
@@ -557,10 +643,15 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     auto first_token = [&](int u) __attribute__((always_inline)) { return (base + (u / PER) * stride) * BS + UT * (u % PER); };
     auto run = [&](Regs& t, int u, bool ok) __attribute__((always_inline)) {
         const int tok0 = first_token(u);
-        if constexpr (kWide)
+        if constexpr (kWide) {
             compute_wide(t, tok0, ok);
-        else
+        } else if constexpr (F8) {
+            TileRegs<__bf16, HS> op;  // the raw codes as bf16 operands
+            fp8_to_operands<HS>(t, op);
+            compute(op, tok0, ok);
+        } else {
             compute(t, tok0, ok);
+        }
     };
     if (nunits > 0) {
         Regs ta, tb;
@@ -598,7 +689,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     for (int jj = 0; jj < 4; ++jj) {
         const int g = 4 * r + jj;
         const float l_g = __shfl(l_tot, g);
-        const float inv = l_g > 0.f ? 1.f / l_g : 0.f;
+        const float inv = l_g > 0.f ? oscale / l_g : 0.f;  // oscale: 1, or the FP8 value scale
         if (g < G) {
 #pragma unroll
             for (int i = 0; i < HS / 16; ++i)
@@ -765,17 +856,20 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
     }
 }
 
-template <typename T, int HS, int BS>
+template <typename T, int HS, int BS, bool F8>
 static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
 {
     constexpr int NW = kDecodeWaves;
+    using C = typename std::conditional<F8, uint8_t, T>::type;
     const dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
-    hipLaunchKernelGGL((paged_decode_partition_kernel<T, HS, BS, NW>), grid, dim3(NW * 64), 0, stream,
-                       (const T*)a.q, (const T*)a.k_cache, (const T*)a.v_cache, a.block_tables, a.seq_lens,
+    const float qscale = a.scale * kLog2e * (F8 ? a.k_scale : 1.0f);
+    hipLaunchKernelGGL((paged_decode_partition_kernel<T, HS, BS, NW, F8>), grid, dim3(NW * 64), 0, stream,
+                       (const T*)a.q, (const C*)a.k_cache, (const C*)a.v_cache, a.block_tables, a.seq_lens,
                        a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq, a.num_blocks, a.partition_blocks,
                        a.max_parts, a.interleave,
-                       (a.num_seqs <= kLptMaxSeqs && a.max_blocks_per_seq < (1 << 23)) ? 1 : 0, a.scale * kLog2e,
-                       a.sched_order, a.sched_lens, a.sched_tables, (T*)a.out, a.ws_o, a.ws_ml);
+                       (a.num_seqs <= kLptMaxSeqs && a.max_blocks_per_seq < (1 << 23)) ? 1 : 0, qscale,
+                       a.sched_order, a.sched_lens, a.sched_tables, F8 ? a.v_scale : 1.0f, (T*)a.out, a.ws_o,
+                       a.ws_ml);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_parts <= 1)
         return e;  // one chunk per sequence: the partition kernel wrote the output
@@ -785,17 +879,21 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool F8>
 static hipError_t launch_dtype(const DecodeArgs& a, hipStream_t stream)
 {
     if (a.head_size == 128)
-        return a.block_size == 16 ? launch_typed<T, 128, 16>(a, stream) : launch_typed<T, 128, 32>(a, stream);
-    return a.block_size == 16 ? launch_typed<T, 64, 16>(a, stream) : launch_typed<T, 64, 32>(a, stream);
+        return a.block_size == 16 ? launch_typed<T, 128, 16, F8>(a, stream) : launch_typed<T, 128, 32, F8>(a, stream);
+    return a.block_size == 16 ? launch_typed<T, 64, 16, F8>(a, stream) : launch_typed<T, 64, 32, F8>(a, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream)
 {
-    return a.dtype == 1 ? launch_dtype<__bf16>(a, stream) : launch_dtype<float>(a, stream);
+    switch (a.dtype) {
+    case 1: return launch_dtype<__bf16, false>(a, stream);  // PKV_BF16
+    case 2: return launch_dtype<__bf16, true>(a, stream);   // PKV_FP8_E4M3
+    default: return launch_dtype<float, false>(a, stream);
+    }
 }
 
 }  // namespace pkv

@@ -57,6 +57,7 @@ struct DecodeArgs {
     int32_t max_parts;        // chunks per sequence: ceil(max_blocks_per_seq / (partition_blocks * kDecodeWaves))
     int32_t interleave;       // 1: a chunk's blocks dealt round-robin to its waves; 0: one contiguous partition per wave
     float scale;
+    float k_scale, v_scale;   // FP8 pools: stored code * scale (1 otherwise)
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
@@ -77,7 +78,8 @@ struct AppendArgs {
     int32_t head_size;
     int32_t block_size;
     int32_t num_blocks;
-    int32_t elem_bytes;  // 2 or 4
+    int32_t elem_bytes;  // pool element: 1 (FP8 codes, bf16 input), 2 or 4
+    float k_inv_scale, v_inv_scale;  // FP8 pools: code = E4M3(fp32(x * inv_scale))
     // Decode step only (block_tables != null): when sched.order is non-null,
     // the launch also writes the longest-first schedule of the batch.
     struct Schedule {

@@ -80,6 +80,26 @@ def f32_from_bf16_bits(bits: np.ndarray) -> np.ndarray:
 
 BF16_NAN = np.uint16(0x7FC0)
 
+# FP8 pools: E4M3 codes (0x7F is a NaN code); per-pool scales, as multiples of
+# the draws' standard deviation, chosen so that the largest draws stay well
+# inside the format's range (|x / scale| < 448 up to ~10 sigma)
+FP8_NAN = np.uint8(0x7F)
+FP8_SCALES = (0.0271, 0.0193)
+
+
+def _fp8_codes(a: np.ndarray, scale: float) -> np.ndarray:
+    """E4M3 codes of a / scale through torch's float8_e4m3fn cast (chunked)."""
+    import torch
+
+    flat = a.reshape(-1)
+    out = np.empty(flat.size, dtype=np.uint8)
+    inv = np.float32(1.0 / scale)
+    for lo in range(0, flat.size, CHUNK):
+        hi = min(flat.size, lo + CHUNK)
+        t = torch.from_numpy(flat[lo:hi] * inv)
+        out[lo:hi] = t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return out.reshape(a.shape)
+
 
 def _rng(seed: int, stream: int, chunk: int = 0) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(stream, chunk))))
@@ -180,7 +200,7 @@ class Workload:
     config: int
     seed: int
     mode: str
-    dtype: str                 # "f32" | "bf16"
+    dtype: str                 # "f32" | "bf16" | "fp8" (E4M3 pool codes; q, new k/v in bf16)
     S: int
     Hq: int
     Hkv: int
@@ -202,6 +222,8 @@ class Workload:
     poison_block: int
     description: str = ""
     extra: dict = field(default_factory=dict)
+    k_scale: float = 1.0       # fp8 pools: stored value = code * scale
+    v_scale: float = 1.0
 
     @property
     def x(self) -> int:
@@ -209,7 +231,7 @@ class Workload:
 
     @property
     def elem_bytes(self) -> int:
-        return 4 if self.dtype == "f32" else 2
+        return {"f32": 4, "bf16": 2, "fp8": 1}[self.dtype]
 
     @property
     def G(self) -> int:
@@ -365,24 +387,38 @@ def make_workload(config: int, mode: str = "parity", *, S: Optional[int] = None,
     Hq_, Hkv_, hs_ = c["Hq"], c["Hkv"], c["hs"]
     if Hq_ % Hkv_:
         raise ValueError("Hq must be a multiple of Hkv")
-    esz = 4 if dt == "f32" else 2
+    esz = {"f32": 4, "bf16": 2, "fp8": 1}[dt]
     x = 16 // esz
-    np_t = np.float32 if dt == "f32" else np.uint16
+    np_t = np.float32 if dt == "f32" else np.uint16   # q and the new k, v (bf16 for fp8 pools)
     std = c["std"]
     q = np.empty((S, Hq_, hs_), dtype=np_t)
     fill_normal(q, seed, STREAM_Q, std)
-    kc = np.empty((nb, Hkv_, hs_ // x, Bsz, x), dtype=np_t)
-    fill_normal(kc, seed, STREAM_K, std)
-    vc = np.empty((nb, Hkv_, hs_, Bsz), dtype=np_t)
-    fill_normal(vc, seed, STREAM_V, std)
+    k_scale = v_scale = 1.0
+    if dt == "fp8":
+        # pool contents as E4M3 codes of the same normal draws divided by a per-pool
+        # scale (torch's float8 cast: stored data, not this method's append)
+        k_scale, v_scale = FP8_SCALES[0] * std, FP8_SCALES[1] * std
+        kf = np.empty((nb, Hkv_, hs_ // x, Bsz, x), dtype=np.float32)
+        fill_normal(kf, seed, STREAM_K, std)
+        kc = _fp8_codes(kf, k_scale)
+        del kf
+        vf = np.empty((nb, Hkv_, hs_, Bsz), dtype=np.float32)
+        fill_normal(vf, seed, STREAM_V, std)
+        vc = _fp8_codes(vf, v_scale)
+        del vf
+    else:
+        kc = np.empty((nb, Hkv_, hs_ // x, Bsz, x), dtype=np_t)
+        fill_normal(kc, seed, STREAM_K, std)
+        vc = np.empty((nb, Hkv_, hs_, Bsz), dtype=np_t)
+        fill_normal(vc, seed, STREAM_V, std)
     new = np.empty((2, S, Hkv_, hs_), dtype=np_t)
     fill_normal(new, seed, STREAM_NEW, std)
 
     # slots that hold no data: NaN (parity) or zero (timing)
     if mode == "parity":
-        bad = np.float32(np.nan) if dt == "f32" else BF16_NAN
+        bad = {"f32": np.float32(np.nan), "bf16": BF16_NAN, "fp8": FP8_NAN}[dt]
     else:
-        bad = np_t(0)
+        bad = kc.dtype.type(0)
     for b in range(nb):
         f = int(pool.fill[b])
         if f < Bsz:
@@ -391,6 +427,7 @@ def make_workload(config: int, mode: str = "parity", *, S: Optional[int] = None,
 
     scale = 1.0 / math.sqrt(hs_)
     return Workload(config=config, seed=seed, mode=mode, dtype=dt, S=S, Hq=Hq_, Hkv=Hkv_,
+                    k_scale=k_scale, v_scale=v_scale,
                     hs=hs_, B=Bsz, num_blocks=nb, M=M, scale=scale,
                     partition_tokens=512 if config == 4 else 0,
                     seq_lens=lens.astype(np.int32), block_tables=tables, q=q,

@@ -45,11 +45,12 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings_and_layout(lib):
     assert lib.pkv_status_string(OK) == b"PKV_OK"
     assert lib.pkv_status_string(WORKSPACE) == b"PKV_ERR_WORKSPACE"
-    assert lib.pkv_layout_version() == 1
+    assert lib.pkv_layout_version() == 2
+    assert lib.pkv_status_string(-5) == b"PKV_ERR_OUT_OF_BLOCKS"
 
 
-def desc(nb=32, hkv=8, B=16, hs=64, dtype=0):
-    return pkv.CacheDesc(nb, hkv, B, hs, dtype)
+def desc(nb=32, hkv=8, B=16, hs=64, dtype=0, k_scale=1.0, v_scale=1.0):
+    return pkv.CacheDesc(nb, hkv, B, hs, dtype, k_scale, v_scale)
 
 
 FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails first
@@ -70,6 +71,10 @@ def test_attention_rejects_bad_arguments(lib):
     assert attn(lib, d=desc(hs=96)) == UNSUPPORTED
     assert attn(lib, d=desc(B=8)) == UNSUPPORTED
     assert attn(lib, d=desc(dtype=7)) == UNSUPPORTED
+    # FP8 pools need positive finite scales
+    assert attn(lib, d=desc(dtype=2, k_scale=0.0)) == INVALID
+    assert attn(lib, d=desc(dtype=2, v_scale=float("inf"))) == INVALID
+    assert attn(lib, d=desc(dtype=2), S=0) == OK
     assert attn(lib, d=desc(nb=0)) == INVALID
     assert attn(lib, M=0) == INVALID
     assert attn(lib, S=-1) == INVALID

@@ -17,7 +17,7 @@ import pkv_inputs as pi
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-5, "bf16": 2e-3}
+TOL = {"f32": 1e-5, "bf16": 2e-3, "fp8": 2e-3}  # fp8 pools: bf16 outputs
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -97,7 +97,7 @@ def check_attention(w, got, ref):
     tol = TOL[w.dtype]
     assert np.isfinite(got).all(), "non-finite output"
     diff = np.abs(got - ref)
-    if w.dtype == "bf16":
+    if w.dtype in ("bf16", "fp8"):  # bf16 outputs
         big = np.abs(ref) >= 1.0
         if big.any():
             announce(f"  {int(big.sum())} outputs with |out| >= 1 held to 1 bf16 ulp; "
