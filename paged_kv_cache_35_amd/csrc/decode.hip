@@ -277,6 +277,60 @@ __device__ __forceinline__ void fp8_to_operands(const Fp8Regs<HS>& raw, TileRegs
     }
 }
 
+// FP8 pools with B = 32: the whole block as one 32-token unit, like the bf16
+// 32-token path.  Key M-tile mp holds tokens 16mp .. 16mp+15 (chunk 4i + r
+// of token 16mp + c; two 128-byte lines per lane group); the value operand is
+// 8 codes per lane, tokens 8r .. 8r+7 of head dim 16i + c (the four lane
+// groups read the dim's whole 32-byte row).
+template <int HS>
+struct Fp8WideRegs {
+    u32x4 k[2][HS / 64];
+    unsigned v[HS / 16][2];
+};
+
+template <int HS>
+__device__ __forceinline__ void load_fp8_wide(Fp8WideRegs<HS>& t, const uint8_t* __restrict__ tile_k,
+                                              const uint8_t* __restrict__ tile_v, int r, int c)
+{
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int mp = 0; mp < 2; ++mp)
+#pragma unroll
+        for (int i = 0; i < HS / 64; ++i)
+            t.k[mp][i] = load_stream((const u32x4*)(tile_k + ((4 * i + r) * 32 + 16 * mp + c) * 16));
+#pragma unroll
+    for (int i = 0; i < HS / 16; ++i) {
+        const u32x2 w = load_stream_v((const u32x2*)(tile_v + (16 * i + c) * 32 + 8 * r));
+        t.v[i][0] = w[0];
+        t.v[i][1] = w[1];
+    }
+}
+
+template <int HS>
+__device__ __forceinline__ void fp8_wide_to_operands(const Fp8WideRegs<HS>& raw, WideRegs<HS>& t)
+{
+#pragma unroll
+    for (int mp = 0; mp < 2; ++mp)
+#pragma unroll
+        for (int i = 0; i < HS / 64; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                unsigned a, b, c, d;
+                fp8x4_to_bf16(raw.k[mp][i][2 * h], a, b);
+                fp8x4_to_bf16(raw.k[mp][i][2 * h + 1], c, d);
+                const u32x4 w = {a, b, c, d};
+                t.k[mp].v[2 * i + h] = __builtin_bit_cast(bf16x8, w);
+            }
+#pragma unroll
+    for (int i = 0; i < HS / 16; ++i) {
+        unsigned a, b, c, d;
+        fp8x4_to_bf16(raw.v[i][0], a, b);
+        fp8x4_to_bf16(raw.v[i][1], c, d);
+        const u32x4 w = {a, b, c, d};
+        t.v[i] = __builtin_bit_cast(bf16x8, w);
+    }
+}
+
 // Scores S^T for one 16-token sub-tile: element j of the result is token
 // 4r + j of the sub-tile, query head c.
 template <typename T, int HS>
@@ -342,10 +396,10 @@ __device__ __forceinline__ void zero_masked_values(TileRegs<T, HS>& t, int tok0,
 
 // Occupancy targets for bf16: three waves per SIMD with 16-token blocks
 // (<= 168 VGPRs, including the MFMA accumulators), two with 32-token units
-// (<= 256); FP8 pools (smaller raw operands) also three.  The fp32 variants
-// (larger operands) are left unconstrained.
+// (<= 256), for bf16 and FP8 pools alike.  The fp32 variants (larger
+// operands) are left unconstrained.
 #define PKV_OCCUPANCY \
-    __attribute__((amdgpu_waves_per_eu(F8 ? 3 : (sizeof(T) == 2 ? (BS == 16 ? 3 : 2) : 1))))
+    __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (BS == 16 ? 3 : 2) : 1)))
 
 // T: element type of q and out (and of the pools unless F8).  F8: the pools
 // hold E4M3 codes (T is bf16); keys are read as code * k_scale (folded into
@@ -363,7 +417,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
 {
     using C = typename std::conditional<F8, uint8_t, T>::type;  // pool element type
     static_assert(!F8 || sizeof(T) == 2, "FP8 pools are read with bf16 queries");
-    constexpr bool kWide = sizeof(T) == 2 && BS == 32 && !F8;  // 32-token units (see WideRegs)
+    constexpr bool kWide = sizeof(T) == 2 && BS == 32;  // 32-token units (see WideRegs, Fp8WideRegs)
     constexpr int UT = kWide ? 32 : 16;                 // tokens per pipeline unit
     constexpr int PER = BS / UT;                        // units per block
     constexpr int TILE = HS * BS;                       // elements per (block, KV head) tile
@@ -624,18 +678,21 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     // steady-state loop always prefetches and the last one or two units are
     // peeled, so every compute is preceded by exactly one batch of loads and
     // the memory-counter waits stay precise.
-    using Regs = typename std::conditional<kWide, WideRegs<HS>,
-                                           typename std::conditional<F8, Fp8Regs<HS>, TileRegs<T, HS>>::type>::type;
+    using Regs = typename std::conditional<
+        F8, typename std::conditional<kWide, Fp8WideRegs<HS>, Fp8Regs<HS>>::type,
+        typename std::conditional<kWide, WideRegs<HS>, TileRegs<T, HS>>::type>::type;
     const int nunits = nb_w * PER;  // 0 for a wave past the end
     auto issue = [&](Regs& t, int u) __attribute__((always_inline)) -> bool {
         const int j = u / PER;
         const C* tk;
         const C* tv;
         const bool ok = tile_ptr_ok(j, tk, tv);
-        if constexpr (kWide)
-            load_wide<HS>(t, tk, tv, r, c);
+        if constexpr (F8 && kWide)
+            load_fp8_wide<HS>(t, tk, tv, r, c);
         else if constexpr (F8)
             load_fp8<HS, BS>(t, tk, tv, u % PER, r, c);
+        else if constexpr (kWide)
+            load_wide<HS>(t, tk, tv, r, c);
         else
             load_tile<T, HS, BS>(t, tk, tv, u % PER, r, c);
         return ok;
@@ -643,7 +700,11 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     auto first_token = [&](int u) __attribute__((always_inline)) { return (base + (u / PER) * stride) * BS + UT * (u % PER); };
     auto run = [&](Regs& t, int u, bool ok) __attribute__((always_inline)) {
         const int tok0 = first_token(u);
-        if constexpr (kWide) {
+        if constexpr (F8 && kWide) {
+            WideRegs<HS> op;  // the raw codes as bf16 operands
+            fp8_wide_to_operands<HS>(t, op);
+            compute_wide(op, tok0, ok);
+        } else if constexpr (kWide) {
             compute_wide(t, tok0, ok);
         } else if constexpr (F8) {
             TileRegs<__bf16, HS> op;  // the raw codes as bf16 operands
