@@ -70,6 +70,11 @@ def _bind(path: str):
     L.orc_fp8_quantize.argtypes = [P, i64, i32, ctypes.c_float, P]
     L.orc_kv_append_fp8.restype = None
     L.orc_kv_append_fp8.argtypes = [P, P, P, i32, i32, i32, i32, i32, ctypes.c_float, ctypes.c_float, P, P]
+    L.orc_multi_token_slot_mapping.restype = None
+    L.orc_multi_token_slot_mapping.argtypes = [P, P, P, i32, i32, i32, P]
+    L.orc_paged_multi_token_attention.restype = ctypes.c_int
+    L.orc_paged_multi_token_attention.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f64, f64, f64,
+                                              P, ctypes.c_int]
     L.orc_paged_attention_units_kv.restype = ctypes.c_int
     L.orc_paged_attention_units_kv.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, i32, f64, f64,
                                                f64, P, i64, P, ctypes.c_int]
@@ -153,6 +158,18 @@ def decode_slot_mapping(block_tables: np.ndarray, seq_lens: np.ndarray, B: int) 
     S, M = t.shape
     out = np.empty(S, dtype=np.int64)
     lib().orc_decode_slot_mapping(_ptr(t), _ptr(L), S, M, B, _ptr(out))
+    return out
+
+
+def multi_token_slot_mapping(block_tables: np.ndarray, seq_lens: np.ndarray, q_start: np.ndarray,
+                             B: int) -> np.ndarray:
+    """Slots of the query rows: row i of sequence s at position L_s - n_s + i."""
+    t = np.ascontiguousarray(block_tables, dtype=np.int32)
+    L = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(q_start, dtype=np.int32)
+    S, M = t.shape
+    out = np.empty(int(qs[-1]), dtype=np.int64)
+    lib().orc_multi_token_slot_mapping(_ptr(t), _ptr(L), _ptr(qs), S, M, B, _ptr(out))
     return out
 
 
@@ -302,3 +319,41 @@ def paged_attention_fp8(q, k_pool, v_pool, block_tables, seq_lens, scale, k_scal
                                        t.shape[1], _dtype_code(q), ORC_FP8, float(k_scale), float(v_scale),
                                        float(scale), uptr, n, _ptr(out), int(threads))
     return out
+
+
+# ---- several query tokens per sequence -------------------------------------
+
+def paged_multi_token_attention(q, q_start, k_pool, v_pool, block_tables, seq_lens, scale, *, k_scale=1.0,
+                            v_scale=1.0, threads=0):
+    """fp64 [rows, Hq, hs]: query row i of sequence s (rows q_start[s] ..
+    q_start[s+1]-1, the last tokens of its seq_lens[s]) attends the positions
+    up to its own (causal).  Pools: fp32, bf16 bits or uint8 E4M3 codes."""
+    q = np.ascontiguousarray(q)
+    rows, Hq, hs = q.shape
+    kv_dt = ORC_FP8 if k_pool.dtype == np.uint8 else _dtype_code(k_pool)
+    Hkv, B = k_pool.shape[1], k_pool.shape[3]
+    t = np.ascontiguousarray(block_tables, dtype=np.int32)
+    L = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    qs = np.ascontiguousarray(q_start, dtype=np.int32)
+    assert qs[-1] == rows and len(qs) == len(L) + 1
+    out = np.empty((rows, Hq, hs), dtype=np.float64)
+    lib().orc_paged_multi_token_attention(_ptr(q), _ptr(qs), _ptr(k_pool), _ptr(v_pool), _ptr(t), _ptr(L), len(L), Hq,
+                                      Hkv, hs, B, t.shape[1], _dtype_code(q), kv_dt, float(k_scale), float(v_scale),
+                                      float(scale), _ptr(out), int(threads))
+    return out
+
+
+def multi_token_step(w, threads=0):
+    """One step with several query tokens per sequence (w.q_start set): slot
+    mapping of the rows, append of all of them into copies of the pools,
+    causal attention.  Returns (slots, k_pool, v_pool, out[fp64])."""
+    slots = multi_token_slot_mapping(w.block_tables, w.seq_lens, w.q_start, w.B)
+    kp = w.k_cache.copy()
+    vp = w.v_cache.copy()
+    if w.dtype == "fp8":
+        kv_append_fp8(w.new_k, w.new_v, slots, kp, vp, fp8_inv_scale(w.k_scale), fp8_inv_scale(w.v_scale))
+    else:
+        kv_append(w.new_k, w.new_v, slots, kp, vp)
+    out = paged_multi_token_attention(w.q, w.q_start, kp, vp, w.block_tables, w.seq_lens, w.scale,
+                                      k_scale=w.k_scale, v_scale=w.v_scale, threads=threads)
+    return slots, kp, vp, out

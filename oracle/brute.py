@@ -59,3 +59,45 @@ def attention(q, k_flat, v_flat, tables, lens, scale, Hq, Hkv, hs, B, is_bf16):
             rows.append(o)
         out.append(rows)
     return out
+
+
+def causal_attention(q, q_start, k_flat, v_flat, tables, lens, scale, Hq, Hkv, hs, B, is_bf16):
+    """Several query rows per sequence with the causal rule: rows q_start[s]
+    .. q_start[s+1]-1 of q (nested list [rows][Hq][hs]) are the last n of the
+    sequence's L tokens, row i at position L - n + i, and each sees the
+    tokens at positions 0 .. its own.  Returns nested list [rows][Hq][hs]."""
+    x = 8 if is_bf16 else 4
+    G = Hq // Hkv
+    out = [None] * q_start[-1]
+    for s in range(len(lens)):
+        L = int(lens[s])
+        n = q_start[s + 1] - q_start[s]
+        for i in range(n):
+            row = q_start[s] + i
+            visible = L - n + i + 1
+            heads = []
+            for h in range(Hq):
+                kvh = h // G
+                scores = []
+                for t in range(visible):
+                    blk = int(tables[s][t // B])
+                    j = t % B
+                    acc = 0.0
+                    for d in range(hs):
+                        kpos = (((blk * Hkv + kvh) * (hs // x) + d // x) * B + j) * x + d % x
+                        acc += _as_float(q[row][h][d], is_bf16) * _as_float(k_flat[kpos], is_bf16)
+                    scores.append(acc * scale)
+                m = max(scores)
+                w = [math.exp(sc - m) for sc in scores]
+                z = sum(w)
+                o = []
+                for d in range(hs):
+                    acc = 0.0
+                    for t in range(visible):
+                        blk = int(tables[s][t // B])
+                        vpos = ((blk * Hkv + kvh) * hs + d) * B + t % B
+                        acc += w[t] * _as_float(v_flat[vpos], is_bf16)
+                    o.append(acc / z)
+                heads.append(o)
+            out[row] = heads
+    return out

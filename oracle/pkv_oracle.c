@@ -160,6 +160,23 @@ void orc_decode_slot_mapping(const int32_t* block_tables, const int32_t* seq_len
     }
 }
 
+/* Several new tokens per sequence: rows q_start[s] .. q_start[s+1]-1 are the
+ * last n_s of sequence s's L_s tokens, so row i of s sits at position
+ * L_s - n_s + i.  A row whose position falls outside 0 .. L_s - 1 gets -1. */
+void orc_multi_token_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens, const int32_t* q_start,
+                                  int32_t S, int32_t M, int32_t B, int64_t* slots)
+{
+    for (int32_t s = 0; s < S; ++s) {
+        int64_t L = seq_lens[s];
+        int64_t n = (int64_t)q_start[s + 1] - q_start[s];
+        for (int64_t i = 0; i < n; ++i) {
+            int64_t pos = L - n + i;
+            slots[q_start[s] + i] =
+                (pos >= 0 && pos < L) ? orc_slot_of_position(block_tables + (size_t)s * M, pos, B) : -1;
+        }
+    }
+}
+
 /* ---- append: copy each new token's K and V into its slot ----------------- */
 
 void orc_kv_append(const void* k, const void* v, const int64_t* slots, int32_t T,
@@ -222,16 +239,16 @@ typedef struct {
     double k_scale, v_scale;   /* pool values are element * scale (1 unless FP8) */
 } orc_problem;
 
-/* Score of logical token t for query head h of sequence s:
- * scale * sum_d q[s,h,d] * K[t,d], where K[t] is found through the table. */
-static double orc_score(const orc_problem* p, int32_t s, int32_t h, int32_t kvh, int64_t t)
+/* Score of logical token t of sequence s for query head h of query row qr:
+ * scale * sum_d q[qr,h,d] * K[t,d], where K[t] is found through the table. */
+static double orc_score(const orc_problem* p, int32_t s, int64_t qr, int32_t h, int32_t kvh, int64_t t)
 {
     int64_t block_idx = t / p->B;
     int64_t slot = t % p->B;
     int64_t block = p->block_tables[(size_t)s * p->M + block_idx];
     double dot = 0.0;
     for (int32_t d = 0; d < p->hs; ++d) {
-        double qd = orc_load(p->q, ((size_t)s * p->Hq + h) * p->hs + d, p->dtype);
+        double qd = orc_load(p->q, ((size_t)qr * p->Hq + h) * p->hs + d, p->dtype);
         double kd = p->k_scale *
                     orc_load(p->k_pool, orc_key_index(block, kvh, slot, d, p->Hkv, p->B, p->hs, p->x), p->kv_dtype);
         dot += qd * kd;
@@ -246,10 +263,10 @@ static double orc_value(const orc_problem* p, int32_t s, int32_t kvh, int64_t t,
                                  p->kv_dtype);
 }
 
-/* Softmax attention of one (sequence, query head) over tokens [t0, t1):
+/* Softmax attention of query row qr, head h of sequence s over tokens [t0, t1):
  * m = max score, w_t = exp(score_t - m), l = sum w_t, o = sum w_t v_t / l.
  * `score` is scratch of length >= t1 - t0.  Returns 0 when the range is empty. */
-static int orc_attend_range(const orc_problem* p, int32_t s, int32_t h, int64_t t0, int64_t t1,
+static int orc_attend_range(const orc_problem* p, int32_t s, int64_t qr, int32_t h, int64_t t0, int64_t t1,
                             double* score, double* m_out, double* l_out, double* o)
 {
     int32_t kvh = h / (p->Hq / p->Hkv);
@@ -261,7 +278,7 @@ static int orc_attend_range(const orc_problem* p, int32_t s, int32_t h, int64_t 
     }
     double m = -INFINITY;
     for (int64_t t = t0; t < t1; ++t) {
-        score[t - t0] = orc_score(p, s, h, kvh, t);
+        score[t - t0] = orc_score(p, s, qr, h, kvh, t);
         if (score[t - t0] > m) m = score[t - t0];
     }
     double l = 0.0;
@@ -320,7 +337,7 @@ int orc_paged_attention_units_kv(const void* q, const void* k_pool, const void* 
             int64_t u = units ? units[i] : i;
             int32_t s = (int32_t)(u / Hq), h = (int32_t)(u % Hq);
             double m, l;
-            orc_attend_range(&p, s, h, 0, seq_lens[s], score, &m, &l, out + (size_t)i * hs);
+            orc_attend_range(&p, s, s, h, 0, seq_lens[s], score, &m, &l, out + (size_t)i * hs);
         }
         free(score);
     }
@@ -379,7 +396,7 @@ int orc_paged_attention_split(const void* q, const void* k_pool, const void* v_p
             /* partials */
             for (int64_t k = 0; k < nparts; ++k) {
                 int64_t t0 = k * P, t1 = (t0 + P < L) ? t0 + P : L;
-                orc_attend_range(&p, s, h, t0, t1, score, &pm[k], &pl[k], po + k * hs);
+                orc_attend_range(&p, s, s, h, t0, t1, score, &pm[k], &pl[k], po + k * hs);
             }
             /* merge */
             double Mx = -INFINITY;
@@ -401,6 +418,45 @@ int orc_paged_attention_split(const void* q, const void* k_pool, const void* v_p
         free(pm);
         free(pl);
         free(po);
+    }
+    return nt;
+}
+
+/* Several query tokens per sequence (chunked prefill, speculative decoding):
+ * the query tokens of sequence s are rows q_start[s] .. q_start[s+1]-1 of q
+ * ([rows][Hq][hs]); they are the last n_s = q_start[s+1] - q_start[s] of its
+ * L_s = seq_lens[s] tokens, in order, so query row i of s sits at position
+ * L_s - n_s + i and attends the tokens at positions 0 .. L_s - n_s + i (the
+ * causal rule: a token sees itself and everything before it).  out has the
+ * layout of q.  Pools of element type kv_dtype (FP8 read as code * scale). */
+int orc_paged_multi_token_attention(const void* q, const int32_t* q_start, const void* k_pool, const void* v_pool,
+                                const int32_t* block_tables, const int32_t* seq_lens, int32_t S, int32_t Hq,
+                                int32_t Hkv, int32_t hs, int32_t B, int32_t M, int32_t dtype, int32_t kv_dtype,
+                                double k_scale, double v_scale, double scale, double* out, int threads)
+{
+    orc_problem p = { q, k_pool, v_pool, block_tables, seq_lens, S, Hq, Hkv, hs, B, M, dtype,
+                      orc_x(kv_dtype), scale, kv_dtype, k_scale, v_scale };
+    int64_t maxL = 0;
+    for (int32_t s = 0; s < S; ++s)
+        if (seq_lens[s] > maxL) maxL = seq_lens[s];
+    int64_t rows = q_start[S];
+    int nt = orc_run_threads(threads);
+#pragma omp parallel num_threads(nt)
+    {
+        double* score = (double*)malloc(sizeof(double) * (size_t)(maxL > 0 ? maxL : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t u = 0; u < rows * Hq; ++u) {
+            int64_t qr = u / Hq;
+            int32_t h = (int32_t)(u % Hq);
+            int32_t s = 0;
+            while (q_start[s + 1] <= qr)
+                ++s;
+            int64_t n = q_start[s + 1] - q_start[s];
+            int64_t pos = (int64_t)seq_lens[s] - n + (qr - q_start[s]);
+            double m, l;
+            orc_attend_range(&p, s, qr, h, 0, pos + 1, score, &m, &l, out + (size_t)u * hs);
+        }
+        free(score);
     }
     return nt;
 }

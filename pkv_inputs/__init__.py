@@ -25,7 +25,11 @@ Workloads (one per decode configuration):
      tails of 1..512 tokens; 32/8 heads, head size 128, B=16.
 
 Every decode step appends one token per sequence at position L-1 and then
-attends over all L tokens.  Before the append the slot of that position holds
+attends over all L tokens.  With `q_lens` (several query tokens per sequence:
+a prefill chunk, or the draft tokens of speculative decoding) sequence s has
+n_s = q_lens[s] query tokens, the last n_s of its L_s, stored as rows
+q_start[s] .. q_start[s+1]-1 of q and of the new k/v; the step appends all of
+them and then attends causally.  Before the append the slot of that position holds
 NaN (parity mode), so a missing or misplaced append shows up in the output.
 
 Pool formats (element type T, x = 16 / sizeof(T) elements per 16-byte chunk):
@@ -212,11 +216,11 @@ class Workload:
     partition_tokens: int      # 0 = implementation's choice
     seq_lens: np.ndarray       # int32 [S]
     block_tables: np.ndarray   # int32 [S, M]
-    q: np.ndarray              # [S, Hq, hs] float32 or uint16 bits
+    q: np.ndarray              # [rows, Hq, hs] float32 or uint16 bits (rows = S for decode)
     k_cache: np.ndarray        # [nb, Hkv, hs/x, B, x]
     v_cache: np.ndarray        # [nb, Hkv, hs, B]
-    new_k: np.ndarray          # [S, Hkv, hs]
-    new_v: np.ndarray          # [S, Hkv, hs]
+    new_k: np.ndarray          # [rows, Hkv, hs]
+    new_v: np.ndarray          # [rows, Hkv, hs]
     ref_count: np.ndarray      # int32 [nb]
     fill: np.ndarray           # int32 [nb] slots holding data before the append
     poison_block: int
@@ -224,6 +228,15 @@ class Workload:
     extra: dict = field(default_factory=dict)
     k_scale: float = 1.0       # fp8 pools: stored value = code * scale
     v_scale: float = 1.0
+    q_start: Optional[np.ndarray] = None  # int32 [S+1]: query rows of each sequence (None: one each)
+
+    @property
+    def rows(self) -> int:
+        return self.S if self.q_start is None else int(self.q_start[-1])
+
+    @property
+    def max_q_len(self) -> int:
+        return 1 if self.q_start is None else int(np.diff(self.q_start).max(initial=0))
 
     @property
     def x(self) -> int:
@@ -294,14 +307,16 @@ def make_workload(config: int, mode: str = "parity", *, S: Optional[int] = None,
                   seed: Optional[int] = None, seq_lens: Optional[list] = None,
                   dtype: Optional[str] = None, hs: Optional[int] = None,
                   B: Optional[int] = None, Hq: Optional[int] = None,
-                  Hkv: Optional[int] = None, contiguous: bool = False) -> Workload:
+                  Hkv: Optional[int] = None, contiguous: bool = False, q_lens=None) -> Workload:
     """Build one decode step's inputs.
 
     mode "parity": slots and blocks that hold no data are NaN (they must never
     influence a result); mode "timing": they are zero.
     The keyword overrides shrink or reshape a configuration for fast tests
     while keeping its structure (for config 5, `len_hi` is the shared prompt
-    length and must be a multiple of B)."""
+    length and must be a multiple of B).  q_lens (an int for every sequence,
+    or one per sequence; each at most the sequence's length, and for config 5
+    within its private tail) gives several query tokens per sequence."""
     if mode not in ("parity", "timing"):
         raise ValueError(mode)
     c = dict(_CFG[config])
@@ -320,6 +335,13 @@ def make_workload(config: int, mode: str = "parity", *, S: Optional[int] = None,
         lens = _draw_lens(config, seed, S, len_lo, len_hi)
     nblk = [-(-int(L) // Bsz) for L in lens]
     M = max(1, max(nblk) if len(nblk) else 1)
+    if q_lens is None:
+        qn = np.ones(S, dtype=np.int64)
+    else:
+        qn = np.broadcast_to(np.asarray(q_lens, dtype=np.int64), (S,)).copy()
+        if (qn < 0).any() or (qn > lens).any():
+            raise ValueError("query tokens must be between 0 and the sequence length")
+    rows = int(qn.sum())
 
     # ---- physical block assignment (allocator fixture) ----
     pg = _rng(seed, STREAM_PERM)
@@ -373,11 +395,13 @@ def make_workload(config: int, mode: str = "parity", *, S: Optional[int] = None,
         pool.write_tokens(0, shared_n * Bsz)  # the prompt is stored once
         for s in range(S):
             # the shared blocks are full, so these tokens land in the tail
-            pool.write_tokens(s, int(lens[s]) - 1 - shared_n * Bsz)
+            if int(lens[s]) - int(qn[s]) < shared_n * Bsz:
+                raise ValueError("query tokens must lie in the private tail")
+            pool.write_tokens(s, int(lens[s]) - int(qn[s]) - shared_n * Bsz)
     else:
         for s in range(S):
             pool.add_sequence(pool.take(nblk[s]))
-            pool.write_tokens(s, int(lens[s]) - 1)
+            pool.write_tokens(s, int(lens[s]) - int(qn[s]))
     tables = np.full((S, M), poison, dtype=np.int32)
     for s, row in enumerate(pool.tables):
         tables[s, :len(row)] = row
@@ -391,7 +415,7 @@ def make_workload(config: int, mode: str = "parity", *, S: Optional[int] = None,
     x = 16 // esz
     np_t = np.float32 if dt == "f32" else np.uint16   # q and the new k, v (bf16 for fp8 pools)
     std = c["std"]
-    q = np.empty((S, Hq_, hs_), dtype=np_t)
+    q = np.empty((rows, Hq_, hs_), dtype=np_t)
     fill_normal(q, seed, STREAM_Q, std)
     k_scale = v_scale = 1.0
     if dt == "fp8":
@@ -411,7 +435,7 @@ def make_workload(config: int, mode: str = "parity", *, S: Optional[int] = None,
         fill_normal(kc, seed, STREAM_K, std)
         vc = np.empty((nb, Hkv_, hs_, Bsz), dtype=np_t)
         fill_normal(vc, seed, STREAM_V, std)
-    new = np.empty((2, S, Hkv_, hs_), dtype=np_t)
+    new = np.empty((2, rows, Hkv_, hs_), dtype=np_t)
     fill_normal(new, seed, STREAM_NEW, std)
 
     # slots that hold no data: NaN (parity) or zero (timing)
@@ -433,7 +457,8 @@ def make_workload(config: int, mode: str = "parity", *, S: Optional[int] = None,
                     seq_lens=lens.astype(np.int32), block_tables=tables, q=q,
                     k_cache=kc, v_cache=vc, new_k=new[0], new_v=new[1],
                     ref_count=pool.ref_count.copy(), fill=pool.fill.copy(),
-                    poison_block=poison, description=c["desc"])
+                    poison_block=poison, description=c["desc"],
+                    q_start=None if q_lens is None else np.concatenate([[0], np.cumsum(qn)]).astype(np.int32))
 
 
 def relabel_blocks(w: Workload, seed: int) -> Workload:

@@ -12,6 +12,7 @@ sys.path.insert(0, os.path.dirname(HERE))
 
 import oracle  # noqa: E402
 import test_oracle_fp8 as F  # noqa: E402
+import test_oracle_multi_token as Q  # noqa: E402
 import test_oracle_pins as T  # noqa: E402
 
 CHECKS = [
@@ -33,6 +34,10 @@ CHECKS = [
     F.test_saturation_beyond_the_range,
     lambda: F.test_fp8_attention_matches_library_sdpa(16, 4),
     F.test_fp8_append_places_codes_of_each_token,
+    Q.test_multi_token_slot_mapping_places_rows_at_the_end,
+    lambda: Q.test_matches_library_causal_attention(1, dict(q_lens=[5, 16, 1, 50])),
+    lambda: Q.test_matches_library_causal_attention(3, dict(S=5, len_lo=16, len_hi=90, q_lens=4)),
+    Q.test_first_row_of_a_full_prefill_returns_the_first_value,
 ]
 
 

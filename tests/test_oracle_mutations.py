@@ -33,6 +33,13 @@ MUTATIONS = [
     ("fp8 ties away from even", "(err == best_err && (c & 1) == 0 && (best & 1) == 1)", "(err == best_err)"),
     ("fp8 overflow to NaN", "if (a > 448.0)\\n        return sign | 0x7E;", "if (a > 448.0)\\n        return sign | 0x7F;"),
     ("fp8 value scale on keys", "double kd = p->k_scale *", "double kd = p->v_scale *"),
+    ("causal limit excludes own token", "orc_attend_range(&p, s, qr, h, 0, pos + 1, score, &m, &l, out + (size_t)u * hs);",
+     "orc_attend_range(&p, s, qr, h, 0, pos, score, &m, &l, out + (size_t)u * hs);"),
+    ("query rows counted from the start", "int64_t pos = (int64_t)seq_lens[s] - n + (qr - q_start[s]);",
+     "int64_t pos = qr - q_start[s];"),
+    ("query row of the sequence", "double qd = orc_load(p->q, ((size_t)qr * p->Hq + h) * p->hs + d, p->dtype);",
+     "double qd = orc_load(p->q, ((size_t)s * p->Hq + h) * p->hs + d, p->dtype);"),
+    ("multi-token slot from the start", "int64_t pos = L - n + i;", "int64_t pos = i;"),
     ("fp8 key chunk of 8", "k_pool[orc_key_index(b, h, off, d, Hkv, B, hs, 16)]", "k_pool[orc_key_index(b, h, off, d, Hkv, B, hs, 8)]"),
 ]
 
