@@ -295,6 +295,85 @@ PKV_API pkv_status paged_decode_step(const void* q, const void* new_k, const voi
 
 /*
  * ---------------------------------------------------------------------------
+ * Several query tokens per sequence: chunked prefill, prefill of the tokens a
+ * prefix-cache lookup missed, and the draft tokens of speculative decoding
+ * ---------------------------------------------------------------------------
+ *
+ * The pages name these users of the paged cache ("vLLM 核心工程深度剖析",
+ * section 6.1 chunked prefill and section 9 speculative decoding; the
+ * cache-structure page, "分配与增长": prefill computes only the tokens that
+ * missed the cache and attends over the hit blocks as they are).  The rule
+ * used here: the query rows of sequence s are rows q_start[s] ..
+ * q_start[s+1]-1 of q, of out and of the new k/v; they are the LAST
+ * n_s = q_start[s+1] - q_start[s] of its seq_lens[s] = L_s tokens, so row i
+ * sits at position L_s - n_s + i, and it attends to the tokens at positions
+ * 0 .. L_s - n_s + i (itself and everything before it).
+ *
+ * Caller contract: q_start (int32 [num_seqs + 1], device) is nondecreasing
+ * from 0 to num_q_rows, 1 <= n_s <= max_q_len and n_s <= L_s for every
+ * sequence that has query rows.  The kernels never access memory outside
+ * the arguments when it is broken: a sequence whose rows fall outside
+ * 0 .. num_q_rows - 1 is skipped, rows past max_q_len are not computed, and
+ * a row whose position is negative (n_s > L_s) attends to nothing and gets
+ * zeros.  q and out: [num_q_rows][num_q_heads][head_size] in the query
+ * type; new k/v: [num_q_rows][num_kv_heads][head_size].
+ */
+
+/*
+ * Bytes of device workspace paged_multi_token_attention needs (0 when each
+ * sequence's table fits one chunk of partitions): one fp32 partial per
+ * (sequence, KV head, tile of 16 (row, group member) pairs, chunk, tile row).
+ * max_q_len <= 0 or an invalid shape gives 0.
+ */
+PKV_API size_t pkv_multi_token_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                               int32_t head_size, int32_t max_q_len, int32_t max_blocks_per_seq,
+                                               int32_t block_size, int32_t partition_tokens);
+
+/*
+ * slot_mapping[q_start[s] + i] = slot of position L_s - n_s + i (the slot
+ * rule of pkv_decode_slot_mapping), or -1 when that position lies outside
+ * 0 .. L_s - 1 or past the table row.  Rows of no sequence are not written.
+ * Asynchronous on `stream`.  PKV_ERR_UNSUPPORTED for num_seqs > 65535.
+ */
+PKV_API pkv_status pkv_multi_token_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens,
+                                                const int32_t* q_start, int32_t num_seqs, int32_t num_q_rows,
+                                                int32_t max_q_len, int32_t max_blocks_per_seq,
+                                                int32_t block_size, int64_t* slot_mapping, void* stream);
+
+/*
+ * Causal paged attention of every query row (rule above) over its
+ * sequence's cached tokens, read through block_tables as in
+ * paged_decode_attention (same pools, scale, partition_tokens and workspace
+ * rules; workspace of pkv_multi_token_workspace_bytes).  The tokens of the
+ * query rows themselves must already be in the cache (kv_cache_append with
+ * pkv_multi_token_slot_mapping, or paged_multi_token_step).
+ * PKV_ERR_UNSUPPORTED for max_q_len > 65535 or num_seqs > 65535.
+ */
+PKV_API pkv_status paged_multi_token_attention(const void* q, const int32_t* q_start, int32_t num_q_rows,
+                                               int32_t max_q_len, const void* k_cache, const void* v_cache,
+                                               const int32_t* block_tables, const int32_t* seq_lens,
+                                               int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                               const pkv_cache_desc* cache, float scale, void* out,
+                                               void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                                               void* stream);
+
+/*
+ * One multi-token step: slot mapping of the rows into slot_mapping (int64
+ * [num_q_rows], device, required), append of new_k/new_v of every row
+ * (kv_cache_append), then paged_multi_token_attention.  Three kernels in
+ * stream order; every argument is checked before the first, so a rejected
+ * call changes nothing.
+ */
+PKV_API pkv_status paged_multi_token_step(const void* q, const void* new_k, const void* new_v, void* k_cache,
+                                          void* v_cache, const int32_t* q_start, int32_t num_q_rows,
+                                          int32_t max_q_len, const int32_t* block_tables, const int32_t* seq_lens,
+                                          int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                          const pkv_cache_desc* cache, float scale, void* out,
+                                          int64_t* slot_mapping, void* workspace, size_t workspace_bytes,
+                                          int32_t partition_tokens, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
  * Block copy and the host block pool (copy-on-write and fork)
  * ---------------------------------------------------------------------------
  */

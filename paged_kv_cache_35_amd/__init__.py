@@ -88,6 +88,16 @@ def library():
         L.paged_decode_step.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, ctypes.POINTER(CacheDesc), f32, P, P, P,
                                         sz, i32, P]
         L.pkv_copy_blocks.restype = i32
+        L.pkv_multi_token_workspace_bytes.restype = sz
+        L.pkv_multi_token_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+        L.pkv_multi_token_slot_mapping.restype = i32
+        L.pkv_multi_token_slot_mapping.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P]
+        L.paged_multi_token_attention.restype = i32
+        L.paged_multi_token_attention.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, i32,
+                                                  ctypes.POINTER(CacheDesc), f32, P, P, sz, i32, P]
+        L.paged_multi_token_step.restype = i32
+        L.paged_multi_token_step.argtypes = [P, P, P, P, P, P, i32, i32, P, P, i32, i32, i32,
+                                             ctypes.POINTER(CacheDesc), f32, P, P, P, sz, i32, P]
         L.pkv_copy_blocks.argtypes = [P, i32, ctypes.POINTER(CacheDesc), P, P, P]
         L.pkv_pool_create.restype = P
         L.pkv_pool_create.argtypes = [i32, i32]
@@ -361,6 +371,118 @@ def decode_step(q, k_cache, v_cache, block_tables, seq_lens, new_k, new_v, scale
     return paged_decode_step(q, new_k, new_v, k_cache, v_cache, block_tables, seq_lens, scale, out=out,
                              slot_mapping=slot_mapping, workspace=workspace, partition_tokens=partition_tokens,
                              stream=stream, k_scale=k_scale, v_scale=v_scale)
+
+
+# ---- several query tokens per sequence -------------------------------------
+# Rows q_start[s] .. q_start[s+1]-1 of q / out / new k, v belong to sequence s
+# and are its last n_s tokens; row i sits at position seq_lens[s] - n_s + i and
+# attends causally.  max_q_len (>= every n_s) is a host int, so that no call
+# waits for the device.
+
+def multi_token_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size, max_q_len, max_blocks_per_seq,
+                                block_size, partition_tokens=0) -> int:
+    return int(library().pkv_multi_token_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size, max_q_len,
+                                                         max_blocks_per_seq, block_size, partition_tokens))
+
+
+def alloc_multi_token_workspace(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                block_tables: torch.Tensor, max_q_len: int,
+                                partition_tokens: int = 0) -> Optional[torch.Tensor]:
+    desc = cache_desc(k_cache, v_cache)
+    n = multi_token_workspace_bytes(block_tables.shape[0], q.shape[1], desc.num_kv_heads, desc.head_size, max_q_len,
+                                    block_tables.shape[1], desc.block_size, partition_tokens)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def _check_rows(q, q_start, block_tables, seq_lens, desc, k_cache):
+    if q.dtype != io_dtype(k_cache):
+        raise ValueError("q must have the pools' dtype")
+    if q.dim() != 3 or q.shape[2] != desc.head_size:
+        raise ValueError("q must be [rows, Hq, head_size]")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32 or q_start.dtype != torch.int32:
+        raise ValueError("block_tables, seq_lens and q_start must be int32")
+    S = block_tables.shape[0]
+    if seq_lens.shape != (S,) or q_start.shape != (S + 1,):
+        raise ValueError("seq_lens must be [S] and q_start [S + 1]")
+    return S
+
+
+def multi_token_slot_mapping(block_tables: torch.Tensor, seq_lens: torch.Tensor, q_start: torch.Tensor,
+                             num_q_rows: int, max_q_len: int, block_size: int, out: Optional[torch.Tensor] = None,
+                             stream=None) -> torch.Tensor:
+    """int64 [num_q_rows]: the slot of each query row's position."""
+    S = block_tables.shape[0]
+    if out is None:
+        out = torch.empty(num_q_rows, dtype=torch.int64, device=block_tables.device)
+    if out.dtype != torch.int64 or out.shape != (num_q_rows,):
+        raise ValueError("slot_mapping must be int64 [rows]")
+    _check("pkv_multi_token_slot_mapping", library().pkv_multi_token_slot_mapping(
+        _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), _dev(q_start, "q_start"), S, num_q_rows,
+        int(max_q_len), block_tables.shape[1], int(block_size), _dev(out, "slot_mapping"), _stream(stream)))
+    return out
+
+
+def paged_multi_token_attention(q: torch.Tensor, q_start: torch.Tensor, max_q_len: int, k_cache: torch.Tensor,
+                                v_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
+                                scale: float, out: Optional[torch.Tensor] = None,
+                                workspace: Optional[torch.Tensor] = None, partition_tokens: int = 0, stream=None,
+                                k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+    """Causal paged attention of every query row over its sequence's cached
+    tokens (the rows' own tokens must already be in the cache)."""
+    desc = cache_desc(k_cache, v_cache, k_scale, v_scale)
+    S = _check_rows(q, q_start, block_tables, seq_lens, desc, k_cache)
+    rows, Hq, _ = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if workspace is None:
+        workspace = alloc_multi_token_workspace(q, k_cache, v_cache, block_tables, max_q_len, partition_tokens)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("paged_multi_token_attention", library().paged_multi_token_attention(
+        _dev(q, "q"), _dev(q_start, "q_start"), rows, int(max_q_len), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), S, Hq,
+        block_tables.shape[1], ctypes.byref(desc), float(scale), _dev(out, "out"), ws_ptr, ws_bytes,
+        int(partition_tokens), _stream(stream)))
+    return out
+
+
+def paged_multi_token_step(q: torch.Tensor, new_k: torch.Tensor, new_v: torch.Tensor, k_cache: torch.Tensor,
+                           v_cache: torch.Tensor, q_start: torch.Tensor, max_q_len: int, block_tables: torch.Tensor,
+                           seq_lens: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
+                           slot_mapping: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           partition_tokens: int = 0, stream=None, k_scale: float = 1.0,
+                           v_scale: float = 1.0) -> torch.Tensor:
+    """Slot mapping of the rows, append of every row's new_k / new_v, then
+    paged_multi_token_attention (three launches on one stream)."""
+    desc = cache_desc(k_cache, v_cache, k_scale, v_scale)
+    S = _check_rows(q, q_start, block_tables, seq_lens, desc, k_cache)
+    rows, Hq, _ = q.shape
+    if new_k.shape != new_v.shape or tuple(new_k.shape) != (rows, desc.num_kv_heads, desc.head_size):
+        raise ValueError("new_k and new_v must be [rows, Hkv, head_size]")
+    if new_k.dtype != io_dtype(k_cache) or new_v.dtype != io_dtype(k_cache):
+        raise ValueError("new_k, new_v and the pools must share a dtype")
+    if slot_mapping is None:
+        slot_mapping = torch.empty(rows, dtype=torch.int64, device=q.device)
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (rows,):
+        raise ValueError("slot_mapping must be int64 [rows]")
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    if workspace is None:
+        workspace = alloc_multi_token_workspace(q, k_cache, v_cache, block_tables, max_q_len, partition_tokens)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("paged_multi_token_step", library().paged_multi_token_step(
+        _dev(q, "q"), _dev(new_k, "new_k"), _dev(new_v, "new_v"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(q_start, "q_start"), rows, int(max_q_len), _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"),
+        S, Hq, block_tables.shape[1], ctypes.byref(desc), float(scale), _dev(out, "out"),
+        _dev(slot_mapping, "slot_mapping"), ws_ptr, ws_bytes, int(partition_tokens), _stream(stream)))
+    return out
 
 
 def copy_blocks(pairs: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:

@@ -276,6 +276,10 @@ pkv_status attention_args(const void* q, const void* k_cache, const void* v_cach
     a.sched_order = nullptr;
     a.sched_lens = nullptr;
     a.sched_tables = nullptr;
+    a.q_start = nullptr;
+    a.num_q_rows = num_seqs;
+    a.max_q_len = 1;
+    a.row_tiles = 1;
     a.q = q;
     a.k_cache = k_cache;
     a.v_cache = v_cache;
@@ -331,6 +335,140 @@ pkv_status paged_decode_attention(const void* q, const void* k_cache, const void
         a.sched_lens = p.lens;
         a.sched_tables = p.tables;
     }
+    return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+}
+
+size_t pkv_multi_token_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_size, int32_t max_q_len, int32_t max_blocks_per_seq,
+                                       int32_t block_size, int32_t partition_tokens)
+{
+    if (num_kv_heads <= 0 || max_q_len <= 0 || num_q_heads % num_kv_heads != 0)
+        return 0;
+    const int32_t P = pkv_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, head_size,
+                                                  max_blocks_per_seq, block_size, partition_tokens);
+    if (P <= 0)
+        return 0;
+    // one fp32 partial (o[hs], m, l) per (sequence, KV head, 16-row tile,
+    // chunk, tile row); none when one chunk covers the table
+    const int64_t cb = (int64_t)(P / block_size) * pkv::kDecodeWaves;
+    const int64_t chunks = (max_blocks_per_seq + cb - 1) / cb;
+    if (chunks <= 1)
+        return 0;
+    const int64_t G = num_q_heads / num_kv_heads;
+    const int64_t tiles = ((int64_t)max_q_len * G + 15) / 16;
+    return (size_t)num_seqs * num_kv_heads * tiles * chunks * 16 * ((size_t)head_size + 2) * sizeof(float);
+}
+
+pkv_status pkv_multi_token_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens,
+                                        const int32_t* q_start, int32_t num_seqs, int32_t num_q_rows,
+                                        int32_t max_q_len, int32_t max_blocks_per_seq, int32_t block_size,
+                                        int64_t* slot_mapping, void* stream)
+{
+    if (num_seqs < 0 || num_q_rows < 0 || max_q_len < 0 || max_blocks_per_seq <= 0 || block_size <= 0)
+        return PKV_ERR_INVALID_ARG;
+    if (num_seqs == 0 || num_q_rows == 0 || max_q_len == 0)
+        return PKV_OK;
+    if (!block_tables || !seq_lens || !q_start || !slot_mapping)
+        return PKV_ERR_INVALID_ARG;
+    if (num_seqs > 65535)
+        return PKV_ERR_UNSUPPORTED;
+    return hip_status(pkv::launch_multi_token_slot_mapping(block_tables, seq_lens, q_start, num_seqs, num_q_rows,
+                                                           max_q_len, max_blocks_per_seq, block_size, slot_mapping,
+                                                           (hipStream_t)stream));
+}
+
+namespace {
+
+// attention_args plus the query-row description of a multi-token call.
+pkv_status multi_token_args(const void* q, const int32_t* q_start, int32_t num_q_rows, int32_t max_q_len,
+                            const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                            const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                            int32_t max_blocks_per_seq, const pkv_cache_desc* cache, float scale, void* out,
+                            void* workspace, size_t workspace_bytes, int32_t partition_tokens, pkv::DecodeArgs& a,
+                            bool& nothing_to_do)
+{
+    if (num_q_rows < 0 || max_q_len < 0)
+        return PKV_ERR_INVALID_ARG;
+    // the decode workspace is never larger than the multi-token one, so the
+    // decode check in attention_args passes whenever the check below does
+    const size_t need = pkv_multi_token_workspace_bytes(num_seqs, num_q_heads, cache ? cache->num_kv_heads : 0,
+                                                        cache ? cache->head_size : 0, max_q_len > 0 ? max_q_len : 1,
+                                                        max_blocks_per_seq, cache ? cache->block_size : 0,
+                                                        partition_tokens);
+    pkv_status st = attention_args(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                                   max_blocks_per_seq, cache, scale, out, workspace,
+                                   need > workspace_bytes ? 0 : workspace_bytes, partition_tokens, a, nothing_to_do);
+    if (st != PKV_OK || nothing_to_do)
+        return st;
+    if (num_q_rows == 0 || max_q_len == 0) {
+        nothing_to_do = true;
+        return PKV_OK;
+    }
+    if (!q_start)
+        return PKV_ERR_INVALID_ARG;
+    const int64_t G = num_q_heads / cache->num_kv_heads;
+    const int64_t tiles = ((int64_t)max_q_len * G + 15) / 16;
+    if (max_q_len > 65535 || tiles * cache->num_kv_heads > INT32_MAX)
+        return PKV_ERR_UNSUPPORTED;
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+        return PKV_ERR_WORKSPACE;
+    a.q_start = q_start;
+    a.num_q_rows = num_q_rows;
+    a.max_q_len = max_q_len;
+    a.row_tiles = (int32_t)tiles;
+    const size_t units = (size_t)num_seqs * cache->num_kv_heads * tiles * a.max_parts * 16;
+    a.ws_o = need > 0 ? (float*)workspace : nullptr;
+    a.ws_ml = need > 0 ? (float*)workspace + units * cache->head_size : nullptr;
+    return PKV_OK;
+}
+
+}  // namespace
+
+pkv_status paged_multi_token_attention(const void* q, const int32_t* q_start, int32_t num_q_rows, int32_t max_q_len,
+                                       const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                       const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
+                                       int32_t max_blocks_per_seq, const pkv_cache_desc* cache, float scale,
+                                       void* out, void* workspace, size_t workspace_bytes, int32_t partition_tokens,
+                                       void* stream)
+{
+    pkv::DecodeArgs a;
+    bool nothing_to_do;
+    const pkv_status st = multi_token_args(q, q_start, num_q_rows, max_q_len, k_cache, v_cache, block_tables,
+                                           seq_lens, num_seqs, num_q_heads, max_blocks_per_seq, cache, scale, out,
+                                           workspace, workspace_bytes, partition_tokens, a, nothing_to_do);
+    if (st != PKV_OK || nothing_to_do)
+        return st;
+    return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+}
+
+pkv_status paged_multi_token_step(const void* q, const void* new_k, const void* new_v, void* k_cache,
+                                  void* v_cache, const int32_t* q_start, int32_t num_q_rows, int32_t max_q_len,
+                                  const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                                  int32_t num_q_heads, int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                                  float scale, void* out, int64_t* slot_mapping, void* workspace,
+                                  size_t workspace_bytes, int32_t partition_tokens, void* stream)
+{
+    // every argument is checked before the first launch, so a rejected call
+    // changes nothing
+    pkv::DecodeArgs a;
+    bool nothing_to_do;
+    pkv_status st = multi_token_args(q, q_start, num_q_rows, max_q_len, k_cache, v_cache, block_tables, seq_lens,
+                                     num_seqs, num_q_heads, max_blocks_per_seq, cache, scale, out, workspace,
+                                     workspace_bytes, partition_tokens, a, nothing_to_do);
+    if (st != PKV_OK || nothing_to_do)
+        return st;
+    if (!new_k || !new_v || !slot_mapping || !aligned16(new_k) || !aligned16(new_v))
+        return PKV_ERR_INVALID_ARG;
+    if (num_seqs > 65535)
+        return PKV_ERR_UNSUPPORTED;
+    st = hip_status(pkv::launch_multi_token_slot_mapping(block_tables, seq_lens, q_start, num_seqs, num_q_rows,
+                                                         max_q_len, max_blocks_per_seq, cache->block_size,
+                                                         slot_mapping, (hipStream_t)stream));
+    if (st != PKV_OK)
+        return st;
+    st = append_common(new_k, new_v, slot_mapping, nullptr, nullptr, 0, num_q_rows, cache, k_cache, v_cache, stream);
+    if (st != PKV_OK)
+        return st;
     return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
 }
 

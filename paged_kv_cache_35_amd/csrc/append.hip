@@ -37,6 +37,34 @@ __global__ void decode_slot_mapping_kernel(const int32_t* __restrict__ block_tab
         slot_mapping[s] = decode_slot(block_tables, seq_lens, s, max_blocks_per_seq, block_size);
 }
 
+// Work-group s, threads over the sequence's query rows i: row q_start[s] + i
+// sits at position L - n + i.  Rows are written only inside 0 .. num_q_rows - 1.
+__global__ void multi_token_slot_mapping_kernel(const int32_t* __restrict__ block_tables,
+                                                const int32_t* __restrict__ seq_lens,
+                                                const int32_t* __restrict__ q_start, int32_t num_q_rows,
+                                                int32_t max_q_len, int32_t max_blocks_per_seq, int32_t block_size,
+                                                int64_t* __restrict__ slot_mapping)
+{
+    const int32_t s = blockIdx.x;
+    const int32_t qs0 = q_start[s];
+    const int32_t qs1 = q_start[s + 1];
+    int32_t n = qs1 - qs0;
+    if (qs0 < 0 || n < 0 || qs1 > num_q_rows)
+        return;
+    n = n < max_q_len ? n : max_q_len;
+    const int32_t L = seq_lens[s];
+    for (int32_t i = threadIdx.x; i < n; i += blockDim.x) {
+        const int64_t pos = (int64_t)L - n + i;
+        const int64_t idx = pos >= 0 ? pos / block_size : -1;
+        int64_t slot = -1;
+        if (pos >= 0 && pos < L && idx < max_blocks_per_seq) {
+            const int64_t block = block_tables[(int64_t)s * max_blocks_per_seq + idx];
+            slot = block < 0 ? -1 : block * block_size + (pos - idx * block_size);
+        }
+        slot_mapping[qs0 + i] = slot;
+    }
+}
+
 constexpr int kAppendThreads = 256;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -254,6 +282,16 @@ hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* seq_l
     const int blocks = (num_seqs + threads - 1) / threads;
     hipLaunchKernelGGL(decode_slot_mapping_kernel, dim3(blocks), dim3(threads), 0, stream, block_tables,
                        seq_lens, num_seqs, max_blocks_per_seq, block_size, slot_mapping);
+    return hipGetLastError();
+}
+
+hipError_t launch_multi_token_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens,
+                                           const int32_t* q_start, int32_t num_seqs, int32_t num_q_rows,
+                                           int32_t max_q_len, int32_t max_blocks_per_seq, int32_t block_size,
+                                           int64_t* slot_mapping, hipStream_t stream)
+{
+    hipLaunchKernelGGL(multi_token_slot_mapping_kernel, dim3(num_seqs), dim3(256), 0, stream, block_tables, seq_lens,
+                       q_start, num_q_rows, max_q_len, max_blocks_per_seq, block_size, slot_mapping);
     return hipGetLastError();
 }
 

@@ -396,15 +396,27 @@ __device__ __forceinline__ void zero_masked_values(TileRegs<T, HS>& t, int tok0,
 
 // Occupancy targets for bf16: three waves per SIMD with 16-token blocks
 // (<= 168 VGPRs, including the MFMA accumulators), two with 32-token units
-// (<= 256), for bf16 and FP8 pools alike.  The fp32 variants (larger
-// operands) are left unconstrained.
+// (<= 256), for bf16 and FP8 pools alike; one wave less for FP8 pools with
+// several query tokens per sequence (the per-row causal limits would spill
+// at the decode targets).  The fp32 variants (larger operands) are left
+// unconstrained.
 #define PKV_OCCUPANCY \
-    __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (BS == 16 ? 3 : 2) : 1)))
+    __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (BS == 16 ? 3 : 2) - (F8 && MQ ? 1 : 0) : 1)))
 
 // T: element type of q and out (and of the pools unless F8).  F8: the pools
 // hold E4M3 codes (T is bf16); keys are read as code * k_scale (folded into
 // qscale) and values as code * v_scale (oscale, applied to the output).
-template <typename T, int HS, int BS, int NW, bool F8>
+//
+// MQ: several query tokens per sequence (a prefill chunk, or the draft
+// tokens of speculative decoding).  Sequence s has the n = q_start[s+1] -
+// q_start[s] query rows q_start[s] .. q_start[s+1]-1 of q and out; they are
+// its last n tokens, so row i sits at position L - n + i and attends the
+// tokens at positions 0 .. L - n + i (causal).  The (row, group member)
+// pairs rho = i * G + g form the MFMA tile's rows, 16 per tile: work-group
+// x = kvh * RT + rt takes rows 16 rt .. 16 rt + 15 of KV head kvh.  Without
+// MQ, sequence s has the one query row s at position L - 1 and the tile's
+// rows are the G heads of the group.
+template <typename T, int HS, int BS, int NW, bool F8, bool MQ>
 __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_kernel(
     const T* __restrict__ q, const typename std::conditional<F8, uint8_t, T>::type* __restrict__ k_cache,
     const typename std::conditional<F8, uint8_t, T>::type* __restrict__ v_cache,
@@ -413,7 +425,8 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     int32_t M, int32_t num_blocks, int32_t PB, int32_t max_parts, int32_t interleave, int32_t lpt, float qscale,
     const int32_t* __restrict__ sched_order, const int32_t* __restrict__ sched_lens,
     const int32_t* __restrict__ sched_tables, float oscale, T* __restrict__ out,
-    float* __restrict__ ws_o, float* __restrict__ ws_ml)
+    float* __restrict__ ws_o, float* __restrict__ ws_ml, const int32_t* __restrict__ q_start, int32_t num_q_rows,
+    int32_t max_q_len, int32_t RT)
 {
     using C = typename std::conditional<F8, uint8_t, T>::type;  // pool element type
     static_assert(!F8 || sizeof(T) == 2, "FP8 pools are read with bf16 queries");
@@ -427,7 +440,8 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     __shared__ int sm_pick;
     static_assert(kLptMaxSeqs <= NW * 16 * HS && kLptMaxSeqs <= 256, "the length ranking reuses the merge buffer and keeps the index in 8 bits");
 
-    const int kvh = blockIdx.x;
+    const int kvh = MQ ? blockIdx.x / RT : blockIdx.x;
+    const int rt = MQ ? blockIdx.x - kvh * RT : 0;  // row tile
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, kept scalar
     const int chunk = blockIdx.z;                                      // NW consecutive partitions
@@ -500,12 +514,40 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     const int32_t* trow = sched_order ? sched_tables + (int64_t)blockIdx.y * M : block_tables + (int64_t)s * M;
     const int32_t id_lane = (lane < PB && tb < M) ? trow[tb] : 0;
 
+    // Query rows: qs0 .. qs0 + n - 1 (MQ), else row s alone.  Rows outside
+    // 0 .. num_q_rows - 1 or beyond max_q_len are never read or written.
+    int qs0 = s, n = 1;
+    if constexpr (MQ) {
+        qs0 = q_start[s];
+        const int qs1 = q_start[s + 1];
+        n = qs1 - qs0;
+        if (qs0 < 0 || n < 0 || qs1 > num_q_rows)
+            n = 0;
+        n = n < max_q_len ? n : max_q_len;
+    }
+    const int nrows = n * G;  // (row, group member) pairs
+    const int tile_rows = MQ ? (nrows - 16 * rt < 16 ? nrows - 16 * rt : 16) : G;  // this tile's real rows
+    if constexpr (MQ) {
+        if (tile_rows <= 0)
+            return;  // uniform: before any barrier
+    }
+
     const int L_in = sched_order ? sched_lens[blockIdx.y] : seq_lens[s];
     const int L = L_in < 0 ? 0 : (L_in > M * BS ? M * BS : L_in);
+    // row rho of the tile, as (query row, head) of out
+    auto out_row = [&](int rho) __attribute__((always_inline)) -> int64_t {
+        const int i = rho / G;
+        return ((int64_t)(qs0 + i) * Hq + (int64_t)kvh * G + (rho - i * G)) * HS;
+    };
     if (L == 0) {
         if (chunk == 0 && w == 0) {
-            for (int idx = lane; idx < G * HS; idx += 64)
-                store_elem(out + ((int64_t)s * Hq + (int64_t)kvh * G) * HS + idx, 0.f);
+            if constexpr (MQ) {
+                for (int idx = lane; idx < tile_rows * HS; idx += 64)
+                    store_elem(out + out_row(16 * rt + idx / HS) + idx % HS, 0.f);
+            } else {
+                for (int idx = lane; idx < G * HS; idx += 64)
+                    store_elem(out + ((int64_t)s * Hq + (int64_t)kvh * G) * HS + idx, 0.f);
+            }
         }
         return;
     }
@@ -517,14 +559,19 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     const int nb_w = interleave ? (cnb > w ? (cnb - w + NW - 1) / NW : 0)
                                 : (base >= nblk ? 0 : ((nblk - base < PB) ? nblk - base : PB));
 
-    // query operand: head c of this KV head's group.  Rows c >= G of the
-    // 16-row MFMA tile are padding: they repeat head c % G, and their results
-    // are never stored.  (Loading real rows rather than zeroing them keeps
-    // the query registers free of any use before the tile loop, so the
+    // query operand: row c of the tile.  Rows past the tile's real rows are
+    // padding: they repeat a real row (head c % G without MQ), and their
+    // results are never stored.  (Loading real rows rather than zeroing them
+    // keeps the query registers free of any use before the tile loop, so the
     // first tile's loads are issued while the query loads are in flight.)
+    // Lq: this lane's row sees the tokens below Lq; Lmin: the least of those
+    // over the tile (the first query row's limit; L without MQ).
+    const int rho_c = MQ ? (16 * rt + c) % nrows : c % G;
+    const int Lq = MQ ? L - n + rho_c / G + 1 : L;
+    const int Lmin = MQ ? L - n + (16 * rt) / G + 1 : L;
     typename Ops<T>::template QReg<HS> qr;
     {
-        const T* qh = q + ((int64_t)s * Hq + (int64_t)kvh * G + c % G) * HS;
+        const T* qh = q + (MQ ? out_row(rho_c) : ((int64_t)s * Hq + (int64_t)kvh * G + c % G) * HS);
         if constexpr (F8) {
             // operand 2i + h holds dims (4i + r)*16 + 8h .. +7 (the FP8 key order)
 #pragma unroll
@@ -591,9 +638,13 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     // tok0 is the sub-tile's first token; an out-of-range block ID was
     // replaced by block 0 and its tokens are all masked (valid below Lt), so
     // the loaded registers are consumed on every path.
+    // Scores of tokens at or past the lane's row limit (Lq, or tok0 for an
+    // invalid block) are masked; values are zeroed from the sequence end on
+    // (Lv), where the slots may hold anything.
     auto compute = [&](TileRegs<T, HS>& t, int tok0, bool ok) __attribute__((always_inline)) {
-        const int Lt = ok ? L : tok0;
-        const bool partial = tok0 + 16 > Lt;
+        const int Lt = ok ? Lq : tok0;
+        const int Lv = ok ? L : tok0;
+        const bool partial = tok0 + 16 > (ok ? Lmin : tok0);
         const f32x4 S = tile_scores<T, HS>(t.k, qr);
         float sc[4];
         float mx = -INFINITY;
@@ -606,7 +657,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
             mx = fmaxf(mx, v);
         }
         if (partial)
-            zero_masked_values<T, HS>(t, tok0, Lt, r);
+            zero_masked_values<T, HS>(t, tok0, Lv, r);
         update_max(mx);
         float p[4];
 #pragma unroll
@@ -622,8 +673,9 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     // probabilities are moved to that order by to_value_order).
     auto compute_wide = [&](WideRegs<HS>& t, int tok0, bool ok) __attribute__((always_inline)) {
         if constexpr (kWide) {
-            const int Lt = ok ? L : tok0;
-            const bool partial = tok0 + 32 > Lt;
+            const int Lt = ok ? Lq : tok0;
+            const int Lv = ok ? L : tok0;
+            const bool partial = tok0 + 32 > (ok ? Lmin : tok0);
             float sc[8];
             float mx = -INFINITY;
 #pragma unroll
@@ -641,7 +693,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
             if (partial) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const bool keep = tok0 + 8 * r + e < Lt;
+                    const bool keep = tok0 + 8 * r + e < Lv;
 #pragma unroll
                     for (int i = 0; i < HS / 16; ++i)
                         t.v[i][e] = keep ? t.v[i][e] : (__bf16)0.f;
@@ -735,11 +787,11 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     }
 
     // ---- merge the work-group's partitions (log-sum-exp) ----
-    // Each wave stages its partition's normalised G x HS result and the (m, l)
-    // of each head in LDS; the work-group then combines them with weights
-    // l_w * 2^(m_w - M) and writes one block per (sequence, KV head, chunk):
-    // the final output when the sequence has a single chunk, otherwise a
-    // partial for the chunk merge kernel.
+    // Each wave stages its partition's normalised tile_rows x HS result and
+    // the (m, l) of each row in LDS; the work-group then combines them with
+    // weights l_w * 2^(m_w - M) and writes one block per (sequence, KV head,
+    // row tile, chunk): the final output when the sequence has a single
+    // chunk, otherwise a partial for the chunk merge kernel.
     float l_tot = l_part + __shfl_xor(l_part, 16);
     l_tot += __shfl_xor(l_tot, 32);
     if (r == 0) {
@@ -748,10 +800,10 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     }
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-        const int g = 4 * r + jj;
+        const int g = 4 * r + jj;  // tile row
         const float l_g = __shfl(l_tot, g);
         const float inv = l_g > 0.f ? oscale / l_g : 0.f;  // oscale: 1, or the FP8 value scale
-        if (g < G) {
+        if (g < tile_rows) {
 #pragma unroll
             for (int i = 0; i < HS / 16; ++i)
                 sm_out[w][g * HS + 16 * i + c] = O[i][jj] * inv;
@@ -762,9 +814,11 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
-    const int64_t hbase = (int64_t)s * Hq + (int64_t)kvh * G;
-    const int64_t blk = ((int64_t)s * Hkv + kvh) * max_parts + chunk;
-    for (int e = threadIdx.x; e < G * HS / 4; e += NW * 64) {  // 4 consecutive elements of head g
+    // partial blocks: [S][Hkv][RT][max_parts] of RPB rows each
+    constexpr int RPB_MQ = 16;
+    const int RPB = MQ ? RPB_MQ : G;
+    const int64_t blk = (((int64_t)s * Hkv + kvh) * (MQ ? RT : 1) + rt) * max_parts + chunk;
+    for (int e = threadIdx.x; e < tile_rows * HS / 4; e += NW * 64) {  // 4 consecutive elements of tile row g
         const int g = (4 * e) / HS;
         float mx = -INFINITY;
 #pragma unroll
@@ -783,7 +837,8 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
         const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
         acc *= inv;
         if (nchunks == 1) {
-            T* dst = out + hbase * HS + 4 * e;  // the group's G heads are adjacent rows of out
+            // without MQ the group's G heads are adjacent rows of out
+            T* dst = out + (MQ ? out_row(16 * rt + g) + (4 * e) % HS : ((int64_t)s * Hq + (int64_t)kvh * G) * HS + 4 * e);
             if constexpr (sizeof(T) == 2) {
                 bf16x4 v;
 #pragma unroll
@@ -794,12 +849,12 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
                 *(f32x4*)dst = acc;
             }
         } else {
-            *(f32x4*)(ws_o + blk * G * HS + 4 * e) = acc;
+            *(f32x4*)(ws_o + blk * RPB * HS + 4 * e) = acc;
             if ((4 * e) % HS == 0) {
                 float2 ml;
                 ml.x = mx;
                 ml.y = lsum;
-                *(float2*)(ws_ml + (blk * G + g) * 2) = ml;
+                *(float2*)(ws_ml + (blk * RPB + g) * 2) = ml;
             }
         }
     }
@@ -847,10 +902,13 @@ __device__ __forceinline__ float block_reduce_sum(float v, float* red)
     return r;
 }
 
-template <typename T, int HS>
+// MQ: one work-group per (query head, sequence, query row i = blockIdx.z);
+// the partials of row rho = i * G + g sit in row tile rho / 16, row rho % 16.
+template <typename T, int HS, bool MQ>
 __global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
     const int32_t* __restrict__ seq_lens, int32_t M, int32_t BS, int32_t CB, int32_t Hq, int32_t Hkv,
-    int32_t max_parts, const float* __restrict__ ws_o, const float* __restrict__ ws_ml, T* __restrict__ out)
+    int32_t max_parts, const float* __restrict__ ws_o, const float* __restrict__ ws_ml, T* __restrict__ out,
+    const int32_t* __restrict__ q_start, int32_t num_q_rows, int32_t max_q_len, int32_t RT)
 {
     constexpr int R = kMergeThreads / HS;  // partition groups
     __shared__ float sm_w[kMergeChunk];
@@ -858,6 +916,19 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
     __shared__ float sm_acc[R][HS];
     const int h = blockIdx.x;
     const int s = blockIdx.y;
+    const int qi = MQ ? blockIdx.z : 0;
+    int qrow = s;
+    if constexpr (MQ) {
+        const int qs0 = q_start[s];
+        const int qs1 = q_start[s + 1];
+        int n = qs1 - qs0;
+        if (qs0 < 0 || n < 0 || qs1 > num_q_rows)
+            n = 0;
+        n = n < max_q_len ? n : max_q_len;
+        if (qi >= n)
+            return;
+        qrow = qs0 + qi;
+    }
     int L = seq_lens[s];
     L = L < 0 ? 0 : (L > M * BS ? M * BS : L);
     const int nblk = (L + BS - 1) / BS;
@@ -868,8 +939,10 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
     const int G = Hq / Hkv;
     const int kvh = h / G;
     const int g = h - kvh * G;
-    const int64_t u0 = ((int64_t)s * Hkv + kvh) * max_parts;
-    auto row = [&](int p) __attribute__((always_inline)) { return (u0 + p) * G + g; };
+    const int rho = qi * G + g;
+    const int RPB = MQ ? 16 : G;
+    const int64_t u0 = (((int64_t)s * Hkv + kvh) * (MQ ? RT : 1) + rho / 16) * max_parts;
+    auto row = [&](int p) __attribute__((always_inline)) { return (u0 + p) * RPB + rho % 16; };
 
     float mx = -INFINITY;
     for (int p = threadIdx.x; p < nparts; p += kMergeThreads)
@@ -891,7 +964,7 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
         }
         __syncthreads();
         const float* base = ws_o + row(c0) * HS + d;
-        const int64_t pstride = (int64_t)G * HS;  // between consecutive partitions
+        const int64_t pstride = (int64_t)RPB * HS;  // between consecutive partitions
         int i = grp;
         for (; i + 7 * R < cn; i += 8 * R) {
             float v[8];
@@ -913,39 +986,46 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
 #pragma unroll
         for (int g = 0; g < R; ++g)
             tot += sm_acc[g][threadIdx.x];
-        store_elem(out + ((int64_t)s * Hq + h) * HS + threadIdx.x, wsum > 0.f ? tot / wsum : 0.f);
+        store_elem(out + ((int64_t)qrow * Hq + h) * HS + threadIdx.x, wsum > 0.f ? tot / wsum : 0.f);
     }
 }
 
-template <typename T, int HS, int BS, bool F8>
+template <typename T, int HS, int BS, bool F8, bool MQ>
 static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
 {
     constexpr int NW = kDecodeWaves;
     using C = typename std::conditional<F8, uint8_t, T>::type;
-    const dim3 grid(a.num_kv_heads, a.num_seqs, a.max_parts);
+    const dim3 grid(a.num_kv_heads * (MQ ? a.row_tiles : 1), a.num_seqs, a.max_parts);
     const float qscale = a.scale * kLog2e * (F8 ? a.k_scale : 1.0f);
-    hipLaunchKernelGGL((paged_decode_partition_kernel<T, HS, BS, NW, F8>), grid, dim3(NW * 64), 0, stream,
+    hipLaunchKernelGGL((paged_decode_partition_kernel<T, HS, BS, NW, F8, MQ>), grid, dim3(NW * 64), 0, stream,
                        (const T*)a.q, (const C*)a.k_cache, (const C*)a.v_cache, a.block_tables, a.seq_lens,
                        a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq, a.num_blocks, a.partition_blocks,
                        a.max_parts, a.interleave,
-                       (a.num_seqs <= kLptMaxSeqs && a.max_blocks_per_seq < (1 << 23)) ? 1 : 0, qscale,
+                       (!MQ && a.num_seqs <= kLptMaxSeqs && a.max_blocks_per_seq < (1 << 23)) ? 1 : 0, qscale,
                        a.sched_order, a.sched_lens, a.sched_tables, F8 ? a.v_scale : 1.0f, (T*)a.out, a.ws_o,
-                       a.ws_ml);
+                       a.ws_ml, a.q_start, a.num_q_rows, a.max_q_len, a.row_tiles);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_parts <= 1)
         return e;  // one chunk per sequence: the partition kernel wrote the output
-    hipLaunchKernelGGL((paged_decode_reduce_kernel<T, HS>), dim3(a.num_q_heads, a.num_seqs), dim3(kMergeThreads), 0,
-                       stream, a.seq_lens, a.max_blocks_per_seq, BS, a.partition_blocks * NW, a.num_q_heads,
-                       a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, (T*)a.out);
+    hipLaunchKernelGGL((paged_decode_reduce_kernel<T, HS, MQ>), dim3(a.num_q_heads, a.num_seqs, MQ ? a.max_q_len : 1),
+                       dim3(kMergeThreads), 0, stream, a.seq_lens, a.max_blocks_per_seq, BS,
+                       a.partition_blocks * NW, a.num_q_heads, a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml,
+                       (T*)a.out, a.q_start, a.num_q_rows, a.max_q_len, a.row_tiles);
     return hipGetLastError();
+}
+
+template <typename T, int HS, int BS, bool F8>
+static hipError_t launch_rows(const DecodeArgs& a, hipStream_t stream)
+{
+    return a.q_start ? launch_typed<T, HS, BS, F8, true>(a, stream) : launch_typed<T, HS, BS, F8, false>(a, stream);
 }
 
 template <typename T, bool F8>
 static hipError_t launch_dtype(const DecodeArgs& a, hipStream_t stream)
 {
     if (a.head_size == 128)
-        return a.block_size == 16 ? launch_typed<T, 128, 16, F8>(a, stream) : launch_typed<T, 128, 32, F8>(a, stream);
-    return a.block_size == 16 ? launch_typed<T, 64, 16, F8>(a, stream) : launch_typed<T, 64, 32, F8>(a, stream);
+        return a.block_size == 16 ? launch_rows<T, 128, 16, F8>(a, stream) : launch_rows<T, 128, 32, F8>(a, stream);
+    return a.block_size == 16 ? launch_rows<T, 64, 16, F8>(a, stream) : launch_rows<T, 64, 32, F8>(a, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream)

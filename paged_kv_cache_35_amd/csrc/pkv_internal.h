@@ -43,8 +43,16 @@ struct DecodeArgs {
     const int32_t* sched_order;
     const int32_t* sched_lens;
     const int32_t* sched_tables;
-    float* ws_o;    // [S][Hkv][max_parts][G][hs] fp32 chunk partials, null when max_parts == 1
-    float* ws_ml;   // [S][Hkv][max_parts][G][2]  fp32 (running max in log2 units, sum)
+    // Several query tokens per sequence (null: one each, row s): rows
+    // q_start[s] .. q_start[s+1]-1 of q and out, at most max_q_len of them.
+    const int32_t* q_start;
+    int32_t num_q_rows;  // rows of q and out
+    int32_t max_q_len;
+    int32_t row_tiles;   // 16-row MFMA tiles per (sequence, KV head): ceil(max_q_len * G / 16); 1 without q_start
+    // fp32 chunk partials, null when max_parts == 1; rows per block RPB = G
+    // (one query row per sequence) or 16 (q_start set)
+    float* ws_o;    // [S][Hkv][row_tiles][max_parts][RPB][hs]
+    float* ws_ml;   // [S][Hkv][row_tiles][max_parts][RPB][2] (running max in log2 units, sum)
     int32_t num_seqs;
     int32_t num_q_heads;
     int32_t num_kv_heads;
@@ -94,6 +102,14 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // Copies whole blocks (block_bytes per pool) for num_pairs (src, dst) pairs.
 hipError_t launch_copy_blocks(const int32_t* pairs, int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,
                               void* k_cache, void* v_cache, hipStream_t stream);
+
+// Slots of the query rows of a multi-token call: row q_start[s] + i of
+// sequence s gets the slot of position L - n + i (-1 when that position is
+// outside the sequence or its table row).
+hipError_t launch_multi_token_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens,
+                                           const int32_t* q_start, int32_t num_seqs, int32_t num_q_rows,
+                                           int32_t max_q_len, int32_t max_blocks_per_seq, int32_t block_size,
+                                           int64_t* slot_mapping, hipStream_t stream);
 
 hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
                                int32_t max_blocks_per_seq, int32_t block_size, int64_t* slot_mapping,

@@ -181,3 +181,57 @@ def test_decode_append_rejects_a_small_schedule(lib):
     need = lib.pkv_decode_schedule_bytes(4, 4)
     assert f(FAKE, FAKE, FAKE, FAKE, 4, 4, ctypes.byref(d), FAKE, FAKE, None, FAKE, need - 1, None) == WORKSPACE
     assert f(FAKE, FAKE, FAKE, FAKE, 0, 4, ctypes.byref(d), FAKE, FAKE, None, FAKE, 0, None) == OK
+
+
+def test_multi_token_workspace_sizes(lib):
+    f = lib.pkv_multi_token_workspace_bytes
+    # one chunk covers the table: none
+    assert f(4, 8, 8, 64, 16, 4, 16, 0) == 0
+    # 1024 blocks of 16 in 512-token partitions: 32 partitions, 8 chunks;
+    # 4 query tokens x G = 4 -> one 16-row tile per (sequence, KV head)
+    assert f(256, 32, 8, 128, 4, 1024, 16, 0) == 256 * 8 * 1 * 8 * 16 * 130 * 4
+    # 512 tokens x G = 4 -> 128 tiles
+    assert f(16, 32, 8, 128, 512, 1024, 16, 0) == 16 * 8 * 128 * 8 * 16 * 130 * 4
+    assert f(16, 32, 8, 128, 0, 1024, 16, 0) == 0
+    assert f(16, 30, 8, 128, 4, 1024, 16, 0) == 0
+
+
+def mq(lib, *, q=FAKE, qs=FAKE, rows=8, mql=2, S=4, Hq=8, M=4, d=None, out=FAKE, ws=None, ws_bytes=0, P=0):
+    d = d or desc()
+    return lib.paged_multi_token_attention(q, qs, rows, mql, FAKE, FAKE, FAKE, FAKE, S, Hq, M, ctypes.byref(d),
+                                           0.125, out, ws, ws_bytes, P, None)
+
+
+def test_multi_token_attention_rejects_bad_arguments(lib):
+    assert mq(lib, qs=None) == INVALID
+    assert mq(lib, rows=-1) == INVALID
+    assert mq(lib, mql=-1) == INVALID
+    assert mq(lib, mql=65536) == UNSUPPORTED
+    assert mq(lib, q=ctypes.c_void_p(0x10008)) == INVALID
+    assert mq(lib, Hq=12) == INVALID
+    need = lib.pkv_multi_token_workspace_bytes(4, 8, 8, 64, 2, 4096, 16, 0)
+    assert need > 0
+    assert mq(lib, M=4096, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
+    # the decode workspace of the same shape is smaller: still refused
+    dec = lib.pkv_decode_workspace_bytes(4, 8, 8, 64, 4096, 16, 0)
+    assert 0 < dec < need
+    assert mq(lib, M=4096, ws=FAKE, ws_bytes=dec) == WORKSPACE
+    # nothing to do
+    assert lib.paged_multi_token_attention(None, None, 0, 0, None, None, None, None, 0, 8, 4, ctypes.byref(desc()),
+                                           0.125, None, None, 0, 0, None) == OK
+
+
+def test_multi_token_step_and_slot_mapping_reject_bad_arguments(lib):
+    d = desc()
+    f = lib.paged_multi_token_step
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 2, FAKE, FAKE, 4, 8, 4, ctypes.byref(d), 0.125, FAKE, FAKE, None, 0,
+            0, None]
+    for i, bad in ((1, None), (2, ctypes.c_void_p(0x10002)), (16, None)):
+        a = list(args)
+        a[i] = bad
+        assert f(*a) == INVALID
+    g = lib.pkv_multi_token_slot_mapping
+    assert g(FAKE, FAKE, None, 4, 8, 2, 4, 16, FAKE, None) == INVALID
+    assert g(FAKE, FAKE, FAKE, 4, 8, 2, 0, 16, FAKE, None) == INVALID
+    assert g(FAKE, FAKE, FAKE, 70000, 8, 2, 4, 16, FAKE, None) == UNSUPPORTED
+    assert g(None, None, None, 0, 0, 0, 4, 16, None, None) == OK

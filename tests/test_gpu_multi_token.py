@@ -1,0 +1,174 @@
+"""GPU parity of attention with several query tokens per sequence (chunked
+prefill, prefix-miss prefill, speculative decoding) against the oracle.
+
+Rule: the n_s query rows of sequence s are its last n_s tokens, row i at
+position L_s - n_s + i attends the positions up to its own.  The rows' own
+keys and values are appended first (slot mapping + append, bit-exact), as in
+a decode step.  Bars as for decode: max-abs error <= 1e-5 (fp32) and <= 2e-3
+(bf16 outputs, with the one-ulp rule for |out| >= 1), appends bit-exact.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import pkv_inputs as pi
+from test_gpu_parity import announce, check_attention, dev, host_bits, host_f64, pkv, same_bytes
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pkv().library()
+    torch.cuda.set_device(0)
+
+
+class MRun:
+    """Slot mapping + append + attention through the separate entry points."""
+
+    def __init__(self, w, partition_tokens=None, max_q_len=None):
+        self.w = w
+        P = w.partition_tokens if partition_tokens is None else partition_tokens
+        self.mql = w.max_q_len if max_q_len is None else max_q_len
+        m = pkv()
+        self.q, self.kc, self.vc = dev(w.q), dev(w.k_cache), dev(w.v_cache)
+        self.bt, self.sl, self.qs = dev(w.block_tables), dev(w.seq_lens), dev(w.q_start)
+        self.nk, self.nv = dev(w.new_k), dev(w.new_v)
+        self.slots = m.multi_token_slot_mapping(self.bt, self.sl, self.qs, w.rows, self.mql, w.B)
+        m.kv_cache_append(self.nk, self.nv, self.slots, self.kc, self.vc, k_scale=w.k_scale, v_scale=w.v_scale)
+        self.out = m.paged_multi_token_attention(self.q, self.qs, self.mql, self.kc, self.vc, self.bt, self.sl,
+                                                 w.scale, partition_tokens=P, k_scale=w.k_scale, v_scale=w.v_scale)
+        torch.cuda.synchronize()
+
+
+def full_check(w, r):
+    slots, kp, vp, ref = oracle.multi_token_step(w)
+    assert np.array_equal(r.slots.cpu().numpy(), slots)
+    assert same_bytes(host_bits(r.kc), kp), "key pool differs after append"
+    assert same_bytes(host_bits(r.vc), vp), "value pool differs after append"
+    check_attention(w, host_f64(r.out), ref)
+
+
+CASES = [
+    # (config, overrides): full prefill from position 0, chunks, drafts, single rows
+    (1, dict(q_lens=[35, 16, 1, 50])),
+    (1, dict(q_lens=[5, 3, 1, 17])),
+    (2, dict(S=5, len_lo=100, len_hi=700, q_lens=[8, 1, 33, 2, 16])),
+    (3, dict(S=12, len_lo=16, len_hi=1500, q_lens=4)),
+    (3, dict(S=6, len_lo=300, len_hi=2500, q_lens=[64, 5, 1, 37, 128, 16])),
+    (4, dict(S=2, len_lo=1500, len_hi=5000, q_lens=[7, 24])),
+    (5, dict(S=8, len_hi=256, q_lens=3)),
+    (3, dict(S=6, len_lo=100, len_hi=1300, dtype="fp8", q_lens=[4, 9, 1, 16, 2, 30])),
+    (4, dict(S=2, len_lo=700, len_hi=3000, dtype="fp8", q_lens=[5, 12])),
+]
+
+
+@pytest.mark.parametrize("cfg,kw", CASES)
+def test_small_multi_token_parity(cfg, kw):
+    w = pi.make_workload(cfg, **kw)
+    announce(f"multi-token config {cfg} {w.dtype}: lens={list(w.seq_lens)} q_start={list(w.q_start)} B={w.B} G={w.G}")
+    full_check(w, MRun(w))
+
+
+@pytest.mark.parametrize("P", [16, 64, 128])
+def test_partition_lengths_and_chunk_merge(P):
+    # short partitions: many chunks per sequence, so the chunk-merge kernel
+    # combines per-row partials, some of which see no token of a row
+    w = pi.make_workload(3, S=4, len_lo=200, len_hi=900, q_lens=[40, 3, 17, 1])
+    announce(f"multi-token partitions of {P}: lens={list(w.seq_lens)}")
+    full_check(w, MRun(w, partition_tokens=P))
+
+
+@pytest.mark.parametrize("dtype,hs,B,Hq,Hkv", [
+    ("f32", 64, 16, 8, 8), ("f32", 128, 32, 8, 2), ("bf16", 64, 16, 8, 8), ("bf16", 64, 32, 16, 2),
+    ("bf16", 128, 16, 16, 1), ("bf16", 128, 32, 12, 4), ("bf16", 64, 16, 24, 8),
+])
+def test_shape_sweep(dtype, hs, B, Hq, Hkv):
+    w = pi.make_workload(3, S=5, len_lo=1, len_hi=700, dtype=dtype, hs=hs, B=B, Hq=Hq, Hkv=Hkv,
+                         seed=11, q_lens=None)
+    q_lens = np.minimum(np.array([1, 6, 13, 2, 40]), w.seq_lens)
+    w = pi.make_workload(3, S=5, len_lo=1, len_hi=700, dtype=dtype, hs=hs, B=B, Hq=Hq, Hkv=Hkv, seed=11,
+                         q_lens=q_lens)
+    announce(f"multi-token shapes {dtype} hs={hs} B={B} Hq={Hq} Hkv={Hkv} q_start={list(w.q_start)}")
+    full_check(w, MRun(w))
+
+
+def test_one_row_each_is_bit_identical_to_decode():
+    w = pi.make_workload(3, S=12, len_lo=16, len_hi=2500, q_lens=1)
+    announce("multi-token with one row per sequence vs decode attention")
+    r = MRun(w)
+    m = pkv()
+    out = m.paged_decode_attention(r.q, r.kc, r.vc, r.bt, r.sl, w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), r.out.view(torch.int16))
+
+
+def test_sequences_without_rows_and_a_larger_max_q_len():
+    # sequences with no query rows in the batch, an empty sequence, and
+    # max_q_len above every n: rows are exactly those of q_start
+    lens = [40, 0, 17, 300, 5]
+    q_lens = [3, 0, 0, 21, 5]
+    w = pi.make_workload(2, seq_lens=lens, q_lens=q_lens)
+    announce(f"rows {q_lens} of lengths {lens}, max_q_len 64")
+    r = MRun(w, max_q_len=64)
+    full_check(w, r)
+
+
+def test_step_matches_the_separate_calls():
+    w = pi.make_workload(3, S=6, len_lo=300, len_hi=2500, q_lens=[64, 5, 1, 37, 128, 16])
+    announce("multi-token step vs slot mapping + append + attention")
+    r = MRun(w)
+    m = pkv()
+    kc, vc = dev(w.k_cache), dev(w.v_cache)
+    slots = torch.empty(w.rows, dtype=torch.int64, device="cuda")
+    out = m.paged_multi_token_step(r.q, r.nk, r.nv, kc, vc, r.qs, w.max_q_len, r.bt, r.sl, w.scale,
+                                   slot_mapping=slots)
+    torch.cuda.synchronize()
+    assert torch.equal(slots, r.slots)
+    assert torch.equal(kc.view(torch.int16), r.kc.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), r.vc.view(torch.int16))
+    assert torch.equal(out.view(torch.int16), r.out.view(torch.int16))
+
+
+def sampled_rows_reference(w, kp, vp, picks):
+    """Oracle rows for sampled (sequence, row) pairs: row i of sequence s is
+    a one-token query at position L - n + i, i.e. decode attention over the
+    first L - n + i + 1 tokens of the same table row."""
+    q = np.stack([w.q[w.q_start[s] + i] for s, i in picks])
+    tables = np.stack([w.block_tables[s] for s, _ in picks])
+    lens = np.array([w.seq_lens[s] - (w.q_start[s + 1] - w.q_start[s]) + i + 1 for s, i in picks], np.int32)
+    if w.dtype == "fp8":
+        return oracle.paged_attention_fp8(q, kp, vp, tables, lens, w.scale, w.k_scale, w.v_scale)
+    return oracle.paged_attention(q, kp, vp, tables, lens, w.scale)
+
+
+@pytest.mark.parametrize("kind", ["spec4", "chunk512"])
+def test_full_size_sampled_rows(kind):
+    # the benchmark's multi-token workloads on the GQA configuration: 4 draft
+    # tokens for each of the 256 sequences, or the last (up to) 512 tokens of
+    # each as a prefill chunk
+    base = pi.make_workload(3)
+    n = 4 if kind == "spec4" else 512
+    w = pi.make_workload(3, q_lens=np.minimum(n, base.seq_lens))
+    del base
+    announce(f"full-size multi-token {kind}: rows={w.rows} max_q_len={w.max_q_len}")
+    r = MRun(w)
+    slots = oracle.multi_token_slot_mapping(w.block_tables, w.seq_lens, w.q_start, w.B)
+    assert np.array_equal(r.slots.cpu().numpy(), slots)
+    kp, vp = w.k_cache.copy(), w.v_cache.copy()
+    oracle.kv_append(w.new_k, w.new_v, slots, kp, vp)
+    assert same_bytes(host_bits(r.kc), kp)
+    assert same_bytes(host_bits(r.vc), vp)
+    g = np.random.default_rng(5)
+    ns = np.diff(w.q_start)
+    picks = []
+    for s in list(g.choice(w.S, size=24, replace=False)) + [int(np.argmax(w.seq_lens))]:
+        for i in {0, int(ns[s]) - 1, int(g.integers(0, ns[s]))}:
+            picks.append((int(s), i))
+    ref = sampled_rows_reference(w, kp, vp, picks)
+    got = host_f64(r.out)[[w.q_start[s] + i for s, i in picks]]
+    check_attention(w, got, ref)
+    assert torch.isfinite(r.out.float()).all().item()
