@@ -70,6 +70,10 @@ def parse():
     ap.add_argument("--copy-blocks", type=int, default=0, metavar="PAIRS",
                     help="instead of the decode step, time pkv_copy_blocks (copy-on-write) of PAIRS random block "
                          "pairs in the configuration's pools and print its own JSON line")
+    ap.add_argument("--q-len", type=int, default=0, metavar="N",
+                    help="instead of the decode step, time the multi-token step (chunked prefill / speculative "
+                         "decoding): the last min(N, L) tokens of every sequence are query rows, appended and then "
+                         "attended causally; prints its own JSON line")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 20 device-to-device copies of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -81,8 +85,135 @@ def device_inputs(w, torch):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
-    return dict(q=t(w.q), kc=t(w.k_cache), vc=t(w.v_cache), bt=t(w.block_tables), sl=t(w.seq_lens),
-                nk=t(w.new_k), nv=t(w.new_v))
+    d = dict(q=t(w.q), kc=t(w.k_cache), vc=t(w.v_cache), bt=t(w.block_tables), sl=t(w.seq_lens),
+             nk=t(w.new_k), nv=t(w.new_v))
+    if w.q_start is not None:
+        d["qs"] = t(w.q_start)
+    return d
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA (fp8 pools are decoded to bf16 operands)
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def multi_token_counts(w):
+    """(KV bytes, attention flops) one multi-token step must move and do: each
+    sequence's L cached tokens once per KV head (keys and values), plus the
+    query and output rows; 2 * hs flops per (row, query head, visible token)
+    for the scores and as many for the value sum."""
+    kv = w.kv_read_bytes()
+    io_elem = 4 if w.dtype == "f32" else 2
+    qo = 2 * w.rows * w.Hq * w.hs * io_elem
+    n = np.diff(w.q_start).astype(np.int64)
+    L = w.seq_lens.astype(np.int64)
+    # row i of s sees L - n + i + 1 tokens: sum over i = n (L - n) + n (n + 1) / 2
+    visible = int((n * (L - n) + n * (n + 1) // 2).sum())
+    return kv + qo, 4 * w.hs * w.Hq * visible
+
+
+def bench_multi_token(args, w, torch, pkv) -> dict:
+    """paged_multi_token_step (slot mapping, append of every query row, causal
+    attention) on the configuration with the last min(q_len, L) tokens of
+    each sequence as query rows; the attention launch timed with events."""
+    copies = [device_inputs(w, torch) for _ in range(max(1, args.rotate))]
+    d0 = copies[0]
+    P = w.partition_tokens if args.partition_tokens is None else args.partition_tokens
+    mql = w.max_q_len
+    ws = pkv.alloc_multi_token_workspace(d0["q"], d0["kc"], d0["vc"], d0["bt"], mql, P)
+    out = torch.empty_like(d0["q"])
+    slots = torch.empty(w.rows, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    sc = dict(k_scale=w.k_scale, v_scale=w.v_scale)
+    turn = [0]
+
+    def step():
+        d = copies[turn[0] % len(copies)]
+        turn[0] += 1
+        pkv.paged_multi_token_step(d["q"], d["nk"], d["nv"], d["kc"], d["vc"], d["qs"], mql, d["bt"], d["sl"],
+                                   w.scale, out=out, slot_mapping=slots, workspace=ws, partition_tokens=P,
+                                   stream=stream, **sc)
+
+    def step_timed(ev):
+        d = copies[turn[0] % len(copies)]
+        turn[0] += 1
+        pkv.multi_token_slot_mapping(d["bt"], d["sl"], d["qs"], w.rows, mql, w.B, out=slots, stream=stream)
+        pkv.kv_cache_append(d["nk"], d["nv"], slots, d["kc"], d["vc"], stream=stream, **sc)
+        ev[0].record(stream)
+        pkv.paged_multi_token_attention(d["q"], d["qs"], mql, d["kc"], d["vc"], d["bt"], d["sl"], w.scale, out=out,
+                                        workspace=ws, partition_tokens=P, stream=stream, **sc)
+        ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e in evs:
+        step_timed(e)
+    torch.cuda.synchronize()
+    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    t = float(attn_ms.mean()) / 1e3
+    nbytes, flops = multi_token_counts(w)
+    peak_tf = MFMA_F32_PEAK_TFLOPS if w.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
+    ridge = peak_tf * 1e12 / (HBM_PEAK_GBPS * 1e9)  # flop per byte where the two roofs meet
+    if flops / nbytes < ridge:
+        roof = {"bound": "hbm", "achieved": round(nbytes / t / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(nbytes / t / 1e9 / HBM_PEAK_GBPS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flops / t / 1e12, 2), "peak": peak_tf, "unit": "TFLOP/s",
+                "frac": round(flops / t / 1e12 / peak_tf, 4)}
+    roof.update({"traffic": None, "kernel": "paged_multi_token_attention: partition kernel (16-row causal tiles)"
+                 + (" + chunk merge kernel" if ws is not None else ""),
+                 "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops,
+                 "arithmetic_intensity": round(flops / nbytes, 2), "ridge_flop_per_byte": round(ridge, 1),
+                 "attained_tflops": round(flops / t / 1e12, 2), "attained_gbps": round(nbytes / t / 1e9, 1),
+                 "launch_us": {"mean": round(t * 1e6, 2), "median": round(float(np.median(attn_ms)) * 1e3, 2)}})
+    return {"metric": "multi-token paged attention query tokens/s (chunked prefill / speculative decoding step)",
+            "value": round(w.rows / (ms_step / 1e3), 1), "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8-e4m3 pools, bf16 q/out"}[w.dtype],
+            "data": "synthetic (seeded N(0,1) q/K/V, shuffled block IDs; no dataset)",
+            "config": {"workload": f"{w.description}; last min({args.q_len}, L) tokens of each sequence are query "
+                                   f"rows", "q_len": args.q_len, "query_rows": w.rows, "max_q_len": mql,
+                       "partition_tokens": P, "kv_bytes_per_step": w.kv_read_bytes()},
+            "kv_read_gbps_step": round(w.kv_read_bytes() / (ms_step / 1e3) / 1e9, 1),
+            "roofline": roof,
+            "cpu_baseline": None if args.no_cpu_baseline else cpu_baseline_multi_token(w, args.cpu_seconds)}
+
+
+def cpu_baseline_multi_token(w, target_s: float) -> dict:
+    """The CPU oracle's causal attention on whole sequences of the workload,
+    one at a time in batch order, until about target_s seconds have passed;
+    query rows per second."""
+    import oracle
+
+    log("timing the CPU oracle sample")
+    rows = 0
+    done = 0
+    t0 = time.perf_counter()
+    for s in range(w.S):
+        a, b = int(w.q_start[s]), int(w.q_start[s + 1])
+        if a == b:
+            continue
+        oracle.paged_multi_token_attention(w.q[a:b], np.array([0, b - a], np.int32), w.k_cache, w.v_cache,
+                                           w.block_tables[s:s + 1], w.seq_lens[s:s + 1], w.scale,
+                                           k_scale=w.k_scale, v_scale=w.v_scale)
+        rows += b - a
+        done += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(rows / el, 2), "unit": "query tokens/s", "cores": int(oracle.max_threads()),
+            "kind": "oracle", "sample": f"causal attention of the first {done} sequences' {rows} query rows (all "
+                                        f"{w.Hq} heads), fp64 C oracle with OpenMP, {el:.1f} s wall"}
 
 
 def calib_copy(mib: int) -> None:
@@ -108,7 +239,7 @@ def bench_copy_blocks(args, w, torch, pkv) -> dict:
     perm = np.random.default_rng(12345).permutation(w.num_blocks)
     pairs = torch.tensor(np.stack([perm[:n], perm[n:2 * n]], axis=1).astype(np.int32), device="cuda")
     stream = torch.cuda.current_stream()
-    elem = 4 if w.dtype == "f32" else 2
+    elem = w.elem_bytes
     block_bytes = w.Hkv * w.B * w.hs * elem
     moved = n * 2 * block_bytes * 2
     turn = [0]
@@ -220,6 +351,14 @@ def main() -> int:
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
     kvdt = "fp8" if args.kv_dtype == "fp8" else None
+    if args.q_len:
+        base = pi.make_workload(args.config, mode="timing", contiguous=args.contiguous, dtype=kvdt)
+        q_lens = np.minimum(args.q_len, base.seq_lens)
+        del base
+        w = pi.make_workload(args.config, mode="timing", contiguous=args.contiguous, dtype=kvdt, q_lens=q_lens)
+        log(f"generated config {args.config} with {w.rows} query rows in {time.perf_counter() - t0:.1f} s")
+        print(json.dumps(bench_multi_token(args, w, torch, pkv)), flush=True)
+        return 0
     w = pi.make_workload(args.config, mode="timing", contiguous=args.contiguous, dtype=kvdt)
     sc = dict(k_scale=w.k_scale, v_scale=w.v_scale)
     log(f"generated config {args.config} ({w.description}) in {time.perf_counter() - t0:.1f} s")
