@@ -114,7 +114,8 @@ typedef enum {
 typedef struct {
     int32_t num_blocks;    /* physical blocks in each pool                     */
     int32_t num_kv_heads;  /* Hkv                                              */
-    int32_t block_size;    /* B: token slots per block; 16 or 32               */
+    int32_t block_size;    /* B: token slots per block; 1, 8, 16, 32 or 64     */
+                           /* (FP8 pools: 16, 32 or 64)                        */
     int32_t head_size;     /* hs: 64 or 128                                    */
     int32_t dtype;         /* pkv_dtype of the pools (and of q, out, k, v,     */
                            /* which are bf16 when the pools are FP8)           */
@@ -202,8 +203,10 @@ PKV_API pkv_status pkv_decode_append(const void* k, const void* v, const int32_t
 /*
  * Context-partition length, in tokens, that paged_decode_attention will use
  * for these sizes.  partition_tokens > 0 requests that length (it must be a
- * multiple of block_size and at most 64 * block_size); 0 lets the library
- * choose.  Returns 0 for invalid sizes.
+ * multiple of block_size and at most 64 * block_size, and for blocks of
+ * fewer than 16 tokens a multiple of 16); 0 lets the library choose
+ * (min(512, 64 * block_size), or the whole table when shorter).  Returns 0
+ * for invalid sizes.
  */
 PKV_API int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t head_size, int32_t max_blocks_per_seq,
@@ -243,7 +246,7 @@ PKV_API size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *                 and lengths gives wrong results.
  * Calls that share a workspace must be ordered on one stream.
  * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED (head_size not 64/128,
- * block_size not 16/32, num_q_heads / num_kv_heads not in 1..16 or not an
+ * block_size not 1/8/16/32/64 or below 16 with FP8 pools, num_q_heads / num_kv_heads not in 1..16 or not an
  * integer), PKV_ERR_WORKSPACE (workspace or schedule too small or
  * misaligned), PKV_ERR_HIP.
  */

@@ -49,14 +49,19 @@ pkv_status check_cache(const pkv_cache_desc* c)
         return PKV_ERR_INVALID_ARG;
     if (c->head_size != 64 && c->head_size != 128)
         return PKV_ERR_UNSUPPORTED;
-    if (c->block_size != 16 && c->block_size != 32)
+    const int32_t B = c->block_size;
+    if (B != 1 && B != 8 && B != 16 && B != 32 && B != 64)
+        return PKV_ERR_UNSUPPORTED;
+    if (c->dtype == PKV_FP8_E4M3 && B < 16)
         return PKV_ERR_UNSUPPORTED;
     return PKV_OK;
 }
 
 // Library choice of the context-partition length: PKV_DEFAULT_PARTITION_TOKENS
-// (512: 32 blocks at B = 16, 16 at B = 32), or one partition when the table is
-// shorter.
+// (512: 32 blocks at B = 16, 16 at B = 32), at most 64 blocks (one block ID
+// per lane of the wave), or one partition when the table is shorter.  Blocks
+// of fewer than 16 tokens are read in 16-token units that must not straddle
+// two partitions: the length is then a multiple of 16.
 #ifndef PKV_DEFAULT_PARTITION_TOKENS
 #define PKV_DEFAULT_PARTITION_TOKENS 512
 #endif
@@ -65,12 +70,12 @@ int32_t resolve_partition_tokens(int32_t max_blocks_per_seq, int32_t block_size,
     if (requested < 0 || max_blocks_per_seq <= 0 || block_size <= 0)
         return 0;
     if (requested > 0) {
-        if (requested % block_size != 0 || requested / block_size > 64)
+        if (requested % block_size != 0 || requested / block_size > 64 || (block_size < 16 && requested % 16 != 0))
             return 0;
         return requested;
     }
     const int64_t whole = (int64_t)max_blocks_per_seq * block_size;
-    const int32_t dflt = PKV_DEFAULT_PARTITION_TOKENS;
+    const int64_t dflt = PKV_DEFAULT_PARTITION_TOKENS < 64 * block_size ? PKV_DEFAULT_PARTITION_TOKENS : 64 * block_size;
     return (int32_t)(whole < dflt ? whole : dflt);
 }
 

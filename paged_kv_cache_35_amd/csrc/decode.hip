@@ -196,18 +196,71 @@ __device__ __forceinline__ void load_tile(TileRegs<T, HS>& t, const T* __restric
     }
 }
 
-template <int HS>
+// 32-token unit m of a block of BS >= 32 tokens (tokens 32m .. 32m+31).
+// Blocks smaller than the 16-token unit (B = 1, 2, 4 or 8; bf16 or fp32):
+// the unit's tokens come from 16 / B consecutive blocks of the wave's
+// partition, so each lane fetches its own block IDs from the wave's list
+// (ids: lane j holds block j; ds_bpermute): key token c of the unit, value
+// tokens 4r .. 4r+3 (one block when B >= 4, else one element per token).
+// An ID outside the pool reads block 0, and the returned 16-bit mask has the
+// bits of that block's tokens clear (valid_blocks: bit j set when ID j is
+// inside the pool), so that compute masks them.
+template <typename T, int HS, int BS>
+__device__ __forceinline__ int load_small(TileRegs<T, HS>& t, const T* __restrict__ k_cache,
+                                          const T* __restrict__ v_cache, int64_t block_stride, int64_t head_off,
+                                          int32_t ids, uint64_t valid_blocks, int32_t num_blocks, int u, int r, int c)
+{
+    static_assert(BS < 16 && 16 % BS == 0, "small-block path");
+    constexpr int X = 16 / (int)sizeof(T);
+    using KV = typename std::conditional<sizeof(T) == 2, bf16x8, f32x4>::type;
+    using VV = typename std::conditional<sizeof(T) == 2, bf16x4, f32x4>::type;
+    auto block_at = [&](int j) __attribute__((always_inline)) -> int64_t {
+        const int32_t id = __shfl(ids, j);
+        return ((uint32_t)id < (uint32_t)num_blocks ? id : 0) * block_stride + head_off;
+    };
+    const int tk = 16 * u + c;
+    const T* kp = k_cache + block_at(tk / BS) + (tk % BS) * X;
+#pragma unroll
+    for (int i = 0; i < HS / (4 * X); ++i)  // chunk 4i + r of token c
+        t.k.v[i] = load_stream((const KV*)(kp + (4 * i + r) * BS * X));
+    if constexpr (BS >= 4) {
+        const int tv = 16 * u + 4 * r;
+        const T* vp = v_cache + block_at(tv / BS) + tv % BS;
+#pragma unroll
+        for (int i = 0; i < HS / 16; ++i)
+            t.v.v[i] = load_stream_v((const VV*)(vp + (16 * i + c) * BS));
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int tv = 16 * u + 4 * r + j;
+            const T* vp = v_cache + block_at(tv / BS) + tv % BS;
+#pragma unroll
+            for (int i = 0; i < HS / 16; ++i)
+                t.v.v[i][j] = load_stream_v(vp + (16 * i + c) * BS);
+        }
+    }
+    int tmask = 0;
+#pragma unroll
+    for (int k = 0; k < 16 / BS; ++k) {
+        const int j = (16 * u) / BS + k;
+        if (j >= 64 || ((valid_blocks >> j) & 1))
+            tmask |= ((1 << BS) - 1) << (k * BS);
+    }
+    return tmask;
+}
+
+template <int HS, int BS>
 __device__ __forceinline__ void load_wide(WideRegs<HS>& t, const __bf16* __restrict__ tile_k,
-                                          const __bf16* __restrict__ tile_v, int r, int c)
+                                          const __bf16* __restrict__ tile_v, int m, int r, int c)
 {
 #pragma unroll
     for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
         for (int i = 0; i < HS / 32; ++i)
-            t.k[mp].v[i] = load_stream((const bf16x8*)(tile_k + ((4 * i + r) * 32 + 16 * mp + c) * 8));
+            t.k[mp].v[i] = load_stream((const bf16x8*)(tile_k + ((4 * i + r) * BS + 32 * m + 16 * mp + c) * 8));
 #pragma unroll
-    for (int i = 0; i < HS / 16; ++i)  // head dim 16i + c, tokens 8r .. 8r+7
-        t.v[i] = load_stream((const bf16x8*)(tile_v + (16 * i + c) * 32 + 8 * r));
+    for (int i = 0; i < HS / 16; ++i)  // head dim 16i + c, tokens 32m + 8r .. +7
+        t.v[i] = load_stream((const bf16x8*)(tile_v + (16 * i + c) * BS + 32 * m + 8 * r));
 }
 
 // FP8 (E4M3) caches, bf16 queries: one 16-token sub-tile as raw codes.
@@ -277,8 +330,7 @@ __device__ __forceinline__ void fp8_to_operands(const Fp8Regs<HS>& raw, TileRegs
     }
 }
 
-// FP8 pools with B = 32: the whole block as one 32-token unit, like the bf16
-// 32-token path.  Key M-tile mp holds tokens 16mp .. 16mp+15 (chunk 4i + r
+// FP8 pools with B >= 32: 32-token units, like the bf16 32-token path.  Key M-tile mp holds tokens 16mp .. 16mp+15 (chunk 4i + r
 // of token 16mp + c; two 128-byte lines per lane group); the value operand is
 // 8 codes per lane, tokens 8r .. 8r+7 of head dim 16i + c (the four lane
 // groups read the dim's whole 32-byte row).
@@ -288,19 +340,19 @@ struct Fp8WideRegs {
     unsigned v[HS / 16][2];
 };
 
-template <int HS>
+template <int HS, int BS>
 __device__ __forceinline__ void load_fp8_wide(Fp8WideRegs<HS>& t, const uint8_t* __restrict__ tile_k,
-                                              const uint8_t* __restrict__ tile_v, int r, int c)
+                                              const uint8_t* __restrict__ tile_v, int m, int r, int c)
 {
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
     for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
         for (int i = 0; i < HS / 64; ++i)
-            t.k[mp][i] = load_stream((const u32x4*)(tile_k + ((4 * i + r) * 32 + 16 * mp + c) * 16));
+            t.k[mp][i] = load_stream((const u32x4*)(tile_k + ((4 * i + r) * BS + 32 * m + 16 * mp + c) * 16));
 #pragma unroll
     for (int i = 0; i < HS / 16; ++i) {
-        const u32x2 w = load_stream_v((const u32x2*)(tile_v + (16 * i + c) * 32 + 8 * r));
+        const u32x2 w = load_stream_v((const u32x2*)(tile_v + (16 * i + c) * BS + 32 * m + 8 * r));
         t.v[i][0] = w[0];
         t.v[i][1] = w[1];
     }
@@ -383,25 +435,36 @@ __device__ __forceinline__ void tile_pv(f32x4 (&O)[HS / 16], const float (&p)[4]
 // Zero the value operand of tokens at or beyond L (tok0 = the sub-tile's
 // first token), so stale or NaN slots never enter the value sum.
 template <typename T, int HS>
-__device__ __forceinline__ void zero_masked_values(TileRegs<T, HS>& t, int tok0, int L, int r)
+__device__ __forceinline__ void zero_masked_values(TileRegs<T, HS>& t, int tok0, int L, int r, int tmask)
 {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        const bool keep = tok0 + 4 * r + j < L;
+        const bool keep = tok0 + 4 * r + j < L && ((tmask >> (4 * r + j)) & 1);
 #pragma unroll
         for (int i = 0; i < HS / 16; ++i)
             t.v.v[i][j] = keep ? t.v.v[i][j] : (T)0.f;
     }
 }
 
-// Occupancy targets for bf16: three waves per SIMD with 16-token blocks
-// (<= 168 VGPRs, including the MFMA accumulators), two with 32-token units
-// (<= 256), for bf16 and FP8 pools alike; one wave less for FP8 pools with
-// several query tokens per sequence (the per-row causal limits would spill
-// at the decode targets).  The fp32 variants (larger operands) are left
-// unconstrained.
-#define PKV_OCCUPANCY \
-    __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? (BS == 16 ? 3 : 2) - (F8 && MQ ? 1 : 0) : 1)))
+// Occupancy targets (waves per SIMD) for bf16 queries: three with 16-token
+// units (<= 168 VGPRs, including the MFMA accumulators), two with 32-token
+// units (<= 256), for bf16 and FP8 pools alike.  Exceptions, where these
+// targets would spill: one-token blocks (per-token value loads) run two;
+// bf16 pools with 64-token blocks and head size 128 run one; FP8 pools with
+// several query tokens per sequence (per-row causal limits) one less.  The
+// fp32 variants (larger operands) are left unconstrained.
+constexpr int decode_waves_per_eu(int elem, int HS, int BS, bool F8, bool MQ)
+{
+    if (elem != 2)
+        return 1;
+    int w = BS == 1 ? 2 : (BS <= 16 ? 3 : 2);
+    if (BS == 64 && HS == 128 && !F8)
+        w = 1;
+    if (F8 && MQ)
+        w -= 1;
+    return w < 1 ? 1 : w;
+}
+#define PKV_OCCUPANCY __attribute__((amdgpu_waves_per_eu(decode_waves_per_eu(sizeof(T), HS, BS, F8, MQ))))
 
 // T: element type of q and out (and of the pools unless F8).  F8: the pools
 // hold E4M3 codes (T is bf16); keys are read as code * k_scale (folded into
@@ -430,9 +493,11 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
 {
     using C = typename std::conditional<F8, uint8_t, T>::type;  // pool element type
     static_assert(!F8 || sizeof(T) == 2, "FP8 pools are read with bf16 queries");
-    constexpr bool kWide = sizeof(T) == 2 && BS == 32;  // 32-token units (see WideRegs, Fp8WideRegs)
+    constexpr bool kWide = sizeof(T) == 2 && BS >= 32;  // 32-token units (see WideRegs, Fp8WideRegs)
+    constexpr bool kSmall = BS < 16;                    // several blocks per unit (see load_small)
+    static_assert(!(kSmall && F8), "FP8 pools need blocks of at least 16 tokens");
     constexpr int UT = kWide ? 32 : 16;                 // tokens per pipeline unit
-    constexpr int PER = BS / UT;                        // units per block
+    constexpr int PER = kSmall ? 1 : BS / UT;           // units per block
     constexpr int TILE = HS * BS;                       // elements per (block, KV head) tile
     __shared__ __attribute__((aligned(16))) float sm_out[NW][16 * HS];  // partition results, for the merge
     __shared__ float sm_m[NW][16];
@@ -502,9 +567,12 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     // mode: the chunk's blocks dealt round-robin to the NW waves, which keeps
     // the waves balanced when a sequence ends inside the chunk.  A wave with
     // no blocks still joins the work-group merge below.
+    // (Blocks smaller than a unit always use contiguous partitions: a unit's
+    // tokens are then consecutive.)
     const int cb0 = chunk * NW * PB;
-    const int base = interleave ? cb0 + w : part * PB;
-    const int stride = interleave ? NW : 1;
+    const bool ilv = !kSmall && interleave;
+    const int base = ilv ? cb0 + w : part * PB;
+    const int stride = ilv ? NW : 1;
     // Physical block IDs of this wave's blocks, one per lane (<= PB <= 64);
     // the tile loop broadcasts them with readlane.  Loaded for all PB lanes
     // within the table row, without waiting for the sequence length, so
@@ -556,7 +624,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
         return;  // the whole work-group is past the end (uniform: before any barrier)
     const int nchunks = (nblk + NW * PB - 1) / (NW * PB);
     const int cnb = (nblk - cb0 < NW * PB) ? nblk - cb0 : NW * PB;
-    const int nb_w = interleave ? (cnb > w ? (cnb - w + NW - 1) / NW : 0)
+    const int nb_w = ilv ? (cnb > w ? (cnb - w + NW - 1) / NW : 0)
                                 : (base >= nblk ? 0 : ((nblk - base < PB) ? nblk - base : PB));
 
     // query operand: row c of the tile.  Rows past the tile's real rows are
@@ -641,10 +709,12 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     // Scores of tokens at or past the lane's row limit (Lq, or tok0 for an
     // invalid block) are masked; values are zeroed from the sequence end on
     // (Lv), where the slots may hold anything.
-    auto compute = [&](TileRegs<T, HS>& t, int tok0, bool ok) __attribute__((always_inline)) {
-        const int Lt = ok ? Lq : tok0;
-        const int Lv = ok ? L : tok0;
-        const bool partial = tok0 + 16 > (ok ? Lmin : tok0);
+    // Small blocks: tmask marks the unit's tokens whose block ID is inside
+    // the pool (ok: all of them).
+    auto compute = [&](TileRegs<T, HS>& t, int tok0, bool ok, int tmask) __attribute__((always_inline)) {
+        const int Lt = (kSmall || ok) ? Lq : tok0;
+        const int Lv = (kSmall || ok) ? L : tok0;
+        const bool partial = tok0 + 16 > ((kSmall || ok) ? Lmin : tok0) || (kSmall && !ok);
         const f32x4 S = tile_scores<T, HS>(t.k, qr);
         float sc[4];
         float mx = -INFINITY;
@@ -652,12 +722,12 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
         for (int jj = 0; jj < 4; ++jj) {
             float v = S[jj] * qscale;
             if (partial)
-                v = (tok0 + 4 * r + jj < Lt) ? v : -INFINITY;
+                v = (tok0 + 4 * r + jj < Lt && ((tmask >> (4 * r + jj)) & 1)) ? v : -INFINITY;
             sc[jj] = v;
             mx = fmaxf(mx, v);
         }
         if (partial)
-            zero_masked_values<T, HS>(t, tok0, Lv, r);
+            zero_masked_values<T, HS>(t, tok0, Lv, r, tmask);
         update_max(mx);
         float p[4];
 #pragma unroll
@@ -733,25 +803,38 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     using Regs = typename std::conditional<
         F8, typename std::conditional<kWide, Fp8WideRegs<HS>, Fp8Regs<HS>>::type,
         typename std::conditional<kWide, WideRegs<HS>, TileRegs<T, HS>>::type>::type;
-    const int nunits = nb_w * PER;  // 0 for a wave past the end
-    auto issue = [&](Regs& t, int u) __attribute__((always_inline)) -> bool {
-        const int j = u / PER;
-        const C* tk;
-        const C* tv;
-        const bool ok = tile_ptr_ok(j, tk, tv);
-        if constexpr (F8 && kWide)
-            load_fp8_wide<HS>(t, tk, tv, r, c);
-        else if constexpr (F8)
-            load_fp8<HS, BS>(t, tk, tv, u % PER, r, c);
-        else if constexpr (kWide)
-            load_wide<HS>(t, tk, tv, r, c);
-        else
-            load_tile<T, HS, BS>(t, tk, tv, u % PER, r, c);
-        return ok;
+    // 0 for a wave past the end
+    const int nunits = kSmall ? (nb_w * BS + UT - 1) / UT : nb_w * PER;
+    // small blocks: bit j set when this wave's block ID j is inside the pool
+    const uint64_t valid_blocks = kSmall ? __ballot((uint32_t)id_lane < (uint32_t)num_blocks) : 0;
+    // returns the unit's token mask (all 16 bits when every block is valid,
+    // 0 for an invalid block of B >= 16)
+    auto issue = [&](Regs& t, int u) __attribute__((always_inline)) -> int {
+        if constexpr (kSmall) {
+            return load_small<T, HS, BS>(t, k_cache, v_cache, (int64_t)Hkv * TILE, (int64_t)kvh * TILE, id_lane,
+                                         valid_blocks, num_blocks, u, r, c);
+        } else {
+            const int j = u / PER;
+            const C* tk;
+            const C* tv;
+            const bool ok = tile_ptr_ok(j, tk, tv);
+            if constexpr (F8 && kWide)
+                load_fp8_wide<HS, BS>(t, tk, tv, u % PER, r, c);
+            else if constexpr (F8)
+                load_fp8<HS, BS>(t, tk, tv, u % PER, r, c);
+            else if constexpr (kWide)
+                load_wide<HS, BS>(t, tk, tv, u % PER, r, c);
+            else
+                load_tile<T, HS, BS>(t, tk, tv, u % PER, r, c);
+            return ok ? 0xFFFF : 0;
+        }
     };
-    auto first_token = [&](int u) __attribute__((always_inline)) { return (base + (u / PER) * stride) * BS + UT * (u % PER); };
-    auto run = [&](Regs& t, int u, bool ok) __attribute__((always_inline)) {
+    auto first_token = [&](int u) __attribute__((always_inline)) {
+        return kSmall ? base * BS + UT * u : (base + (u / PER) * stride) * BS + UT * (u % PER);
+    };
+    auto run = [&](Regs& t, int u, int tmask) __attribute__((always_inline)) {
         const int tok0 = first_token(u);
+        const bool ok = tmask == 0xFFFF;
         if constexpr (F8 && kWide) {
             WideRegs<HS> op;  // the raw codes as bf16 operands
             fp8_wide_to_operands<HS>(t, op);
@@ -761,15 +844,15 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
         } else if constexpr (F8) {
             TileRegs<__bf16, HS> op;  // the raw codes as bf16 operands
             fp8_to_operands<HS>(t, op);
-            compute(op, tok0, ok);
+            compute(op, tok0, ok, 0xFFFF);
         } else {
-            compute(t, tok0, ok);
+            compute(t, tok0, ok, kSmall ? tmask : 0xFFFF);
         }
     };
     if (nunits > 0) {
         Regs ta, tb;
-        bool ok_a = issue(ta, 0);
-        bool ok_b = false;
+        int ok_a = issue(ta, 0);
+        int ok_b = 0;
         int u = 0;
         for (; u + 2 < nunits; u += 2) {
             ok_b = issue(tb, u + 1);
@@ -1020,12 +1103,26 @@ static hipError_t launch_rows(const DecodeArgs& a, hipStream_t stream)
     return a.q_start ? launch_typed<T, HS, BS, F8, true>(a, stream) : launch_typed<T, HS, BS, F8, false>(a, stream);
 }
 
+template <typename T, int HS, bool F8>
+static hipError_t launch_block(const DecodeArgs& a, hipStream_t stream)
+{
+    switch (a.block_size) {
+    case 16: return launch_rows<T, HS, 16, F8>(a, stream);
+    case 32: return launch_rows<T, HS, 32, F8>(a, stream);
+    case 64: return launch_rows<T, HS, 64, F8>(a, stream);
+    default:
+        if constexpr (F8) {
+            return hipErrorInvalidValue;  // rejected on the host: FP8 pools need B >= 16
+        } else {
+            return a.block_size == 8 ? launch_rows<T, HS, 8, F8>(a, stream) : launch_rows<T, HS, 1, F8>(a, stream);
+        }
+    }
+}
+
 template <typename T, bool F8>
 static hipError_t launch_dtype(const DecodeArgs& a, hipStream_t stream)
 {
-    if (a.head_size == 128)
-        return a.block_size == 16 ? launch_rows<T, 128, 16, F8>(a, stream) : launch_rows<T, 128, 32, F8>(a, stream);
-    return a.block_size == 16 ? launch_rows<T, 64, 16, F8>(a, stream) : launch_rows<T, 64, 32, F8>(a, stream);
+    return a.head_size == 128 ? launch_block<T, 128, F8>(a, stream) : launch_block<T, 64, F8>(a, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream)

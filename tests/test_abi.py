@@ -69,7 +69,9 @@ def test_attention_rejects_bad_arguments(lib):
     assert attn(lib, Hq=12) == INVALID                      # Hq % Hkv != 0
     assert attn(lib, Hq=8 * 32, d=desc(hkv=8)) == UNSUPPORTED  # group of 32 query heads
     assert attn(lib, d=desc(hs=96)) == UNSUPPORTED
-    assert attn(lib, d=desc(B=8)) == UNSUPPORTED
+    assert attn(lib, d=desc(B=4)) == UNSUPPORTED
+    assert attn(lib, d=desc(B=128)) == UNSUPPORTED
+    assert attn(lib, d=desc(B=8, dtype=2)) == UNSUPPORTED  # FP8 pools need B >= 16
     assert attn(lib, d=desc(dtype=7)) == UNSUPPORTED
     # FP8 pools need positive finite scales
     assert attn(lib, d=desc(dtype=2, k_scale=0.0)) == INVALID
@@ -235,3 +237,18 @@ def test_multi_token_step_and_slot_mapping_reject_bad_arguments(lib):
     assert g(FAKE, FAKE, FAKE, 4, 8, 2, 0, 16, FAKE, None) == INVALID
     assert g(FAKE, FAKE, FAKE, 70000, 8, 2, 4, 16, FAKE, None) == UNSUPPORTED
     assert g(None, None, None, 0, 0, 0, 4, 16, None, None) == OK
+
+
+def test_partition_lengths_for_every_block_size(lib):
+    f = lib.pkv_decode_partition_tokens
+    # default: 512 tokens, at most 64 blocks of the wave's list
+    assert f(4, 8, 8, 64, 1024, 1, 0) == 64
+    assert f(4, 8, 8, 64, 1024, 8, 0) == 512
+    assert f(4, 8, 8, 64, 1024, 64, 0) == 512
+    assert f(4, 8, 8, 64, 3, 8, 0) == 24          # a short table: one partition
+    # requested: blocks below 16 tokens need a multiple of 16
+    assert f(4, 8, 8, 64, 1024, 8, 24) == 0
+    assert f(4, 8, 8, 64, 1024, 8, 32) == 32
+    assert f(4, 8, 8, 64, 1024, 1, 48) == 48
+    assert f(4, 8, 8, 64, 1024, 1, 80) == 0       # 80 blocks of one token
+    assert f(4, 8, 8, 64, 1024, 64, 4096) == 4096

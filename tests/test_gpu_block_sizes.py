@@ -1,0 +1,107 @@
+"""GPU parity across block sizes B = 1, 8, 16, 32, 64 (the block-size
+trade-off of the pages: "PagedAttention 笔记", block-size discussion, and the
+deep-dive page's block-size notes): decode and multi-token attention, bf16,
+fp32 and (B >= 16) FP8 pools, against the oracle.  Blocks of fewer than 16
+tokens are read in 16-token units made of several blocks; B = 64 in 32-token
+units.  Also: a block ID outside the pool skips that block's tokens, for
+every block size.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import pkv_inputs as pi
+from test_gpu_fp8 import check_step, run_fp8
+from test_gpu_multi_token import MRun, full_check
+from test_gpu_parity import Run, announce, check_attention, dev, host_bits, host_f64, pkv, same_bytes
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pkv().library()
+    torch.cuda.set_device(0)
+
+
+@pytest.mark.parametrize("B", [1, 8, 64])
+@pytest.mark.parametrize("dtype,hs,Hq,Hkv", [("bf16", 128, 32, 8), ("bf16", 64, 8, 8), ("f32", 128, 8, 2),
+                                             ("f32", 64, 4, 4)])
+def test_decode_parity(B, dtype, hs, Hq, Hkv):
+    w = pi.make_workload(3, S=7, len_lo=1, len_hi=1400, dtype=dtype, hs=hs, Hq=Hq, Hkv=Hkv, B=B, seed=21)
+    announce(f"decode B={B} {dtype} hs={hs} Hq={Hq} Hkv={Hkv} lens={list(w.seq_lens)}")
+    r = Run(w)
+    slots, kp, vp, ref = oracle.decode_step(w)
+    assert np.array_equal(r.slots.cpu().numpy(), slots)
+    assert same_bytes(host_bits(r.kc), kp)
+    assert same_bytes(host_bits(r.vc), vp)
+    check_attention(w, host_f64(r.out), ref)
+
+
+@pytest.mark.parametrize("B,P", [(1, 16), (1, 48), (8, 16), (8, 128), (64, 64), (64, 1024)])
+def test_partition_lengths(B, P):
+    w = pi.make_workload(3, S=5, len_lo=100, len_hi=2000, B=B, seed=22)
+    announce(f"decode B={B} P={P} lens={list(w.seq_lens)}")
+    r = Run(w, partition_tokens=P)
+    check_attention(w, host_f64(r.out), oracle.decode_step(w)[3])
+
+
+@pytest.mark.parametrize("B", [1, 8, 64])
+def test_multi_token_parity(B):
+    w0 = pi.make_workload(3, S=6, len_lo=20, len_hi=1200, B=B, seed=23)
+    q_lens = np.minimum([1, 4, 17, 40, 3, 64], w0.seq_lens)
+    w = pi.make_workload(3, S=6, len_lo=20, len_hi=1200, B=B, seed=23, q_lens=q_lens)
+    announce(f"multi-token B={B} lens={list(w.seq_lens)} q_start={list(w.q_start)}")
+    full_check(w, MRun(w))
+
+
+@pytest.mark.parametrize("mq", [False, True])
+def test_fp8_pools_with_64_token_blocks(mq):
+    kw = dict(S=6, len_lo=30, len_hi=1500, B=64, dtype="fp8", seed=24)
+    if mq:
+        kw["q_lens"] = [2, 5, 1, 9, 16, 3]
+    w = pi.make_workload(3, **kw)
+    announce(f"fp8 B=64 {'multi-token' if mq else 'decode'} lens={list(w.seq_lens)}")
+    if mq:
+        full_check(w, MRun(w))
+    else:
+        check_step(w, *run_fp8(w))
+        check_step(w, *run_fp8(w, step=True))
+
+
+def test_fp8_pools_refuse_small_blocks():
+    w = pi.make_workload(3, S=2, len_lo=20, len_hi=40, B=16, dtype="fp8", seed=25)
+    m = pkv()
+    kc = torch.zeros((4, w.Hkv, w.hs // 16, 8, 16), dtype=torch.uint8, device="cuda")
+    vc = torch.zeros((4, w.Hkv, w.hs, 8), dtype=torch.uint8, device="cuda")
+    with pytest.raises(m.PkvError):
+        m.paged_decode_attention(dev(w.q), kc, vc, dev(w.block_tables), dev(w.seq_lens), w.scale,
+                                 k_scale=w.k_scale, v_scale=w.v_scale)
+
+
+@pytest.mark.parametrize("B", [1, 8, 16, 32, 64])
+@pytest.mark.parametrize("bad", [-1, 1 << 30])
+def test_block_id_outside_the_pool_skips_its_tokens(B, bad):
+    # one full block in the middle of sequence 0 gets an ID outside the pool:
+    # the result is attention over the other tokens, i.e. the oracle on the
+    # table without that entry and the length shortened by B
+    w = pi.make_workload(2, seq_lens=[40 * 8 + 5, 300, 64], B=B, seed=26)
+    j = (w.seq_lens[0] // B) // 2
+    assert (j + 1) * B <= w.seq_lens[0] - 1  # a full block, not the appended token's
+    announce(f"B={B}: block {j} of sequence 0 -> {bad}")
+    r = Run(w)
+    m = pkv()
+    bt = r.bt.clone()
+    bt[0, j] = bad
+    out = m.paged_decode_attention(r.q, r.kc, r.vc, bt, r.sl, w.scale)
+    torch.cuda.synchronize()
+    kp, vp = host_bits(r.kc), host_bits(r.vc)
+    tables = w.block_tables.copy()
+    tables[0, j:-1] = w.block_tables[0, j + 1:]
+    lens = w.seq_lens.copy()
+    lens[0] -= B
+    ref = oracle.paged_attention(w.q, kp, vp, tables, lens, w.scale)
+    check_attention(w, host_f64(out), ref)
