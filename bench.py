@@ -74,6 +74,11 @@ def parse():
                     help="instead of the decode step, time the multi-token step (chunked prefill / speculative "
                          "decoding): the last min(N, L) tokens of every sequence are query rows, appended and then "
                          "attended causally; prints its own JSON line")
+    ap.add_argument("--block-size", type=int, default=0, metavar="B",
+                    help="override the configuration's block size (1, 8, 16, 32 or 64; same lengths and values)")
+    ap.add_argument("--block-size-sweep", action="store_true",
+                    help="instead of the decode step, time the attention launch of the configuration at every block "
+                         "size 1, 8, 16, 32, 64, with shuffled and with contiguous block IDs; prints one JSON line")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="instead of the benchmark, run 20 device-to-device copies of MIB MiB (counter calibration)")
     return ap.parse_args()
@@ -274,6 +279,85 @@ def bench_copy_blocks(args, w, torch, pkv) -> dict:
             "cpu_baseline": None}
 
 
+SWEEP_BLOCK_SIZES = (1, 8, 16, 32, 64)
+
+
+def time_attention(w, torch, pkv, steps: int, warmup: int, rotate: int) -> np.ndarray:
+    """Per-launch microseconds of paged_decode_attention on the workload
+    (after its decode append with the longest-first schedule), bracketed by
+    events on the launch stream."""
+    copies = [device_inputs(w, torch) for _ in range(max(1, rotate))]
+    d0 = copies[0]
+    P = w.partition_tokens
+    ws = pkv.alloc_workspace(d0["q"], d0["kc"], d0["vc"], d0["bt"], P)
+    sched = pkv.alloc_schedule(d0["bt"])
+    out = torch.empty_like(d0["q"])
+    slots = torch.empty(w.S, dtype=torch.int64, device="cuda")
+    stream = torch.cuda.current_stream()
+    sc = dict(k_scale=w.k_scale, v_scale=w.v_scale)
+
+    def one(i, ev=None):
+        d = copies[i % len(copies)]
+        pkv.decode_append(d["nk"], d["nv"], d["bt"], d["sl"], d["kc"], d["vc"], slot_mapping=slots, schedule=sched,
+                          stream=stream, **sc)
+        if ev:
+            ev[0].record(stream)
+        pkv.paged_decode_attention(d["q"], d["kc"], d["vc"], d["bt"], d["sl"], w.scale, out=out, workspace=ws,
+                                   partition_tokens=P, schedule=sched, stream=stream, **sc)
+        if ev:
+            ev[1].record(stream)
+
+    for i in range(warmup):
+        one(i)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i, e in enumerate(evs):
+        one(i, e)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    del copies
+    torch.cuda.empty_cache()
+    return us
+
+
+def bench_block_size_sweep(args, torch, pkv, pi) -> dict:
+    """The configuration's attention at each block size: KV-read GB/s with
+    shuffled block IDs (paged) and with each sequence's blocks adjacent
+    (contiguous), plus the share of allocated slots that hold tokens."""
+    rows = []
+    for B in SWEEP_BLOCK_SIZES:
+        row = {"block_size": B}
+        for layout in ("paged", "contiguous"):
+            w = pi.make_workload(args.config, mode="timing", B=B, contiguous=(layout == "contiguous"))
+            us = time_attention(w, torch, pkv, args.steps, args.warmup, args.rotate)
+            gbps = w.kv_read_bytes() / (us.mean() * 1e-6) / 1e9
+            row[layout] = {"attention_us": round(float(us.mean()), 2), "median_us": round(float(np.median(us)), 2),
+                           "kv_read_gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4)}
+            log(f"B={B} {layout}: {us.mean():.1f} us, {gbps:.0f} GB/s")
+            if layout == "paged":
+                nblk = -(-w.seq_lens.astype(np.int64) // B)
+                row["slot_utilisation"] = round(float(w.seq_lens.sum() / (nblk.sum() * B)), 5)
+                row["partition_tokens"] = int(pkv.decode_partition_tokens(w.S, w.Hq, w.Hkv, w.hs, w.M, B, 0))
+                desc = w.description
+                kvb = w.kv_read_bytes()
+            del w
+        row["paged_over_contiguous"] = round(row["paged"]["attention_us"] / row["contiguous"]["attention_us"], 4)
+        rows.append(row)
+    best = max(rows, key=lambda r: r["paged"]["kv_read_gbps"])
+    return {"metric": "paged decode attention KV-read GB/s per block size (block-size trade-off)",
+            "value": best["paged"]["kv_read_gbps"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(best["paged"]["attention_us"] / 1e3, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,1) q/K/V; no dataset)",
+            "config": {"workload": f"{desc}, block size swept", "block_sizes": list(SWEEP_BLOCK_SIZES),
+                       "kv_bytes_per_launch": kvb, "best_block_size": best["block_size"]},
+            "sweep": rows, "roofline": {"bound": "hbm", "achieved": best["paged"]["kv_read_gbps"],
+                                        "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                        "frac": best["paged"]["frac_hbm_peak"], "traffic": None,
+                                        "kernel": "paged_decode_attention at the best block size"},
+            "cpu_baseline": None}
+
+
 def kernel_sources_sha256(paths) -> str:
     import hashlib
 
@@ -351,15 +435,20 @@ def main() -> int:
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
     kvdt = "fp8" if args.kv_dtype == "fp8" else None
+    if args.block_size_sweep:
+        print(json.dumps(bench_block_size_sweep(args, torch, pkv, pi)), flush=True)
+        return 0
+    bkw = {"B": args.block_size} if args.block_size else {}
     if args.q_len:
-        base = pi.make_workload(args.config, mode="timing", contiguous=args.contiguous, dtype=kvdt)
+        base = pi.make_workload(args.config, mode="timing", contiguous=args.contiguous, dtype=kvdt, **bkw)
         q_lens = np.minimum(args.q_len, base.seq_lens)
         del base
-        w = pi.make_workload(args.config, mode="timing", contiguous=args.contiguous, dtype=kvdt, q_lens=q_lens)
+        w = pi.make_workload(args.config, mode="timing", contiguous=args.contiguous, dtype=kvdt, q_lens=q_lens,
+                             **bkw)
         log(f"generated config {args.config} with {w.rows} query rows in {time.perf_counter() - t0:.1f} s")
         print(json.dumps(bench_multi_token(args, w, torch, pkv)), flush=True)
         return 0
-    w = pi.make_workload(args.config, mode="timing", contiguous=args.contiguous, dtype=kvdt)
+    w = pi.make_workload(args.config, mode="timing", contiguous=args.contiguous, dtype=kvdt, **bkw)
     sc = dict(k_scale=w.k_scale, v_scale=w.v_scale)
     log(f"generated config {args.config} ({w.description}) in {time.perf_counter() - t0:.1f} s")
     if args.copy_blocks:
@@ -427,7 +516,8 @@ def main() -> int:
     attn_avg_s = float(attn_ms.mean()) / 1e3
     achieved = kv_bytes / attn_avg_s / 1e9
     traffic_path = args.traffic or os.path.join(ROOT, "profiles", TRAFFIC_RECORDS.get(args.config, ""))
-    traffic = None if w.dtype == "fp8" else measured_traffic(traffic_path, args.config, P_used, args.contiguous)
+    traffic = None if (w.dtype == "fp8" or args.block_size) else measured_traffic(traffic_path, args.config, P_used,
+                                                                                      args.contiguous)
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": ("paged_decode_attention with the step's longest-first schedule: "
@@ -442,7 +532,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
-        cpu = cpu_baseline(pi.make_workload(args.config, mode="timing", dtype=kvdt), args.cpu_seconds)
+        cpu = cpu_baseline(pi.make_workload(args.config, mode="timing", dtype=kvdt, **bkw), args.cpu_seconds)
     value = kv_bytes / (ms_step / 1e3) / 1e9
     rec = {
         "metric": "paged decode attention KV-read GB/s (% of HBM peak) + decode tokens/s, 1 GPU",

@@ -196,7 +196,6 @@ __device__ __forceinline__ void load_tile(TileRegs<T, HS>& t, const T* __restric
     }
 }
 
-// 32-token unit m of a block of BS >= 32 tokens (tokens 32m .. 32m+31).
 // Blocks smaller than the 16-token unit (B = 1, 2, 4 or 8; bf16 or fp32):
 // the unit's tokens come from 16 / B consecutive blocks of the wave's
 // partition, so each lane fetches its own block IDs from the wave's list
@@ -249,6 +248,16 @@ __device__ __forceinline__ int load_small(TileRegs<T, HS>& t, const T* __restric
     return tmask;
 }
 
+// 32-token unit m of a block of BS >= 32 tokens (tokens 32m .. 32m+31).
+// With BS = 64 a unit reads half of each value row and the next unit the
+// other half: those loads go through the caches normally (a streaming load
+// of half a line left the other half to be fetched from HBM again).
+template <typename V>
+__device__ __forceinline__ V load_value_part(const V* p, bool whole_rows)
+{
+    return whole_rows ? load_stream(p) : *p;
+}
+
 template <int HS, int BS>
 __device__ __forceinline__ void load_wide(WideRegs<HS>& t, const __bf16* __restrict__ tile_k,
                                           const __bf16* __restrict__ tile_v, int m, int r, int c)
@@ -260,7 +269,7 @@ __device__ __forceinline__ void load_wide(WideRegs<HS>& t, const __bf16* __restr
             t.k[mp].v[i] = load_stream((const bf16x8*)(tile_k + ((4 * i + r) * BS + 32 * m + 16 * mp + c) * 8));
 #pragma unroll
     for (int i = 0; i < HS / 16; ++i)  // head dim 16i + c, tokens 32m + 8r .. +7
-        t.v[i] = load_stream((const bf16x8*)(tile_v + (16 * i + c) * BS + 32 * m + 8 * r));
+        t.v[i] = load_value_part((const bf16x8*)(tile_v + (16 * i + c) * BS + 32 * m + 8 * r), BS == 32);
 }
 
 // FP8 (E4M3) caches, bf16 queries: one 16-token sub-tile as raw codes.
@@ -352,7 +361,7 @@ __device__ __forceinline__ void load_fp8_wide(Fp8WideRegs<HS>& t, const uint8_t*
             t.k[mp][i] = load_stream((const u32x4*)(tile_k + ((4 * i + r) * BS + 32 * m + 16 * mp + c) * 16));
 #pragma unroll
     for (int i = 0; i < HS / 16; ++i) {
-        const u32x2 w = load_stream_v((const u32x2*)(tile_v + (16 * i + c) * BS + 32 * m + 8 * r));
+        const u32x2 w = load_value_part((const u32x2*)(tile_v + (16 * i + c) * BS + 32 * m + 8 * r), BS == 32);
         t.v[i][0] = w[0];
         t.v[i][1] = w[1];
     }
