@@ -323,8 +323,21 @@ PKV_API pkv_status paged_decode_step(const void* q, const void* new_k, const voi
  */
 
 /*
- * Bytes of device workspace paged_multi_token_attention needs (0 when each
- * sequence's table fits one chunk of partitions): one fp32 partial per
+ * partition_tokens of the multi-token calls may also be PKV_PARTITION_NONE:
+ * the unpartitioned kernel, whose work-groups take 128 rows each and walk
+ * the whole visible context with the keys and values staged in LDS (no
+ * workspace; bf16 and FP8 pools with blocks of 16 tokens or more, else
+ * PKV_ERR_UNSUPPORTED).  With 0 the library picks it when every (sequence,
+ * KV head) has at least 64 rows and the batch gives it at least 512
+ * work-groups, and the partitioned kernel otherwise; a positive length
+ * always selects the partitioned kernel.  Both compute the same rule.
+ */
+#define PKV_PARTITION_NONE (-1)
+
+/*
+ * Bytes of device workspace paged_multi_token_attention needs with the
+ * partitioned kernel (0 when each sequence's table fits one chunk of
+ * partitions; the unpartitioned kernel needs none): one fp32 partial per
  * (sequence, KV head, tile of 16 (row, group member) pairs, chunk, tile row).
  * max_q_len <= 0 or an invalid shape gives 0.
  */
@@ -342,6 +355,21 @@ PKV_API pkv_status pkv_multi_token_slot_mapping(const int32_t* block_tables, con
                                                 const int32_t* q_start, int32_t num_seqs, int32_t num_q_rows,
                                                 int32_t max_q_len, int32_t max_blocks_per_seq,
                                                 int32_t block_size, int64_t* slot_mapping, void* stream);
+
+/*
+ * Stores new_k / new_v of every query row (rule above) in the slot of its
+ * position, bit for bit as kv_cache_append with pkv_multi_token_slot_mapping
+ * would (FP8 pools: the same quantization), but block by block: the rows
+ * that land in one block are written together, so the value rows of the
+ * block are written along their length instead of one element per token.
+ * Rows whose position is negative, past the table row or in a block outside
+ * the pool are skipped.  Asynchronous on `stream`.  PKV_ERR_UNSUPPORTED for
+ * num_seqs > 65535.
+ */
+PKV_API pkv_status pkv_multi_token_append(const void* k, const void* v, const int32_t* q_start, int32_t num_q_rows,
+                                          int32_t max_q_len, const int32_t* block_tables, const int32_t* seq_lens,
+                                          int32_t num_seqs, int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                                          void* k_cache, void* v_cache, void* stream);
 
 /*
  * Causal paged attention of every query row (rule above) over its
@@ -363,7 +391,7 @@ PKV_API pkv_status paged_multi_token_attention(const void* q, const int32_t* q_s
 /*
  * One multi-token step: slot mapping of the rows into slot_mapping (int64
  * [num_q_rows], device, required), append of new_k/new_v of every row
- * (kv_cache_append), then paged_multi_token_attention.  Three kernels in
+ * (pkv_multi_token_append), then paged_multi_token_attention.  Three kernels in
  * stream order; every argument is checked before the first, so a rejected
  * call changes nothing.
  */

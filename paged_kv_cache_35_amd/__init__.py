@@ -92,6 +92,8 @@ def library():
         L.pkv_multi_token_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
         L.pkv_multi_token_slot_mapping.restype = i32
         L.pkv_multi_token_slot_mapping.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P]
+        L.pkv_multi_token_append.restype = i32
+        L.pkv_multi_token_append.argtypes = [P, P, P, i32, i32, P, P, i32, i32, ctypes.POINTER(CacheDesc), P, P, P]
         L.paged_multi_token_attention.restype = i32
         L.paged_multi_token_attention.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, i32,
                                                   ctypes.POINTER(CacheDesc), f32, P, P, sz, i32, P]
@@ -374,6 +376,10 @@ def decode_step(q, k_cache, v_cache, block_tables, seq_lens, new_k, new_v, scale
 
 
 # ---- several query tokens per sequence -------------------------------------
+# partition_tokens: 0 = library's choice, > 0 = the partitioned kernel with
+# that length, PARTITION_NONE = the unpartitioned (prefill) kernel.
+PARTITION_NONE = -1
+
 # Rows q_start[s] .. q_start[s+1]-1 of q / out / new k, v belong to sequence s
 # and are its last n_s tokens; row i sits at position seq_lens[s] - n_s + i and
 # attends causally.  max_q_len (>= every n_s) is a host int, so that no call
@@ -422,6 +428,25 @@ def multi_token_slot_mapping(block_tables: torch.Tensor, seq_lens: torch.Tensor,
         _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), _dev(q_start, "q_start"), S, num_q_rows,
         int(max_q_len), block_tables.shape[1], int(block_size), _dev(out, "slot_mapping"), _stream(stream)))
     return out
+
+
+def multi_token_append(k: torch.Tensor, v: torch.Tensor, q_start: torch.Tensor, max_q_len: int,
+                       block_tables: torch.Tensor, seq_lens: torch.Tensor, k_cache: torch.Tensor,
+                       v_cache: torch.Tensor, stream=None, k_scale: float = 1.0, v_scale: float = 1.0) -> None:
+    """Stores k[r], v[r] ([rows, Hkv, hs]) of every query row in the slot of
+    its position, block by block."""
+    desc = cache_desc(k_cache, v_cache, k_scale, v_scale)
+    if k.shape != v.shape or k.dim() != 3 or tuple(k.shape[1:]) != (desc.num_kv_heads, desc.head_size):
+        raise ValueError("k and v must be [rows, Hkv, head_size]")
+    if k.dtype != io_dtype(k_cache) or v.dtype != io_dtype(k_cache):
+        raise ValueError("k, v and the pools must share a dtype")
+    S = block_tables.shape[0]
+    if q_start.dtype != torch.int32 or q_start.shape != (S + 1,):
+        raise ValueError("q_start must be int32 [S + 1]")
+    _check("pkv_multi_token_append", library().pkv_multi_token_append(
+        _dev(k, "k"), _dev(v, "v"), _dev(q_start, "q_start"), k.shape[0], int(max_q_len),
+        _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), S, block_tables.shape[1],
+        ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _stream(stream)))
 
 
 def paged_multi_token_attention(q: torch.Tensor, q_start: torch.Tensor, max_q_len: int, k_cache: torch.Tensor,

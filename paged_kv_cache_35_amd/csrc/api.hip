@@ -116,10 +116,10 @@ pkv_status pkv_decode_slot_mapping(const int32_t* block_tables, const int32_t* s
 
 namespace {
 
-pkv_status append_common(const void* k, const void* v, int64_t* slot_mapping, const int32_t* block_tables,
-                         const int32_t* seq_lens, int32_t max_blocks_per_seq, int32_t num_tokens,
-                         const pkv_cache_desc* cache, void* k_cache, void* v_cache, void* stream,
-                         pkv::AppendArgs::Schedule sched = {nullptr, nullptr, nullptr})
+pkv::AppendArgs append_args(const void* k, const void* v, int64_t* slot_mapping, const int32_t* block_tables,
+                            const int32_t* seq_lens, int32_t max_blocks_per_seq, int32_t num_tokens,
+                            const pkv_cache_desc* cache, void* k_cache, void* v_cache,
+                            pkv::AppendArgs::Schedule sched = {nullptr, nullptr, nullptr})
 {
     pkv::AppendArgs a;
     a.sched = sched;
@@ -140,6 +140,16 @@ pkv_status append_common(const void* k, const void* v, int64_t* slot_mapping, co
     // FP8: both sides of the append multiply by the fp32 reciprocal of the scale
     a.k_inv_scale = cache->dtype == PKV_FP8_E4M3 ? 1.0f / cache->k_scale : 1.0f;
     a.v_inv_scale = cache->dtype == PKV_FP8_E4M3 ? 1.0f / cache->v_scale : 1.0f;
+    return a;
+}
+
+pkv_status append_common(const void* k, const void* v, int64_t* slot_mapping, const int32_t* block_tables,
+                         const int32_t* seq_lens, int32_t max_blocks_per_seq, int32_t num_tokens,
+                         const pkv_cache_desc* cache, void* k_cache, void* v_cache, void* stream,
+                         pkv::AppendArgs::Schedule sched = {nullptr, nullptr, nullptr})
+{
+    const pkv::AppendArgs a = append_args(k, v, slot_mapping, block_tables, seq_lens, max_blocks_per_seq, num_tokens,
+                                          cache, k_cache, v_cache, sched);
     return hip_status(pkv::launch_append(a, (hipStream_t)stream));
 }
 
@@ -242,7 +252,8 @@ namespace {
 pkv_status attention_args(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                           const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                           const pkv_cache_desc* cache, float scale, void* out, void* workspace,
-                          size_t workspace_bytes, int32_t partition_tokens, pkv::DecodeArgs& a, bool& nothing_to_do)
+                          size_t workspace_bytes, int32_t partition_tokens, pkv::DecodeArgs& a, bool& nothing_to_do,
+                          bool check_workspace = true)
 {
     nothing_to_do = false;
     if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
@@ -275,7 +286,7 @@ pkv_status attention_args(const void* q, const void* k_cache, const void* v_cach
         return PKV_ERR_UNSUPPORTED;
     const size_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, Hkv, cache->head_size,
                                                    max_blocks_per_seq, cache->block_size, partition_tokens);
-    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    if (check_workspace && need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
         return PKV_ERR_WORKSPACE;
 
     a.sched_order = nullptr;
@@ -382,7 +393,50 @@ pkv_status pkv_multi_token_slot_mapping(const int32_t* block_tables, const int32
                                                            (hipStream_t)stream));
 }
 
+pkv_status pkv_multi_token_append(const void* k, const void* v, const int32_t* q_start, int32_t num_q_rows,
+                                  int32_t max_q_len, const int32_t* block_tables, const int32_t* seq_lens,
+                                  int32_t num_seqs, int32_t max_blocks_per_seq, const pkv_cache_desc* cache,
+                                  void* k_cache, void* v_cache, void* stream)
+{
+    if (num_seqs < 0 || num_q_rows < 0 || max_q_len < 0 || max_blocks_per_seq <= 0)
+        return PKV_ERR_INVALID_ARG;
+    const pkv_status st = check_cache(cache);
+    if (st != PKV_OK)
+        return st;
+    if (!k_cache || !v_cache || !aligned16(k_cache) || !aligned16(v_cache))
+        return PKV_ERR_INVALID_ARG;
+    if (num_seqs == 0 || num_q_rows == 0 || max_q_len == 0)
+        return PKV_OK;
+    if (!k || !v || !q_start || !block_tables || !seq_lens || !aligned16(k) || !aligned16(v))
+        return PKV_ERR_INVALID_ARG;
+    if (num_seqs > 65535 || (int64_t)max_q_len / cache->block_size + 2 > 65535)
+        return PKV_ERR_UNSUPPORTED;
+    const pkv::AppendArgs a = append_args(k, v, nullptr, block_tables, seq_lens, max_blocks_per_seq, num_q_rows,
+                                          cache, k_cache, v_cache);
+    return hip_status(pkv::launch_multi_token_append(a, q_start, num_seqs, num_q_rows, max_q_len, (hipStream_t)stream));
+}
+
 namespace {
+
+// The library's choice for a multi-token call (partition_tokens == 0): the
+// prefill kernel when every (sequence, KV head) has at least 64 rows (query
+// tokens x group size) and the batch gives it at least 512 work-groups (two
+// per compute unit); otherwise the partitioned decode kernel, which splits
+// long contexts over work-groups.  A requested partition length always
+// selects the partitioned kernel.
+constexpr int64_t kPrefillMinRows = 64;
+constexpr int64_t kPrefillMinGroups = 512;
+
+hipError_t launch_multi_token(const pkv::DecodeArgs& a, int32_t partition_tokens, hipStream_t stream)
+{
+    const int64_t G = a.num_q_heads / a.num_kv_heads;
+    if (partition_tokens == PKV_PARTITION_NONE)
+        return pkv::launch_prefill(a, stream);
+    if (partition_tokens == 0 && pkv::prefill_supported(a) && (int64_t)a.max_q_len * G >= kPrefillMinRows &&
+        pkv::prefill_work_groups(a) >= kPrefillMinGroups && pkv::prefill_work_groups(a) <= INT32_MAX)
+        return pkv::launch_prefill(a, stream);
+    return pkv::launch_decode(a, stream);
+}
 
 // attention_args plus the query-row description of a multi-token call.
 pkv_status multi_token_args(const void* q, const int32_t* q_start, int32_t num_q_rows, int32_t max_q_len,
@@ -394,15 +448,19 @@ pkv_status multi_token_args(const void* q, const int32_t* q_start, int32_t num_q
 {
     if (num_q_rows < 0 || max_q_len < 0)
         return PKV_ERR_INVALID_ARG;
+    // PKV_PARTITION_NONE: the unpartitioned (prefill) kernel, no workspace
+    const bool unpartitioned = partition_tokens == PKV_PARTITION_NONE;
+    const int32_t P = unpartitioned ? 0 : partition_tokens;
     // the decode workspace is never larger than the multi-token one, so the
     // decode check in attention_args passes whenever the check below does
-    const size_t need = pkv_multi_token_workspace_bytes(num_seqs, num_q_heads, cache ? cache->num_kv_heads : 0,
-                                                        cache ? cache->head_size : 0, max_q_len > 0 ? max_q_len : 1,
-                                                        max_blocks_per_seq, cache ? cache->block_size : 0,
-                                                        partition_tokens);
+    const size_t need = unpartitioned ? 0
+                                      : pkv_multi_token_workspace_bytes(
+                                            num_seqs, num_q_heads, cache ? cache->num_kv_heads : 0,
+                                            cache ? cache->head_size : 0, max_q_len > 0 ? max_q_len : 1,
+                                            max_blocks_per_seq, cache ? cache->block_size : 0, P);
     pkv_status st = attention_args(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
                                    max_blocks_per_seq, cache, scale, out, workspace,
-                                   need > workspace_bytes ? 0 : workspace_bytes, partition_tokens, a, nothing_to_do);
+                                   need > workspace_bytes ? 0 : workspace_bytes, P, a, nothing_to_do, !unpartitioned);
     if (st != PKV_OK || nothing_to_do)
         return st;
     if (num_q_rows == 0 || max_q_len == 0) {
@@ -424,6 +482,8 @@ pkv_status multi_token_args(const void* q, const int32_t* q_start, int32_t num_q
     const size_t units = (size_t)num_seqs * cache->num_kv_heads * tiles * a.max_parts * 16;
     a.ws_o = need > 0 ? (float*)workspace : nullptr;
     a.ws_ml = need > 0 ? (float*)workspace + units * cache->head_size : nullptr;
+    if (unpartitioned && (!pkv::prefill_supported(a) || pkv::prefill_work_groups(a) > INT32_MAX))
+        return PKV_ERR_UNSUPPORTED;
     return PKV_OK;
 }
 
@@ -443,7 +503,7 @@ pkv_status paged_multi_token_attention(const void* q, const int32_t* q_start, in
                                            workspace, workspace_bytes, partition_tokens, a, nothing_to_do);
     if (st != PKV_OK || nothing_to_do)
         return st;
-    return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+    return hip_status(launch_multi_token(a, partition_tokens, (hipStream_t)stream));
 }
 
 pkv_status paged_multi_token_step(const void* q, const void* new_k, const void* new_v, void* k_cache,
@@ -471,10 +531,12 @@ pkv_status paged_multi_token_step(const void* q, const void* new_k, const void* 
                                                          slot_mapping, (hipStream_t)stream));
     if (st != PKV_OK)
         return st;
-    st = append_common(new_k, new_v, slot_mapping, nullptr, nullptr, 0, num_q_rows, cache, k_cache, v_cache, stream);
+    const pkv::AppendArgs ap = append_args(new_k, new_v, nullptr, block_tables, seq_lens, max_blocks_per_seq,
+                                           num_q_rows, cache, k_cache, v_cache);
+    st = hip_status(pkv::launch_multi_token_append(ap, q_start, num_seqs, num_q_rows, max_q_len, (hipStream_t)stream));
     if (st != PKV_OK)
         return st;
-    return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+    return hip_status(launch_multi_token(a, partition_tokens, (hipStream_t)stream));
 }
 
 pkv_status paged_decode_step(const void* q, const void* new_k, const void* new_v, void* k_cache, void* v_cache,

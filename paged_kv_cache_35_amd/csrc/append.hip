@@ -323,4 +323,121 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream)
     return a.block_tables ? launch_append_impl<true>(a, stream) : launch_append_impl<false>(a, stream);
 }
 
+// Append of the query rows of a multi-token call, block by block.  The rows
+// of sequence s are its last n tokens (positions L - n .. L - 1), so the
+// rows that land in one block are consecutive slots of it: work-group
+// (segment g, KV head h, sequence s) writes the rows of the g-th block they
+// touch.  Keys go out as 16-byte chunks, consecutive tokens side by side in
+// a chunk row; values are staged through LDS ([token][hs], rows read whole)
+// and written along the block's [hs][B] rows, consecutive tokens side by
+// side, instead of one scattered element per token.  The slots are those of
+// pkv_multi_token_slot_mapping and the bytes those of kv_cache_append
+// (FP8: the same quantize16 / single-code conversion).  Rows whose position
+// is negative, past the table row or in a block outside the pool are
+// skipped.
+template <typename E>
+__global__ __launch_bounds__(kAppendThreads) void multi_token_append_kernel(
+    const uint8_t* __restrict__ k, const uint8_t* __restrict__ v, const int32_t* __restrict__ block_tables,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ q_start, int32_t num_q_rows,
+    int32_t max_q_len, int32_t M, u32x4* __restrict__ k_cache, E* __restrict__ v_cache, int32_t Hkv,
+    int32_t hs, int32_t B, int32_t num_blocks, float k_inv_scale, float v_inv_scale)
+{
+    constexpr bool Q8 = sizeof(E) == 1;
+    constexpr int X = 16 / sizeof(E);             // pool elements per 16-byte chunk
+    constexpr int IB = Q8 ? 2 : (int)sizeof(E);    // input bytes per element (bf16 for FP8 pools)
+    extern __shared__ __attribute__((aligned(16))) uint8_t vs_raw[];  // [B][hs * IB + 4]
+    const int g = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+    const int qs0 = q_start[s], qs1 = q_start[s + 1];
+    int n = qs1 - qs0;
+    if (qs0 < 0 || n < 0 || qs1 > num_q_rows)
+        return;
+    n = n < max_q_len ? n : max_q_len;
+    const int L = seq_lens[s];
+    const int P0 = L - n;  // position of row 0
+    const int first = P0 > 0 ? P0 : 0;
+    const int b = first / B + g;  // table index of this segment's block
+    const int seg0 = b * B > first ? b * B : first;
+    const int seg1 = (b + 1) * B < L ? (b + 1) * B : L;
+    if (n <= 0 || seg0 >= seg1 || b >= M)
+        return;
+    const int64_t id = block_tables[(int64_t)s * M + b];
+    if (id < 0 || id >= num_blocks)
+        return;
+    const int cnt = seg1 - seg0, off0 = seg0 - b * B;
+    const int64_t row0 = qs0 + (seg0 - P0);
+    const int64_t in_row = (int64_t)Hkv * hs * IB;  // bytes of one input row
+    const int CH = hs / X;                          // key chunks per head
+    const int row_bytes = hs * IB + 4;              // LDS row, padded
+
+    // keys: chunk f of token j, token fastest
+    for (int it = threadIdx.x; it < CH * cnt; it += kAppendThreads) {
+        const int f = it / cnt, j = it - f * cnt;
+        const uint8_t* src = k + (row0 + j) * in_row + ((int64_t)h * hs + (int64_t)f * X) * IB;
+        u32x4 val;
+        if constexpr (Q8) {
+            const u32x4 in[2] = {*(const u32x4*)src, *(const u32x4*)(src + 16)};
+            val = quantize16(in, k_inv_scale);
+        } else {
+            val = *(const u32x4*)src;
+        }
+        __builtin_nontemporal_store(val, &k_cache[((id * Hkv + h) * CH + f) * B + off0 + j]);
+    }
+    // values: stage the rows, then write along the block rows
+    const int pieces = hs * IB / 16;
+    for (int it = threadIdx.x; it < cnt * pieces; it += kAppendThreads) {
+        const int j = it / pieces, pc = it - j * pieces;
+        const u32x4 val = *(const u32x4*)(v + (row0 + j) * in_row + (int64_t)h * hs * IB + pc * 16);
+        uint32_t* dst = (uint32_t*)(vs_raw + j * row_bytes + pc * 16);
+        dst[0] = val[0];
+        dst[1] = val[1];
+        dst[2] = val[2];
+        dst[3] = val[3];
+    }
+    __syncthreads();
+    E* vdst = v_cache + (id * Hkv + h) * (int64_t)hs * B + off0;
+    for (int it = threadIdx.x; it < hs * cnt; it += kAppendThreads) {
+        const int d = it / cnt, j = it - d * cnt;
+        const uint8_t* e = vs_raw + j * row_bytes + d * IB;
+        E out;
+        if constexpr (Q8) {
+            const uint32_t bits = (uint32_t)(*(const uint16_t*)e) << 16;
+            const float x = fminf(fmaxf(__builtin_bit_cast(float, bits) * v_inv_scale, -448.0f), 448.0f);
+            out = (E)(__builtin_amdgcn_cvt_pk_fp8_f32(x, x, 0, false) & 0xFF);
+        } else {
+            out = *(const E*)e;
+        }
+        __builtin_nontemporal_store(out, &vdst[(int64_t)d * B + j]);
+    }
+}
+
+hipError_t launch_multi_token_append(const AppendArgs& a, const int32_t* q_start, int32_t num_seqs, int32_t num_q_rows,
+                                     int32_t max_q_len, hipStream_t stream)
+{
+    // segments: the blocks max_q_len consecutive positions can touch
+    const int segs = (max_q_len + a.block_size - 1) / a.block_size + 1;
+    const dim3 grid(segs, a.num_kv_heads, num_seqs);
+    const int ib = a.elem_bytes == 1 ? 2 : a.elem_bytes;
+    const size_t lds = (size_t)a.block_size * (a.head_size * ib + 4);
+    switch (a.elem_bytes) {
+    case 1:
+        hipLaunchKernelGGL(multi_token_append_kernel<uint8_t>, grid, dim3(kAppendThreads), lds, stream,
+                           (const uint8_t*)a.k, (const uint8_t*)a.v, a.block_tables, a.seq_lens, q_start, num_q_rows,
+                           max_q_len, a.max_blocks_per_seq, (u32x4*)a.k_cache, (uint8_t*)a.v_cache, a.num_kv_heads,
+                           a.head_size, a.block_size, a.num_blocks, a.k_inv_scale, a.v_inv_scale);
+        break;
+    case 2:
+        hipLaunchKernelGGL(multi_token_append_kernel<uint16_t>, grid, dim3(kAppendThreads), lds, stream,
+                           (const uint8_t*)a.k, (const uint8_t*)a.v, a.block_tables, a.seq_lens, q_start, num_q_rows,
+                           max_q_len, a.max_blocks_per_seq, (u32x4*)a.k_cache, (uint16_t*)a.v_cache, a.num_kv_heads,
+                           a.head_size, a.block_size, a.num_blocks, a.k_inv_scale, a.v_inv_scale);
+        break;
+    default:
+        hipLaunchKernelGGL(multi_token_append_kernel<uint32_t>, grid, dim3(kAppendThreads), lds, stream,
+                           (const uint8_t*)a.k, (const uint8_t*)a.v, a.block_tables, a.seq_lens, q_start, num_q_rows,
+                           max_q_len, a.max_blocks_per_seq, (u32x4*)a.k_cache, (uint32_t*)a.v_cache, a.num_kv_heads,
+                           a.head_size, a.block_size, a.num_blocks, a.k_inv_scale, a.v_inv_scale);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace pkv

@@ -1,0 +1,69 @@
+// Device helpers shared by the attention kernels (decode.hip, prefill.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace pkv {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleSlack = 8.0f;  // log2 units: probabilities stay <= 256
+
+// Key row c of M-tile mp of a 32-token unit holds token 16*mp + c, so each
+// key load reads 16 consecutive 16-byte chunks (256 contiguous bytes per
+// lane group: whole 128-byte lines for the streaming loads).  The score
+// layout then gives lane group r tokens 4r .. 4r+3 (M-tile 0) and
+// 16+4r .. 16+4r+3 (M-tile 1), while the value MFMA wants tokens
+// 8r .. 8r+7 in lane group r; to_value_order moves the probabilities there.
+//
+// With X_r / Y_r the four values of lane group r from M-tile 0 / 1, lane
+// group r needs (X_{2r}, X_{2r+1}) for r < 2 and (Y_{2r-4}, Y_{2r-3}) for
+// r >= 2.  v_permlane32_swap exchanges lane groups 2,3 of its first operand
+// with groups 0,1 of its second: (X0 X1 Y0 Y1), (X2 X3 Y2 Y3).
+// v_permlane16_swap exchanges odd groups of the first with even groups of
+// the second: (X0 X2 Y0 Y2), (X1 X3 Y1 Y3) -- the first and second four
+// tokens of each lane group.
+//
+// Written as inline assembly because the compiler at hand, given the two
+// swap builtins chained, keeps only the first result of the second swap
+// (the second comes back as a copy of the first).  Both registers are read
+// and written in place; the s_nop 1 before each swap gives the two wait
+// states the swaps need after a vector write of their operands, and the one
+// after covers a read of their results.
+__device__ __forceinline__ void to_value_order(float& x, float& y)
+{
+    asm volatile(
+        "s_nop 1\n\t"
+        "v_permlane32_swap_b32 %0, %1\n\t"
+        "s_nop 1\n\t"
+        "v_permlane16_swap_b32 %0, %1\n\t"
+        "s_nop 1"
+        : "+v"(x), "+v"(y));
+}
+
+__device__ __forceinline__ void store_elem(__bf16* p, float x) { *p = (__bf16)x; }
+__device__ __forceinline__ void store_elem(float* p, float x) { *p = x; }
+
+// Four E4M3 codes (one dword) to four bf16: v_cvt_pk_f32_fp8 gives the exact
+// values in fp32, and an E4M3 value has at most 4 significant bits, so its
+// fp32 pattern's upper half is the same value in bf16.  Element e of the
+// result is code e (byte e of w).
+__device__ __forceinline__ unsigned upper_halves(float x0, float x1)
+{
+    return (__builtin_bit_cast(unsigned, x0) >> 16) | (__builtin_bit_cast(unsigned, x1) & 0xFFFF0000u);
+}
+
+__device__ __forceinline__ void fp8x4_to_bf16(unsigned w, unsigned& lo, unsigned& hi)
+{
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);  // codes 0, 1
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);   // codes 2, 3
+    lo = upper_halves(a[0], a[1]);
+    hi = upper_halves(b[0], b[1]);
+}
+
+}  // namespace pkv

@@ -70,6 +70,14 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Multi-token attention with many rows per (sequence, KV head): the
+// prefill kernel (prefill.hip) takes 128 rows per work-group over the whole
+// visible context, no partitions and no workspace.  Supported for bf16 and
+// FP8 pools with blocks of 16 tokens or more.
+bool prefill_supported(const DecodeArgs& a);
+int64_t prefill_work_groups(const DecodeArgs& a);
+hipError_t launch_prefill(const DecodeArgs& a, hipStream_t stream);
+
 struct AppendArgs {
     const void* k;
     const void* v;
@@ -98,6 +106,11 @@ struct AppendArgs {
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+
+// Append of the rows of a multi-token call (a.block_tables, a.seq_lens set;
+// a.slot_mapping unused): the rows landing in one block are written together.
+hipError_t launch_multi_token_append(const AppendArgs& a, const int32_t* q_start, int32_t num_seqs, int32_t num_q_rows,
+                                     int32_t max_q_len, hipStream_t stream);
 
 // Copies whole blocks (block_bytes per pool) for num_pairs (src, dst) pairs.
 hipError_t launch_copy_blocks(const int32_t* pairs, int32_t num_pairs, int32_t num_blocks, int64_t block_bytes,

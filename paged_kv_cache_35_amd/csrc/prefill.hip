@@ -1,0 +1,439 @@
+// Causal paged attention for many query rows per sequence (long prefill
+// chunks): the rows of one (sequence, KV head) in blocks of 128, with the
+// sequence's keys and values staged through LDS once per work-group and
+// shared by its four waves.
+//
+// What is computed is the multi-token rule of paged_multi_token_attention:
+// the n query rows of sequence s are its last n tokens, row i at position
+// L - n + i attends positions 0 .. L - n + i, through the block table as in
+// decode (cache-structure page, "软件地址翻译"; chunked prefill on the
+// "vLLM 核心工程深度剖析" page, section 6.1).
+//
+// How it maps onto CDNA4:
+//  * Work-group (KV head, row block, sequence), 4 waves, 32 rows per wave as
+//    two 16-row MFMA tiles; a row is a (query token, group member) pair.
+//  * The keys and values are walked in 32-token units.  All 256 threads copy
+//    the next unit from the pools into the other LDS stage (bf16; FP8 codes
+//    are converted on the way) while the waves compute on this one: one
+//    barrier per unit.  Keys sit in LDS as [hs/8][32 tokens] 16-byte
+//    chunks, so a lane's 16-byte read is the A operand of
+//    v_mfma_f32_16x16x32_bf16 (token row c, 8 head dims) and a lane group
+//    reads 256 contiguous bytes.  Values sit as [hs][32 tokens + 8]: the 8
+//    padding elements make the 16-byte reads of 16 consecutive head dims hit
+//    distinct banks.
+//  * Each wave reads one unit's key and value operands once from LDS and
+//    uses them for both of its row tiles (scores, then the value sum with the
+//    probabilities moved to the value order by to_value_order, hi + lo bf16
+//    parts as in decode).
+//  * Causal: a lane's row has its own limit; a wave stops computing at its
+//    last row's limit, and the work-group stops loading at its last row's.
+//  * The K/V loads use the caches normally: the other row blocks of the same
+//    (sequence, KV head) read the same tiles.
+//  * The block IDs of 64 consecutive blocks sit one per lane and each thread
+//    fetches the one it needs with ds_bpermute; the next 64 are loaded while
+//    the current ones are in use.  An ID outside the pool reads block 0 and
+//    its tokens are masked (the same rule as decode).
+#include <type_traits>
+
+#include "attn_common.h"
+#include "pkv_internal.h"
+
+namespace pkv {
+
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = kPfWaves * 64;
+constexpr int kPfTiles = 2;                       // 16-row MFMA tiles per wave
+constexpr int kPfRows = kPfWaves * kPfTiles * 16; // rows per work-group
+constexpr int kPfUnit = 32;                       // tokens per staged unit
+constexpr int kPfVRow = kPfUnit + 8;              // LDS value row (elements), padded
+constexpr int kXcds = 8;                          // MI355X: 8 XCDs of 32 compute units
+
+template <int HS>
+struct PfStage {
+    bf16x8 k[HS / 8][kPfUnit];        // chunk f (head dims 8f .. 8f+7) of token t
+    __bf16 v[HS][kPfVRow];            // head dim d, token t
+};
+
+// Global reads of one unit: 4 * HS key and 4 * HS value pieces of 16 bytes
+// (bf16: 8 elements), or 2 * HS of each (FP8: 16 codes); a thread takes
+// pieces tid, tid + 256, ...
+template <int HS, bool F8>
+struct PfPieces {
+    static constexpr int P = F8 ? 2 * HS : 4 * HS;  // pieces of each kind
+    static constexpr int N = (P + kPfThreads - 1) / kPfThreads;
+    u32x4 k[N];
+    u32x4 v[N];
+};
+
+// 16 E4M3 codes to 16 bf16 (two 16-byte halves, codes 0-7 and 8-15).
+__device__ __forceinline__ void fp8x16_to_bf16(const u32x4& w, u32x4& lo, u32x4& hi)
+{
+    unsigned e[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        fp8x4_to_bf16(w[i], e[2 * i], e[2 * i + 1]);
+    lo = (u32x4){e[0], e[1], e[2], e[3]};
+    hi = (u32x4){e[4], e[5], e[6], e[7]};
+}
+
+template <int HS, int BS, bool F8>
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2))) void paged_prefill_kernel(
+    const __bf16* __restrict__ q, const typename std::conditional<F8, uint8_t, __bf16>::type* __restrict__ k_cache,
+    const typename std::conditional<F8, uint8_t, __bf16>::type* __restrict__ v_cache,
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ q_start, int32_t num_q_rows, int32_t max_q_len, int32_t Hq, int32_t Hkv, int32_t M,
+    int32_t num_blocks, int32_t RB, float qscale, float oscale, __bf16* __restrict__ out)
+{
+    using C = typename std::conditional<F8, uint8_t, __bf16>::type;
+    static_assert(BS >= 16 && (BS % 16) == 0, "blocks of 16, 32 or 64 tokens");
+    constexpr int TILE = HS * BS;  // elements of one (block, KV head) tile
+    __shared__ PfStage<HS> stage[2];
+
+    // XCD-aware order: work-groups are dealt to the 8 XCDs round-robin by
+    // their linear index, and each XCD has its own L2.  The row blocks of one
+    // (sequence, KV head) read the same keys and values, so consecutive
+    // logical indices are mapped to one XCD: physical index p runs on XCD
+    // p % 8, and XCD x takes the x-th contiguous share of the logical range.
+    const int64_t N = (int64_t)gridDim.x;
+    const int64_t p = blockIdx.x;
+    const int64_t xcd = p % kXcds, slot = p / kXcds;
+    const int64_t q8 = N / kXcds, rem = N % kXcds;
+    const int64_t logical = (xcd < rem ? xcd * (q8 + 1) : rem * (q8 + 1) + (xcd - rem) * q8) + slot;
+    const int rb = (int)(logical % RB);
+    const int kvh = (int)((logical / RB) % Hkv);
+    const int s = (int)(logical / ((int64_t)RB * Hkv));
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane >> 4;
+    const int c = lane & 15;
+    const int G = Hq / Hkv;
+
+    int qs0 = q_start[s];
+    const int qs1 = q_start[s + 1];
+    int n = qs1 - qs0;
+    if (qs0 < 0 || n < 0 || qs1 > num_q_rows)
+        n = 0;
+    n = n < max_q_len ? n : max_q_len;
+    const int nrows = n * G;
+    const int row0 = rb * kPfRows;
+    if (row0 >= nrows)
+        return;  // uniform, before any barrier
+    const int L_in = seq_lens[s];
+    const int L = L_in < 0 ? 0 : (L_in > M * BS ? M * BS : L_in);
+    auto out_row = [&](int rho) __attribute__((always_inline)) -> int64_t {
+        const int i = rho / G;
+        return ((int64_t)(qs0 + i) * Hq + (int64_t)kvh * G + (rho - i * G)) * HS;
+    };
+    const int last_row = (row0 + kPfRows < nrows ? row0 + kPfRows : nrows) - 1;
+    if (L == 0) {
+        for (int idx = tid; idx < (last_row - row0 + 1) * HS; idx += kPfThreads)
+            out[out_row(row0 + idx / HS) + idx % HS] = (__bf16)0.f;
+        return;
+    }
+    // row rho sees the tokens below L - n + rho / G + 1 (at least 0)
+    auto limit = [&](int rho) __attribute__((always_inline)) {
+        const int v = L - n + rho / G + 1;
+        return v < 0 ? 0 : v;
+    };
+    const int L_wg = limit(last_row);                     // this work-group's last token + 1
+    const int nunits = (L_wg + kPfUnit - 1) / kPfUnit;
+    const int wrow0 = row0 + w * kPfTiles * 16;           // this wave's first row
+    const int wlast = (wrow0 + kPfTiles * 16 < nrows ? wrow0 + kPfTiles * 16 : nrows) - 1;
+    const int L_w = wrow0 < nrows ? limit(wlast) : 0;     // this wave computes tokens below L_w
+
+    // query operands and per-lane row limits of the two tiles; padding rows
+    // repeat a real row and are never stored
+    bf16x8 qr[kPfTiles][HS / 32];
+    int Lq[kPfTiles];
+    int Lmin[kPfTiles];
+#pragma unroll
+    for (int kt = 0; kt < kPfTiles; ++kt) {
+        const int tb = wrow0 + kt * 16;
+        const int rho = (tb + c) % nrows;
+        Lq[kt] = limit(rho);
+        Lmin[kt] = limit(tb < nrows ? tb : nrows - 1);
+        const __bf16* qh = q + out_row(rho);
+#pragma unroll
+        for (int i = 0; i < HS / 32; ++i)
+            qr[kt][i] = *(const bf16x8*)(qh + 32 * i + 8 * r);
+    }
+
+    f32x4 O[kPfTiles][HS / 16];
+    float m_run[kPfTiles], l_part[kPfTiles];
+#pragma unroll
+    for (int kt = 0; kt < kPfTiles; ++kt) {
+        m_run[kt] = -1e30f;
+        l_part[kt] = 0.f;
+#pragma unroll
+        for (int i = 0; i < HS / 16; ++i)
+            O[kt][i] = (f32x4)0.f;
+    }
+
+    // ---- block IDs: a window of 64 table entries, one per lane ----
+    const int32_t* trow = block_tables + (int64_t)s * M;
+    int win = 0;
+    int32_t ids = lane < M ? trow[lane] : 0;
+    int32_t ids_next = 64 + lane < M ? trow[64 + lane] : 0;
+    const int64_t head_off = (int64_t)kvh * TILE;
+    const int64_t block_stride = (int64_t)Hkv * TILE;
+    // offset of table entry j (inside the window) in the pool, block 0 when
+    // the ID is outside the pool
+    auto block_at = [&](int j) __attribute__((always_inline)) -> int64_t {
+        const int32_t id = __shfl(ids, j - win);
+        return ((uint32_t)id < (uint32_t)num_blocks ? id : 0) * block_stride + head_off;
+    };
+
+    // ---- staging: this thread's pieces of unit u ----
+    PfPieces<HS, F8> pc;
+    auto fetch = [&](int u) __attribute__((always_inline)) {
+        const int t0 = u * kPfUnit;
+        if (t0 / BS >= win + 64) {  // uniform: the unit's first block left the window
+            win += 64;
+            ids = ids_next;
+            ids_next = win + 64 + lane < M ? trow[win + 64 + lane] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < PfPieces<HS, F8>::N; ++k) {
+            const int p = tid + k * kPfThreads;
+            if (PfPieces<HS, F8>::P % kPfThreads != 0 && p >= PfPieces<HS, F8>::P)
+                break;
+            if constexpr (F8) {
+                // key chunk f16 (16 head dims) of token t; value codes of head
+                // dim d, tokens 16h .. 16h+15
+                const int f16 = p / kPfUnit, t = p % kPfUnit;
+                const int T = t0 + t;
+                pc.k[k] = *(
+                    (const u32x4*)(k_cache + block_at(T / BS) + ((int64_t)f16 * BS + T % BS) * 16));
+                const int d = p / 2, h = p % 2;
+                const int Tv = t0 + 16 * h;
+                pc.v[k] = *(
+                    (const u32x4*)(v_cache + block_at(Tv / BS) + (int64_t)d * BS + Tv % BS));
+            } else {
+                // key chunk f (8 head dims) of token t; value head dim d,
+                // tokens 8 q8 .. 8 q8 + 7
+                const int f = p / kPfUnit, t = p % kPfUnit;
+                const int T = t0 + t;
+                pc.k[k] = *(
+                    (const u32x4*)(k_cache + block_at(T / BS) + ((int64_t)f * BS + T % BS) * 8));
+                const int d = p / 4, q8 = p % 4;
+                const int Tv = t0 + 8 * q8;
+                pc.v[k] = *(
+                    (const u32x4*)(v_cache + block_at(Tv / BS) + (int64_t)d * BS + Tv % BS));
+            }
+        }
+    };
+    auto deposit = [&](PfStage<HS>& st) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < PfPieces<HS, F8>::N; ++k) {
+            const int p = tid + k * kPfThreads;
+            if (PfPieces<HS, F8>::P % kPfThreads != 0 && p >= PfPieces<HS, F8>::P)
+                break;
+            if constexpr (F8) {
+                const int f16 = p / kPfUnit, t = p % kPfUnit;
+                u32x4 lo, hi;
+                fp8x16_to_bf16(pc.k[k], lo, hi);
+                st.k[2 * f16][t] = __builtin_bit_cast(bf16x8, lo);
+                st.k[2 * f16 + 1][t] = __builtin_bit_cast(bf16x8, hi);
+                const int d = p / 2, h = p % 2;
+                fp8x16_to_bf16(pc.v[k], lo, hi);
+                *(u32x4*)&st.v[d][16 * h] = lo;
+                *(u32x4*)&st.v[d][16 * h + 8] = hi;
+            } else {
+                const int f = p / kPfUnit, t = p % kPfUnit;
+                st.k[f][t] = __builtin_bit_cast(bf16x8, pc.k[k]);
+                const int d = p / 4, q8 = p % 4;
+                *(u32x4*)&st.v[d][8 * q8] = pc.v[k];
+            }
+        }
+    };
+    // tokens of unit u whose block ID is inside the pool (bit t: token 32u + t)
+    auto unit_mask = [&](int u) __attribute__((always_inline)) -> unsigned {
+        const uint64_t valid = __ballot((uint32_t)ids < (uint32_t)num_blocks);
+        if constexpr (BS >= kPfUnit) {
+            return ((valid >> ((u * kPfUnit) / BS - win)) & 1) ? 0xFFFFFFFFu : 0u;
+        } else {
+            const int j = (u * kPfUnit) / BS - win;  // two blocks of 16
+            return (((valid >> j) & 1) ? 0x0000FFFFu : 0u) | (((valid >> (j + 1)) & 1) ? 0xFFFF0000u : 0u);
+        }
+    };
+
+    auto compute = [&](const PfStage<HS>& st, int u, unsigned tmask) __attribute__((always_inline)) {
+        const int t0 = u * kPfUnit;
+        // scores of both row tiles, one key M-tile (16 tokens) at a time
+        f32x4 S[kPfTiles][2];
+#pragma unroll
+        for (int mp = 0; mp < 2; ++mp) {
+            bf16x8 kop[HS / 32];
+#pragma unroll
+            for (int i = 0; i < HS / 32; ++i)
+                kop[i] = st.k[4 * i + r][16 * mp + c];
+#pragma unroll
+            for (int kt = 0; kt < kPfTiles; ++kt) {
+                S[kt][mp] = (f32x4)0.f;
+#pragma unroll
+                for (int i = 0; i < HS / 32; ++i)
+                    S[kt][mp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[i], qr[kt][i], S[kt][mp], 0, 0, 0);
+            }
+        }
+        bf16x8 vop[HS / 16];
+#pragma unroll
+        for (int i = 0; i < HS / 16; ++i)
+            vop[i] = *(const bf16x8*)&st.v[16 * i + c][8 * r];
+        const bool all_valid = tmask == 0xFFFFFFFFu;
+        if (t0 + kPfUnit > L || !all_valid) {
+            // value slots past the sequence or in a skipped block may hold
+            // anything: zero them so that 0 * NaN never reaches the sum
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int tt = 8 * r + e;
+                const bool keep = t0 + tt < L && ((tmask >> tt) & 1);
+#pragma unroll
+                for (int i = 0; i < HS / 16; ++i)
+                    vop[i][e] = keep ? vop[i][e] : (__bf16)0.f;
+            }
+        }
+#pragma unroll
+        for (int kt = 0; kt < kPfTiles; ++kt) {
+            const bool partial = t0 + kPfUnit > Lmin[kt] || !all_valid;
+            float sc[8];
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mp = 0; mp < 2; ++mp) {
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int tt = 16 * mp + 4 * r + jj;
+                    float v = S[kt][mp][jj] * qscale;
+                    if (partial)
+                        v = (t0 + tt < Lq[kt] && ((tmask >> tt) & 1)) ? v : -INFINITY;
+                    sc[4 * mp + jj] = v;
+                    mx = fmaxf(mx, v);
+                }
+            }
+            mx = fmaxf(mx, __shfl_xor(mx, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            if (__ballot(mx > m_run[kt] + kRescaleSlack) != 0) {
+                const float m_new = fmaxf(m_run[kt], mx);
+                const float alpha = __builtin_amdgcn_exp2f(m_run[kt] - m_new);
+                m_run[kt] = m_new;
+                l_part[kt] *= alpha;
+                float a_row[4];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    a_row[jj] = __shfl(alpha, 4 * r + jj);
+#pragma unroll
+                for (int i = 0; i < HS / 16; ++i)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        O[kt][i][jj] *= a_row[jj];
+            }
+            float pv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                pv[e] = __builtin_amdgcn_exp2f(sc[e] - m_run[kt]);
+                l_part[kt] += pv[e];
+            }
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                to_value_order(pv[jj], pv[4 + jj]);  // pv[e] is now token 8r + e
+            bf16x8 hi, lo;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const __bf16 hb = (__bf16)pv[e];
+                hi[e] = hb;
+                lo[e] = (__bf16)(pv[e] - (float)hb);
+            }
+#pragma unroll
+            for (int i = 0; i < HS / 16; ++i) {
+                O[kt][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, vop[i], O[kt][i], 0, 0, 0);
+                O[kt][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, vop[i], O[kt][i], 0, 0, 0);
+            }
+        }
+    };
+
+    // ---- the unit loop: fetch u+1 while computing u, one barrier per unit ----
+    fetch(0);
+    unsigned mask_cur = unit_mask(0);
+    deposit(stage[0]);
+    __syncthreads();
+    for (int u = 0; u < nunits; ++u) {
+        unsigned mask_next = 0;
+        if (u + 1 < nunits) {
+            fetch(u + 1);
+            mask_next = unit_mask(u + 1);
+        }
+        if (u * kPfUnit < L_w)  // uniform per wave: this wave's rows see some of the unit
+            compute(stage[u & 1], u, mask_cur);
+        if (u + 1 < nunits)
+            deposit(stage[(u + 1) & 1]);
+        mask_cur = mask_next;
+        __syncthreads();
+    }
+
+    // ---- normalise and store the rows ----
+#pragma unroll
+    for (int kt = 0; kt < kPfTiles; ++kt) {
+        float l_tot = l_part[kt] + __shfl_xor(l_part[kt], 16);
+        l_tot += __shfl_xor(l_tot, 32);
+        const int tb = wrow0 + kt * 16;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int g = 4 * r + jj;
+            const float l_g = __shfl(l_tot, g);
+            const float inv = l_g > 0.f ? oscale / l_g : 0.f;
+            if (tb + g < nrows) {
+                __bf16* dst = out + out_row(tb + g);
+#pragma unroll
+                for (int i = 0; i < HS / 16; ++i)
+                    dst[16 * i + c] = (__bf16)(O[kt][i][jj] * inv);
+            }
+        }
+    }
+}
+
+template <int HS, int BS, bool F8>
+static hipError_t launch_prefill_typed(const DecodeArgs& a, hipStream_t stream)
+{
+    using C = typename std::conditional<F8, uint8_t, __bf16>::type;
+    const int G = a.num_q_heads / a.num_kv_heads;
+    const int RB = (a.max_q_len * G + kPfRows - 1) / kPfRows;
+    const float qscale = a.scale * kLog2e * (F8 ? a.k_scale : 1.0f);
+    const int64_t groups = (int64_t)a.num_seqs * a.num_kv_heads * RB;  // < 2^31: checked on the host
+    hipLaunchKernelGGL((paged_prefill_kernel<HS, BS, F8>), dim3((unsigned)groups), dim3(kPfThreads), 0,
+                       stream, (const __bf16*)a.q, (const C*)a.k_cache, (const C*)a.v_cache, a.block_tables,
+                       a.seq_lens, a.q_start, a.num_q_rows, a.max_q_len, a.num_q_heads, a.num_kv_heads,
+                       a.max_blocks_per_seq, a.num_blocks, RB, qscale, F8 ? a.v_scale : 1.0f, (__bf16*)a.out);
+    return hipGetLastError();
+}
+
+template <int HS, bool F8>
+static hipError_t launch_prefill_block(const DecodeArgs& a, hipStream_t stream)
+{
+    switch (a.block_size) {
+    case 16: return launch_prefill_typed<HS, 16, F8>(a, stream);
+    case 32: return launch_prefill_typed<HS, 32, F8>(a, stream);
+    default: return launch_prefill_typed<HS, 64, F8>(a, stream);
+    }
+}
+
+bool prefill_supported(const DecodeArgs& a)
+{
+    return (a.dtype == 1 || a.dtype == 2) && a.block_size >= 16 && (a.head_size == 64 || a.head_size == 128) &&
+           a.q_start != nullptr;
+}
+
+int64_t prefill_work_groups(const DecodeArgs& a)
+{
+    const int64_t G = a.num_q_heads / a.num_kv_heads;
+    return (int64_t)a.num_seqs * a.num_kv_heads * ((a.max_q_len * G + kPfRows - 1) / kPfRows);
+}
+
+hipError_t launch_prefill(const DecodeArgs& a, hipStream_t stream)
+{
+    const bool f8 = a.dtype == 2;  // PKV_FP8_E4M3
+    if (a.head_size == 128)
+        return f8 ? launch_prefill_block<128, true>(a, stream) : launch_prefill_block<128, false>(a, stream);
+    return f8 ? launch_prefill_block<64, true>(a, stream) : launch_prefill_block<64, false>(a, stream);
+}
+
+}  // namespace pkv

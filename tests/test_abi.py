@@ -252,3 +252,12 @@ def test_partition_lengths_for_every_block_size(lib):
     assert f(4, 8, 8, 64, 1024, 1, 48) == 48
     assert f(4, 8, 8, 64, 1024, 1, 80) == 0       # 80 blocks of one token
     assert f(4, 8, 8, 64, 1024, 64, 4096) == 4096
+
+
+def test_unpartitioned_multi_token_kernel_support(lib):
+    # PKV_PARTITION_NONE needs bf16 or FP8 pools with blocks of 16 tokens or more
+    assert mq(lib, P=-1, d=desc(dtype=0)) == UNSUPPORTED
+    assert mq(lib, P=-1, d=desc(dtype=1, B=8)) == UNSUPPORTED
+    # and no workspace, whatever the table length
+    assert lib.paged_multi_token_attention(FAKE, None, 8, 2, FAKE, FAKE, FAKE, FAKE, 4, 8, 4096,
+                                           ctypes.byref(desc(dtype=1)), 0.125, FAKE, None, 0, -1, None) == INVALID

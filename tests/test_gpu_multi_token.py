@@ -172,3 +172,100 @@ def test_full_size_sampled_rows(kind):
     got = host_f64(r.out)[[w.q_start[s] + i for s, i in picks]]
     check_attention(w, got, ref)
     assert torch.isfinite(r.out.float()).all().item()
+
+
+PREFILL_CASES = [c for c in CASES if c[1].get("dtype", pi._CFG[c[0]]["dtype"]) != "f32"] + [
+    # rows spanning several 128-row blocks, long contexts, both block sizes
+    (3, dict(S=3, len_lo=600, len_hi=2500, q_lens=[300, 64, 129])),
+    (4, dict(S=1, len_lo=3000, len_hi=3000, q_lens=[200])),
+    (2, dict(S=2, len_lo=900, len_hi=1200, q_lens=[900, 130])),
+    (3, dict(S=3, len_lo=200, len_hi=700, dtype="fp8", q_lens=[100, 37, 150])),
+]
+
+
+@pytest.mark.parametrize("cfg,kw", PREFILL_CASES)
+def test_unpartitioned_kernel_parity(cfg, kw):
+    w = pi.make_workload(cfg, **kw)
+    announce(f"unpartitioned multi-token config {cfg} {w.dtype}: lens={list(w.seq_lens)} q_start={list(w.q_start)} "
+             f"B={w.B} G={w.G}")
+    full_check(w, MRun(w, partition_tokens=pkv().PARTITION_NONE))
+
+
+@pytest.mark.parametrize("B", [16, 32, 64])
+def test_unpartitioned_kernel_block_sizes_and_a_skipped_block(B):
+    w = pi.make_workload(3, S=3, len_lo=300, len_hi=900, B=B, seed=31, q_lens=[40, 100, 7])
+    announce(f"unpartitioned B={B}: lens={list(w.seq_lens)}")
+    r = MRun(w, partition_tokens=pkv().PARTITION_NONE)
+    full_check(w, r)
+    # a block ID outside the pool in sequence 1 (a full block before the rows):
+    # its tokens are skipped, the same as the oracle on the table without it
+    m = pkv()
+    j = 1
+    bt = r.bt.clone()
+    bt[1, j] = -3
+    out = m.paged_multi_token_attention(r.q, r.qs, w.max_q_len, r.kc, r.vc, bt, r.sl, w.scale,
+                                        partition_tokens=m.PARTITION_NONE)
+    out_p = m.paged_multi_token_attention(r.q, r.qs, w.max_q_len, r.kc, r.vc, bt, r.sl, w.scale,
+                                          partition_tokens=64)
+    torch.cuda.synchronize()
+    kp, vp = host_bits(r.kc), host_bits(r.vc)
+    tables = w.block_tables.copy()
+    tables[1, j:-1] = w.block_tables[1, j + 1:]
+    lens = w.seq_lens.copy()
+    lens[1] -= B
+    ref = oracle.paged_multi_token_attention(w.q, w.q_start, kp, vp, tables, lens, w.scale)
+    check_attention(w, host_f64(out), ref)
+    check_attention(w, host_f64(out_p), ref)
+
+
+def test_library_choice_between_the_kernels_gives_the_same_rule():
+    # enough rows and work-groups for the library to pick the unpartitioned
+    # kernel with partition_tokens = 0; the partitioned kernel on the same
+    # input agrees within the tolerance, and both match the oracle
+    w = pi.make_workload(3, S=24, len_lo=100, len_hi=600, seed=32, q_lens=16)
+    announce(f"library choice: {w.S} sequences x 16 rows, G={w.G}")
+    r = MRun(w, partition_tokens=0)
+    full_check(w, r)
+    m = pkv()
+    out_p = m.paged_multi_token_attention(r.q, r.qs, w.max_q_len, r.kc, r.vc, r.bt, r.sl, w.scale,
+                                          partition_tokens=512)
+    torch.cuda.synchronize()
+    d = (out_p.float() - r.out.float()).abs().max().item()
+    announce(f"  partitioned vs library's choice: max difference {d:.3g}")
+    assert d <= 4e-3
+
+
+@pytest.mark.parametrize("dtype,B", [("bf16", 16), ("bf16", 1), ("bf16", 8), ("bf16", 32), ("bf16", 64), ("f32", 16),
+                                     ("f32", 64), ("fp8", 16), ("fp8", 64)])
+def test_block_wise_append_equals_the_slot_append(dtype, B):
+    # pkv_multi_token_append against kv_cache_append through the rows' slot
+    # mapping: whole pools bit-identical, and equal to the oracle's pools;
+    # also with a block ID outside the pool and lengths shortened below the
+    # row count (rows at negative positions are skipped by both)
+    w = pi.make_workload(3, S=5, len_lo=20, len_hi=400, dtype=dtype, B=B, seed=33, q_lens=None)
+    q_lens = np.minimum([1, 70, 17, 130, 5], w.seq_lens)
+    w = pi.make_workload(3, S=5, len_lo=20, len_hi=400, dtype=dtype, B=B, seed=33, q_lens=q_lens)
+    announce(f"block-wise append {dtype} B={B}: lens={list(w.seq_lens)} q_start={list(w.q_start)}")
+    m = pkv()
+    sc = dict(k_scale=w.k_scale, v_scale=w.v_scale)
+    bt, qs = dev(w.block_tables), dev(w.q_start)
+    nk, nv = dev(w.new_k), dev(w.new_v)
+    for variant in ("plain", "bad block", "short"):
+        sl = dev(w.seq_lens)
+        if variant == "bad block":
+            bt = dev(w.block_tables)
+            bt[3, 1] = w.num_blocks + 7
+        if variant == "short":
+            sl = sl - 3
+        kc1, vc1 = dev(w.k_cache), dev(w.v_cache)
+        kc2, vc2 = dev(w.k_cache), dev(w.v_cache)
+        slots = m.multi_token_slot_mapping(bt, sl, qs, w.rows, w.max_q_len, w.B)
+        m.kv_cache_append(nk, nv, slots, kc1, vc1, **sc)
+        m.multi_token_append(nk, nv, qs, w.max_q_len, bt, sl, kc2, vc2, **sc)
+        torch.cuda.synchronize()
+        assert same_bytes(host_bits(kc2), host_bits(kc1)), variant
+        assert same_bytes(host_bits(vc2), host_bits(vc1)), variant
+        if variant == "plain":
+            ref_slots, kp, vp, _ = oracle.multi_token_step(w)
+            assert same_bytes(host_bits(kc2), kp)
+            assert same_bytes(host_bits(vc2), vp)
