@@ -12,15 +12,19 @@
 // How it maps onto CDNA4:
 //  * Work-group (KV head, row block, sequence), 4 waves, 32 rows per wave as
 //    two 16-row MFMA tiles; a row is a (query token, group member) pair.
-//  * The keys and values are walked in 32-token units.  All 256 threads copy
-//    the next unit from the pools into the other LDS stage (bf16; FP8 codes
-//    are converted on the way) while the waves compute on this one: one
-//    barrier per unit.  Keys sit in LDS as [hs/8][32 tokens] 16-byte
-//    chunks, so a lane's 16-byte read is the A operand of
-//    v_mfma_f32_16x16x32_bf16 (token row c, 8 head dims) and a lane group
-//    reads 256 contiguous bytes.  Values sit as [hs][32 tokens + 8]: the 8
-//    padding elements make the 16-byte reads of 16 consecutive head dims hit
-//    distinct banks.
+//  * The keys and values are walked in 32-token units staged in LDS, one
+//    barrier per unit.  bf16 pools: three stages, filled by direct
+//    global-to-LDS loads (global_load_lds_dwordx4: lane i of a wave
+//    instruction lands at base + 16 i) issued two units ahead, so no
+//    registers hold data in flight.  FP8 pools: two stages, the next unit's
+//    codes loaded into registers and converted to bf16 on the way into LDS.
+//    Keys sit in LDS as [hs/8][32 tokens] 16-byte chunks, so a lane's
+//    16-byte read is the A operand of v_mfma_f32_16x16x32_bf16 (token row c,
+//    8 head dims) and a lane group reads 256 contiguous bytes.  Values sit
+//    as [hs][32 tokens] in four 16-byte slots per row; for the 16-byte reads
+//    of 16 consecutive head dims to hit distinct banks, the slots of row d
+//    are permuted (slot q holds tokens 8 (q ^ ((d / 4) % 4)) ..) in the bf16
+//    path, and the rows are padded by 8 elements in the FP8 path.
 //  * Each wave reads one unit's key and value operands once from LDS and
 //    uses them for both of its row tiles (scores, then the value sum with the
 //    probabilities moved to the value order by to_value_order, hi + lo bf16
@@ -53,6 +57,15 @@ struct PfStage {
     bf16x8 k[HS / 8][kPfUnit];        // chunk f (head dims 8f .. 8f+7) of token t
     __bf16 v[HS][kPfVRow];            // head dim d, token t
 };
+
+// s_waitcnt with vmcnt(n) and the other counters left alone (gfx9
+// encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Global reads of one unit: 4 * HS key and 4 * HS value pieces of 16 bytes
 // (bf16: 8 elements), or 2 * HS of each (FP8: 16 codes); a thread takes
@@ -87,7 +100,11 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     using C = typename std::conditional<F8, uint8_t, __bf16>::type;
     static_assert(BS >= 16 && (BS % 16) == 0, "blocks of 16, 32 or 64 tokens");
     constexpr int TILE = HS * BS;  // elements of one (block, KV head) tile
-    __shared__ PfStage<HS> stage[2];
+    // LDS stages of 16-byte slots: keys [hs/8][32] first, then values
+    constexpr int NST = F8 ? 2 : 3;
+    constexpr int STAGE_SLOTS = F8 ? (int)(sizeof(PfStage<HS>) / 16) : HS * 8;
+    constexpr int KSLOTS = HS * 4;
+    __shared__ bf16x8 lds[NST * STAGE_SLOTS];
 
     // XCD-aware order: work-groups are dealt to the 8 XCDs round-robin by
     // their linear index, and each XCD has its own L2.  The row blocks of one
@@ -258,7 +275,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         }
     };
 
-    auto compute = [&](const PfStage<HS>& st, int u, unsigned tmask) __attribute__((always_inline)) {
+    auto compute = [&](const bf16x8* kst, const bf16x8* vst, int u, unsigned tmask) __attribute__((always_inline)) {
         const int t0 = u * kPfUnit;
         // scores of both row tiles, one key M-tile (16 tokens) at a time
         f32x4 S[kPfTiles][2];
@@ -267,7 +284,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
             bf16x8 kop[HS / 32];
 #pragma unroll
             for (int i = 0; i < HS / 32; ++i)
-                kop[i] = st.k[4 * i + r][16 * mp + c];
+                kop[i] = kst[(4 * i + r) * kPfUnit + 16 * mp + c];
 #pragma unroll
             for (int kt = 0; kt < kPfTiles; ++kt) {
                 S[kt][mp] = (f32x4)0.f;
@@ -278,8 +295,10 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         }
         bf16x8 vop[HS / 16];
 #pragma unroll
-        for (int i = 0; i < HS / 16; ++i)
-            vop[i] = *(const bf16x8*)&st.v[16 * i + c][8 * r];
+        for (int i = 0; i < HS / 16; ++i) {
+            const int d = 16 * i + c;
+            vop[i] = F8 ? vst[d * (kPfVRow / 8) + r] : vst[d * 4 + (r ^ ((d >> 2) & 3))];
+        }
         const bool all_valid = tmask == 0xFFFFFFFFu;
         if (t0 + kPfUnit > L || !all_valid) {
             // value slots past the sequence or in a skipped block may hold
@@ -352,22 +371,99 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     };
 
     // ---- the unit loop: fetch u+1 while computing u, one barrier per unit ----
-    fetch(0);
-    unsigned mask_cur = unit_mask(0);
-    deposit(stage[0]);
-    __syncthreads();
-    for (int u = 0; u < nunits; ++u) {
-        unsigned mask_next = 0;
-        if (u + 1 < nunits) {
-            fetch(u + 1);
-            mask_next = unit_mask(u + 1);
-        }
-        if (u * kPfUnit < L_w)  // uniform per wave: this wave's rows see some of the unit
-            compute(stage[u & 1], u, mask_cur);
-        if (u + 1 < nunits)
-            deposit(stage[(u + 1) & 1]);
-        mask_cur = mask_next;
+    if constexpr (F8) {
+        // ---- register staging: fetch u+1 while computing u ----
+        PfStage<HS>* stage = reinterpret_cast<PfStage<HS>*>(lds);
+        fetch(0);
+        unsigned mask_cur = unit_mask(0);
+        deposit(stage[0]);
         __syncthreads();
+        for (int u = 0; u < nunits; ++u) {
+            unsigned mask_next = 0;
+            if (u + 1 < nunits) {
+                fetch(u + 1);
+                mask_next = unit_mask(u + 1);
+            }
+            if (u * kPfUnit < L_w)  // uniform per wave: this wave's rows see some of the unit
+                compute(&stage[u & 1].k[0][0], lds + (u & 1) * STAGE_SLOTS + KSLOTS, u, mask_cur);
+            if (u + 1 < nunits)
+                deposit(stage[(u + 1) & 1]);
+            mask_cur = mask_next;
+            __syncthreads();
+        }
+    } else {
+        // ---- direct global-to-LDS loads, two units ahead, three stages ----
+        // This thread's slots: key slot p = tid + 256 k is chunk p / 32 of
+        // token p % 32 = tid % 32; value slot p is row d = p / 4, holding
+        // tokens 8 q8 .. 8 q8 + 7 with q8 = (p % 4) ^ ((d / 4) % 4), the same
+        // q8 for every k.
+        constexpr int NP = (4 * HS) / kPfThreads;  // slots of each kind per thread
+        constexpr int NDMA = 2 * NP;               // load instructions per wave per unit
+        const int tK = tid % kPfUnit;
+        const int q8 = (tid & 3) ^ ((tid >> 4) & 3);
+        // Block IDs: a unit spans at most two table entries, j0 = 32 v / BS
+        // and j0 + 1 (B = 16), read with scalar loads (uniform addresses) one
+        // unit before the unit's loads are issued; each lane picks the entry
+        // of its key token and of its value tokens.  Entries past the row are
+        // read at its last index (their tokens are past the sequence).
+        auto entries = [&](int v, int32_t& e0, int32_t& e1) __attribute__((always_inline)) {
+            const int j0 = (v * kPfUnit) / BS;
+            e0 = trow[j0 < M ? j0 : M - 1];
+            e1 = trow[j0 + 1 < M ? j0 + 1 : M - 1];
+        };
+        auto pick = [&](int v, int token, int32_t e0, int32_t e1) __attribute__((always_inline)) -> int32_t {
+            return (v * kPfUnit + token) / BS == (v * kPfUnit) / BS ? e0 : e1;
+        };
+        auto base_of = [&](int32_t id) __attribute__((always_inline)) -> int64_t {
+            return ((uint32_t)id < (uint32_t)num_blocks ? id : 0) * block_stride + head_off;
+        };
+        // loads of unit v into stage v % NST (every iteration issues them,
+        // also past the last unit, into the free stage: a fixed count per
+        // iteration for the waits below)
+        auto issue = [&](int v, int32_t e0, int32_t e1) __attribute__((always_inline)) {
+            __attribute__((address_space(3))) bf16x8* sb =
+                (__attribute__((address_space(3))) bf16x8*)(lds + (v % NST) * STAGE_SLOTS);
+            const int64_t kb = base_of(pick(v, tK, e0, e1)) + (int64_t)((v * kPfUnit + tK) % BS) * 8;
+            const int64_t vb = base_of(pick(v, 8 * q8, e0, e1)) + (v * kPfUnit + 8 * q8) % BS;
+#pragma unroll
+            for (int k = 0; k < NP; ++k) {
+                const int f = tid / kPfUnit + k * (kPfThreads / kPfUnit);
+                const int d = tid / 4 + k * (kPfThreads / 4);
+                const int slot = k * kPfThreads + w * 64;  // this wave's 64 slots
+                __builtin_amdgcn_global_load_lds((const void*)(k_cache + kb + (int64_t)f * BS * 8), sb + slot, 16,
+                                                 0, 0);
+                __builtin_amdgcn_global_load_lds((const void*)(v_cache + vb + (int64_t)d * BS), sb + KSLOTS + slot,
+                                                 16, 0, 0);
+            }
+        };
+        // entries of units u (a), u+1 (b), u+2 (c)
+        int32_t a0, a1, b0, b1, c0, c1;
+        entries(0, a0, a1);
+        entries(1, b0, b1);
+        entries(2, c0, c1);
+        issue(0, a0, a1);
+        issue(1, b0, b1);
+        for (int u = 0; u < nunits; ++u) {
+            // issued before this point, in order: ..., loads(u), loads(u+1).
+            // This wave's loads of unit u have landed once at most NDMA are
+            // outstanding; the barrier makes every wave's part visible and
+            // frees the stage of unit u-1
+            wait_vmcnt<NDMA>();
+            __syncthreads();
+            int32_t d0, d1;
+            entries(u + 3, d0, d1);
+            issue(u + 2, c0, c1);
+            // tokens of unit u whose block ID is inside the pool
+            const bool ok0 = (uint32_t)a0 < (uint32_t)num_blocks, ok1 = (uint32_t)a1 < (uint32_t)num_blocks;
+            const unsigned tmask = BS >= kPfUnit ? (ok0 ? 0xFFFFFFFFu : 0u)
+                                                 : ((ok0 ? 0x0000FFFFu : 0u) | (ok1 ? 0xFFFF0000u : 0u));
+            if (u * kPfUnit < L_w)  // uniform per wave: this wave's rows see some of the unit
+                compute(lds + (u % NST) * STAGE_SLOTS, lds + (u % NST) * STAGE_SLOTS + KSLOTS, u, tmask);
+            a0 = b0; a1 = b1; b0 = c0; b1 = c1; c0 = d0; c1 = d1;
+        }
+        // the last two iterations' loads still write LDS: wait before the
+        // work-group's LDS can be handed to another
+        wait_vmcnt<0>();
     }
 
     // ---- normalise and store the rows ----
