@@ -142,7 +142,7 @@ def bench_multi_token(args, w, torch, pkv) -> dict:
         d = copies[turn[0] % len(copies)]
         turn[0] += 1
         pkv.multi_token_slot_mapping(d["bt"], d["sl"], d["qs"], w.rows, mql, w.B, out=slots, stream=stream)
-        pkv.kv_cache_append(d["nk"], d["nv"], slots, d["kc"], d["vc"], stream=stream, **sc)
+        pkv.multi_token_append(d["nk"], d["nv"], d["qs"], mql, d["bt"], d["sl"], d["kc"], d["vc"], stream=stream, **sc)
         ev[0].record(stream)
         pkv.paged_multi_token_attention(d["q"], d["qs"], mql, d["kc"], d["vc"], d["bt"], d["sl"], w.scale, out=out,
                                         workspace=ws, partition_tokens=P, stream=stream, **sc)
