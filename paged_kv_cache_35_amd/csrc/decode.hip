@@ -1026,6 +1026,75 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
     }
 }
 
+// Chunk merge for several query rows per sequence: one work-group per
+// (row tile, KV head, sequence), 16 threads per tile row, each owning 8
+// consecutive head dims (two 16-byte loads per partial).  The row's running
+// maxima are reduced over the chunks first, then every thread accumulates
+// its dims over all chunks with weights l_p * 2^(m_p - M).
+template <typename T, int HS>
+__global__ __launch_bounds__(256) void paged_multi_token_reduce_kernel(
+    const int32_t* __restrict__ seq_lens, int32_t M, int32_t BS, int32_t CB, int32_t Hq, int32_t Hkv,
+    int32_t max_parts, const float* __restrict__ ws_o, const float* __restrict__ ws_ml, T* __restrict__ out,
+    const int32_t* __restrict__ q_start, int32_t num_q_rows, int32_t max_q_len, int32_t RT)
+{
+    static_assert(HS % 16 == 0 && HS / 16 <= 8, "16 threads per row, at most 8 dims each");
+    constexpr int DPT = HS / 16;  // head dims per thread
+    const int rt = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+    const int G = Hq / Hkv;
+    const int qs0 = q_start[s], qs1 = q_start[s + 1];
+    int n = qs1 - qs0;
+    if (qs0 < 0 || n < 0 || qs1 > num_q_rows)
+        return;
+    n = n < max_q_len ? n : max_q_len;
+    int L = seq_lens[s];
+    L = L < 0 ? 0 : (L > M * BS ? M * BS : L);
+    const int nblk = (L + BS - 1) / BS;
+    const int nparts = (nblk + CB - 1) / CB;
+    if (nparts <= 1 || 16 * rt >= n * G)
+        return;  // one chunk: the partition kernel wrote the rows
+    const int rl = threadIdx.x / 16;          // tile row
+    const int q = threadIdx.x % 16;           // dims q*DPT .. q*DPT + DPT - 1
+    const int rho = 16 * rt + rl;
+    const bool live = rho < n * G;
+    const int64_t blk0 = (((int64_t)s * Hkv + kvh) * RT + rt) * max_parts;  // block of chunk 0
+    float mx = -INFINITY;
+    for (int p = q; p < nparts; p += 16) {
+        const float2 ml = *(const float2*)(ws_ml + ((blk0 + p) * 16 + rl) * 2);
+        if (ml.y > 0.f)
+            mx = fmaxf(mx, ml.x);
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1)
+        mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+    float acc[DPT];
+#pragma unroll
+    for (int k = 0; k < DPT; ++k)
+        acc[k] = 0.f;
+    float wsum = 0.f;
+    for (int p = 0; p < nparts; ++p) {
+        const float2 ml = *(const float2*)(ws_ml + ((blk0 + p) * 16 + rl) * 2);
+        const float wgt = ml.y > 0.f ? ml.y * __builtin_amdgcn_exp2f(ml.x - mx) : 0.f;
+        wsum += wgt;
+        const float* src = ws_o + ((blk0 + p) * 16 + rl) * HS + q * DPT;
+#pragma unroll
+        for (int k = 0; k < DPT; k += 4) {
+            const f32x4 v = *(const f32x4*)(src + k);
+            acc[k] += wgt * v[0];
+            acc[k + 1] += wgt * v[1];
+            acc[k + 2] += wgt * v[2];
+            acc[k + 3] += wgt * v[3];
+        }
+    }
+    if (!live)
+        return;
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    const int i = rho / G;
+    T* dst = out + ((int64_t)(qs0 + i) * Hq + (int64_t)kvh * G + (rho - i * G)) * HS + q * DPT;
+#pragma unroll
+    for (int k = 0; k < DPT; ++k)
+        store_elem(dst + k, acc[k] * inv);
+}
+
 template <typename T, int HS, int BS, bool F8, bool MQ>
 static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
 {
@@ -1043,10 +1112,16 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_parts <= 1)
         return e;  // one chunk per sequence: the partition kernel wrote the output
-    hipLaunchKernelGGL((paged_decode_reduce_kernel<T, HS, MQ>), dim3(a.num_q_heads, a.num_seqs, MQ ? a.max_q_len : 1),
-                       dim3(kMergeThreads), 0, stream, a.seq_lens, a.max_blocks_per_seq, BS,
-                       a.partition_blocks * NW, a.num_q_heads, a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml,
-                       (T*)a.out, a.q_start, a.num_q_rows, a.max_q_len, a.row_tiles);
+    if constexpr (MQ)
+        hipLaunchKernelGGL((paged_multi_token_reduce_kernel<T, HS>), dim3(a.row_tiles, a.num_kv_heads, a.num_seqs),
+                           dim3(256), 0, stream, a.seq_lens, a.max_blocks_per_seq, BS, a.partition_blocks * NW,
+                           a.num_q_heads, a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, (T*)a.out, a.q_start,
+                           a.num_q_rows, a.max_q_len, a.row_tiles);
+    else
+        hipLaunchKernelGGL((paged_decode_reduce_kernel<T, HS, false>), dim3(a.num_q_heads, a.num_seqs),
+                           dim3(kMergeThreads), 0, stream, a.seq_lens, a.max_blocks_per_seq, BS,
+                           a.partition_blocks * NW, a.num_q_heads, a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml,
+                           (T*)a.out, a.q_start, a.num_q_rows, a.max_q_len, a.row_tiles);
     return hipGetLastError();
 }
 
