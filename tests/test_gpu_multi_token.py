@@ -269,3 +269,16 @@ def test_block_wise_append_equals_the_slot_append(dtype, B):
             ref_slots, kp, vp, _ = oracle.multi_token_step(w)
             assert same_bytes(host_bits(kc2), kp)
             assert same_bytes(host_bits(vc2), vp)
+
+
+@pytest.mark.parametrize("dtype,hs,B,Hq,Hkv", [
+    ("bf16", 64, 16, 8, 8), ("bf16", 64, 32, 16, 2), ("bf16", 64, 64, 4, 4), ("bf16", 128, 16, 16, 1),
+    ("bf16", 128, 32, 12, 4), ("fp8", 64, 16, 8, 2), ("fp8", 128, 64, 16, 2), ("fp8", 64, 32, 4, 4),
+])
+def test_unpartitioned_kernel_shapes(dtype, hs, B, Hq, Hkv):
+    w0 = pi.make_workload(3, S=4, len_lo=1, len_hi=900, dtype=dtype, hs=hs, B=B, Hq=Hq, Hkv=Hkv, seed=34)
+    q_lens = np.minimum([3, 70, 200, 1], w0.seq_lens)
+    w = pi.make_workload(3, S=4, len_lo=1, len_hi=900, dtype=dtype, hs=hs, B=B, Hq=Hq, Hkv=Hkv, seed=34,
+                         q_lens=q_lens)
+    announce(f"unpartitioned {dtype} hs={hs} B={B} Hq={Hq} Hkv={Hkv} lens={list(w.seq_lens)} q_start={list(w.q_start)}")
+    full_check(w, MRun(w, partition_tokens=pkv().PARTITION_NONE))
