@@ -36,6 +36,7 @@
 //    zeroed by selection, so stale or NaN pool contents never reach a sum.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_common.h"
@@ -940,89 +941,86 @@ __device__ __forceinline__ float block_reduce_sum(float v, float* red)
 
 // MQ: one work-group per (query head, sequence, query row i = blockIdx.z);
 // the partials of row rho = i * G + g sit in row tile rho / 16, row rho % 16.
-template <typename T, int HS, bool MQ>
+// Persistent over (sequence rank, query head) pairs: work-group b takes
+// pairs b, b + gridDim.x, ...  Rank y is the y-th sequence of the
+// longest-first schedule when one is given (the sequences that span several
+// chunks come first, so the work spreads over the first work-groups), else
+// sequence y.  Pairs of single-chunk sequences are skipped.
+constexpr int kMergeGroups = 2048;
+
+template <typename T, int HS>
 __global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
-    const int32_t* __restrict__ seq_lens, int32_t M, int32_t BS, int32_t CB, int32_t Hq, int32_t Hkv,
-    int32_t max_parts, const float* __restrict__ ws_o, const float* __restrict__ ws_ml, T* __restrict__ out,
-    const int32_t* __restrict__ q_start, int32_t num_q_rows, int32_t max_q_len, int32_t RT)
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sched_order,
+    const int32_t* __restrict__ sched_lens, int32_t S, int32_t M, int32_t BS, int32_t CB, int32_t Hq, int32_t Hkv,
+    int32_t max_parts, const float* __restrict__ ws_o, const float* __restrict__ ws_ml, T* __restrict__ out)
 {
     constexpr int R = kMergeThreads / HS;  // partition groups
     __shared__ float sm_w[kMergeChunk];
     __shared__ float sm_red[kMergeThreads / 64];
     __shared__ float sm_acc[R][HS];
-    const int h = blockIdx.x;
-    const int s = blockIdx.y;
-    const int qi = MQ ? blockIdx.z : 0;
-    int qrow = s;
-    if constexpr (MQ) {
-        const int qs0 = q_start[s];
-        const int qs1 = q_start[s + 1];
-        int n = qs1 - qs0;
-        if (qs0 < 0 || n < 0 || qs1 > num_q_rows)
-            n = 0;
-        n = n < max_q_len ? n : max_q_len;
-        if (qi >= n)
-            return;
-        qrow = qs0 + qi;
-    }
-    int L = seq_lens[s];
-    L = L < 0 ? 0 : (L > M * BS ? M * BS : L);
-    const int nblk = (L + BS - 1) / BS;
-    const int nparts = (nblk + CB - 1) / CB;  // chunks of CB blocks
-    if (nparts <= 1)
-        return;
-    // chunk p of head h = kvh * G + g: row g of block (s, kvh, p)
     const int G = Hq / Hkv;
-    const int kvh = h / G;
-    const int g = h - kvh * G;
-    const int rho = qi * G + g;
-    const int RPB = MQ ? 16 : G;
-    const int64_t u0 = (((int64_t)s * Hkv + kvh) * (MQ ? RT : 1) + rho / 16) * max_parts;
-    auto row = [&](int p) __attribute__((always_inline)) { return (u0 + p) * RPB + rho % 16; };
+    const int64_t pairs = (int64_t)S * Hq;
+    for (int64_t pr = blockIdx.x; pr < pairs; pr += gridDim.x) {
+        const int y = (int)(pr / Hq);
+        const int h = (int)(pr - (int64_t)y * Hq);
+        const int s = sched_order ? sched_order[y] : y;
+        int L = sched_order ? sched_lens[y] : seq_lens[s];
+        L = L < 0 ? 0 : (L > M * BS ? M * BS : L);
+        const int nblk = (L + BS - 1) / BS;
+        const int nparts = (nblk + CB - 1) / CB;  // chunks of CB blocks
+        if (nparts <= 1)
+            continue;  // uniform: the partition kernel wrote this output
+        // chunk p of head h = kvh * G + g: row g of block (s, kvh, p)
+        const int kvh = h / G;
+        const int g = h - kvh * G;
+        const int64_t u0 = ((int64_t)s * Hkv + kvh) * max_parts;
+        auto row = [&](int p) __attribute__((always_inline)) { return (u0 + p) * G + g; };
 
-    float mx = -INFINITY;
-    for (int p = threadIdx.x; p < nparts; p += kMergeThreads)
-        if (ws_ml[2 * row(p) + 1] > 0.f)
-            mx = fmaxf(mx, ws_ml[2 * row(p)]);
-    mx = block_reduce_max(mx, sm_red);
+        float mx = -INFINITY;
+        for (int p = threadIdx.x; p < nparts; p += kMergeThreads)
+            if (ws_ml[2 * row(p) + 1] > 0.f)
+                mx = fmaxf(mx, ws_ml[2 * row(p)]);
+        mx = block_reduce_max(mx, sm_red);
 
-    const int d = threadIdx.x % HS;
-    const int grp = threadIdx.x / HS;
-    float acc = 0.f, wpart = 0.f;
-    for (int c0 = 0; c0 < nparts; c0 += kMergeChunk) {
-        const int cn = nparts - c0 < kMergeChunk ? nparts - c0 : kMergeChunk;
-        __syncthreads();  // previous chunk's weights fully consumed
-        for (int i = threadIdx.x; i < cn; i += kMergeThreads) {
-            const float l = ws_ml[2 * row(c0 + i) + 1];
-            const float wgt = l > 0.f ? l * __builtin_amdgcn_exp2f(ws_ml[2 * row(c0 + i)] - mx) : 0.f;
-            sm_w[i] = wgt;
-            wpart += wgt;
+        const int d = threadIdx.x % HS;
+        const int grp = threadIdx.x / HS;
+        float acc = 0.f, wpart = 0.f;
+        for (int c0 = 0; c0 < nparts; c0 += kMergeChunk) {
+            const int cn = nparts - c0 < kMergeChunk ? nparts - c0 : kMergeChunk;
+            __syncthreads();  // previous chunk's weights fully consumed
+            for (int i = threadIdx.x; i < cn; i += kMergeThreads) {
+                const float l = ws_ml[2 * row(c0 + i) + 1];
+                const float wgt = l > 0.f ? l * __builtin_amdgcn_exp2f(ws_ml[2 * row(c0 + i)] - mx) : 0.f;
+                sm_w[i] = wgt;
+                wpart += wgt;
+            }
+            __syncthreads();
+            const float* base = ws_o + row(c0) * HS + d;
+            const int64_t pstride = (int64_t)G * HS;  // between consecutive partitions
+            int i = grp;
+            for (; i + 7 * R < cn; i += 8 * R) {
+                float v[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    v[k] = base[(int64_t)(i + k * R) * pstride];
+#pragma unroll
+                for (int k = 0; k < 8; ++k)
+                    acc += sm_w[i + k * R] * v[k];
+            }
+            for (; i < cn; i += R)
+                acc += sm_w[i] * base[(int64_t)i * pstride];
         }
+        const float wsum = block_reduce_sum(wpart, sm_red);
+        sm_acc[grp][d] = acc;
         __syncthreads();
-        const float* base = ws_o + row(c0) * HS + d;
-        const int64_t pstride = (int64_t)RPB * HS;  // between consecutive partitions
-        int i = grp;
-        for (; i + 7 * R < cn; i += 8 * R) {
-            float v[8];
+        if (threadIdx.x < HS) {
+            float tot = 0.f;
 #pragma unroll
-            for (int k = 0; k < 8; ++k)
-                v[k] = base[(int64_t)(i + k * R) * pstride];
-#pragma unroll
-            for (int k = 0; k < 8; ++k)
-                acc += sm_w[i + k * R] * v[k];
+            for (int k = 0; k < R; ++k)
+                tot += sm_acc[k][threadIdx.x];
+            store_elem(out + ((int64_t)s * Hq + h) * HS + threadIdx.x, wsum > 0.f ? tot / wsum : 0.f);
         }
-        for (; i < cn; i += R)
-            acc += sm_w[i] * base[(int64_t)i * pstride];
-    }
-    const float wsum = block_reduce_sum(wpart, sm_red);
-    sm_acc[grp][d] = acc;
-    __syncthreads();
-    if (threadIdx.x < HS) {
-        float tot = 0.f;
-#pragma unroll
-        for (int g = 0; g < R; ++g)
-            tot += sm_acc[g][threadIdx.x];
-        store_elem(out + ((int64_t)qrow * Hq + h) * HS + threadIdx.x, wsum > 0.f ? tot / wsum : 0.f);
+        __syncthreads();  // sm_acc and sm_w are reused by the next pair
     }
 }
 
@@ -1118,10 +1116,11 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
                            a.num_q_heads, a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, (T*)a.out, a.q_start,
                            a.num_q_rows, a.max_q_len, a.row_tiles);
     else
-        hipLaunchKernelGGL((paged_decode_reduce_kernel<T, HS, false>), dim3(a.num_q_heads, a.num_seqs),
-                           dim3(kMergeThreads), 0, stream, a.seq_lens, a.max_blocks_per_seq, BS,
-                           a.partition_blocks * NW, a.num_q_heads, a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml,
-                           (T*)a.out, a.q_start, a.num_q_rows, a.max_q_len, a.row_tiles);
+        hipLaunchKernelGGL((paged_decode_reduce_kernel<T, HS>),
+                           dim3((unsigned)std::min<int64_t>((int64_t)a.num_q_heads * a.num_seqs, kMergeGroups)),
+                           dim3(kMergeThreads), 0, stream, a.seq_lens, a.sched_order, a.sched_lens, a.num_seqs,
+                           a.max_blocks_per_seq, BS, a.partition_blocks * NW, a.num_q_heads, a.num_kv_heads,
+                           a.max_parts, a.ws_o, a.ws_ml, (T*)a.out);
     return hipGetLastError();
 }
 

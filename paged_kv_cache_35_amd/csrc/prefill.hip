@@ -187,11 +187,15 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
             O[kt][i] = (f32x4)0.f;
     }
 
-    // ---- block IDs: a window of 64 table entries, one per lane ----
+    // ---- FP8 register path: block IDs in a window of 64 table entries, one per lane ----
     const int32_t* trow = block_tables + (int64_t)s * M;
+    // (register path only; the bf16 path reads table entries with scalar loads)
     int win = 0;
-    int32_t ids = lane < M ? trow[lane] : 0;
-    int32_t ids_next = 64 + lane < M ? trow[64 + lane] : 0;
+    int32_t ids = 0, ids_next = 0;
+    if constexpr (F8) {
+        ids = lane < M ? trow[lane] : 0;
+        ids_next = 64 + lane < M ? trow[64 + lane] : 0;
+    }
     const int64_t head_off = (int64_t)kvh * TILE;
     const int64_t block_stride = (int64_t)Hkv * TILE;
     // offset of table entry j (inside the window) in the pool, block 0 when
