@@ -46,6 +46,19 @@ __device__ __forceinline__ void to_value_order(float& x, float& y)
         : "+v"(x), "+v"(y));
 }
 
+// Maximum over the four lane groups (lanes c, c + 16, c + 32, c + 48) of
+// each column c, with the same two lane-group swaps (no LDS round trip):
+// after v_permlane32_swap of two copies, lane l holds x[l] and x[l ^ 32];
+// after v_permlane16_swap of two copies of that maximum, x[l ^ 16] joins.
+__device__ __forceinline__ float max_over_lane_groups(float x)
+{
+    float a = x, b = x;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+    float c = fmaxf(a, b), d = c;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(c), "+v"(d));
+    return fmaxf(c, d);
+}
+
 __device__ __forceinline__ void store_elem(__bf16* p, float x) { *p = (__bf16)x; }
 __device__ __forceinline__ void store_elem(float* p, float x) { *p = x; }
 

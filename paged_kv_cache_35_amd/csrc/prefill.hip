@@ -319,22 +319,27 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
         for (int kt = 0; kt < kPfTiles; ++kt) {
             const bool partial = t0 + kPfUnit > Lmin[kt] || !all_valid;
+            // raw scores; the scale is applied inside the exponent (qscale > 0
+            // keeps the maximum where it is)
             float sc[8];
-            float mx = -INFINITY;
 #pragma unroll
-            for (int mp = 0; mp < 2; ++mp) {
+            for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int tt = 16 * mp + 4 * r + jj;
-                    float v = S[kt][mp][jj] * qscale;
-                    if (partial)
-                        v = (t0 + tt < Lq[kt] && ((tmask >> tt) & 1)) ? v : -INFINITY;
-                    sc[4 * mp + jj] = v;
-                    mx = fmaxf(mx, v);
-                }
+                for (int jj = 0; jj < 4; ++jj)
+                    sc[4 * mp + jj] = S[kt][mp][jj];
+            if (partial) {
+                asm volatile("" ::: "memory");  // a real branch: most units need no masking
+#pragma unroll
+                for (int mp = 0; mp < 2; ++mp)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        const int tt = 16 * mp + 4 * r + jj;
+                        sc[4 * mp + jj] = (t0 + tt < Lq[kt] && ((tmask >> tt) & 1)) ? sc[4 * mp + jj] : -INFINITY;
+                    }
             }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                             fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+            mx = max_over_lane_groups(mx) * qscale;
             if (__ballot(mx > m_run[kt] + kRescaleSlack) != 0) {
                 const float m_new = fmaxf(m_run[kt], mx);
                 const float alpha = __builtin_amdgcn_exp2f(m_run[kt] - m_new);
@@ -353,7 +358,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
             float pv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                pv[e] = __builtin_amdgcn_exp2f(sc[e] - m_run[kt]);
+                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], qscale, -m_run[kt]));
                 l_part[kt] += pv[e];
             }
 #pragma unroll
