@@ -364,13 +364,19 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
                 to_value_order(pv[jj], pv[4 + jj]);  // pv[e] is now token 8r + e
-            bf16x8 hi, lo;
+            // hi = bf16(p) two at a time; lo = bf16(p - hi), with hi read back
+            // from the packed pair by shifts (exact)
+            u32x4 hw, lw;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const __bf16 hb = (__bf16)pv[e];
-                hi[e] = hb;
-                lo[e] = (__bf16)(pv[e] - (float)hb);
+            for (int e = 0; e < 4; ++e) {
+                const f32x2 pp = {pv[2 * e], pv[2 * e + 1]};
+                const unsigned hb = __builtin_bit_cast(unsigned, __builtin_convertvector(pp, bf16x2));
+                const f32x2 rem = {pp[0] - __builtin_bit_cast(float, hb << 16),
+                                   pp[1] - __builtin_bit_cast(float, hb & 0xFFFF0000u)};
+                hw[e] = hb;
+                lw[e] = __builtin_bit_cast(unsigned, __builtin_convertvector(rem, bf16x2));
             }
+            const bf16x8 hi = __builtin_bit_cast(bf16x8, hw), lo = __builtin_bit_cast(bf16x8, lw);
 #pragma unroll
             for (int i = 0; i < HS / 16; ++i) {
                 O[kt][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, vop[i], O[kt][i], 0, 0, 0);
@@ -412,7 +418,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         const int q8 = (tid & 3) ^ ((tid >> 4) & 3);
         // Block IDs: a unit spans at most two table entries, j0 = 32 v / BS
         // and j0 + 1 (B = 16), read with scalar loads (uniform addresses) one
-        // unit before the unit's loads are issued; each lane picks the entry
+        // unit before the unit's loads are issued; each lane takes the entry
         // of its key token and of its value tokens.  Entries past the row are
         // read at its last index (their tokens are past the sequence).
         auto entries = [&](int v, int32_t& e0, int32_t& e1) __attribute__((always_inline)) {
@@ -420,20 +426,24 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
             e0 = trow[j0 < M ? j0 : M - 1];
             e1 = trow[j0 + 1 < M ? j0 + 1 : M - 1];
         };
-        auto pick = [&](int v, int token, int32_t e0, int32_t e1) __attribute__((always_inline)) -> int32_t {
-            return (v * kPfUnit + token) / BS == (v * kPfUnit) / BS ? e0 : e1;
-        };
         auto base_of = [&](int32_t id) __attribute__((always_inline)) -> int64_t {
             return ((uint32_t)id < (uint32_t)num_blocks ? id : 0) * block_stride + head_off;
         };
         // loads of unit v into stage v % NST (every iteration issues them,
         // also past the last unit, into the free stage: a fixed count per
         // iteration for the waits below)
+        // A unit starts a block (B <= 32) or half of one (B = 64), so which of
+        // the two entries a lane's token uses, and its offset in the block up
+        // to the unit's start, do not depend on the unit.
+        const bool k_second = BS == 16 && tK >= 16, v_second = BS == 16 && q8 >= 2;
+        const int k_off = (tK % BS) * 8, v_off = (8 * q8) % BS;
         auto issue = [&](int v, int32_t e0, int32_t e1) __attribute__((always_inline)) {
             __attribute__((address_space(3))) bf16x8* sb =
                 (__attribute__((address_space(3))) bf16x8*)(lds + (v % NST) * STAGE_SLOTS);
-            const int64_t kb = base_of(pick(v, tK, e0, e1)) + (int64_t)((v * kPfUnit + tK) % BS) * 8;
-            const int64_t vb = base_of(pick(v, 8 * q8, e0, e1)) + (v * kPfUnit + 8 * q8) % BS;
+            const int64_t b0 = base_of(e0), b1 = base_of(e1);  // uniform
+            const int unit_off = (v * kPfUnit) % BS;           // 32 in the second half of a 64-token block
+            const int64_t kb = (k_second ? b1 : b0) + k_off + unit_off * 8;
+            const int64_t vb = (v_second ? b1 : b0) + v_off + unit_off;
 #pragma unroll
             for (int k = 0; k < NP; ++k) {
                 const int f = tid / kPfUnit + k * (kPfThreads / kPfUnit);
