@@ -316,49 +316,46 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                     vop[i][e] = keep ? vop[i][e] : (__bf16)0.f;
             }
         }
+        // raw scores; the scale is applied inside the exponent (qscale > 0
+        // keeps the maximum where it is)
+        float sc[kPfTiles][8];
 #pragma unroll
-        for (int kt = 0; kt < kPfTiles; ++kt) {
-            const bool partial = t0 + kPfUnit > Lmin[kt] || !all_valid;
-            // raw scores; the scale is applied inside the exponent (qscale > 0
-            // keeps the maximum where it is)
-            float sc[8];
+        for (int kt = 0; kt < kPfTiles; ++kt)
 #pragma unroll
             for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj)
-                    sc[4 * mp + jj] = S[kt][mp][jj];
-            if (partial) {
-                asm volatile("" ::: "memory");  // a real branch: most units need no masking
+                    sc[kt][4 * mp + jj] = S[kt][mp][jj];
+        if (t0 + kPfUnit > Lmin[0] || t0 + kPfUnit > Lmin[1] || !all_valid) {
+            asm volatile("" ::: "memory");  // a real branch: most units need no masking
+#pragma unroll
+            for (int kt = 0; kt < kPfTiles; ++kt)
 #pragma unroll
                 for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
                         const int tt = 16 * mp + 4 * r + jj;
-                        sc[4 * mp + jj] = (t0 + tt < Lq[kt] && ((tmask >> tt) & 1)) ? sc[4 * mp + jj] : -INFINITY;
+                        sc[kt][4 * mp + jj] =
+                            (t0 + tt < Lq[kt] && ((tmask >> tt) & 1)) ? sc[kt][4 * mp + jj] : -INFINITY;
                     }
-            }
-            float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                             fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        }
+        // Online softmax of tile kt up to the bf16 hi / lo probability
+        // operands.  The running maximum is raised only when a score exceeds
+        // it by more than kRescaleSlack; the accumulators are rescaled by the
+        // caller (rescale_tile) before the next value sum into them.
+        auto softmax = [&](int kt, bf16x8& hi, bf16x8& lo, float& alpha) __attribute__((always_inline)) -> bool {
+            float mx = fmaxf(fmaxf(fmaxf(sc[kt][0], sc[kt][1]), fmaxf(sc[kt][2], sc[kt][3])),
+                             fmaxf(fmaxf(sc[kt][4], sc[kt][5]), fmaxf(sc[kt][6], sc[kt][7])));
             mx = max_over_lane_groups(mx) * qscale;
-            if (__ballot(mx > m_run[kt] + kRescaleSlack) != 0) {
-                const float m_new = fmaxf(m_run[kt], mx);
-                const float alpha = __builtin_amdgcn_exp2f(m_run[kt] - m_new);
-                m_run[kt] = m_new;
-                l_part[kt] *= alpha;
-                float a_row[4];
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
-                    a_row[jj] = __shfl(alpha, 4 * r + jj);
-#pragma unroll
-                for (int i = 0; i < HS / 16; ++i)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        O[kt][i][jj] *= a_row[jj];
-            }
+            const bool raise = __ballot(mx > m_run[kt] + kRescaleSlack) != 0;  // uniform
+            const float m_new = raise ? fmaxf(m_run[kt], mx) : m_run[kt];
+            alpha = __builtin_amdgcn_exp2f(m_run[kt] - m_new);  // 1 unless raised
+            m_run[kt] = m_new;
+            l_part[kt] *= alpha;
             float pv[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[e], qscale, -m_run[kt]));
+                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][e], qscale, -m_new));
                 l_part[kt] += pv[e];
             }
 #pragma unroll
@@ -376,13 +373,45 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                 hw[e] = hb;
                 lw[e] = __builtin_bit_cast(unsigned, __builtin_convertvector(rem, bf16x2));
             }
-            const bf16x8 hi = __builtin_bit_cast(bf16x8, hw), lo = __builtin_bit_cast(bf16x8, lw);
+            hi = __builtin_bit_cast(bf16x8, hw);
+            lo = __builtin_bit_cast(bf16x8, lw);
+            return raise;
+        };
+        auto rescale_tile = [&](int kt, float alpha) __attribute__((always_inline)) {
+            float a_row[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                a_row[jj] = __shfl(alpha, 4 * r + jj);
+#pragma unroll
+            for (int i = 0; i < HS / 16; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj)
+                    O[kt][i][jj] *= a_row[jj];
+        };
+        auto value_sum = [&](int kt, const bf16x8& hi, const bf16x8& lo) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < HS / 16; ++i) {
                 O[kt][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, vop[i], O[kt][i], 0, 0, 0);
                 O[kt][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, vop[i], O[kt][i], 0, 0, 0);
             }
+        };
+        // tile 0, then tile 1's softmax (vector work) written next to tile
+        // 0's value sum (matrix work) so the two can be issued interleaved;
+        // tile 1's rescale waits until after that
+        bf16x8 hi0, lo0, hi1, lo1;
+        float a0, a1;
+        if (softmax(0, hi0, lo0, a0))
+            rescale_tile(0, a0);
+        value_sum(0, hi0, lo0);
+        const bool raise1 = softmax(1, hi1, lo1, a1);
+#pragma unroll
+        for (int k = 0; k < 2 * (HS / 16); ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four vector instructions
         }
+        if (raise1)
+            rescale_tile(1, a1);
+        value_sum(1, hi1, lo1);
     };
 
     // ---- the unit loop: fetch u+1 while computing u, one barrier per unit ----
