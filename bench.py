@@ -372,7 +372,7 @@ def measured_traffic(path, config: int, partition_tokens: int, contiguous: bool)
     """HBM bytes per attention launch from a counter record, or None when the
     record is missing or was taken on another workload or another version of
     the kernel sources."""
-    if not path or not os.path.exists(path) or contiguous:
+    if not path or not os.path.isfile(path) or contiguous:
         return None
     with open(path) as f:
         rec = json.load(f)

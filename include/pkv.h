@@ -168,11 +168,15 @@ PKV_API pkv_status kv_cache_append(const void* k, const void* v, const int64_t* 
  * the sequences in decreasing number of blocks (ties by index), with their
  * lengths and block-table rows in that order, so that the attention kernel
  * starts the longest sequences first and no long one is left running alone
- * at the end.  This is a scheduling aid of this library, not part of the
- * method: results are bit-identical with and without it.
- * Returns its size in bytes for these sizes (int32 order[S], lens[S], each
- * rounded up to 16 bytes, then tables[S][max_blocks_per_seq]), or 0 when no
- * schedule is used (num_seqs <= 1 or num_seqs > 4096).
+ * at the end.  It also lists the chunks of the library's default
+ * partitioning (partition_tokens == 0) in that order, so that an attention
+ * call with the default partitioning starts every chunk of the longest
+ * sequences first.  This is a scheduling aid of this library, not part of
+ * the method: results are bit-identical with and without it.
+ * Returns its size in bytes for these sizes (int32 order[S], lens[S] and
+ * tables[S][max_blocks_per_seq], each rounded up to 16 bytes, a count padded
+ * to 16 bytes and the chunk list uint32 [S][ceil(max_blocks_per_seq / 4)][2]),
+ * or 0 when no schedule is used (num_seqs <= 1 or num_seqs > 4096).
  */
 PKV_API size_t pkv_decode_schedule_bytes(int32_t num_seqs, int32_t max_blocks_per_seq);
 

@@ -26,13 +26,46 @@ int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : (dtype == PKV_FP8_
 
 size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
 
-// Longest-first schedule: int32 order [S], lens [S] (each rounded up to 16
-// bytes), tables [S][M].
-pkv::AppendArgs::Schedule schedule_parts(void* schedule, int32_t num_seqs)
+// Library choice of the context-partition length: PKV_DEFAULT_PARTITION_TOKENS
+// (512: 32 blocks at B = 16, 16 at B = 32), at most 64 blocks (one block ID
+// per lane of the wave), or one partition when the table is shorter.  Blocks
+// of fewer than 16 tokens are read in 16-token units that must not straddle
+// two partitions: the length is then a multiple of 16.
+#ifndef PKV_DEFAULT_PARTITION_TOKENS
+#define PKV_DEFAULT_PARTITION_TOKENS 512
+#endif
+int32_t resolve_partition_tokens(int32_t max_blocks_per_seq, int32_t block_size, int32_t requested)
+{
+    if (requested < 0 || max_blocks_per_seq <= 0 || block_size <= 0)
+        return 0;
+    if (requested > 0) {
+        if (requested % block_size != 0 || requested / block_size > 64 || (block_size < 16 && requested % 16 != 0))
+            return 0;
+        return requested;
+    }
+    const int64_t whole = (int64_t)max_blocks_per_seq * block_size;
+    const int64_t dflt = PKV_DEFAULT_PARTITION_TOKENS < 64 * block_size ? PKV_DEFAULT_PARTITION_TOKENS : 64 * block_size;
+    return (int32_t)(whole < dflt ? whole : dflt);
+}
+
+// Longest-first schedule: int32 order [S], lens [S], tables [S][M] (each
+// rounded up to 16 bytes), the chunk count (padded to 16 bytes) and the chunk
+// list [S][ceil(M / 4)] of (rank and chunk, sequence) pairs (a chunk has at
+// least 4 blocks: one per wave).
+size_t schedule_items_capacity(int32_t num_seqs, int32_t max_blocks_per_seq)
+{
+    return (size_t)num_seqs * (((size_t)max_blocks_per_seq + 3) / 4);
+}
+
+pkv::AppendArgs::Schedule schedule_parts(void* schedule, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                         int32_t block_size)
 {
     char* base = (char*)schedule;
     const size_t vec = round_up((size_t)num_seqs * 4, 16);
-    return {(int32_t*)base, (int32_t*)(base + vec), (int32_t*)(base + 2 * vec)};
+    char* after_tables = base + 2 * vec + round_up((size_t)num_seqs * max_blocks_per_seq * 4, 16);
+    const int32_t P = resolve_partition_tokens(max_blocks_per_seq, block_size, 0);  // the library's default
+    return {(int32_t*)base, (int32_t*)(base + vec), (int32_t*)(base + 2 * vec), (int32_t*)after_tables,
+            (uint32_t*)(after_tables + 16), (P / block_size) * pkv::kDecodeWaves};
 }
 
 // Validates a pool descriptor; returns PKV_OK or the status to report.
@@ -57,27 +90,6 @@ pkv_status check_cache(const pkv_cache_desc* c)
     return PKV_OK;
 }
 
-// Library choice of the context-partition length: PKV_DEFAULT_PARTITION_TOKENS
-// (512: 32 blocks at B = 16, 16 at B = 32), at most 64 blocks (one block ID
-// per lane of the wave), or one partition when the table is shorter.  Blocks
-// of fewer than 16 tokens are read in 16-token units that must not straddle
-// two partitions: the length is then a multiple of 16.
-#ifndef PKV_DEFAULT_PARTITION_TOKENS
-#define PKV_DEFAULT_PARTITION_TOKENS 512
-#endif
-int32_t resolve_partition_tokens(int32_t max_blocks_per_seq, int32_t block_size, int32_t requested)
-{
-    if (requested < 0 || max_blocks_per_seq <= 0 || block_size <= 0)
-        return 0;
-    if (requested > 0) {
-        if (requested % block_size != 0 || requested / block_size > 64 || (block_size < 16 && requested % 16 != 0))
-            return 0;
-        return requested;
-    }
-    const int64_t whole = (int64_t)max_blocks_per_seq * block_size;
-    const int64_t dflt = PKV_DEFAULT_PARTITION_TOKENS < 64 * block_size ? PKV_DEFAULT_PARTITION_TOKENS : 64 * block_size;
-    return (int32_t)(whole < dflt ? whole : dflt);
-}
 
 }  // namespace
 
@@ -119,7 +131,7 @@ namespace {
 pkv::AppendArgs append_args(const void* k, const void* v, int64_t* slot_mapping, const int32_t* block_tables,
                             const int32_t* seq_lens, int32_t max_blocks_per_seq, int32_t num_tokens,
                             const pkv_cache_desc* cache, void* k_cache, void* v_cache,
-                            pkv::AppendArgs::Schedule sched = {nullptr, nullptr, nullptr})
+                            pkv::AppendArgs::Schedule sched = {})
 {
     pkv::AppendArgs a;
     a.sched = sched;
@@ -146,7 +158,7 @@ pkv::AppendArgs append_args(const void* k, const void* v, int64_t* slot_mapping,
 pkv_status append_common(const void* k, const void* v, int64_t* slot_mapping, const int32_t* block_tables,
                          const int32_t* seq_lens, int32_t max_blocks_per_seq, int32_t num_tokens,
                          const pkv_cache_desc* cache, void* k_cache, void* v_cache, void* stream,
-                         pkv::AppendArgs::Schedule sched = {nullptr, nullptr, nullptr})
+                         pkv::AppendArgs::Schedule sched = {})
 {
     const pkv::AppendArgs a = append_args(k, v, slot_mapping, block_tables, seq_lens, max_blocks_per_seq, num_tokens,
                                           cache, k_cache, v_cache, sched);
@@ -178,7 +190,8 @@ size_t pkv_decode_schedule_bytes(int32_t num_seqs, int32_t max_blocks_per_seq)
 {
     if (num_seqs <= 1 || num_seqs > pkv::kScheduleMaxSeqs || max_blocks_per_seq <= 0)
         return 0;
-    return 2 * round_up((size_t)num_seqs * 4, 16) + (size_t)num_seqs * max_blocks_per_seq * 4;
+    return 2 * round_up((size_t)num_seqs * 4, 16) + round_up((size_t)num_seqs * max_blocks_per_seq * 4, 16) + 16 +
+           schedule_items_capacity(num_seqs, max_blocks_per_seq) * 8;
 }
 
 pkv_status pkv_decode_append(const void* k, const void* v, const int32_t* block_tables, const int32_t* seq_lens,
@@ -197,12 +210,12 @@ pkv_status pkv_decode_append(const void* k, const void* v, const int32_t* block_
         return PKV_OK;
     if (!k || !v || !block_tables || !seq_lens || !aligned16(k) || !aligned16(v))
         return PKV_ERR_INVALID_ARG;
-    pkv::AppendArgs::Schedule sched = {nullptr, nullptr, nullptr};
+    pkv::AppendArgs::Schedule sched = {};
     const size_t sb = pkv_decode_schedule_bytes(num_seqs, max_blocks_per_seq);
     if (schedule && sb > 0) {
         if (schedule_bytes < sb || !aligned16(schedule))
             return PKV_ERR_WORKSPACE;
-        sched = schedule_parts(schedule, num_seqs);
+        sched = schedule_parts(schedule, num_seqs, max_blocks_per_seq, cache->block_size);
     }
     return append_common(k, v, slot_mapping, block_tables, seq_lens, max_blocks_per_seq, num_seqs, cache, k_cache,
                          v_cache, stream, sched);
@@ -246,6 +259,15 @@ size_t pkv_decode_step_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
 }
 
 namespace {
+
+// The chunk list serves batches above kLptMaxSeqs sequences (smaller ones
+// are launched with each sequence's chunks consecutive in the grid, which
+// needs no list); its launch is one-dimensional: one work-group per (KV
+// head, possible chunk), kept below 2^24 work-groups of 256 threads.
+bool listed_grid_fits(const pkv::DecodeArgs& a)
+{
+    return a.num_seqs > pkv::kLptMaxSeqs && (int64_t)a.num_kv_heads * a.num_seqs * a.max_parts < (int64_t)1 << 24;
+}
 
 // Validates the attention arguments and fills the launch description; no
 // GPU work.  PKV_OK with *nothing_to_do set when num_seqs == 0.
@@ -292,6 +314,8 @@ pkv_status attention_args(const void* q, const void* k_cache, const void* v_cach
     a.sched_order = nullptr;
     a.sched_lens = nullptr;
     a.sched_tables = nullptr;
+    a.sched_count = nullptr;
+    a.sched_items = nullptr;
     a.q_start = nullptr;
     a.num_q_rows = num_seqs;
     a.max_q_len = 1;
@@ -346,10 +370,15 @@ pkv_status paged_decode_attention(const void* q, const void* k_cache, const void
     if (schedule && sb > 0) {
         if (schedule_bytes < sb || !aligned16(schedule))
             return PKV_ERR_WORKSPACE;
-        const pkv::AppendArgs::Schedule p = schedule_parts(const_cast<int32_t*>(schedule), num_seqs);
+        const pkv::AppendArgs::Schedule p =
+            schedule_parts(const_cast<int32_t*>(schedule), num_seqs, max_blocks_per_seq, cache->block_size);
         a.sched_order = p.order;
         a.sched_lens = p.lens;
         a.sched_tables = p.tables;
+        if (partition_tokens == 0 && listed_grid_fits(a)) {  // the partitioning the chunk list was written for
+            a.sched_count = p.count;
+            a.sched_items = p.items;
+        }
     }
     return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
 }
@@ -563,15 +592,20 @@ pkv_status paged_decode_step(const void* q, const void* new_k, const void* new_v
         return PKV_ERR_WORKSPACE;
     // the append launch writes the longest-first schedule after the
     // attention partials; the attention launch reads it
-    pkv::AppendArgs::Schedule sched = {nullptr, nullptr, nullptr};
+    pkv::AppendArgs::Schedule sched = {};
     if (pkv_decode_schedule_bytes(num_seqs, max_blocks_per_seq) > 0) {
         const size_t attn = pkv_decode_workspace_bytes(num_seqs, num_q_heads, cache->num_kv_heads,
                                                        cache->head_size, max_blocks_per_seq, cache->block_size,
                                                        partition_tokens);
-        sched = schedule_parts((char*)workspace + round_up(attn, 256), num_seqs);
+        sched = schedule_parts((char*)workspace + round_up(attn, 256), num_seqs, max_blocks_per_seq,
+                               cache->block_size);
         a.sched_order = sched.order;
         a.sched_lens = sched.lens;
         a.sched_tables = sched.tables;
+        if (partition_tokens == 0 && listed_grid_fits(a)) {
+            a.sched_count = sched.count;
+            a.sched_items = sched.items;
+        }
     }
     st = append_common(new_k, new_v, slot_mapping, block_tables, seq_lens, max_blocks_per_seq, num_seqs, cache,
                        k_cache, v_cache, stream, sched);

@@ -76,6 +76,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // work-group of sequence i writes order[y] = i, lens[y] = seq_lens[i] and
 // copies its block-table row to tables[y], so that an attention work-group
 // finds its sequence, length and row from y alone, with no dependent load.
+// It also places its chunks (of the default partitioning) in the chunk list
+// (see write_schedule), so that the attention launch starts the largest
+// chunks first.
 //
 // The loads (every length, the row) do not depend on the rank, so they are
 // issued when the work-group starts, together with the token's loads; the
@@ -103,38 +106,80 @@ __device__ __forceinline__ void prefetch_schedule(SchedulePrefetch& p, int32_t i
 
 __device__ void write_schedule(const SchedulePrefetch& p, int32_t i, int32_t S,
                                const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ block_tables,
-                               int32_t M, int32_t B, int32_t* __restrict__ order, int32_t* __restrict__ lens,
-                               int32_t* __restrict__ tables)
+                               int32_t M, int32_t B, const AppendArgs::Schedule& sc)
 {
-    __shared__ int sm_part[kAppendThreads / 64];
+    constexpr int NW = kAppendThreads / 64;
+    __shared__ int sm_part[6][NW];
     const int64_t cap = (int64_t)M * B;
     auto blocks_of = [&](int32_t L) {
         const int64_t Lc = L < 0 ? 0 : (L > cap ? cap : L);
         return (Lc + B - 1) / B;
     };
+    // Chunks of the default partitioning: floor(k / CB) full chunks of CB
+    // blocks and, when blocks remain (or the sequence is empty: its zero
+    // output is written by the work-group of its one chunk), one partial
+    // chunk of k % CB blocks.  The chunk list is ordered by decreasing size
+    // (longest processing time first): every full chunk, by sequence index,
+    // then the partial chunks by decreasing size, ties by sequence index.
+    const int64_t CB = sc.chunk_blocks;
     const int32_t Li = seq_lens[i];
     const int64_t ki = blocks_of(Li);
-    int cnt = 0;
+    const int64_t full_i = ki / CB, rem_i = ki % CB;
+    const bool part_i = rem_i > 0 || ki == 0;
+    int acc[6] = {0, 0, 0, 0, 0, 0};  // rank, full before, full all, larger partials, equal partials before, chunks
+    auto count = [&](int j, int32_t Lj) __attribute__((always_inline)) {
+        const int64_t kj = blocks_of(Lj);
+        const int64_t fj = kj / CB, rj = kj % CB;
+        const bool pj = rj > 0 || kj == 0;
+        acc[0] += (kj > ki || (kj == ki && j < i)) ? 1 : 0;
+        acc[1] += j < i ? (int)fj : 0;
+        acc[2] += (int)fj;
+        acc[3] += (pj && rj > rem_i) ? 1 : 0;
+        acc[4] += (pj && rj == rem_i && j < i) ? 1 : 0;
+        acc[5] += (int)fj + (pj ? 1 : 0);
+    };
 #pragma unroll
     for (int t = 0; t < kSchedRegs; ++t) {
         const int j = threadIdx.x + t * kAppendThreads;
-        const int64_t kj = blocks_of(p.len[t]);
-        cnt += (j < S && (kj > ki || (kj == ki && j < i))) ? 1 : 0;
+        if (j < S)
+            count(j, p.len[t]);
     }
-    for (int j = threadIdx.x + kSchedRegs * kAppendThreads; j < S; j += kAppendThreads) {
-        const int64_t kj = blocks_of(seq_lens[j]);
-        cnt += (kj > ki || (kj == ki && j < i)) ? 1 : 0;
-    }
+    for (int j = threadIdx.x + kSchedRegs * kAppendThreads; j < S; j += kAppendThreads)
+        count(j, seq_lens[j]);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        cnt += __shfl_xor(cnt, o);
-    if ((threadIdx.x & 63) == 0)
-        sm_part[threadIdx.x >> 6] = cnt;
+    for (int a = 0; a < 6; ++a) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1)
+            acc[a] += __shfl_xor(acc[a], o);
+        if ((threadIdx.x & 63) == 0)
+            sm_part[a][threadIdx.x >> 6] = acc[a];
+    }
     __syncthreads();
-    int y = 0;
+    int tot[6] = {0, 0, 0, 0, 0, 0};
 #pragma unroll
-    for (int k = 0; k < kAppendThreads / 64; ++k)
-        y += sm_part[k];
+    for (int a = 0; a < 6; ++a)
+#pragma unroll
+        for (int k = 0; k < NW; ++k)
+            tot[a] += sm_part[a][k];
+    const int y = tot[0];
+    uint2* items = reinterpret_cast<uint2*>(sc.items);
+    for (int c = threadIdx.x; c < (int)full_i; c += kAppendThreads) {
+        uint2 it;
+        it.x = (uint32_t)y | ((uint32_t)c << 16);
+        it.y = (uint32_t)i;
+        items[tot[1] + c] = it;
+    }
+    if (threadIdx.x == 0 && part_i) {
+        uint2 it;
+        it.x = (uint32_t)y | ((uint32_t)full_i << 16);
+        it.y = (uint32_t)i;
+        items[tot[2] + tot[3] + tot[4]] = it;
+    }
+    if (threadIdx.x == 0 && i == 0)
+        *sc.count = tot[5];
+    int32_t* __restrict__ order = sc.order;
+    int32_t* __restrict__ lens = sc.lens;
+    int32_t* __restrict__ tables = sc.tables;
     if (threadIdx.x == 0) {
         order[y] = i;
         lens[y] = Li;
@@ -270,8 +315,7 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
         store_token<E>(kval, vval, slot, ci, k_cache, v_cache, num_kv_heads, head_size, block_size);
     }
     if (sched_wg)
-        write_schedule(pre, i, gridDim.x, seq_lens, block_tables, max_blocks_per_seq, block_size, sched.order,
-                       sched.lens, sched.tables);
+        write_schedule(pre, i, gridDim.x, seq_lens, block_tables, max_blocks_per_seq, block_size, sched);
 }
 
 hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,

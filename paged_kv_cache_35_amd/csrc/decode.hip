@@ -443,7 +443,8 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     const int32_t* __restrict__ sched_order, const int32_t* __restrict__ sched_lens,
     const int32_t* __restrict__ sched_tables, float oscale, T* __restrict__ out,
     float* __restrict__ ws_o, float* __restrict__ ws_ml, const int32_t* __restrict__ q_start, int32_t num_q_rows,
-    int32_t max_q_len, int32_t RT)
+    int32_t max_q_len, int32_t RT, const int32_t* __restrict__ sched_count, const uint32_t* __restrict__ sched_items,
+    int32_t rank_in_z)
 {
     using C = typename std::conditional<F8, uint8_t, T>::type;  // pool element type
     static_assert(!F8 || sizeof(T) == 2, "FP8 pools are read with bf16 queries");
@@ -459,11 +460,37 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     __shared__ int sm_pick;
     static_assert(kLptMaxSeqs <= NW * 16 * HS && kLptMaxSeqs <= 256, "the length ranking reuses the merge buffer and keeps the index in 8 bits");
 
-    const int kvh = MQ ? blockIdx.x / RT : blockIdx.x;
-    const int rt = MQ ? blockIdx.x - kvh * RT : 0;  // row tile
+    // Work-group -> (KV head, row tile, rank y, chunk).  With the schedule's
+    // chunk list (1-D grid, large batches): work-group x takes KV head
+    // x % Hkv of listed chunk x / Hkv, so the largest chunks start first,
+    // whichever sequence they belong to, and the unused work-groups (chunks
+    // past the list's end) come last.  Otherwise blockIdx.x covers the KV
+    // heads (and row tiles) and y, z the ranks and chunks: rank in z (chunks
+    // of one sequence consecutive) for small batches, where few work-groups
+    // find themselves past their sequence's end, rank in y otherwise.
+    int kvh, rt = 0, yr, chunk, s_listed = 0;
+    if (!MQ && sched_items) {
+        const int item = blockIdx.x / Hkv;
+        kvh = blockIdx.x - item * Hkv;
+        if (item >= *sched_count)
+            return;  // uniform, before any barrier
+        const uint2 it = reinterpret_cast<const uint2*>(sched_items)[item];
+        yr = (int)(it.x & 0xFFFFu);
+        chunk = (int)(it.x >> 16);
+        s_listed = (int)it.y;  // the sequence of rank yr, without another dependent load
+        // a list that does not belong to this launch (caller error) must not
+        // send a work-group outside its sequences or chunks
+        const int S_grid = (int)(gridDim.x / ((unsigned)Hkv * max_parts));
+        if (yr >= S_grid || chunk >= max_parts || (unsigned)s_listed >= (unsigned)S_grid)
+            return;
+    } else {
+        kvh = MQ ? blockIdx.x / RT : blockIdx.x;
+        rt = MQ ? blockIdx.x - kvh * RT : 0;  // row tile
+        yr = rank_in_z ? blockIdx.z : blockIdx.y;
+        chunk = rank_in_z ? blockIdx.y : blockIdx.z;
+    }
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, kept scalar
-    const int chunk = blockIdx.z;                                      // NW consecutive partitions
     const int part = chunk * NW + w;                                   // this wave's partition
     const int r = lane >> 4;
     const int c = lane & 15;
@@ -479,16 +506,17 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     // - Stand-alone call on a small batch (lpt): every work-group ranks the
     //   batch in LDS (the merge buffer, unused until the merge) by the key
     //   (blocks << 8) | (255 - index), distinct per sequence, and keeps the
-    //   one of rank y.  Only the first chunk of each sequence
-    //   (blockIdx.z == 0) is placed this way: a work-group of blockIdx.z > 0
-    //   learns that its sequence has no such chunk from one length load.
-    int s = blockIdx.y;
+    //   one of rank y.  Only the first chunk of each sequence is placed
+    //   this way (later chunks take sequence y): a work-group of a later
+    //   chunk learns that its sequence has no such chunk from one length
+    //   load.
+    int s = yr;
     if (sched_order) {
         // schedule given (decode step): rank y's sequence, length and table
         // row are read below from y alone
-        s = sched_order[blockIdx.y];
+        s = sched_items ? s_listed : sched_order[yr];
     } else if (lpt && chunk == 0) {
-        const int S = gridDim.y;  // <= kLptMaxSeqs = 256, M < 2^23 (checked on the host)
+        const int S = rank_in_z ? gridDim.z : gridDim.y;  // <= kLptMaxSeqs = 256, M < 2^23 (checked on the host)
         unsigned* sm_key = reinterpret_cast<unsigned*>(&sm_out[0][0]);
         const int cap = M * BS;
         for (int i = threadIdx.x; i < S; i += NW * 64) {
@@ -509,7 +537,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
                 rank += (j + 2 < S && k4.z > key) ? 1 : 0;
                 rank += (j + 3 < S && k4.w > key) ? 1 : 0;
             }
-            if (rank == (int)blockIdx.y)
+            if (rank == yr)
                 sm_pick = cand;
         }
         __syncthreads();
@@ -533,7 +561,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     // that this load and the length load are in flight together; entries
     // past the sequence's blocks are never used.
     const int tb = base + lane * stride;
-    const int32_t* trow = sched_order ? sched_tables + (int64_t)blockIdx.y * M : block_tables + (int64_t)s * M;
+    const int32_t* trow = sched_order ? sched_tables + (int64_t)yr * M : block_tables + (int64_t)s * M;
     const int32_t id_lane = (lane < PB && tb < M) ? trow[tb] : 0;
 
     // Query rows: qs0 .. qs0 + n - 1 (MQ), else row s alone.  Rows outside
@@ -554,7 +582,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
             return;  // uniform: before any barrier
     }
 
-    const int L_in = sched_order ? sched_lens[blockIdx.y] : seq_lens[s];
+    const int L_in = sched_order ? sched_lens[yr] : seq_lens[s];
     const int L = L_in < 0 ? 0 : (L_in > M * BS ? M * BS : L_in);
     // row rho of the tile, as (query row, head) of out
     auto out_row = [&](int rho) __attribute__((always_inline)) -> int64_t {
@@ -1098,7 +1126,11 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
 {
     constexpr int NW = kDecodeWaves;
     using C = typename std::conditional<F8, uint8_t, T>::type;
-    const dim3 grid(a.num_kv_heads * (MQ ? a.row_tiles : 1), a.num_seqs, a.max_parts);
+    const bool listed = !MQ && a.sched_items;
+    const int rank_in_z = !MQ && a.num_seqs <= kLptMaxSeqs ? 1 : 0;
+    const dim3 grid = listed      ? dim3((unsigned)((int64_t)a.num_kv_heads * a.num_seqs * a.max_parts))
+                      : rank_in_z ? dim3(a.num_kv_heads, a.max_parts, a.num_seqs)
+                                  : dim3(a.num_kv_heads * (MQ ? a.row_tiles : 1), a.num_seqs, a.max_parts);
     const float qscale = a.scale * kLog2e * (F8 ? a.k_scale : 1.0f);
     hipLaunchKernelGGL((paged_decode_partition_kernel<T, HS, BS, NW, F8, MQ>), grid, dim3(NW * 64), 0, stream,
                        (const T*)a.q, (const C*)a.k_cache, (const C*)a.v_cache, a.block_tables, a.seq_lens,
@@ -1106,7 +1138,8 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
                        a.max_parts, a.interleave,
                        (!MQ && a.num_seqs <= kLptMaxSeqs && a.max_blocks_per_seq < (1 << 23)) ? 1 : 0, qscale,
                        a.sched_order, a.sched_lens, a.sched_tables, F8 ? a.v_scale : 1.0f, (T*)a.out, a.ws_o,
-                       a.ws_ml, a.q_start, a.num_q_rows, a.max_q_len, a.row_tiles);
+                       a.ws_ml, a.q_start, a.num_q_rows, a.max_q_len, a.row_tiles, a.sched_count, a.sched_items,
+                       rank_in_z);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_parts <= 1)
         return e;  // one chunk per sequence: the partition kernel wrote the output

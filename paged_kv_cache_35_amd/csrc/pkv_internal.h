@@ -43,6 +43,11 @@ struct DecodeArgs {
     const int32_t* sched_order;
     const int32_t* sched_lens;
     const int32_t* sched_tables;
+    // With the schedule's chunk list (default partitioning only): one
+    // work-group per listed chunk and KV head, all chunks of the longest
+    // sequence first (null: one work-group per (KV head, rank, chunk)).
+    const int32_t* sched_count;
+    const uint32_t* sched_items;
     // Several query tokens per sequence (null: one each, row s): rows
     // q_start[s] .. q_start[s+1]-1 of q and out, at most max_q_len of them.
     const int32_t* q_start;
@@ -102,6 +107,13 @@ struct AppendArgs {
         int32_t* order;  // [num_tokens] sequence of rank y
         int32_t* lens;   // [num_tokens] seq_lens[order[y]]
         int32_t* tables; // [num_tokens][max_blocks_per_seq] block_tables[order[y]]
+        // The chunks of the library's default partitioning (chunk_blocks
+        // blocks each, the last one partial; at least one per sequence) by
+        // decreasing size: items[2k] = y | (chunk << 16) with y the
+        // sequence's rank, items[2k + 1] = order[y]; count = their number.
+        int32_t* count;
+        uint32_t* items; // [num_tokens * ceil(max_blocks_per_seq / 4)][2]
+        int32_t chunk_blocks;
     } sched;
 };
 

@@ -112,17 +112,20 @@ def test_workspace_and_partition_sizes(lib):
 
 
 def test_schedule_and_step_workspace_sizes(lib):
-    # order[S] and lens[S], each rounded up to 16 bytes, then tables[S][M]
-    assert lib.pkv_decode_schedule_bytes(64, 128) == 2 * 256 + 64 * 128 * 4
-    assert lib.pkv_decode_schedule_bytes(5, 3) == 2 * 32 + 5 * 3 * 4
-    assert lib.pkv_decode_schedule_bytes(4096, 8) == 2 * 4096 * 4 + 4096 * 8 * 4
+    # order[S], lens[S] and tables[S][M], each rounded up to 16 bytes, then
+    # a 16-byte count and the chunk list [S][ceil(M / 4)] of uint32 pairs
+    def sched(S, M):
+        return 2 * (-(-S * 4 // 16) * 16) + (-(-S * M * 4 // 16) * 16) + 16 + S * (-(-M // 4)) * 8
+    assert lib.pkv_decode_schedule_bytes(64, 128) == 2 * 256 + 64 * 128 * 4 + 16 + 64 * 32 * 8
+    assert lib.pkv_decode_schedule_bytes(5, 3) == 2 * 32 + 64 + 16 + 5 * 1 * 8
+    assert lib.pkv_decode_schedule_bytes(4096, 8) == sched(4096, 8)
     # no schedule for a single sequence or above 4096 sequences
     assert lib.pkv_decode_schedule_bytes(1, 128) == 0
     assert lib.pkv_decode_schedule_bytes(4097, 8) == 0
     # step = attention partials rounded up to 256 bytes + schedule
-    assert lib.pkv_decode_step_workspace_bytes(64, 32, 32, 128, 128, 16, 0) == 2 * 256 + 64 * 128 * 4
+    assert lib.pkv_decode_step_workspace_bytes(64, 32, 32, 128, 128, 16, 0) == sched(64, 128)
     attn = 64 * 32 * 8 * 130 * 4
-    assert lib.pkv_decode_step_workspace_bytes(64, 32, 32, 128, 1024, 16, 0) == attn + 2 * 256 + 64 * 1024 * 4
+    assert lib.pkv_decode_step_workspace_bytes(64, 32, 32, 128, 1024, 16, 0) == attn + sched(64, 1024)
     assert lib.pkv_decode_step_workspace_bytes(1, 8, 8, 64, 4, 16, 0) == 0
 
 

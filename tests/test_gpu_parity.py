@@ -246,6 +246,22 @@ def test_schedule_contents(cfg):
     assert np.array_equal(raw[:S], order)
     assert np.array_equal(raw[vec:vec + S], lens)
     assert np.array_equal(raw[2 * vec:2 * vec + S * w.M].reshape(S, w.M), tables)
+    # the chunk list of the default partitioning (CB = 4 partitions of
+    # min(512 tokens, 64 blocks, the table) each): every full chunk (CB
+    # blocks) by sequence index, then the partial chunks (blocks % CB, or an
+    # empty sequence's one chunk) by decreasing size, ties by index
+    P = min(512, 64 * w.B, w.M * w.B)
+    CB = (P // w.B) * 4
+    L = np.clip(w.seq_lens.astype(np.int64), 0, w.M * w.B)
+    blocks = -(-L // w.B)
+    rank = {int(s): y for y, s in enumerate(order)}
+    full = [(rank[s] | (c << 16), s) for s in range(S) for c in range(int(blocks[s] // CB))]
+    parts = [(-(int(blocks[s] % CB)), s) for s in range(S) if blocks[s] % CB or blocks[s] == 0]
+    items = full + [(rank[s] | (int(blocks[s] // CB) << 16), s) for _, s in sorted(parts)]
+    base = 2 * vec + -(-S * w.M // 4) * 4
+    assert raw[base] == len(items)
+    got = raw[base + 4:base + 4 + 2 * len(items)].view(np.uint32).reshape(-1, 2)
+    assert np.array_equal(got, np.array(items, np.uint32).reshape(-1, 2))
 
 
 @pytest.mark.parametrize("S", [4096, 4097])
