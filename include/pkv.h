@@ -169,9 +169,10 @@ PKV_API pkv_status kv_cache_append(const void* k, const void* v, const int64_t* 
  * lengths and block-table rows in that order, so that the attention kernel
  * starts the longest sequences first and no long one is left running alone
  * at the end.  It also lists the chunks of the library's default
- * partitioning (partition_tokens == 0) in that order, so that an attention
- * call with the default partitioning starts every chunk of the longest
- * sequences first.  This is a scheduling aid of this library, not part of
+ * partitioning (partition_tokens == 0) by decreasing size (the full chunks
+ * first, then the partial ones), so that an attention call with the default
+ * partitioning on a large batch starts the largest chunks first.  This is a
+ * scheduling aid of this library, not part of
  * the method: results are bit-identical with and without it.
  * Returns its size in bytes for these sizes (int32 order[S], lens[S] and
  * tables[S][max_blocks_per_seq], each rounded up to 16 bytes, a count padded
