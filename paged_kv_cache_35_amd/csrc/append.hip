@@ -5,6 +5,8 @@
 // by the cache write as block_id = slot / B and offset = slot % B.  The copy
 // is bit-exact (16-byte moves for keys, element moves for values; no float
 // arithmetic).
+#include <type_traits>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -222,44 +224,31 @@ __device__ __forceinline__ u32x4 quantize16(const u32x4 (&in)[2], float inv_scal
     return out;
 }
 
-// Stores 16-byte chunk ci (of the Hkv * hs / X chunks of a token) of the key
-// and value at `slot`: key chunk f of KV head h lands at
-// ((b*Hkv + h)*(hs/X) + f)*B*X + off*X, value head dims f*X .. f*X + X - 1
-// one element each at ((b*Hkv + h)*hs + d)*B + off.
-template <typename E>
-__device__ __forceinline__ void store_token(u32x4 kval, u32x4 vval, int64_t slot, int32_t ci,
-                                            u32x4* __restrict__ k_cache, E* __restrict__ v_cache,
-                                            int32_t num_kv_heads, int32_t head_size, int32_t block_size)
+// The E4M3 code of one bf16 value times inv_scale: the same product, clamp
+// and rounding as one element of quantize16.
+__device__ __forceinline__ uint8_t quantize1(uint16_t bf16_bits, float inv_scale)
 {
-    constexpr int X = 16 / sizeof(E);
-    const int32_t chunks_per_head = head_size / X;
-    const int64_t b = slot / block_size;
-    const int32_t off = (int32_t)(slot - b * block_size);
-    const int32_t h = ci / chunks_per_head;
-    const int32_t f = ci - h * chunks_per_head;
-    // streaming stores: the written lines are not re-read by this kernel
-    __builtin_nontemporal_store(kval, &k_cache[((b * num_kv_heads + h) * chunks_per_head + f) * block_size + off]);
-    union {
-        u32x4 u;
-        E e[X];
-    } val;
-    val.u = vval;
-    E* vdst = v_cache + ((b * num_kv_heads + h) * head_size + (int64_t)f * X) * block_size + off;
-#pragma unroll
-    for (int e = 0; e < X; ++e)
-        __builtin_nontemporal_store(val.e[e], &vdst[(int64_t)e * block_size]);
+    const float x = fminf(fmaxf(__builtin_bit_cast(float, (uint32_t)bf16_bits << 16) * inv_scale, -448.0f), 448.0f);
+    return (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x, x, 0, false) & 0xFF);
 }
 
-// Token i = blockIdx.x; each thread moves one 16-byte chunk of the token's
-// key and one of its value (chunk ci = blockIdx.y * 256 + threadIdx.x of the
-// Hkv * hs / X chunks; see store_token).  The token's data is loaded before the slot is known, so the loads overlap
-// the slot lookup.  FROM_TABLE: the slot is the decode slot of sequence i
-// (computed from block_tables / seq_lens and also written to slot_mapping);
-// otherwise it is read from slot_mapping.  A negative or out-of-range slot
-// skips the token.
+// Token i = blockIdx.x.  Keys: each thread moves one 16-byte chunk (chunk
+// ci = blockIdx.y * 256 + threadIdx.x of the token's Hkv * hs / X chunks);
+// chunk f of KV head h lands at ((b*Hkv + h)*(hs/X) + f)*B*X + off*X.
+// Values: the same work-group moves the same X * 256 elements of the token's
+// Hkv * hs, one element per thread and store, consecutive threads on
+// consecutive head dims: element d of head h lands at
+// ((b*Hkv + h)*hs + d)*B + off, so the 64 stores of a wave fall B elements
+// apart and share cache lines (4 per 128-byte line at B = 16, bf16), where
+// one 16-byte chunk per thread would send each store of the wave to 64
+// different lines.  The token's data is loaded before the slot is known, so
+// the loads overlap the slot lookup.  FROM_TABLE: the slot is the decode
+// slot of sequence i (computed from block_tables / seq_lens and also written
+// to slot_mapping); otherwise it is read from slot_mapping.  A negative or
+// out-of-range slot skips the token.
 //
 // The stores cover only part of each 32-byte sector (16 of 32 bytes of a key
-// sector, 2 or 4 bytes of a value row), and the memory system merges them
+// sector, 1, 2 or 4 bytes of a value row), and the memory system merges them
 // with the old contents.  Writing whole sectors instead (reading the
 // neighbouring bytes first) makes this kernel faster on its own, but the
 // attention launch that follows slows down by more than that gain: a decode
@@ -277,23 +266,30 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     constexpr int X = 16 / sizeof(E);
     constexpr bool Q8 = sizeof(E) == 1;  // FP8 pools: bf16 input, 2 input pieces per pool chunk
     constexpr int IN = Q8 ? 2 : 1;
+    using VIn = typename std::conditional<Q8, uint16_t, E>::type;  // one input value element
     const int32_t i = blockIdx.x;
     const int32_t nchunks = num_kv_heads * (head_size / X);
+    const int32_t nelem = num_kv_heads * head_size;
     const int32_t ci = blockIdx.y * kAppendThreads + threadIdx.x;
+    const int32_t e0 = blockIdx.y * kAppendThreads * X + threadIdx.x;  // first value element
     const bool active = ci < nchunks;
     const bool sched_wg = FROM_TABLE && sched.order && blockIdx.y == 0;  // uniform per work-group
     SchedulePrefetch pre;
     if (sched_wg)
         prefetch_schedule(pre, i, gridDim.x, seq_lens, block_tables, max_blocks_per_seq);
-    u32x4 kin[IN], vin[IN];
+    u32x4 kin[IN];
+    VIn vin[X];
 #pragma unroll
     for (int p = 0; p < IN; ++p) {
         kin[p] = (u32x4){0u, 0u, 0u, 0u};
-        vin[p] = (u32x4){0u, 0u, 0u, 0u};
-        if (active) {
+        if (active)
             kin[p] = k[((int64_t)i * nchunks + ci) * IN + p];
-            vin[p] = v[((int64_t)i * nchunks + ci) * IN + p];
-        }
+    }
+    const VIn* vrow = reinterpret_cast<const VIn*>(v) + (int64_t)i * nelem;
+#pragma unroll
+    for (int e = 0; e < X; ++e) {
+        const int32_t idx = e0 + e * kAppendThreads;
+        vin[e] = idx < nelem ? vrow[idx] : (VIn)0;
     }
     int64_t slot;
     if constexpr (FROM_TABLE) {
@@ -303,16 +299,33 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     } else {
         slot = slot_mapping[i];
     }
-    if (slot >= 0 && active && slot / block_size < num_blocks) {  // out-of-range slot: skipped, never written
-        u32x4 kval, vval;
-        if constexpr (Q8) {
-            kval = quantize16(kin, k_inv_scale);
-            vval = quantize16(vin, v_inv_scale);
-        } else {
-            kval = kin[0];
-            vval = vin[0];
+    if (slot >= 0 && slot / block_size < num_blocks) {  // out-of-range slot: skipped, never written
+        const int64_t b = slot / block_size;
+        const int32_t off = (int32_t)(slot - b * block_size);
+        // streaming stores: the written lines are not re-read by this kernel
+        if (active) {
+            const int32_t cph = head_size / X;  // key chunks per head
+            const int32_t h = ci / cph, f = ci - h * cph;
+            u32x4 kval;
+            if constexpr (Q8)
+                kval = quantize16(kin, k_inv_scale);
+            else
+                kval = kin[0];
+            __builtin_nontemporal_store(kval, &k_cache[((b * num_kv_heads + h) * cph + f) * block_size + off]);
         }
-        store_token<E>(kval, vval, slot, ci, k_cache, v_cache, num_kv_heads, head_size, block_size);
+#pragma unroll
+        for (int e = 0; e < X; ++e) {
+            const int32_t idx = e0 + e * kAppendThreads;
+            if (idx < nelem) {
+                E val;
+                if constexpr (Q8)
+                    val = quantize1(vin[e], v_inv_scale);
+                else
+                    val = vin[e];
+                // element idx = h * hs + d of the token sits at ((b*Hkv + h)*hs + d)*B + off
+                __builtin_nontemporal_store(val, &v_cache[(b * num_kv_heads * head_size + idx) * block_size + off]);
+            }
+        }
     }
     if (sched_wg)
         write_schedule(pre, i, gridDim.x, seq_lens, block_tables, max_blocks_per_seq, block_size, sched);
@@ -443,13 +456,10 @@ __global__ __launch_bounds__(kAppendThreads) void multi_token_append_kernel(
         const int d = it / cnt, j = it - d * cnt;
         const uint8_t* e = vs_raw + j * row_bytes + d * IB;
         E out;
-        if constexpr (Q8) {
-            const uint32_t bits = (uint32_t)(*(const uint16_t*)e) << 16;
-            const float x = fminf(fmaxf(__builtin_bit_cast(float, bits) * v_inv_scale, -448.0f), 448.0f);
-            out = (E)(__builtin_amdgcn_cvt_pk_fp8_f32(x, x, 0, false) & 0xFF);
-        } else {
+        if constexpr (Q8)
+            out = quantize1(*(const uint16_t*)e, v_inv_scale);
+        else
             out = *(const E*)e;
-        }
         __builtin_nontemporal_store(out, &vdst[(int64_t)d * B + j]);
     }
 }
