@@ -124,7 +124,9 @@ def bench_multi_token(args, w, torch, pkv) -> dict:
     d0 = copies[0]
     P = w.partition_tokens if args.partition_tokens is None else args.partition_tokens
     mql = w.max_q_len
+    ws_step = pkv.alloc_multi_token_step_workspace(d0["q"], d0["kc"], d0["vc"], d0["bt"], mql, P)
     ws = pkv.alloc_multi_token_workspace(d0["q"], d0["kc"], d0["vc"], d0["bt"], mql, P)
+    sched = pkv.alloc_schedule(d0["bt"])
     out = torch.empty_like(d0["q"])
     slots = torch.empty(w.rows, dtype=torch.int64, device="cuda")
     stream = torch.cuda.current_stream()
@@ -135,17 +137,20 @@ def bench_multi_token(args, w, torch, pkv) -> dict:
         d = copies[turn[0] % len(copies)]
         turn[0] += 1
         pkv.paged_multi_token_step(d["q"], d["nk"], d["nv"], d["kc"], d["vc"], d["qs"], mql, d["bt"], d["sl"],
-                                   w.scale, out=out, slot_mapping=slots, workspace=ws, partition_tokens=P,
+                                   w.scale, out=out, slot_mapping=slots, workspace=ws_step, partition_tokens=P,
                                    stream=stream, **sc)
 
     def step_timed(ev):
+        # the same step through its three entry points (the slot mapping
+        # also writes the longest-first schedule), events around the attention
         d = copies[turn[0] % len(copies)]
         turn[0] += 1
-        pkv.multi_token_slot_mapping(d["bt"], d["sl"], d["qs"], w.rows, mql, w.B, out=slots, stream=stream)
+        pkv.multi_token_slot_mapping(d["bt"], d["sl"], d["qs"], w.rows, mql, w.B, out=slots, schedule=sched,
+                                     stream=stream)
         pkv.multi_token_append(d["nk"], d["nv"], d["qs"], mql, d["bt"], d["sl"], d["kc"], d["vc"], stream=stream, **sc)
         ev[0].record(stream)
         pkv.paged_multi_token_attention(d["q"], d["qs"], mql, d["kc"], d["vc"], d["bt"], d["sl"], w.scale, out=out,
-                                        workspace=ws, partition_tokens=P, stream=stream, **sc)
+                                        workspace=ws, partition_tokens=P, schedule=sched, stream=stream, **sc)
         ev[1].record(stream)
 
     for _ in range(args.warmup):

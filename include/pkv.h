@@ -351,15 +351,34 @@ PKV_API size_t pkv_multi_token_workspace_bytes(int32_t num_seqs, int32_t num_q_h
                                                int32_t block_size, int32_t partition_tokens);
 
 /*
+ * Bytes of device workspace of paged_multi_token_step with the batch's
+ * longest-first schedule: the attention partials
+ * (pkv_multi_token_workspace_bytes), rounded up to 256, plus the schedule
+ * (pkv_decode_schedule_bytes); just the partials when no schedule applies
+ * (PKV_PARTITION_NONE, or num_seqs outside 2 .. 4096).
+ */
+PKV_API size_t pkv_multi_token_step_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                    int32_t head_size, int32_t max_q_len,
+                                                    int32_t max_blocks_per_seq, int32_t block_size,
+                                                    int32_t partition_tokens);
+
+/*
  * slot_mapping[q_start[s] + i] = slot of position L_s - n_s + i (the slot
  * rule of pkv_decode_slot_mapping), or -1 when that position lies outside
  * 0 .. L_s - 1 or past the table row.  Rows of no sequence are not written.
- * Asynchronous on `stream`.  PKV_ERR_UNSUPPORTED for num_seqs > 65535.
+ *   schedule  device buffer of schedule_bytes >= pkv_decode_schedule_bytes
+ *             receiving the batch's longest-first schedule (the layout
+ *             pkv_decode_append writes, from block_tables and seq_lens), or
+ *             NULL; ignored when that size is 0
+ * Asynchronous on `stream`.  PKV_ERR_UNSUPPORTED for num_seqs > 65535;
+ * PKV_ERR_WORKSPACE for a schedule buffer that is too small or not 16-byte
+ * aligned.
  */
 PKV_API pkv_status pkv_multi_token_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens,
                                                 const int32_t* q_start, int32_t num_seqs, int32_t num_q_rows,
                                                 int32_t max_q_len, int32_t max_blocks_per_seq,
-                                                int32_t block_size, int64_t* slot_mapping, void* stream);
+                                                int32_t block_size, int64_t* slot_mapping, int32_t* schedule,
+                                                size_t schedule_bytes, void* stream);
 
 /*
  * Stores new_k / new_v of every query row (rule above) in the slot of its
@@ -382,7 +401,11 @@ PKV_API pkv_status pkv_multi_token_append(const void* k, const void* v, const in
  * paged_decode_attention (same pools, scale, partition_tokens and workspace
  * rules; workspace of pkv_multi_token_workspace_bytes).  The tokens of the
  * query rows themselves must already be in the cache (kv_cache_append with
- * pkv_multi_token_slot_mapping, or paged_multi_token_step).
+ * pkv_multi_token_slot_mapping, or paged_multi_token_step).  schedule:
+ * the longest-first schedule pkv_multi_token_slot_mapping (or
+ * pkv_decode_append) wrote for these same block_tables and seq_lens, or
+ * NULL, as in paged_decode_attention (the partitioned kernel reads it; the
+ * results are bit-identical either way).
  * PKV_ERR_UNSUPPORTED for max_q_len > 65535 or num_seqs > 65535.
  */
 PKV_API pkv_status paged_multi_token_attention(const void* q, const int32_t* q_start, int32_t num_q_rows,
@@ -391,14 +414,18 @@ PKV_API pkv_status paged_multi_token_attention(const void* q, const int32_t* q_s
                                                int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
                                                const pkv_cache_desc* cache, float scale, void* out,
                                                void* workspace, size_t workspace_bytes, int32_t partition_tokens,
-                                               void* stream);
+                                               const int32_t* schedule, size_t schedule_bytes, void* stream);
 
 /*
  * One multi-token step: slot mapping of the rows into slot_mapping (int64
  * [num_q_rows], device, required), append of new_k/new_v of every row
  * (pkv_multi_token_append), then paged_multi_token_attention.  Three kernels in
  * stream order; every argument is checked before the first, so a rejected
- * call changes nothing.
+ * call changes nothing.  With a workspace of
+ * pkv_multi_token_step_workspace_bytes the slot mapping launch also writes
+ * the batch's longest-first schedule there and the partitioned attention
+ * reads it; a workspace of pkv_multi_token_workspace_bytes runs the step
+ * without one (bit-identical results).
  */
 PKV_API pkv_status paged_multi_token_step(const void* q, const void* new_k, const void* new_v, void* k_cache,
                                           void* v_cache, const int32_t* q_start, int32_t num_q_rows,

@@ -91,12 +91,14 @@ def library():
         L.pkv_multi_token_workspace_bytes.restype = sz
         L.pkv_multi_token_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
         L.pkv_multi_token_slot_mapping.restype = i32
-        L.pkv_multi_token_slot_mapping.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P]
+        L.pkv_multi_token_step_workspace_bytes.restype = sz
+        L.pkv_multi_token_step_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
+        L.pkv_multi_token_slot_mapping.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P, sz, P]
         L.pkv_multi_token_append.restype = i32
         L.pkv_multi_token_append.argtypes = [P, P, P, i32, i32, P, P, i32, i32, ctypes.POINTER(CacheDesc), P, P, P]
         L.paged_multi_token_attention.restype = i32
         L.paged_multi_token_attention.argtypes = [P, P, i32, i32, P, P, P, P, i32, i32, i32,
-                                                  ctypes.POINTER(CacheDesc), f32, P, P, sz, i32, P]
+                                                  ctypes.POINTER(CacheDesc), f32, P, P, sz, i32, P, sz, P]
         L.paged_multi_token_step.restype = i32
         L.paged_multi_token_step.argtypes = [P, P, P, P, P, P, i32, i32, P, P, i32, i32, i32,
                                              ctypes.POINTER(CacheDesc), f32, P, P, P, sz, i32, P]
@@ -402,6 +404,32 @@ def alloc_multi_token_workspace(q: torch.Tensor, k_cache: torch.Tensor, v_cache:
     return torch.empty(n, dtype=torch.uint8, device=q.device)
 
 
+def multi_token_step_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size, max_q_len, max_blocks_per_seq,
+                                     block_size, partition_tokens=0) -> int:
+    return int(library().pkv_multi_token_step_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size,
+                                                              max_q_len, max_blocks_per_seq, block_size,
+                                                              partition_tokens))
+
+
+def alloc_multi_token_step_workspace(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                     block_tables: torch.Tensor, max_q_len: int,
+                                     partition_tokens: int = 0) -> Optional[torch.Tensor]:
+    """Workspace of paged_multi_token_step: the attention partials plus the
+    batch's longest-first schedule."""
+    desc = cache_desc(k_cache, v_cache)
+    n = multi_token_step_workspace_bytes(block_tables.shape[0], q.shape[1], desc.num_kv_heads, desc.head_size,
+                                         max_q_len, block_tables.shape[1], desc.block_size, partition_tokens)
+    if n == 0:
+        return None
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def _sched(schedule: Optional[torch.Tensor]):
+    if schedule is None:
+        return None, 0
+    return _dev(schedule, "schedule"), schedule.numel() * schedule.element_size()
+
+
 def _check_rows(q, q_start, block_tables, seq_lens, desc, k_cache):
     if q.dtype != io_dtype(k_cache):
         raise ValueError("q must have the pools' dtype")
@@ -417,8 +445,10 @@ def _check_rows(q, q_start, block_tables, seq_lens, desc, k_cache):
 
 def multi_token_slot_mapping(block_tables: torch.Tensor, seq_lens: torch.Tensor, q_start: torch.Tensor,
                              num_q_rows: int, max_q_len: int, block_size: int, out: Optional[torch.Tensor] = None,
-                             stream=None) -> torch.Tensor:
-    """int64 [num_q_rows]: the slot of each query row's position."""
+                             schedule: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """int64 [num_q_rows]: the slot of each query row's position.  Also
+    writes the batch's longest-first schedule to `schedule` (from
+    alloc_schedule) if given."""
     S = block_tables.shape[0]
     if out is None:
         out = torch.empty(num_q_rows, dtype=torch.int64, device=block_tables.device)
@@ -426,7 +456,8 @@ def multi_token_slot_mapping(block_tables: torch.Tensor, seq_lens: torch.Tensor,
         raise ValueError("slot_mapping must be int64 [rows]")
     _check("pkv_multi_token_slot_mapping", library().pkv_multi_token_slot_mapping(
         _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), _dev(q_start, "q_start"), S, num_q_rows,
-        int(max_q_len), block_tables.shape[1], int(block_size), _dev(out, "slot_mapping"), _stream(stream)))
+        int(max_q_len), block_tables.shape[1], int(block_size), _dev(out, "slot_mapping"), *_sched(schedule),
+        _stream(stream)))
     return out
 
 
@@ -452,10 +483,13 @@ def multi_token_append(k: torch.Tensor, v: torch.Tensor, q_start: torch.Tensor, 
 def paged_multi_token_attention(q: torch.Tensor, q_start: torch.Tensor, max_q_len: int, k_cache: torch.Tensor,
                                 v_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor,
                                 scale: float, out: Optional[torch.Tensor] = None,
-                                workspace: Optional[torch.Tensor] = None, partition_tokens: int = 0, stream=None,
-                                k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+                                workspace: Optional[torch.Tensor] = None, partition_tokens: int = 0,
+                                schedule: Optional[torch.Tensor] = None, stream=None, k_scale: float = 1.0,
+                                v_scale: float = 1.0) -> torch.Tensor:
     """Causal paged attention of every query row over its sequence's cached
-    tokens (the rows' own tokens must already be in the cache)."""
+    tokens (the rows' own tokens must already be in the cache).  `schedule`:
+    the one multi_token_slot_mapping wrote for these tables and lengths, or
+    None."""
     desc = cache_desc(k_cache, v_cache, k_scale, v_scale)
     S = _check_rows(q, q_start, block_tables, seq_lens, desc, k_cache)
     rows, Hq, _ = q.shape
@@ -471,7 +505,7 @@ def paged_multi_token_attention(q: torch.Tensor, q_start: torch.Tensor, max_q_le
         _dev(q, "q"), _dev(q_start, "q_start"), rows, int(max_q_len), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), S, Hq,
         block_tables.shape[1], ctypes.byref(desc), float(scale), _dev(out, "out"), ws_ptr, ws_bytes,
-        int(partition_tokens), _stream(stream)))
+        int(partition_tokens), *_sched(schedule), _stream(stream)))
     return out
 
 
@@ -499,7 +533,8 @@ def paged_multi_token_step(q: torch.Tensor, new_k: torch.Tensor, new_v: torch.Te
     if out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("out must match q")
     if workspace is None:
-        workspace = alloc_multi_token_workspace(q, k_cache, v_cache, block_tables, max_q_len, partition_tokens)
+        workspace = alloc_multi_token_step_workspace(q, k_cache, v_cache, block_tables, max_q_len,
+                                                     partition_tokens)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("paged_multi_token_step", library().paged_multi_token_step(

@@ -263,10 +263,43 @@ namespace {
 // The chunk list serves batches above kLptMaxSeqs sequences (smaller ones
 // are launched with each sequence's chunks consecutive in the grid, which
 // needs no list); its launch is one-dimensional: one work-group per (KV
-// head, possible chunk), kept below 2^24 work-groups of 256 threads.
+// head, row tile, possible chunk), kept below 2^24 work-groups of 256
+// threads.
 bool listed_grid_fits(const pkv::DecodeArgs& a)
 {
-    return a.num_seqs > pkv::kLptMaxSeqs && (int64_t)a.num_kv_heads * a.num_seqs * a.max_parts < (int64_t)1 << 24;
+    return a.num_seqs > pkv::kLptMaxSeqs &&
+           (int64_t)a.num_kv_heads * a.row_tiles * a.num_seqs * a.max_parts < (int64_t)1 << 24;
+}
+
+// Points the attention launch at a schedule written for the same tables and
+// lengths: order, lengths and table rows always; the chunk list only with
+// the default partitioning it was written for, on large batches.
+void use_schedule(pkv::DecodeArgs& a, const pkv::AppendArgs::Schedule& p, int32_t partition_tokens)
+{
+    a.sched_order = p.order;
+    a.sched_lens = p.lens;
+    a.sched_tables = p.tables;
+    if (partition_tokens == 0 && listed_grid_fits(a)) {
+        a.sched_count = p.count;
+        a.sched_items = p.items;
+    }
+}
+
+// A caller's schedule buffer: PKV_OK with *used set when it is given and a
+// schedule applies to this batch, PKV_ERR_WORKSPACE when it is too small or
+// misaligned.
+pkv_status caller_schedule(const int32_t* schedule, size_t schedule_bytes, int32_t num_seqs,
+                           int32_t max_blocks_per_seq, int32_t block_size, pkv::AppendArgs::Schedule& p, bool& used)
+{
+    used = false;
+    const size_t sb = pkv_decode_schedule_bytes(num_seqs, max_blocks_per_seq);
+    if (!schedule || sb == 0)
+        return PKV_OK;
+    if (schedule_bytes < sb || !aligned16(schedule))
+        return PKV_ERR_WORKSPACE;
+    p = schedule_parts(const_cast<int32_t*>(schedule), num_seqs, max_blocks_per_seq, block_size);
+    used = true;
+    return PKV_OK;
 }
 
 // Validates the attention arguments and fills the launch description; no
@@ -366,20 +399,14 @@ pkv_status paged_decode_attention(const void* q, const void* k_cache, const void
                                          partition_tokens, a, nothing_to_do);
     if (st != PKV_OK || nothing_to_do)
         return st;
-    const size_t sb = pkv_decode_schedule_bytes(num_seqs, max_blocks_per_seq);
-    if (schedule && sb > 0) {
-        if (schedule_bytes < sb || !aligned16(schedule))
-            return PKV_ERR_WORKSPACE;
-        const pkv::AppendArgs::Schedule p =
-            schedule_parts(const_cast<int32_t*>(schedule), num_seqs, max_blocks_per_seq, cache->block_size);
-        a.sched_order = p.order;
-        a.sched_lens = p.lens;
-        a.sched_tables = p.tables;
-        if (partition_tokens == 0 && listed_grid_fits(a)) {  // the partitioning the chunk list was written for
-            a.sched_count = p.count;
-            a.sched_items = p.items;
-        }
-    }
+    pkv::AppendArgs::Schedule p;
+    bool used;
+    const pkv_status ss = caller_schedule(schedule, schedule_bytes, num_seqs, max_blocks_per_seq, cache->block_size,
+                                          p, used);
+    if (ss != PKV_OK)
+        return ss;
+    if (used)
+        use_schedule(a, p, partition_tokens);
     return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
 }
 
@@ -407,7 +434,8 @@ size_t pkv_multi_token_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, in
 pkv_status pkv_multi_token_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens,
                                         const int32_t* q_start, int32_t num_seqs, int32_t num_q_rows,
                                         int32_t max_q_len, int32_t max_blocks_per_seq, int32_t block_size,
-                                        int64_t* slot_mapping, void* stream)
+                                        int64_t* slot_mapping, int32_t* schedule, size_t schedule_bytes,
+                                        void* stream)
 {
     if (num_seqs < 0 || num_q_rows < 0 || max_q_len < 0 || max_blocks_per_seq <= 0 || block_size <= 0)
         return PKV_ERR_INVALID_ARG;
@@ -417,9 +445,15 @@ pkv_status pkv_multi_token_slot_mapping(const int32_t* block_tables, const int32
         return PKV_ERR_INVALID_ARG;
     if (num_seqs > 65535)
         return PKV_ERR_UNSUPPORTED;
+    pkv::AppendArgs::Schedule sched = {};
+    bool used;
+    const pkv_status ss = caller_schedule(schedule, schedule_bytes, num_seqs, max_blocks_per_seq, block_size, sched,
+                                          used);
+    if (ss != PKV_OK)
+        return ss;
     return hip_status(pkv::launch_multi_token_slot_mapping(block_tables, seq_lens, q_start, num_seqs, num_q_rows,
                                                            max_q_len, max_blocks_per_seq, block_size, slot_mapping,
-                                                           (hipStream_t)stream));
+                                                           sched, (hipStream_t)stream));
 }
 
 pkv_status pkv_multi_token_append(const void* k, const void* v, const int32_t* q_start, int32_t num_q_rows,
@@ -456,15 +490,18 @@ namespace {
 constexpr int64_t kPrefillMinRows = 64;
 constexpr int64_t kPrefillMinGroups = 512;
 
-hipError_t launch_multi_token(const pkv::DecodeArgs& a, int32_t partition_tokens, hipStream_t stream)
+bool picks_prefill(const pkv::DecodeArgs& a, int32_t partition_tokens)
 {
     const int64_t G = a.num_q_heads / a.num_kv_heads;
     if (partition_tokens == PKV_PARTITION_NONE)
-        return pkv::launch_prefill(a, stream);
-    if (partition_tokens == 0 && pkv::prefill_supported(a) && (int64_t)a.max_q_len * G >= kPrefillMinRows &&
-        pkv::prefill_work_groups(a) >= kPrefillMinGroups && pkv::prefill_work_groups(a) <= INT32_MAX)
-        return pkv::launch_prefill(a, stream);
-    return pkv::launch_decode(a, stream);
+        return true;
+    return partition_tokens == 0 && pkv::prefill_supported(a) && (int64_t)a.max_q_len * G >= kPrefillMinRows &&
+           pkv::prefill_work_groups(a) >= kPrefillMinGroups && pkv::prefill_work_groups(a) <= INT32_MAX;
+}
+
+hipError_t launch_multi_token(const pkv::DecodeArgs& a, int32_t partition_tokens, hipStream_t stream)
+{
+    return picks_prefill(a, partition_tokens) ? pkv::launch_prefill(a, stream) : pkv::launch_decode(a, stream);
 }
 
 // attention_args plus the query-row description of a multi-token call.
@@ -523,7 +560,7 @@ pkv_status paged_multi_token_attention(const void* q, const int32_t* q_start, in
                                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_q_heads,
                                        int32_t max_blocks_per_seq, const pkv_cache_desc* cache, float scale,
                                        void* out, void* workspace, size_t workspace_bytes, int32_t partition_tokens,
-                                       void* stream)
+                                       const int32_t* schedule, size_t schedule_bytes, void* stream)
 {
     pkv::DecodeArgs a;
     bool nothing_to_do;
@@ -532,7 +569,31 @@ pkv_status paged_multi_token_attention(const void* q, const int32_t* q_start, in
                                            workspace, workspace_bytes, partition_tokens, a, nothing_to_do);
     if (st != PKV_OK || nothing_to_do)
         return st;
+    pkv::AppendArgs::Schedule p;
+    bool used;
+    const pkv_status ss = caller_schedule(schedule, schedule_bytes, num_seqs, max_blocks_per_seq, cache->block_size,
+                                          p, used);
+    if (ss != PKV_OK)
+        return ss;
+    if (used)
+        use_schedule(a, p, partition_tokens);
     return hip_status(launch_multi_token(a, partition_tokens, (hipStream_t)stream));
+}
+
+size_t pkv_multi_token_step_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                            int32_t head_size, int32_t max_q_len, int32_t max_blocks_per_seq,
+                                            int32_t block_size, int32_t partition_tokens)
+{
+    if (num_kv_heads <= 0 || max_q_len <= 0 || num_q_heads % num_kv_heads != 0)
+        return 0;
+    const size_t attn = pkv_multi_token_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size, max_q_len,
+                                                        max_blocks_per_seq, block_size, partition_tokens);
+    if (partition_tokens == PKV_PARTITION_NONE ||
+        pkv_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq, block_size,
+                                    partition_tokens) <= 0)
+        return attn;
+    const size_t sb = pkv_decode_schedule_bytes(num_seqs, max_blocks_per_seq);
+    return sb == 0 ? attn : round_up(attn, 256) + sb;
 }
 
 pkv_status paged_multi_token_step(const void* q, const void* new_k, const void* new_v, void* k_cache,
@@ -555,9 +616,24 @@ pkv_status paged_multi_token_step(const void* q, const void* new_k, const void* 
         return PKV_ERR_INVALID_ARG;
     if (num_seqs > 65535)
         return PKV_ERR_UNSUPPORTED;
+    // With room for it (pkv_multi_token_step_workspace_bytes), the slot
+    // mapping launch writes the longest-first schedule after the attention
+    // partials and the attention launch reads it; a workspace of
+    // pkv_multi_token_workspace_bytes runs the same step without it.
+    // (Not written when the unpartitioned kernel runs: it does not use it.)
+    pkv::AppendArgs::Schedule sched = {};
+    const size_t attn = pkv_multi_token_workspace_bytes(num_seqs, num_q_heads, cache->num_kv_heads,
+                                                        cache->head_size, max_q_len, max_blocks_per_seq,
+                                                        cache->block_size, partition_tokens);
+    const size_t sb = pkv_decode_schedule_bytes(num_seqs, max_blocks_per_seq);
+    if (!picks_prefill(a, partition_tokens) && sb > 0 && workspace && workspace_bytes >= round_up(attn, 256) + sb) {
+        sched = schedule_parts((char*)workspace + round_up(attn, 256), num_seqs, max_blocks_per_seq,
+                               cache->block_size);
+        use_schedule(a, sched, partition_tokens);
+    }
     st = hip_status(pkv::launch_multi_token_slot_mapping(block_tables, seq_lens, q_start, num_seqs, num_q_rows,
                                                          max_q_len, max_blocks_per_seq, cache->block_size,
-                                                         slot_mapping, (hipStream_t)stream));
+                                                         slot_mapping, sched, (hipStream_t)stream));
     if (st != PKV_OK)
         return st;
     const pkv::AppendArgs ap = append_args(new_k, new_v, nullptr, block_tables, seq_lens, max_blocks_per_seq,
@@ -599,13 +675,7 @@ pkv_status paged_decode_step(const void* q, const void* new_k, const void* new_v
                                                        partition_tokens);
         sched = schedule_parts((char*)workspace + round_up(attn, 256), num_seqs, max_blocks_per_seq,
                                cache->block_size);
-        a.sched_order = sched.order;
-        a.sched_lens = sched.lens;
-        a.sched_tables = sched.tables;
-        if (partition_tokens == 0 && listed_grid_fits(a)) {
-            a.sched_count = sched.count;
-            a.sched_items = sched.items;
-        }
+        use_schedule(a, sched, partition_tokens);
     }
     st = append_common(new_k, new_v, slot_mapping, block_tables, seq_lens, max_blocks_per_seq, num_seqs, cache,
                        k_cache, v_cache, stream, sched);

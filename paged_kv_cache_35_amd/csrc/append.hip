@@ -39,33 +39,6 @@ __global__ void decode_slot_mapping_kernel(const int32_t* __restrict__ block_tab
         slot_mapping[s] = decode_slot(block_tables, seq_lens, s, max_blocks_per_seq, block_size);
 }
 
-// Work-group s, threads over the sequence's query rows i: row q_start[s] + i
-// sits at position L - n + i.  Rows are written only inside 0 .. num_q_rows - 1.
-__global__ void multi_token_slot_mapping_kernel(const int32_t* __restrict__ block_tables,
-                                                const int32_t* __restrict__ seq_lens,
-                                                const int32_t* __restrict__ q_start, int32_t num_q_rows,
-                                                int32_t max_q_len, int32_t max_blocks_per_seq, int32_t block_size,
-                                                int64_t* __restrict__ slot_mapping)
-{
-    const int32_t s = blockIdx.x;
-    const int32_t qs0 = q_start[s];
-    const int32_t qs1 = q_start[s + 1];
-    int32_t n = qs1 - qs0;
-    if (qs0 < 0 || n < 0 || qs1 > num_q_rows)
-        return;
-    n = n < max_q_len ? n : max_q_len;
-    const int32_t L = seq_lens[s];
-    for (int32_t i = threadIdx.x; i < n; i += blockDim.x) {
-        const int64_t pos = (int64_t)L - n + i;
-        const int64_t idx = pos >= 0 ? pos / block_size : -1;
-        int64_t slot = -1;
-        if (pos >= 0 && pos < L && idx < max_blocks_per_seq) {
-            const int64_t block = block_tables[(int64_t)s * max_blocks_per_seq + idx];
-            slot = block < 0 ? -1 : block * block_size + (pos - idx * block_size);
-        }
-        slot_mapping[qs0 + i] = slot;
-    }
-}
 
 constexpr int kAppendThreads = 256;
 
@@ -196,6 +169,42 @@ __device__ void write_schedule(const SchedulePrefetch& p, int32_t i, int32_t S,
     const int32_t* src = block_tables + (int64_t)i * M;
     for (int m = threadIdx.x + kSchedRegs * kAppendThreads; m < M; m += kAppendThreads)
         dst[m] = src[m];
+}
+
+// Slots of the query rows of a multi-token call: row i of sequence s (n
+// rows) holds position L - n + i; rows outside 0 .. L - 1 or past the table
+// row get -1.  One work-group per sequence.  With sched.order set (multi-token
+// step), each work-group also writes its sequence's entry of the
+// longest-first schedule (write_schedule), whatever its rows.
+__global__ __launch_bounds__(kAppendThreads) void multi_token_slot_mapping_kernel(
+    const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ q_start, int32_t num_q_rows, int32_t max_q_len, int32_t max_blocks_per_seq,
+    int32_t block_size, int64_t* __restrict__ slot_mapping, AppendArgs::Schedule sched)
+{
+    const int32_t s = blockIdx.x;
+    const bool sched_wg = sched.order != nullptr;
+    SchedulePrefetch pre;
+    if (sched_wg)
+        prefetch_schedule(pre, s, gridDim.x, seq_lens, block_tables, max_blocks_per_seq);
+    const int32_t qs0 = q_start[s];
+    const int32_t qs1 = q_start[s + 1];
+    int32_t n = qs1 - qs0;
+    if (qs0 < 0 || n < 0 || qs1 > num_q_rows)
+        n = 0;  // rows of no valid range: none written
+    n = n < max_q_len ? n : max_q_len;
+    const int32_t L = seq_lens[s];
+    for (int32_t i = threadIdx.x; i < n; i += blockDim.x) {
+        const int64_t pos = (int64_t)L - n + i;
+        const int64_t idx = pos >= 0 ? pos / block_size : -1;
+        int64_t slot = -1;
+        if (pos >= 0 && pos < L && idx < max_blocks_per_seq) {
+            const int64_t block = block_tables[(int64_t)s * max_blocks_per_seq + idx];
+            slot = block < 0 ? -1 : block * block_size + (pos - idx * block_size);
+        }
+        slot_mapping[qs0 + i] = slot;
+    }
+    if (sched_wg)
+        write_schedule(pre, s, gridDim.x, seq_lens, block_tables, max_blocks_per_seq, block_size, sched);
 }
 
 // FP8 pools: the E4M3 codes of 16 bf16 values times inv_scale, as one
@@ -345,10 +354,12 @@ hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* seq_l
 hipError_t launch_multi_token_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens,
                                            const int32_t* q_start, int32_t num_seqs, int32_t num_q_rows,
                                            int32_t max_q_len, int32_t max_blocks_per_seq, int32_t block_size,
-                                           int64_t* slot_mapping, hipStream_t stream)
+                                           int64_t* slot_mapping, const AppendArgs::Schedule& sched,
+                                           hipStream_t stream)
 {
-    hipLaunchKernelGGL(multi_token_slot_mapping_kernel, dim3(num_seqs), dim3(256), 0, stream, block_tables, seq_lens,
-                       q_start, num_q_rows, max_q_len, max_blocks_per_seq, block_size, slot_mapping);
+    hipLaunchKernelGGL(multi_token_slot_mapping_kernel, dim3(num_seqs), dim3(kAppendThreads), 0, stream,
+                       block_tables, seq_lens, q_start, num_q_rows, max_q_len, max_blocks_per_seq, block_size,
+                       slot_mapping, sched);
     return hipGetLastError();
 }
 

@@ -461,17 +461,21 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     static_assert(kLptMaxSeqs <= NW * 16 * HS && kLptMaxSeqs <= 256, "the length ranking reuses the merge buffer and keeps the index in 8 bits");
 
     // Work-group -> (KV head, row tile, rank y, chunk).  With the schedule's
-    // chunk list (1-D grid, large batches): work-group x takes KV head
-    // x % Hkv of listed chunk x / Hkv, so the largest chunks start first,
+    // chunk list (1-D grid, large batches): work-group x takes (KV head, row
+    // tile) pair x % HR of listed chunk x / HR (HR = Hkv, times the row tiles
+    // with MQ), so the largest chunks start first,
     // whichever sequence they belong to, and the unused work-groups (chunks
     // past the list's end) come last.  Otherwise blockIdx.x covers the KV
     // heads (and row tiles) and y, z the ranks and chunks: rank in z (chunks
     // of one sequence consecutive) for small batches, where few work-groups
     // find themselves past their sequence's end, rank in y otherwise.
     int kvh, rt = 0, yr, chunk, s_listed = 0;
-    if (!MQ && sched_items) {
-        const int item = blockIdx.x / Hkv;
-        kvh = blockIdx.x - item * Hkv;
+    if (sched_items) {
+        const int HR = MQ ? Hkv * RT : Hkv;  // (KV head, row tile) pairs
+        const int item = blockIdx.x / HR;
+        const int xr = blockIdx.x - item * HR;
+        kvh = MQ ? xr / RT : xr;
+        rt = MQ ? xr - kvh * RT : 0;
         if (item >= *sched_count)
             return;  // uniform, before any barrier
         const uint2 it = reinterpret_cast<const uint2*>(sched_items)[item];
@@ -480,7 +484,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
         s_listed = (int)it.y;  // the sequence of rank yr, without another dependent load
         // a list that does not belong to this launch (caller error) must not
         // send a work-group outside its sequences or chunks
-        const int S_grid = (int)(gridDim.x / ((unsigned)Hkv * max_parts));
+        const int S_grid = (int)(gridDim.x / ((unsigned)HR * max_parts));
         if (yr >= S_grid || chunk >= max_parts || (unsigned)s_listed >= (unsigned)S_grid)
             return;
     } else {
@@ -563,6 +567,9 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     const int tb = base + lane * stride;
     const int32_t* trow = sched_order ? sched_tables + (int64_t)yr * M : block_tables + (int64_t)s * M;
     const int32_t id_lane = (lane < PB && tb < M) ? trow[tb] : 0;
+    // The length is loaded next, before anything waits (the query-row bounds
+    // below may end the work-group), so that both loads are in flight at once.
+    const int L_in = sched_order ? sched_lens[yr] : seq_lens[s];
 
     // Query rows: qs0 .. qs0 + n - 1 (MQ), else row s alone.  Rows outside
     // 0 .. num_q_rows - 1 or beyond max_q_len are never read or written.
@@ -582,7 +589,6 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
             return;  // uniform: before any barrier
     }
 
-    const int L_in = sched_order ? sched_lens[yr] : seq_lens[s];
     const int L = L_in < 0 ? 0 : (L_in > M * BS ? M * BS : L_in);
     // row rho of the tile, as (query row, head) of out
     auto out_row = [&](int rho) __attribute__((always_inline)) -> int64_t {
@@ -1126,17 +1132,18 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
 {
     constexpr int NW = kDecodeWaves;
     using C = typename std::conditional<F8, uint8_t, T>::type;
-    const bool listed = !MQ && a.sched_items;
-    const int rank_in_z = !MQ && a.num_seqs <= kLptMaxSeqs ? 1 : 0;
-    const dim3 grid = listed      ? dim3((unsigned)((int64_t)a.num_kv_heads * a.num_seqs * a.max_parts))
-                      : rank_in_z ? dim3(a.num_kv_heads, a.max_parts, a.num_seqs)
-                                  : dim3(a.num_kv_heads * (MQ ? a.row_tiles : 1), a.num_seqs, a.max_parts);
+    const bool listed = a.sched_items != nullptr;
+    const int rank_in_z = a.num_seqs <= kLptMaxSeqs ? 1 : 0;
+    const int64_t HR = (int64_t)a.num_kv_heads * (MQ ? a.row_tiles : 1);  // (KV head, row tile) pairs
+    const dim3 grid = listed      ? dim3((unsigned)(HR * a.num_seqs * a.max_parts))
+                      : rank_in_z ? dim3((unsigned)HR, a.max_parts, a.num_seqs)
+                                  : dim3((unsigned)HR, a.num_seqs, a.max_parts);
     const float qscale = a.scale * kLog2e * (F8 ? a.k_scale : 1.0f);
     hipLaunchKernelGGL((paged_decode_partition_kernel<T, HS, BS, NW, F8, MQ>), grid, dim3(NW * 64), 0, stream,
                        (const T*)a.q, (const C*)a.k_cache, (const C*)a.v_cache, a.block_tables, a.seq_lens,
                        a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq, a.num_blocks, a.partition_blocks,
                        a.max_parts, a.interleave,
-                       (!MQ && a.num_seqs <= kLptMaxSeqs && a.max_blocks_per_seq < (1 << 23)) ? 1 : 0, qscale,
+                       (a.num_seqs <= kLptMaxSeqs && a.max_blocks_per_seq < (1 << 23)) ? 1 : 0, qscale,
                        a.sched_order, a.sched_lens, a.sched_tables, F8 ? a.v_scale : 1.0f, (T*)a.out, a.ws_o,
                        a.ws_ml, a.q_start, a.num_q_rows, a.max_q_len, a.row_tiles, a.sched_count, a.sched_items,
                        rank_in_z);

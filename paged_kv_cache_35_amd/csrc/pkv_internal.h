@@ -134,7 +134,8 @@ hipError_t launch_copy_blocks(const int32_t* pairs, int32_t num_pairs, int32_t n
 hipError_t launch_multi_token_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens,
                                            const int32_t* q_start, int32_t num_seqs, int32_t num_q_rows,
                                            int32_t max_q_len, int32_t max_blocks_per_seq, int32_t block_size,
-                                           int64_t* slot_mapping, hipStream_t stream);
+                                           int64_t* slot_mapping, const AppendArgs::Schedule& sched,
+                                           hipStream_t stream);
 
 hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
                                int32_t max_blocks_per_seq, int32_t block_size, int64_t* slot_mapping,

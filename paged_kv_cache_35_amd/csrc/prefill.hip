@@ -97,7 +97,6 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     const int32_t* __restrict__ q_start, int32_t num_q_rows, int32_t max_q_len, int32_t Hq, int32_t Hkv, int32_t M,
     int32_t num_blocks, int32_t RB, float qscale, float oscale, __bf16* __restrict__ out)
 {
-    using C = typename std::conditional<F8, uint8_t, __bf16>::type;
     static_assert(BS >= 16 && (BS % 16) == 0, "blocks of 16, 32 or 64 tokens");
     constexpr int TILE = HS * BS;  // elements of one (block, KV head) tile
     // LDS stages of 16-byte slots: keys [hs/8][32] first, then values

@@ -32,7 +32,8 @@ def test_header_declares_the_entry_points():
     for n in ("paged_decode_attention", "kv_cache_append", "pkv_decode_slot_mapping",
               "pkv_decode_workspace_bytes", "pkv_decode_partition_tokens", "pkv_status_string",
               "pkv_layout_version", "pkv_last_hip_error", "paged_decode_step", "pkv_decode_append",
-              "pkv_decode_schedule_bytes", "pkv_decode_step_workspace_bytes"):
+              "pkv_decode_schedule_bytes", "pkv_decode_step_workspace_bytes", "paged_multi_token_attention",
+              "pkv_multi_token_step_workspace_bytes", "pkv_multi_token_slot_mapping"):
         assert n in names
 
 
@@ -188,6 +189,32 @@ def test_decode_append_rejects_a_small_schedule(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, 0, 4, ctypes.byref(d), FAKE, FAKE, None, FAKE, 0, None) == OK
 
 
+def test_multi_token_attention_rejects_a_small_schedule(lib):
+    need = lib.pkv_decode_schedule_bytes(4, 4)
+    f = lib.paged_multi_token_attention
+    assert f(FAKE, FAKE, 8, 2, FAKE, FAKE, FAKE, FAKE, 4, 8, 4, ctypes.byref(desc()), 0.125, FAKE, None, 0, 0, FAKE,
+             need - 1, None) == WORKSPACE
+
+
+def test_multi_token_step_workspace_sizes(lib):
+    f = lib.pkv_multi_token_step_workspace_bytes
+    attn = lib.pkv_multi_token_workspace_bytes
+    sched = lib.pkv_decode_schedule_bytes
+    # partials rounded up to 256, then the schedule
+    a = attn(256, 32, 8, 128, 4, 1024, 16, 0)
+    assert a > 0 and f(256, 32, 8, 128, 4, 1024, 16, 0) == (a + 255) // 256 * 256 + sched(256, 1024)
+    # no partials (one chunk covers the table): the schedule alone
+    assert attn(64, 32, 32, 128, 8, 128, 16, 0) == 0
+    assert f(64, 32, 32, 128, 8, 128, 16, 0) == sched(64, 128)
+    # no schedule: one sequence, more than 4096, or the unpartitioned kernel
+    assert f(1, 32, 8, 128, 4, 1024, 16, 0) == attn(1, 32, 8, 128, 4, 1024, 16, 0)
+    assert f(4097, 32, 8, 128, 4, 8, 16, 0) == attn(4097, 32, 8, 128, 4, 8, 16, 0)
+    assert f(16, 32, 8, 128, 512, 1024, 16, -1) == 0
+    # invalid shapes: 0
+    assert f(16, 30, 8, 128, 4, 1024, 16, 0) == 0
+    assert f(16, 32, 8, 128, 0, 1024, 16, 0) == 0
+
+
 def test_multi_token_workspace_sizes(lib):
     f = lib.pkv_multi_token_workspace_bytes
     # one chunk covers the table: none
@@ -204,7 +231,7 @@ def test_multi_token_workspace_sizes(lib):
 def mq(lib, *, q=FAKE, qs=FAKE, rows=8, mql=2, S=4, Hq=8, M=4, d=None, out=FAKE, ws=None, ws_bytes=0, P=0):
     d = d or desc()
     return lib.paged_multi_token_attention(q, qs, rows, mql, FAKE, FAKE, FAKE, FAKE, S, Hq, M, ctypes.byref(d),
-                                           0.125, out, ws, ws_bytes, P, None)
+                                           0.125, out, ws, ws_bytes, P, None, 0, None)
 
 
 def test_multi_token_attention_rejects_bad_arguments(lib):
@@ -223,7 +250,7 @@ def test_multi_token_attention_rejects_bad_arguments(lib):
     assert mq(lib, M=4096, ws=FAKE, ws_bytes=dec) == WORKSPACE
     # nothing to do
     assert lib.paged_multi_token_attention(None, None, 0, 0, None, None, None, None, 0, 8, 4, ctypes.byref(desc()),
-                                           0.125, None, None, 0, 0, None) == OK
+                                           0.125, None, None, 0, 0, None, 0, None) == OK
 
 
 def test_multi_token_step_and_slot_mapping_reject_bad_arguments(lib):
@@ -236,10 +263,14 @@ def test_multi_token_step_and_slot_mapping_reject_bad_arguments(lib):
         a[i] = bad
         assert f(*a) == INVALID
     g = lib.pkv_multi_token_slot_mapping
-    assert g(FAKE, FAKE, None, 4, 8, 2, 4, 16, FAKE, None) == INVALID
-    assert g(FAKE, FAKE, FAKE, 4, 8, 2, 0, 16, FAKE, None) == INVALID
-    assert g(FAKE, FAKE, FAKE, 70000, 8, 2, 4, 16, FAKE, None) == UNSUPPORTED
-    assert g(None, None, None, 0, 0, 0, 4, 16, None, None) == OK
+    assert g(FAKE, FAKE, None, 4, 8, 2, 4, 16, FAKE, None, 0, None) == INVALID
+    assert g(FAKE, FAKE, FAKE, 4, 8, 2, 0, 16, FAKE, None, 0, None) == INVALID
+    assert g(FAKE, FAKE, FAKE, 70000, 8, 2, 4, 16, FAKE, None, 0, None) == UNSUPPORTED
+    assert g(None, None, None, 0, 0, 0, 4, 16, None, None, 0, None) == OK
+    # a schedule buffer that is too small or misaligned
+    need = lib.pkv_decode_schedule_bytes(4, 4)
+    assert g(FAKE, FAKE, FAKE, 4, 8, 2, 4, 16, FAKE, FAKE, need - 1, None) == WORKSPACE
+    assert g(FAKE, FAKE, FAKE, 4, 8, 2, 4, 16, FAKE, ctypes.c_void_p(0x10008), need, None) == WORKSPACE
 
 
 def test_partition_lengths_for_every_block_size(lib):
@@ -263,4 +294,5 @@ def test_unpartitioned_multi_token_kernel_support(lib):
     assert mq(lib, P=-1, d=desc(dtype=1, B=8)) == UNSUPPORTED
     # and no workspace, whatever the table length
     assert lib.paged_multi_token_attention(FAKE, None, 8, 2, FAKE, FAKE, FAKE, FAKE, 4, 8, 4096,
-                                           ctypes.byref(desc(dtype=1)), 0.125, FAKE, None, 0, -1, None) == INVALID
+                                           ctypes.byref(desc(dtype=1)), 0.125, FAKE, None, 0, -1, None, 0,
+                                           None) == INVALID

@@ -7,6 +7,8 @@ keys and values are appended first (slot mapping + append, bit-exact), as in
 a decode step.  Bars as for decode: max-abs error <= 1e-5 (fp32) and <= 2e-3
 (bf16 outputs, with the one-ulp rule for |out| >= 1), appends bit-exact.
 """
+from types import SimpleNamespace
+
 import numpy as np
 import pytest
 
@@ -282,3 +284,62 @@ def test_unpartitioned_kernel_shapes(dtype, hs, B, Hq, Hkv):
                          q_lens=q_lens)
     announce(f"unpartitioned {dtype} hs={hs} B={B} Hq={Hq} Hkv={Hkv} lens={list(w.seq_lens)} q_start={list(w.q_start)}")
     full_check(w, MRun(w, partition_tokens=pkv().PARTITION_NONE))
+
+
+# Longest-first schedule of a multi-token batch: written by the slot mapping
+# launch (as the decode append writes it) and read by the partitioned
+# attention, in rank order below 65 sequences and through the chunk list
+# (one work-group per listed chunk, KV head and row tile) above.  Results
+# must not depend on it.
+@pytest.mark.parametrize("S,q_lens", [(48, 4), (80, 4), (80, 9), (72, 1)])
+def test_step_with_schedule_bit_identical_to_the_separate_calls(S, q_lens):
+    w = pi.make_workload(3, S=S, len_lo=16, len_hi=3000, q_lens=q_lens)
+    announce(f"multi-token step with schedule: S={S} q_lens={q_lens} rows={w.rows} max_len={int(w.seq_lens.max())}")
+    r = MRun(w)
+    m = pkv()
+    ws = m.alloc_multi_token_step_workspace(r.q, r.kc, r.vc, r.bt, w.max_q_len)
+    plain = m.alloc_multi_token_workspace(r.q, r.kc, r.vc, r.bt, w.max_q_len)
+    assert ws is not None and ws.numel() > (plain.numel() if plain is not None else 0)
+    kc, vc = dev(w.k_cache), dev(w.v_cache)
+    slots = torch.empty(w.rows, dtype=torch.int64, device="cuda")
+    out = m.paged_multi_token_step(r.q, r.nk, r.nv, kc, vc, r.qs, w.max_q_len, r.bt, r.sl, w.scale,
+                                   slot_mapping=slots, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(slots, r.slots)
+    assert torch.equal(kc.view(torch.int16), r.kc.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), r.vc.view(torch.int16))
+    assert torch.equal(out.view(torch.int16), r.out.view(torch.int16))
+
+
+def test_step_with_schedule_matches_the_oracle():
+    w = pi.make_workload(3, S=70, len_lo=16, len_hi=2600, q_lens=6)
+    announce(f"multi-token step with schedule vs oracle: S=70 rows={w.rows}")
+    m = pkv()
+    q, kc, vc = dev(w.q), dev(w.k_cache), dev(w.v_cache)
+    bt, sl, qs = dev(w.block_tables), dev(w.seq_lens), dev(w.q_start)
+    slots = torch.empty(w.rows, dtype=torch.int64, device="cuda")
+    out = m.paged_multi_token_step(q, dev(w.new_k), dev(w.new_v), kc, vc, qs, w.max_q_len, bt, sl, w.scale,
+                                   slot_mapping=slots)
+    torch.cuda.synchronize()
+    full_check(w, SimpleNamespace(slots=slots, kc=kc, vc=vc, out=out))
+
+
+@pytest.mark.parametrize("S", [40, 90])
+def test_attention_with_a_caller_schedule(S):
+    # multi_token_slot_mapping writes the same schedule bytes as the decode
+    # append for the same tables and lengths, and the stand-alone attention
+    # gives the same bits with it as without it
+    w = pi.make_workload(3, S=S, len_lo=16, len_hi=3000, q_lens=3)
+    announce(f"multi-token attention with a caller schedule: S={S}")
+    r = MRun(w)
+    m = pkv()
+    sched = m.alloc_schedule(r.bt).zero_()  # zeroed: the padding is compared too
+    slots = m.multi_token_slot_mapping(r.bt, r.sl, r.qs, w.rows, w.max_q_len, w.B, schedule=sched)
+    out = m.paged_multi_token_attention(r.q, r.qs, w.max_q_len, r.kc, r.vc, r.bt, r.sl, w.scale, schedule=sched)
+    dsched = m.alloc_schedule(r.bt).zero_()
+    kc, vc = dev(w.k_cache), dev(w.v_cache)
+    m.decode_append(r.nk[:S].contiguous(), r.nv[:S].contiguous(), r.bt, r.sl, kc, vc, schedule=dsched)
+    torch.cuda.synchronize()
+    assert torch.equal(slots, r.slots)
+    assert torch.equal(out.view(torch.int16), r.out.view(torch.int16))
+    assert torch.equal(sched, dsched)
