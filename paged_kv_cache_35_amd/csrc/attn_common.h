@@ -52,13 +52,14 @@ __device__ __forceinline__ void to_value_order(float& x, float& y)
 // each column c, with the same two lane-group swaps (no LDS round trip):
 // after v_permlane32_swap of two copies, lane l holds x[l] and x[l ^ 32];
 // after v_permlane16_swap of two copies of that maximum, x[l ^ 16] joins.
+// (IEEE maximum: a NaN among the inputs gives NaN.)
 __device__ __forceinline__ float max_over_lane_groups(float x)
 {
     float a = x, b = x;
     asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-    float c = fmaxf(a, b), d = c;
+    float c = __builtin_elementwise_maximum(a, b), d = c;
     asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(c), "+v"(d));
-    return fmaxf(c, d);
+    return __builtin_elementwise_maximum(c, d);
 }
 
 __device__ __forceinline__ void store_elem(__bf16* p, float x) { *p = (__bf16)x; }

@@ -18,17 +18,20 @@
 //    instruction lands at base + 16 i) issued two units ahead, so no
 //    registers hold data in flight.  FP8 pools: two stages, the next unit's
 //    codes loaded into registers and converted to bf16 on the way into LDS.
-//    Keys sit in LDS as [hs/8][32 tokens] 16-byte chunks, so a lane's
-//    16-byte read is the A operand of v_mfma_f32_16x16x32_bf16 (token row c,
-//    8 head dims) and a lane group reads 256 contiguous bytes.  Values sit
+//    Keys sit in LDS as [hs/8][32 positions] 16-byte chunks, so a lane's
+//    16-byte read is the A operand of v_mfma_f32_16x16x32_bf16 (position
+//    row c, 8 head dims) and a lane group reads 256 contiguous bytes.
+//    Position 16 mp + m holds token key_token(16 mp + m) = 8 (m / 4) + 4 mp
+//    + m % 4: the scores of M-tiles mp = 0, 1 then give lane group r the
+//    tokens 8r .. 8r+7 in order, which is the token order of the value MFMA's
+//    operands, so the probabilities need no exchange between lanes.  Values sit
 //    as [hs][32 tokens] in four 16-byte slots per row; for the 16-byte reads
 //    of 16 consecutive head dims to hit distinct banks, the slots of row d
 //    are permuted (slot q holds tokens 8 (q ^ ((d / 4) % 4)) ..) in the bf16
 //    path, and the rows are padded by 8 elements in the FP8 path.
 //  * Each wave reads one unit's key and value operands once from LDS and
-//    uses them for both of its row tiles (scores, then the value sum with the
-//    probabilities moved to the value order by to_value_order, hi + lo bf16
-//    parts as in decode).
+//    uses them for both of its row tiles (scores, then the value sum with
+//    hi + lo bf16 probability parts as in decode).
 //  * Causal: a lane's row has its own limit; a wave stops computing at its
 //    last row's limit, and the work-group stops loading at its last row's.
 //  * The K/V loads use the caches normally: the other row blocks of the same
@@ -49,6 +52,12 @@ constexpr int kPfThreads = kPfWaves * 64;
 constexpr int kPfTiles = 2;                       // 16-row MFMA tiles per wave
 constexpr int kPfRows = kPfWaves * kPfTiles * 16; // rows per work-group
 constexpr int kPfUnit = 32;                       // tokens per staged unit
+
+// The token whose key sits at LDS key position pos of a unit (see above).
+__device__ __forceinline__ int key_token(int pos)
+{
+    return 8 * ((pos & 15) >> 2) + 4 * (pos >> 4) + (pos & 3);
+}
 constexpr int kPfVRow = kPfUnit + 8;              // LDS value row (elements), padded
 constexpr int kXcds = 8;                          // MI355X: 8 XCDs of 32 compute units
 
@@ -221,8 +230,8 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
             if constexpr (F8) {
                 // key chunk f16 (16 head dims) of token t; value codes of head
                 // dim d, tokens 16h .. 16h+15
-                const int f16 = p / kPfUnit, t = p % kPfUnit;
-                const int T = t0 + t;
+                const int f16 = p / kPfUnit, t = p % kPfUnit;  // LDS position t
+                const int T = t0 + key_token(t);
                 pc.k[k] = *(
                     (const u32x4*)(k_cache + block_at(T / BS) + ((int64_t)f16 * BS + T % BS) * 16));
                 const int d = p / 2, h = p % 2;
@@ -232,8 +241,8 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
             } else {
                 // key chunk f (8 head dims) of token t; value head dim d,
                 // tokens 8 q8 .. 8 q8 + 7
-                const int f = p / kPfUnit, t = p % kPfUnit;
-                const int T = t0 + t;
+                const int f = p / kPfUnit, t = p % kPfUnit;  // LDS position t
+                const int T = t0 + key_token(t);
                 pc.k[k] = *(
                     (const u32x4*)(k_cache + block_at(T / BS) + ((int64_t)f * BS + T % BS) * 8));
                 const int d = p / 4, q8 = p % 4;
@@ -333,7 +342,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                 for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) {
-                        const int tt = 16 * mp + 4 * r + jj;
+                        const int tt = key_token(16 * mp + 4 * r + jj);  // = 8r + 4mp + jj
                         sc[kt][4 * mp + jj] =
                             (t0 + tt < Lq[kt] && ((tmask >> tt) & 1)) ? sc[kt][4 * mp + jj] : -INFINITY;
                     }
@@ -343,23 +352,25 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         // it by more than kRescaleSlack; the accumulators are rescaled by the
         // caller (rescale_tile) before the next value sum into them.
         auto softmax = [&](int kt, bf16x8& hi, bf16x8& lo, float& alpha) __attribute__((always_inline)) -> bool {
-            float mx = fmaxf(fmaxf(fmaxf(sc[kt][0], sc[kt][1]), fmaxf(sc[kt][2], sc[kt][3])),
-                             fmaxf(fmaxf(sc[kt][4], sc[kt][5]), fmaxf(sc[kt][6], sc[kt][7])));
+            // IEEE maximum (NaN-propagating): three-operand instructions
+            // that need no canonicalization of the matrix results, unlike fmaxf
+            float mx = __builtin_elementwise_maximum(
+                __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[kt][0], sc[kt][1]),
+                                              __builtin_elementwise_maximum(sc[kt][2], sc[kt][3])),
+                __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[kt][4], sc[kt][5]),
+                                              __builtin_elementwise_maximum(sc[kt][6], sc[kt][7])));
             mx = max_over_lane_groups(mx) * qscale;
             const bool raise = __ballot(mx > m_run[kt] + kRescaleSlack) != 0;  // uniform
             const float m_new = raise ? fmaxf(m_run[kt], mx) : m_run[kt];
             alpha = __builtin_amdgcn_exp2f(m_run[kt] - m_new);  // 1 unless raised
             m_run[kt] = m_new;
             l_part[kt] *= alpha;
-            float pv[8];
+            float pv[8];  // pv[e]: token 8r + e (key_token order)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][e], qscale, -m_new));
                 l_part[kt] += pv[e];
             }
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                to_value_order(pv[jj], pv[4 + jj]);  // pv[e] is now token 8r + e
             // hi = bf16(p) two at a time; lo = bf16(p - hi), with hi read back
             // from the packed pair by shifts (exact)
             u32x4 hw, lw;
@@ -436,13 +447,13 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         }
     } else {
         // ---- direct global-to-LDS loads, two units ahead, three stages ----
-        // This thread's slots: key slot p = tid + 256 k is chunk p / 32 of
-        // token p % 32 = tid % 32; value slot p is row d = p / 4, holding
+        // This thread's slots: key slot p = tid + 256 k is chunk p / 32 at
+        // position p % 32 = tid % 32, token key_token(tid % 32); value slot p is row d = p / 4, holding
         // tokens 8 q8 .. 8 q8 + 7 with q8 = (p % 4) ^ ((d / 4) % 4), the same
         // q8 for every k.
         constexpr int NP = (4 * HS) / kPfThreads;  // slots of each kind per thread
         constexpr int NDMA = 2 * NP;               // load instructions per wave per unit
-        const int tK = tid % kPfUnit;
+        const int tK = key_token(tid % kPfUnit);
         const int q8 = (tid & 3) ^ ((tid >> 4) & 3);
         // Block IDs: a unit spans at most two table entries, j0 = 32 v / BS
         // and j0 + 1 (B = 16), read with scalar loads (uniform addresses) one
