@@ -101,6 +101,30 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0   # dense bf16 MFMA (fp8 pools are decoded to bf1
 MFMA_F32_PEAK_TFLOPS = 157.3
 
 
+def stream_read_ceiling(torch, pkv, nbytes: int = 2 << 30, reps: int = 20) -> dict:
+    """The GPU's practical read bandwidth: the library's streaming-read probe
+    over a 2 GiB buffer (best of two grid sizes, events around `reps` reads),
+    reported next to the kernels' rates as the ceiling they can approach."""
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    best = (0.0, 0)
+    for wg in (2048, 8192):
+        for _ in range(3):
+            pkv.probe_stream_read(buf, out, wg, stream=stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            pkv.probe_stream_read(buf, out, wg, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        gbps = nbytes * reps / (a.elapsed_time(b) / 1e3) / 1e9
+        best = max(best, (gbps, wg))
+    del buf, out
+    torch.cuda.empty_cache()
+    return {"gbps": round(best[0], 1), "work_groups": best[1], "bytes": nbytes}
+
+
 def multi_token_counts(w):
     """(KV bytes, attention flops) one multi-token step must move and do: each
     sequence's L cached tokens once per KV head (keys and values), plus the
@@ -179,12 +203,17 @@ def bench_multi_token(args, w, torch, pkv) -> dict:
     else:
         roof = {"bound": "mfma", "achieved": round(flops / t / 1e12, 2), "peak": peak_tf, "unit": "TFLOP/s",
                 "frac": round(flops / t / 1e12 / peak_tf, 4)}
-    roof.update({"traffic": None, "kernel": "paged_multi_token_attention: partition kernel (16-row causal tiles)"
-                 + (" + chunk merge kernel" if ws is not None else ""),
+    which = pkv.multi_token_kernel(d0["q"], d0["kc"], d0["vc"], d0["bt"], mql, P)
+    roof.update({"traffic": None, "kernel": "paged_multi_token_attention: " + (
+                     "unpartitioned kernel (128 rows per work-group, whole visible context)" if which == "unpartitioned"
+                     else "partition kernel (16-row causal tiles)" + (" + chunk merge kernel" if ws is not None else "")),
                  "algorithmic_bytes_per_launch": nbytes, "algorithmic_flops_per_launch": flops,
                  "arithmetic_intensity": round(flops / nbytes, 2), "ridge_flop_per_byte": round(ridge, 1),
                  "attained_tflops": round(flops / t / 1e12, 2), "attained_gbps": round(nbytes / t / 1e9, 1),
                  "launch_us": {"mean": round(t * 1e6, 2), "median": round(float(np.median(attn_ms)) * 1e3, 2)}})
+    if roof["bound"] == "hbm":
+        sr = stream_read_ceiling(torch, pkv)
+        roof.update({"stream_read": sr, "frac_of_stream_read": round(nbytes / t / 1e9 / sr["gbps"], 4)})
     return {"metric": "multi-token paged attention query tokens/s (chunked prefill / speculative decoding step)",
             "value": round(w.rows / (ms_step / 1e3), 1), "unit": "query tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
@@ -534,6 +563,9 @@ def main() -> int:
                 "launch_us": {"mean": round(attn_avg_s * 1e6, 2), "median": round(float(np.median(attn_ms)) * 1e3, 2),
                               "p10": round(float(np.percentile(attn_ms, 10)) * 1e3, 2),
                               "p90": round(float(np.percentile(attn_ms, 90)) * 1e3, 2)}}
+    # the measured read ceiling of this GPU, beside the 8 TB/s peak
+    sr = stream_read_ceiling(torch, pkv)
+    roofline.update({"stream_read": sr, "frac_of_stream_read": round(achieved / sr["gbps"], 4)})
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")

@@ -340,6 +340,15 @@ PKV_API pkv_status paged_decode_step(const void* q, const void* new_k, const voi
 #define PKV_PARTITION_NONE (-1)
 
 /*
+ * Which kernel paged_multi_token_attention runs for these sizes: 1 for the
+ * unpartitioned kernel, 0 for the partitioned one, -1 for sizes it rejects
+ * (invalid descriptor or head counts, or PKV_PARTITION_NONE where the
+ * unpartitioned kernel is not supported).
+ */
+PKV_API int32_t pkv_multi_token_kernel(int32_t num_seqs, int32_t num_q_heads, int32_t max_q_len,
+                                       const pkv_cache_desc* cache, int32_t partition_tokens);
+
+/*
  * Bytes of device workspace paged_multi_token_attention needs with the
  * partitioned kernel (0 when each sequence's table fits one chunk of
  * partitions; the unpartitioned kernel needs none): one fp32 partial per
@@ -528,6 +537,27 @@ PKV_API int32_t pkv_pool_block_table(const pkv_block_pool* pool, int64_t seq, in
 PKV_API pkv_status pkv_pool_export(const pkv_block_pool* pool, const int64_t* seqs, int32_t num_seqs,
                                    int32_t max_blocks_per_seq, int32_t pad_block, int32_t* block_tables,
                                    int32_t* seq_lens);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Measurement aid
+ * ---------------------------------------------------------------------------
+ *
+ * Streaming-read probe: reads `bytes` of the device buffer `buf` once with
+ * `work_groups` work-groups of 256 threads (each the next contiguous share,
+ * eight 16-byte non-temporal loads in flight per thread), so that a caller
+ * timing it gets the GPU's practical read bandwidth, the ceiling of the
+ * bandwidth-bound kernels above.  Not part of the attention method.
+ *   buf          device buffer, 16-byte aligned; bytes a multiple of 16
+ *   out          device buffer of 4 bytes; a thread writes 0x9E3779B9 there
+ *                when the XOR of the 32-bit words it read equals that value
+ *                (so that no load can be dropped), and nothing otherwise
+ *   work_groups  1 .. 1048576
+ * Asynchronous on `stream`.  PKV_ERR_INVALID_ARG for a null or misaligned
+ * pointer, a size that is not a multiple of 16, or work_groups out of range.
+ */
+PKV_API pkv_status pkv_probe_stream_read(const void* buf, size_t bytes, void* out, int32_t work_groups,
+                                         void* stream);
 
 #ifdef __cplusplus
 }

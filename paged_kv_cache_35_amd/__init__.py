@@ -103,6 +103,10 @@ def library():
         L.paged_multi_token_step.argtypes = [P, P, P, P, P, P, i32, i32, P, P, i32, i32, i32,
                                              ctypes.POINTER(CacheDesc), f32, P, P, P, sz, i32, P]
         L.pkv_copy_blocks.argtypes = [P, i32, ctypes.POINTER(CacheDesc), P, P, P]
+        L.pkv_multi_token_kernel.restype = i32
+        L.pkv_multi_token_kernel.argtypes = [i32, i32, i32, ctypes.POINTER(CacheDesc), i32]
+        L.pkv_probe_stream_read.restype = i32
+        L.pkv_probe_stream_read.argtypes = [P, sz, P, i32, P]
         L.pkv_pool_create.restype = P
         L.pkv_pool_create.argtypes = [i32, i32]
         L.pkv_pool_create_with_free_list.restype = P
@@ -404,6 +408,18 @@ def alloc_multi_token_workspace(q: torch.Tensor, k_cache: torch.Tensor, v_cache:
     return torch.empty(n, dtype=torch.uint8, device=q.device)
 
 
+def multi_token_kernel(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                       max_q_len: int, partition_tokens: int = 0) -> str:
+    """'unpartitioned' or 'partitioned': the kernel paged_multi_token_attention
+    runs for these sizes."""
+    desc = cache_desc(k_cache, v_cache)
+    k = library().pkv_multi_token_kernel(block_tables.shape[0], q.shape[1], int(max_q_len), ctypes.byref(desc),
+                                         int(partition_tokens))
+    if k < 0:
+        raise ValueError("these sizes are rejected by paged_multi_token_attention")
+    return "unpartitioned" if k == 1 else "partitioned"
+
+
 def multi_token_step_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size, max_q_len, max_blocks_per_seq,
                                      block_size, partition_tokens=0) -> int:
     return int(library().pkv_multi_token_step_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size,
@@ -543,6 +559,17 @@ def paged_multi_token_step(q: torch.Tensor, new_k: torch.Tensor, new_v: torch.Te
         S, Hq, block_tables.shape[1], ctypes.byref(desc), float(scale), _dev(out, "out"),
         _dev(slot_mapping, "slot_mapping"), ws_ptr, ws_bytes, int(partition_tokens), _stream(stream)))
     return out
+
+
+def probe_stream_read(buf: torch.Tensor, out: torch.Tensor, work_groups: int, stream=None) -> None:
+    """One streaming read of the whole of `buf` (a measurement aid: time it to
+    get the GPU's practical read bandwidth); `out` is a 4-byte device buffer."""
+    if not buf.is_contiguous() or (buf.numel() * buf.element_size()) % 16 != 0:
+        raise ValueError("buf must be contiguous and a multiple of 16 bytes")
+    if out.numel() * out.element_size() < 4:
+        raise ValueError("out must hold 4 bytes")
+    _check("pkv_probe_stream_read", library().pkv_probe_stream_read(
+        _dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(out, "out"), int(work_groups), _stream(stream)))
 
 
 def copy_blocks(pairs: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:

@@ -490,13 +490,21 @@ namespace {
 constexpr int64_t kPrefillMinRows = 64;
 constexpr int64_t kPrefillMinGroups = 512;
 
-bool picks_prefill(const pkv::DecodeArgs& a, int32_t partition_tokens)
+bool picks_prefill_sizes(int32_t dtype, int32_t block_size, int32_t head_size, int64_t num_seqs,
+                         int64_t num_q_heads, int64_t num_kv_heads, int64_t max_q_len, int32_t partition_tokens)
 {
-    const int64_t G = a.num_q_heads / a.num_kv_heads;
     if (partition_tokens == PKV_PARTITION_NONE)
         return true;
-    return partition_tokens == 0 && pkv::prefill_supported(a) && (int64_t)a.max_q_len * G >= kPrefillMinRows &&
-           pkv::prefill_work_groups(a) >= kPrefillMinGroups && pkv::prefill_work_groups(a) <= INT32_MAX;
+    const int64_t G = num_q_heads / num_kv_heads;
+    const int64_t wgs = pkv::prefill_work_groups(num_seqs, num_q_heads, num_kv_heads, max_q_len);
+    return partition_tokens == 0 && pkv::prefill_shape_supported(dtype, block_size, head_size) &&
+           max_q_len * G >= kPrefillMinRows && wgs >= kPrefillMinGroups && wgs <= INT32_MAX;
+}
+
+bool picks_prefill(const pkv::DecodeArgs& a, int32_t partition_tokens)
+{
+    return picks_prefill_sizes(a.dtype, a.block_size, a.head_size, a.num_seqs, a.num_q_heads, a.num_kv_heads,
+                               a.max_q_len, partition_tokens);
 }
 
 hipError_t launch_multi_token(const pkv::DecodeArgs& a, int32_t partition_tokens, hipStream_t stream)
@@ -578,6 +586,21 @@ pkv_status paged_multi_token_attention(const void* q, const int32_t* q_start, in
     if (used)
         use_schedule(a, p, partition_tokens);
     return hip_status(launch_multi_token(a, partition_tokens, (hipStream_t)stream));
+}
+
+int32_t pkv_multi_token_kernel(int32_t num_seqs, int32_t num_q_heads, int32_t max_q_len,
+                               const pkv_cache_desc* cache, int32_t partition_tokens)
+{
+    if (check_cache(cache) != PKV_OK || num_seqs < 0 || num_q_heads <= 0 || max_q_len < 0 ||
+        num_q_heads % cache->num_kv_heads != 0 || partition_tokens < PKV_PARTITION_NONE)
+        return -1;
+    if (partition_tokens == PKV_PARTITION_NONE &&
+        !pkv::prefill_shape_supported(cache->dtype, cache->block_size, cache->head_size))
+        return -1;
+    return picks_prefill_sizes(cache->dtype, cache->block_size, cache->head_size, num_seqs, num_q_heads,
+                               cache->num_kv_heads, max_q_len, partition_tokens)
+               ? 1
+               : 0;
 }
 
 size_t pkv_multi_token_step_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -704,6 +727,15 @@ pkv_status pkv_copy_blocks(const int32_t* pairs, int32_t num_pairs, const pkv_ca
         (int64_t)cache->num_kv_heads * cache->block_size * cache->head_size * elem_bytes(cache->dtype);
     return hip_status(pkv::launch_copy_blocks(pairs, num_pairs, cache->num_blocks, block_bytes, k_cache, v_cache,
                                               (hipStream_t)stream));
+}
+
+pkv_status pkv_probe_stream_read(const void* buf, size_t bytes, void* out, int32_t work_groups, void* stream)
+{
+    if (!buf || !out || !aligned16(buf) || bytes % 16 != 0 || work_groups < 1 || work_groups > (1 << 20))
+        return PKV_ERR_INVALID_ARG;
+    if (bytes == 0)
+        return PKV_OK;
+    return hip_status(pkv::launch_stream_read(buf, bytes, out, work_groups, (hipStream_t)stream));
 }
 
 }  // extern "C"

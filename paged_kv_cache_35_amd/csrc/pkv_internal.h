@@ -75,11 +75,17 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Streaming-read probe (probe.hip): reads bytes (a multiple of 16) of buf
+// with work_groups work-groups; out receives at most one 4-byte marker.
+hipError_t launch_stream_read(const void* buf, size_t bytes, void* out, int32_t work_groups, hipStream_t stream);
+
 // Multi-token attention with many rows per (sequence, KV head): the
 // prefill kernel (prefill.hip) takes 128 rows per work-group over the whole
 // visible context, no partitions and no workspace.  Supported for bf16 and
 // FP8 pools with blocks of 16 tokens or more.
+bool prefill_shape_supported(int32_t dtype, int32_t block_size, int32_t head_size);
 bool prefill_supported(const DecodeArgs& a);
+int64_t prefill_work_groups(int64_t num_seqs, int64_t num_q_heads, int64_t num_kv_heads, int64_t max_q_len);
 int64_t prefill_work_groups(const DecodeArgs& a);
 hipError_t launch_prefill(const DecodeArgs& a, hipStream_t stream);
 

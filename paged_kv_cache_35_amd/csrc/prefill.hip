@@ -570,16 +570,25 @@ static hipError_t launch_prefill_block(const DecodeArgs& a, hipStream_t stream)
     }
 }
 
+bool prefill_shape_supported(int32_t dtype, int32_t block_size, int32_t head_size)
+{
+    return (dtype == 1 || dtype == 2) && block_size >= 16 && (head_size == 64 || head_size == 128);
+}
+
+int64_t prefill_work_groups(int64_t num_seqs, int64_t num_q_heads, int64_t num_kv_heads, int64_t max_q_len)
+{
+    const int64_t G = num_q_heads / num_kv_heads;
+    return num_seqs * num_kv_heads * ((max_q_len * G + kPfRows - 1) / kPfRows);
+}
+
 bool prefill_supported(const DecodeArgs& a)
 {
-    return (a.dtype == 1 || a.dtype == 2) && a.block_size >= 16 && (a.head_size == 64 || a.head_size == 128) &&
-           a.q_start != nullptr;
+    return prefill_shape_supported(a.dtype, a.block_size, a.head_size) && a.q_start != nullptr;
 }
 
 int64_t prefill_work_groups(const DecodeArgs& a)
 {
-    const int64_t G = a.num_q_heads / a.num_kv_heads;
-    return (int64_t)a.num_seqs * a.num_kv_heads * ((a.max_q_len * G + kPfRows - 1) / kPfRows);
+    return prefill_work_groups(a.num_seqs, a.num_q_heads, a.num_kv_heads, a.max_q_len);
 }
 
 hipError_t launch_prefill(const DecodeArgs& a, hipStream_t stream)

@@ -215,6 +215,39 @@ def test_multi_token_step_workspace_sizes(lib):
     assert f(16, 32, 8, 128, 0, 1024, 16, 0) == 0
 
 
+def test_multi_token_kernel_choice(lib):
+    f = lib.pkv_multi_token_kernel
+    bf16 = desc(hkv=8, hs=128, dtype=1)
+    # 512 query tokens x G = 4 on 256 sequences: the unpartitioned kernel
+    assert f(256, 32, 512, ctypes.byref(bf16), 0) == 1
+    # 4 draft tokens (16 rows per KV head): the partitioned kernel
+    assert f(256, 32, 4, ctypes.byref(bf16), 0) == 0
+    # too few work-groups (2 sequences x 8 KV heads x 16 row blocks)
+    assert f(2, 32, 512, ctypes.byref(bf16), 0) == 0
+    # a requested partition length always selects the partitioned kernel
+    assert f(256, 32, 512, ctypes.byref(bf16), 512) == 0
+    # PKV_PARTITION_NONE: the unpartitioned kernel where it is supported
+    assert f(4, 32, 4, ctypes.byref(bf16), -1) == 1
+    assert f(4, 32, 4, ctypes.byref(desc(hkv=8, hs=128, dtype=0)), -1) == -1   # fp32 pools
+    assert f(4, 32, 4, ctypes.byref(desc(hkv=8, hs=128, B=8, dtype=1)), -1) == -1
+    assert f(256, 32, 512, ctypes.byref(desc(hkv=8, hs=128, dtype=0)), 0) == 0  # fp32: partitioned
+    # rejected sizes
+    assert f(4, 30, 4, ctypes.byref(bf16), 0) == -1
+    assert f(4, 32, 4, None, 0) == -1
+    assert f(4, 32, 4, ctypes.byref(bf16), -2) == -1
+
+
+def test_stream_probe_rejects_bad_arguments(lib):
+    f = lib.pkv_probe_stream_read
+    assert f(None, 1024, FAKE, 64, None) == INVALID
+    assert f(FAKE, 1024, None, 64, None) == INVALID
+    assert f(ctypes.c_void_p(0x10008), 1024, FAKE, 64, None) == INVALID
+    assert f(FAKE, 1000, FAKE, 64, None) == INVALID
+    assert f(FAKE, 1024, FAKE, 0, None) == INVALID
+    assert f(FAKE, 1024, FAKE, (1 << 20) + 1, None) == INVALID
+    assert f(FAKE, 0, FAKE, 64, None) == OK  # nothing to read
+
+
 def test_multi_token_workspace_sizes(lib):
     f = lib.pkv_multi_token_workspace_bytes
     # one chunk covers the table: none
