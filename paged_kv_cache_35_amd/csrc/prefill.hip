@@ -408,10 +408,17 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         // tile 0, then tile 1's softmax (vector work) written next to tile
         // 0's value sum (matrix work) so the two can be issued interleaved;
         // tile 1's rescale waits until after that
+        // The value sums (and tile 1's softmax between them) run at raised
+        // wave priority: of the two waves sharing a SIMD, the one with
+        // matrix work ready issues it first while the other computes its
+        // scores and softmax, which keeps the matrix pipe busier (measured
+        // 3 to 5 % faster on 512-token chunks; priority over the scores as
+        // well, or over tile 0's value sum only, was not faster).
         bf16x8 hi0, lo0, hi1, lo1;
         float a0, a1;
         if (softmax(0, hi0, lo0, a0))
             rescale_tile(0, a0);
+        __builtin_amdgcn_s_setprio(1);
         value_sum(0, hi0, lo0);
         const bool raise1 = softmax(1, hi1, lo1, a1);
 #pragma unroll
@@ -422,6 +429,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         if (raise1)
             rescale_tile(1, a1);
         value_sum(1, hi1, lo1);
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // ---- the unit loop: fetch u+1 while computing u, one barrier per unit ----
