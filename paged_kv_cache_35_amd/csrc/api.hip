@@ -26,14 +26,12 @@ int elem_bytes(int32_t dtype) { return dtype == PKV_F32 ? 4 : (dtype == PKV_FP8_
 
 size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
 
-// Library choice of the context-partition length: PKV_DEFAULT_PARTITION_TOKENS
+// Library choice of the context-partition length: kDefaultPartitionTokens
 // (512: 32 blocks at B = 16, 16 at B = 32), at most 64 blocks (one block ID
 // per lane of the wave), or one partition when the table is shorter.  Blocks
 // of fewer than 16 tokens are read in 16-token units that must not straddle
 // two partitions: the length is then a multiple of 16.
-#ifndef PKV_DEFAULT_PARTITION_TOKENS
-#define PKV_DEFAULT_PARTITION_TOKENS 512
-#endif
+constexpr int64_t kDefaultPartitionTokens = 512;
 int32_t resolve_partition_tokens(int32_t max_blocks_per_seq, int32_t block_size, int32_t requested)
 {
     if (requested < 0 || max_blocks_per_seq <= 0 || block_size <= 0)
@@ -44,7 +42,7 @@ int32_t resolve_partition_tokens(int32_t max_blocks_per_seq, int32_t block_size,
         return requested;
     }
     const int64_t whole = (int64_t)max_blocks_per_seq * block_size;
-    const int64_t dflt = PKV_DEFAULT_PARTITION_TOKENS < 64 * block_size ? PKV_DEFAULT_PARTITION_TOKENS : 64 * block_size;
+    const int64_t dflt = kDefaultPartitionTokens < 64 * block_size ? kDefaultPartitionTokens : 64 * block_size;
     return (int32_t)(whole < dflt ? whole : dflt);
 }
 

@@ -101,36 +101,12 @@ struct WideRegs {
     bf16x8 v[HS / 16];
 };
 
-
-
 // K/V tiles are read exactly once per call: streaming (non-temporal) loads
 // keep them from displacing reusable lines (queries, tables, partials).
-#ifndef PKV_STREAMING_LOADS
-#define PKV_STREAMING_LOADS 1
-#endif
-
-#ifndef PKV_STREAMING_V
-#define PKV_STREAMING_V PKV_STREAMING_LOADS
-#endif
-
 template <typename V>
 __device__ __forceinline__ V load_stream(const V* p)
 {
-#if PKV_STREAMING_LOADS
     return __builtin_nontemporal_load(p);
-#else
-    return *p;
-#endif
-}
-
-template <typename V>
-__device__ __forceinline__ V load_stream_v(const V* p)
-{
-#if PKV_STREAMING_V
-    return __builtin_nontemporal_load(p);
-#else
-    return *p;
-#endif
 }
 
 // Issue the loads of 16-token sub-tile m of one (block, KV head) tile.
@@ -151,9 +127,9 @@ __device__ __forceinline__ void load_tile(TileRegs<T, HS>& t, const T* __restric
 #pragma unroll
     for (int i = 0; i < HS / 16; ++i) {  // head dim 16i + c, tokens 16m + 4r .. +3
         if constexpr (sizeof(T) == 2)
-            t.v.v[i] = load_stream_v((const bf16x4*)(tile_v + (16 * i + c) * BS + 16 * m + 4 * r));
+            t.v.v[i] = load_stream((const bf16x4*)(tile_v + (16 * i + c) * BS + 16 * m + 4 * r));
         else
-            t.v.v[i] = load_stream_v((const f32x4*)(tile_v + (16 * i + c) * BS + 16 * m + 4 * r));
+            t.v.v[i] = load_stream((const f32x4*)(tile_v + (16 * i + c) * BS + 16 * m + 4 * r));
     }
 }
 
@@ -188,7 +164,7 @@ __device__ __forceinline__ int load_small(TileRegs<T, HS>& t, const T* __restric
         const T* vp = v_cache + block_at(tv / BS) + tv % BS;
 #pragma unroll
         for (int i = 0; i < HS / 16; ++i)
-            t.v.v[i] = load_stream_v((const VV*)(vp + (16 * i + c) * BS));
+            t.v.v[i] = load_stream((const VV*)(vp + (16 * i + c) * BS));
     } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -196,7 +172,7 @@ __device__ __forceinline__ int load_small(TileRegs<T, HS>& t, const T* __restric
             const T* vp = v_cache + block_at(tv / BS) + tv % BS;
 #pragma unroll
             for (int i = 0; i < HS / 16; ++i)
-                t.v.v[i][j] = load_stream_v(vp + (16 * i + c) * BS);
+                t.v.v[i][j] = load_stream(vp + (16 * i + c) * BS);
         }
     }
     int tmask = 0;
@@ -257,9 +233,8 @@ __device__ __forceinline__ void load_fp8(Fp8Regs<HS>& t, const uint8_t* __restri
         t.k[i] = load_stream((const u32x4*)(tile_k + ((4 * i + r) * BS + 16 * m + c) * 16));
 #pragma unroll
     for (int i = 0; i < HS / 16; ++i)
-        t.v[i] = load_stream_v((const unsigned*)(tile_v + (16 * i + c) * BS + 16 * m + 4 * r));
+        t.v[i] = load_stream((const unsigned*)(tile_v + (16 * i + c) * BS + 16 * m + 4 * r));
 }
-
 
 template <int HS>
 __device__ __forceinline__ void fp8_to_operands(const Fp8Regs<HS>& raw, TileRegs<__bf16, HS>& t)
@@ -284,10 +259,11 @@ __device__ __forceinline__ void fp8_to_operands(const Fp8Regs<HS>& raw, TileRegs
     }
 }
 
-// FP8 pools with B >= 32: 32-token units, like the bf16 32-token path.  Key M-tile mp holds tokens 16mp .. 16mp+15 (chunk 4i + r
-// of token 16mp + c; two 128-byte lines per lane group); the value operand is
-// 8 codes per lane, tokens 8r .. 8r+7 of head dim 16i + c (the four lane
-// groups read the dim's whole 32-byte row).
+// FP8 pools with B >= 32: 32-token units, like the bf16 32-token path.  Key
+// M-tile mp holds tokens 16mp .. 16mp+15 (chunk 4i + r of token 16mp + c;
+// two 128-byte lines per lane group); the value operand is 8 codes per lane,
+// tokens 8r .. 8r+7 of head dim 16i + c (the four lane groups read the dim's
+// whole 32-byte row).
 template <int HS>
 struct Fp8WideRegs {
     u32x4 k[2][HS / 64];
@@ -458,7 +434,8 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     __shared__ float sm_m[NW][16];
     __shared__ float sm_l[NW][16];
     __shared__ int sm_pick;
-    static_assert(kLptMaxSeqs <= NW * 16 * HS && kLptMaxSeqs <= 256, "the length ranking reuses the merge buffer and keeps the index in 8 bits");
+    static_assert(kLptMaxSeqs <= NW * 16 * HS && kLptMaxSeqs <= 256,
+                  "the length ranking reuses the merge buffer and keeps the index in 8 bits");
 
     // Work-group -> (KV head, row tile, rank y, chunk).  With the schedule's
     // chunk list (1-D grid, large batches): work-group x takes (KV head, row
@@ -909,7 +886,8 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
         acc *= inv;
         if (nchunks == 1) {
             // without MQ the group's G heads are adjacent rows of out
-            T* dst = out + (MQ ? out_row(16 * rt + g) + (4 * e) % HS : ((int64_t)s * Hq + (int64_t)kvh * G) * HS + 4 * e);
+            T* dst = out + (MQ ? out_row(16 * rt + g) + (4 * e) % HS
+                               : ((int64_t)s * Hq + (int64_t)kvh * G) * HS + 4 * e);
             if constexpr (sizeof(T) == 2) {
                 bf16x4 v;
 #pragma unroll

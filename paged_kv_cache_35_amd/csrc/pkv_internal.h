@@ -10,23 +10,17 @@ namespace pkv {
 
 // Waves per work-group of the partition kernel: each wave attends over one
 // context partition and the work-group merges its NW partitions, so one
-// work-group covers a chunk of NW partitions (compile-time tuning knob).
-#ifndef PKV_DECODE_WAVES
-#define PKV_DECODE_WAVES 4
-#endif
-constexpr int kDecodeWaves = PKV_DECODE_WAVES;
+// work-group covers a chunk of NW partitions.
+constexpr int kDecodeWaves = 4;
 
 // A stand-alone attention call on up to this many sequences is scheduled
 // longest first by the attention kernel itself (each work-group ranks all
 // lengths: O(S^2 / threads) work, which outweighs the gain on larger batches).
-#ifndef PKV_LPT_MAX_SEQS
-#define PKV_LPT_MAX_SEQS 64
-#endif
+constexpr int kLptMaxSeqs = 64;
 // The decode step's append launch writes a longest-first schedule for
 // batches of up to this many sequences (each of its work-groups reads all
 // lengths once).
 constexpr int kScheduleMaxSeqs = 4096;
-constexpr int kLptMaxSeqs = PKV_LPT_MAX_SEQS;
 
 // Problem description shared by the decode launchers; every field has been
 // validated on the host before a launcher sees it.
@@ -68,7 +62,8 @@ struct DecodeArgs {
     int32_t dtype;            // pkv_dtype
     int32_t partition_blocks; // blocks per context partition (<= 64), one wave each
     int32_t max_parts;        // chunks per sequence: ceil(max_blocks_per_seq / (partition_blocks * kDecodeWaves))
-    int32_t interleave;       // 1: a chunk's blocks dealt round-robin to its waves; 0: one contiguous partition per wave
+    int32_t interleave;       // 1: a chunk's blocks dealt round-robin to its waves;
+                              // 0: one contiguous partition per wave
     float scale;
     float k_scale, v_scale;   // FP8 pools: stored code * scale (1 otherwise)
 };
