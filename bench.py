@@ -59,6 +59,7 @@ def parse():
     ap.add_argument("--contiguous", action="store_true",
                     help="diagnostic: each sequence's blocks adjacent in the pool (paged vs contiguous storage)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the graph-replay timing of the decode step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--traffic", type=str, default=None,
                     help="record of measured HBM bytes per attention launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, "
@@ -546,6 +547,37 @@ def main() -> int:
     attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
     log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, attention median {np.median(attn_ms) * 1e3:.1f} us")
 
+    # the same steps replayed from a HIP graph (one step per input copy),
+    # as a serving loop would run them: reported beside the eager figure
+    graph_info = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for d in copies:
+                    pkv.paged_decode_step(d["q"], d["nk"], d["nv"], d["kc"], d["vc"], d["bt"], d["sl"], w.scale,
+                                          out=out, slot_mapping=slots, workspace=ws_step, partition_tokens=P,
+                                          stream=side, **sc)
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // len(copies))
+        for _ in range(2):
+            g.replay()
+        # replay() launches on the current stream: time it there
+        ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ga.record(stream)
+        for _ in range(reps):
+            g.replay()
+        gb.record(stream)
+        torch.cuda.synchronize()
+        g_ms = ga.elapsed_time(gb) / (reps * len(copies))
+        graph_info = {"ms_per_step": round(g_ms, 5), "kv_read_gbps": round(w.kv_read_bytes() / (g_ms / 1e3) / 1e9, 1),
+                      "steps": reps * len(copies)}
+        del g
+        log(f"graph replay: {g_ms * 1e3:.1f} us/step")
+
     kv_bytes = w.kv_read_bytes()
     attn_avg_s = float(attn_ms.mean()) / 1e3
     achieved = kv_bytes / attn_avg_s / 1e9
@@ -592,6 +624,7 @@ def main() -> int:
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s": round(w.S / (ms_step / 1e3), 1),
         "attention_calls_per_s": round(1.0 / attn_avg_s, 1),
+        "graph_replay": graph_info,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
