@@ -418,10 +418,13 @@ def measured_traffic(path, config: int, partition_tokens: int, contiguous: bool)
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, target_s: float) -> dict:
+def cpu_baseline(w, target_s: float, gpu=None) -> dict:
     """Time the CPU oracle (fp64, as it stands) on the workload's attention:
     whole passes over every (sequence, query head), repeated until about
-    target_s seconds of wall time have passed."""
+    target_s seconds of wall time have passed.  gpu: (out, k_cache, v_cache)
+    of the timed GPU run on the same inputs; its output is then compared with
+    the last pass's and its pools with the oracle's appended pools, byte for
+    byte (returned under "parity")."""
     import oracle
 
     slots = oracle.decode_slot_mapping(w.block_tables, w.seq_lens, w.B)
@@ -436,19 +439,36 @@ def cpu_baseline(w, target_s: float) -> dict:
     t0 = time.perf_counter()
     while True:
         if w.dtype == "fp8":
-            oracle.paged_attention_fp8(w.q, kp, vp, w.block_tables, w.seq_lens, w.scale, w.k_scale, w.v_scale)
+            ref = oracle.paged_attention_fp8(w.q, kp, vp, w.block_tables, w.seq_lens, w.scale, w.k_scale, w.v_scale)
         else:
-            _, used = oracle.paged_attention(w.q, kp, vp, w.block_tables, w.seq_lens, w.scale,
-                                             return_threads=True)
+            ref, used = oracle.paged_attention(w.q, kp, vp, w.block_tables, w.seq_lens, w.scale,
+                                               return_threads=True)
         passes += 1
         if time.perf_counter() - t0 >= target_s:
             break
     el = time.perf_counter() - t0
     bytes_read = passes * w.kv_read_bytes()
-    return {"value": round(bytes_read / el / 1e9, 4), "unit": "GB/s", "cores": int(used), "kind": "oracle",
-            "sample": f"{passes} full passes of the workload's attention (all {w.S} sequences x {w.Hq} query "
-                      f"heads), fp64 C oracle with OpenMP, {el:.1f} s wall on {used} threads; "
-                      f"same KV-byte accounting as value"}
+    res = {"value": round(bytes_read / el / 1e9, 4), "unit": "GB/s", "cores": int(used), "kind": "oracle",
+           "sample": f"{passes} full passes of the workload's attention (all {w.S} sequences x {w.Hq} query "
+                     f"heads), fp64 C oracle with OpenMP, {el:.1f} s wall on {used} threads; "
+                     f"same KV-byte accounting as value"}
+    if gpu is not None:
+        import torch
+
+        out, kc, vc = gpu
+
+        def host_bytes(t):
+            return (t.view(torch.int16) if t.dtype == torch.bfloat16 else t).cpu().numpy().tobytes()
+
+        err = float(np.abs(out.float().cpu().numpy().astype(np.float64) - ref).max())
+        tol = 1e-5 if w.dtype == "f32" else 2e-3
+        res["parity"] = {
+            "max_abs_err": err, "tolerance": tol, "within_tolerance": err <= tol,
+            "append_bit_exact": host_bytes(kc) == np.ascontiguousarray(kp).tobytes()
+            and host_bytes(vc) == np.ascontiguousarray(vp).tobytes(),
+            "checked": "the timed run's output (every sequence and query head) against the last oracle pass, "
+                       "and both pools of its first input copy byte for byte against the oracle's append"}
+    return res
 
 
 def main() -> int:
@@ -512,9 +532,10 @@ def main() -> int:
 
     def step_timed(ev):
         # the same step through the two entry points it is made of, with
-        # events around the attention launch
+        # events around the append launch and around the attention launch
         d = copies[turn[0] % len(copies)]
         turn[0] += 1
+        ev[2].record(stream)
         pkv.decode_append(d["nk"], d["nv"], d["bt"], d["sl"], d["kc"], d["vc"], slot_mapping=slots, schedule=sched,
                           stream=stream, **sc)
         ev[0].record(stream)
@@ -539,12 +560,13 @@ def main() -> int:
     ms_step = start.elapsed_time(end) / args.steps
 
     # the attention call alone, bracketed by events on the same stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     for e in evs:
         step_timed(e)
     torch.cuda.synchronize()
-    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    append_ms = np.array([e[2].elapsed_time(e[0]) for e in evs])
     log(f"timed {args.steps} steps: {ms_step * 1e3:.1f} us/step, attention median {np.median(attn_ms) * 1e3:.1f} us")
 
     # the same steps replayed from a HIP graph (one step per input copy),
@@ -601,7 +623,8 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample")
-        cpu = cpu_baseline(pi.make_workload(args.config, mode="timing", dtype=kvdt, **bkw), args.cpu_seconds)
+        cpu = cpu_baseline(pi.make_workload(args.config, mode="timing", contiguous=args.contiguous, dtype=kvdt,
+                                            **bkw), args.cpu_seconds, gpu=(out, copies[0]["kc"], copies[0]["vc"]))
     value = kv_bytes / (ms_step / 1e3) / 1e9
     rec = {
         "metric": "paged decode attention KV-read GB/s (% of HBM peak) + decode tokens/s, 1 GPU",
@@ -624,6 +647,8 @@ def main() -> int:
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s": round(w.S / (ms_step / 1e3), 1),
         "attention_calls_per_s": round(1.0 / attn_avg_s, 1),
+        "append_us": {"mean": round(float(append_ms.mean()) * 1e3, 2),
+                      "median": round(float(np.median(append_ms)) * 1e3, 2)},
         "graph_replay": graph_info,
         "roofline": roofline,
         "cpu_baseline": cpu,
