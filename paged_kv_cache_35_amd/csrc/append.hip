@@ -58,7 +58,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // The loads (every length, the row) do not depend on the rank, so they are
 // issued when the work-group starts, together with the token's loads; the
 // first kSchedRegs * 256 lengths and row entries are held in registers and
-// the rest, if any, read in a loop at the end.
+// the rest, if any, read at the end.
 constexpr int kSchedRegs = 4;
 
 struct SchedulePrefetch {
@@ -166,9 +166,22 @@ __device__ void write_schedule(const SchedulePrefetch& p, int32_t i, int32_t S,
         if (m < M)
             dst[m] = p.row[t];
     }
+    // the rest of a long row: four independent loads in flight per thread
     const int32_t* src = block_tables + (int64_t)i * M;
-    for (int m = threadIdx.x + kSchedRegs * kAppendThreads; m < M; m += kAppendThreads)
-        dst[m] = src[m];
+    for (int m0 = threadIdx.x + kSchedRegs * kAppendThreads; m0 < M; m0 += 4 * kAppendThreads) {
+        int32_t v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int m = m0 + k * kAppendThreads;
+            v[k] = m < M ? src[m] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int m = m0 + k * kAppendThreads;
+            if (m < M)
+                dst[m] = v[k];
+        }
+    }
 }
 
 // Slots of the query rows of a multi-token call: row i of sequence s (n
