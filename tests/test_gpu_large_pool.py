@@ -81,3 +81,26 @@ def test_multi_token_step_past_2g_elements():
                                           partition_tokens=m.PARTITION_NONE)
     torch.cuda.synchronize()
     check_attention(w, host_f64(out_u), ref)
+
+
+def test_copy_blocks_past_2g_elements():
+    # copy-on-write copies between blocks past element 2^31: whole blocks of
+    # both pools, the other blocks untouched
+    w = pi.make_workload(3, S=2, len_lo=300, len_hi=600)
+    per_block = w.Hkv * w.hs * w.B
+    shift = (1 << 31) // per_block + 11
+    announce(f"block copies on pools of {(w.num_blocks + shift) * per_block} elements")
+    m = pkv()
+    kc, vc = big_pools(w, shift)
+    src = np.array([0, 5, w.num_blocks - 1]) + shift
+    dst = np.array([w.num_blocks - 2, 9, 3]) + shift
+    before_k, before_v = kc.clone(), vc.clone()
+    pairs = torch.from_numpy(np.stack([src, dst], 1).astype(np.int32)).cuda()  # [n, 2]
+    m.copy_blocks(pairs, kc, vc)
+    torch.cuda.synchronize()
+    bits = (lambda t: t.view(torch.int16))
+    for a, b in zip(src, dst):
+        assert torch.equal(bits(kc[b]), bits(before_k[a])) and torch.equal(bits(vc[b]), bits(before_v[a]))
+    untouched = [i for i in range(shift, shift + w.num_blocks) if i not in set(dst.tolist())][:4] + [shift - 1]
+    for i in untouched:
+        assert torch.equal(bits(kc[i]), bits(before_k[i])) and torch.equal(bits(vc[i]), bits(before_v[i]))
