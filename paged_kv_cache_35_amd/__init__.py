@@ -154,6 +154,12 @@ def _dev(t: torch.Tensor, name: str) -> int:
     return t.data_ptr()
 
 
+def _sched(schedule: Optional[torch.Tensor]):
+    if schedule is None:
+        return None, 0
+    return _dev(schedule, "schedule"), schedule.numel() * schedule.element_size()
+
+
 def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: float = 1.0,
                v_scale: float = 1.0) -> CacheDesc:
     """Descriptor of a key/value pool pair in the documented layouts (the
@@ -236,8 +242,7 @@ def decode_append(k: torch.Tensor, v: torch.Tensor, block_tables: torch.Tensor, 
         _dev(k, "k"), _dev(v, "v"), _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), S,
         block_tables.shape[1], ctypes.byref(desc), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(slot_mapping, "slot_mapping") if slot_mapping is not None else None,
-        _dev(schedule, "schedule") if schedule is not None else None,
-        schedule.numel() * schedule.element_size() if schedule is not None else 0, _stream(stream)))
+        *_sched(schedule), _stream(stream)))
     return slot_mapping
 
 
@@ -325,8 +330,7 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     _check("paged_decode_attention", library().paged_decode_attention(
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables"),
         _dev(seq_lens, "seq_lens"), S, Hq, M, ctypes.byref(desc), float(scale), _dev(out, "out"), ws_ptr, ws_bytes,
-        int(partition_tokens), _dev(schedule, "schedule") if schedule is not None else None,
-        schedule.numel() * schedule.element_size() if schedule is not None else 0, _stream(stream)))
+        int(partition_tokens), *_sched(schedule), _stream(stream)))
     return out
 
 
@@ -438,12 +442,6 @@ def alloc_multi_token_step_workspace(q: torch.Tensor, k_cache: torch.Tensor, v_c
     if n == 0:
         return None
     return torch.empty(n, dtype=torch.uint8, device=q.device)
-
-
-def _sched(schedule: Optional[torch.Tensor]):
-    if schedule is None:
-        return None, 0
-    return _dev(schedule, "schedule"), schedule.numel() * schedule.element_size()
 
 
 def _check_rows(q, q_start, block_tables, seq_lens, desc, k_cache):
