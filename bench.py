@@ -617,6 +617,11 @@ def main() -> int:
                 "launch_us": {"mean": round(attn_avg_s * 1e6, 2), "median": round(float(np.median(attn_ms)) * 1e3, 2),
                               "p10": round(float(np.percentile(attn_ms, 10)) * 1e3, 2),
                               "p90": round(float(np.percentile(attn_ms, 90)) * 1e3, 2)}}
+    # shared blocks (a shared prefix): the distinct bytes read, beside the logical ones
+    unique = w.unique_kv_bytes()
+    if unique < kv_bytes:
+        roofline.update({"unique_bytes_per_launch": unique,
+                         "achieved_unique_gbps": round(unique / attn_avg_s / 1e9, 1)})
     # the measured read ceiling of this GPU, beside the 8 TB/s peak
     sr = stream_read_ceiling(torch, pkv)
     roofline.update({"stream_read": sr, "frac_of_stream_read": round(achieved / sr["gbps"], 4)})
