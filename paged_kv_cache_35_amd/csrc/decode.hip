@@ -1036,6 +1036,58 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
     }
 }
 
+// Chunk merge for launches with few chunks per sequence (at most
+// kFewChunks): one wave per (sequence rank, query head) pair, persistent over
+// the pairs, each lane taking 4 consecutive head dims and summing the chunks
+// in increasing order; no LDS, no barrier.  (With many chunks, the work-group
+// of the kernel above spreads a pair's chunks over its threads instead.)
+constexpr int kFewChunks = 8;
+constexpr int kFewMergeWaves = 8192;
+
+template <typename T, int HS>
+__global__ __launch_bounds__(64) void paged_decode_reduce_few_kernel(
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sched_order,
+    const int32_t* __restrict__ sched_lens, int32_t S, int32_t M, int32_t BS, int32_t CB, int32_t Hq, int32_t Hkv,
+    int32_t max_parts, const float* __restrict__ ws_o, const float* __restrict__ ws_ml, T* __restrict__ out)
+{
+    constexpr int Q = HS / 4;  // lanes with work: 4 head dims each
+    const int G = Hq / Hkv;
+    const int64_t pairs = (int64_t)S * Hq;
+    for (int64_t pr = blockIdx.x; pr < pairs; pr += gridDim.x) {
+        const int y = (int)(pr / Hq);
+        const int h = (int)(pr - (int64_t)y * Hq);
+        const int s = sched_order ? sched_order[y] : y;
+        int L = sched_order ? sched_lens[y] : seq_lens[s];
+        L = L < 0 ? 0 : (L > M * BS ? M * BS : L);
+        const int nblk = (L + BS - 1) / BS;
+        const int nparts = (nblk + CB - 1) / CB;  // chunks of CB blocks
+        if (nparts <= 1 || threadIdx.x >= Q)
+            continue;  // single chunk: the partition kernel wrote this output
+        const int kvh = h / G;
+        const int g = h - kvh * G;
+        const int d = 4 * threadIdx.x;
+        const int64_t u0 = ((int64_t)s * Hkv + kvh) * max_parts;
+        float mx = -INFINITY;
+        for (int p = 0; p < nparts; ++p) {
+            const float2 ml = *(const float2*)(ws_ml + 2 * ((u0 + p) * G + g));
+            if (ml.y > 0.f)
+                mx = fmaxf(mx, ml.x);
+        }
+        float wsum = 0.f;
+        f32x4 acc = (f32x4)0.f;
+        for (int p = 0; p < nparts; ++p) {
+            const float2 ml = *(const float2*)(ws_ml + 2 * ((u0 + p) * G + g));
+            const float wgt = ml.y > 0.f ? ml.y * __builtin_amdgcn_exp2f(ml.x - mx) : 0.f;
+            wsum += wgt;
+            acc += wgt * *(const f32x4*)(ws_o + ((u0 + p) * G + g) * HS + d);
+        }
+        T* dst = out + ((int64_t)s * Hq + h) * HS + d;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            store_elem(dst + k, wsum > 0.f ? acc[k] / wsum : 0.f);
+    }
+}
+
 // Chunk merge for several query rows per sequence: one work-group per
 // (row tile, KV head, sequence), 16 threads per tile row, each owning 8
 // consecutive head dims (two 16-byte loads per partial).  The row's running
@@ -1133,6 +1185,12 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
                            dim3(256), 0, stream, a.seq_lens, a.max_blocks_per_seq, BS, a.partition_blocks * NW,
                            a.num_q_heads, a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, (T*)a.out, a.q_start,
                            a.num_q_rows, a.max_q_len, a.row_tiles);
+    else if (a.max_parts <= kFewChunks)
+        hipLaunchKernelGGL((paged_decode_reduce_few_kernel<T, HS>),
+                           dim3((unsigned)std::min<int64_t>((int64_t)a.num_q_heads * a.num_seqs, kFewMergeWaves)),
+                           dim3(64), 0, stream, a.seq_lens, a.sched_order, a.sched_lens, a.num_seqs,
+                           a.max_blocks_per_seq, BS, a.partition_blocks * NW, a.num_q_heads, a.num_kv_heads,
+                           a.max_parts, a.ws_o, a.ws_ml, (T*)a.out);
     else
         hipLaunchKernelGGL((paged_decode_reduce_kernel<T, HS>),
                            dim3((unsigned)std::min<int64_t>((int64_t)a.num_q_heads * a.num_seqs, kMergeGroups)),
