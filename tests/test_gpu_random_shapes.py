@@ -1,0 +1,103 @@
+"""Seeded random small shapes through the whole decode step and the whole
+multi-token step, against the oracle: element type, head size, block size,
+group size, batch size, lengths (with empty sequences, one-token ones and
+full tables) and partition length drawn from a fixed seed, so the cases are
+the same on every run.  Appends bit-exact, outputs within the bars."""
+import numpy as np
+import pytest
+
+import oracle
+import pkv_inputs as pi
+from test_gpu_parity import announce, check_attention, dev, host_bits, host_f64, pkv, same_bytes
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pkv().library()
+    torch.cuda.set_device(0)
+
+
+def draw_case(rng, multi, unpartitioned=False):
+    dtype = ["f32", "bf16", "bf16", "fp8"][rng.integers(4)]
+    if unpartitioned:
+        dtype = ["bf16", "fp8"][rng.integers(2)]
+    hs = [64, 128][rng.integers(2)]
+    blocks = [16, 32, 64] if (dtype == "fp8" or unpartitioned) else [1, 8, 16, 32, 64]
+    B = blocks[rng.integers(len(blocks))]
+    Hkv = [1, 2, 4, 8][rng.integers(4)]
+    G = [1, 2, 4, 8][rng.integers(4)]
+    S = int(rng.integers(1, 41))
+    cap = 1500 if B == 1 else 2500
+    lens = rng.integers(1, cap, S)
+    for k in range(S):  # some special lengths
+        u = rng.random()
+        lens[k] = 0 if u < 0.08 else (1 if u < 0.14 else (B if u < 0.2 else lens[k]))
+    if S > 1 and lens.max() == 0:
+        lens[0] = 5
+    # partition length: the library's, or a requested one that fits the block size
+    P = 0
+    if rng.random() < 0.4:
+        mult = B if B >= 16 else 16
+        P = int(mult * rng.integers(1, max(2, (64 * B) // mult + 1)))
+        P = min(P, 64 * B)
+    q_lens = None
+    if multi:
+        q_lens = [int(min(L, rng.integers(1, 24))) if L > 0 else 0 for L in lens]
+        if unpartitioned:
+            P = -1  # the unpartitioned kernel
+    return dict(dtype=dtype, hs=hs, B=B, Hkv=Hkv, Hq=Hkv * G, seq_lens=[int(x) for x in lens], q_lens=q_lens, P=P)
+
+
+_rng = np.random.default_rng(20260211)
+DECODE = [draw_case(_rng, False) for _ in range(24)]
+MULTI = [draw_case(_rng, True) for _ in range(12)] + [draw_case(_rng, True, unpartitioned=True) for _ in range(4)]
+
+
+def case_id(c):
+    return f"{c['dtype']}-hs{c['hs']}-B{c['B']}-{c['Hq']}x{c['Hkv']}-S{len(c['seq_lens'])}-P{c['P']}"
+
+
+def workload(c):
+    kw = dict(dtype=c["dtype"], hs=c["hs"], B=c["B"], Hq=c["Hq"], Hkv=c["Hkv"], seq_lens=c["seq_lens"])
+    if c["q_lens"] is not None:
+        kw["q_lens"] = c["q_lens"]
+    return pi.make_workload(3, **kw)
+
+
+@pytest.mark.parametrize("c", DECODE, ids=[case_id(c) for c in DECODE])
+def test_random_decode_step(c):
+    w = workload(c)
+    announce(f"random decode step {case_id(c)} lens={c['seq_lens']}")
+    m = pkv()
+    q, kc, vc, bt, sl = dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_tables), dev(w.seq_lens)
+    slots = torch.empty(w.S, dtype=torch.int64, device="cuda")
+    out = m.paged_decode_step(q, dev(w.new_k), dev(w.new_v), kc, vc, bt, sl, w.scale, slot_mapping=slots,
+                              partition_tokens=c["P"], k_scale=w.k_scale, v_scale=w.v_scale)
+    torch.cuda.synchronize()
+    ref_slots, kp, vp, ref = oracle.decode_step(w)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    assert same_bytes(host_bits(kc), kp) and same_bytes(host_bits(vc), vp)
+    check_attention(w, host_f64(out), ref)
+
+
+@pytest.mark.parametrize("c", MULTI, ids=[case_id(c) for c in MULTI])
+def test_random_multi_token_step(c):
+    w = workload(c)
+    announce(f"random multi-token step {case_id(c)} lens={c['seq_lens']} q_lens={c['q_lens']}")
+    m = pkv()
+    q, kc, vc, bt, sl, qs = (dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_tables), dev(w.seq_lens),
+                             dev(w.q_start))
+    slots = torch.empty(w.rows, dtype=torch.int64, device="cuda")
+    out = m.paged_multi_token_step(q, dev(w.new_k), dev(w.new_v), kc, vc, qs, w.max_q_len, bt, sl, w.scale,
+                                   slot_mapping=slots, partition_tokens=c["P"], k_scale=w.k_scale,
+                                   v_scale=w.v_scale)
+    torch.cuda.synchronize()
+    ref_slots, kp, vp, ref = oracle.multi_token_step(w)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+    assert same_bytes(host_bits(kc), kp) and same_bytes(host_bits(vc), vp)
+    check_attention(w, host_f64(out), ref)
