@@ -424,3 +424,35 @@ def test_step_full_config(cfg):
     ref = oracle.paged_attention_units(w.q, kp, vp, w.block_tables, w.seq_lens, w.scale, units)
     check_attention(w, host_f64(out).reshape(-1, w.hs)[units], ref)
     assert torch.isfinite(out.float()).all().item()
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_lengths_outside_the_table_are_clamped(cfg):
+    # caller contract violations the kernels must contain: a length above
+    # max_blocks_per_seq * B reads the whole table row (as that maximum), a
+    # negative length reads nothing (zero output); bit-identical to the
+    # clamped lengths, with and without a schedule, and the step's append
+    # skips both (slot -1)
+    w = pi.make_workload(cfg, S=6, len_lo=40, len_hi=300)
+    cap = w.M * w.B
+    announce(f"lengths outside the table: config {cfg} M={w.M} B={w.B}")
+    m = pkv()
+    q, kc, vc, bt = dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_tables)
+    bad = w.seq_lens.copy()
+    bad[1] = cap + 1000
+    bad[3] = -7
+    clamped = np.clip(bad, 0, cap).astype(np.int32)
+    sl_bad, sl_ok = dev(bad.astype(np.int32)), dev(clamped)
+    ref = m.paged_decode_attention(q, kc, vc, bt, sl_ok, w.scale)
+    got = m.paged_decode_attention(q, kc, vc, bt, sl_bad, w.scale)
+    sched = m.alloc_schedule(bt)
+    kc2, vc2 = kc.clone(), vc.clone()
+    slots = m.decode_append(dev(w.new_k), dev(w.new_v), bt, sl_bad, kc2, vc2,
+                            slot_mapping=torch.empty(w.S, dtype=torch.int64, device="cuda"), schedule=sched)
+    got_s = m.paged_decode_attention(q, kc, vc, bt, sl_bad, w.scale, schedule=sched)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+    assert torch.equal(got_s.view(torch.int16), ref.view(torch.int16))
+    assert torch.all(got[3] == 0)
+    s = slots.cpu().numpy()
+    assert s[1] == -1 and s[3] == -1
