@@ -343,3 +343,37 @@ def test_attention_with_a_caller_schedule(S):
     assert torch.equal(slots, r.slots)
     assert torch.equal(out.view(torch.int16), r.out.view(torch.int16))
     assert torch.equal(sched, dsched)
+
+
+@pytest.mark.parametrize("P", [0, 64, -1])
+def test_broken_row_ranges_are_contained(P):
+    # caller contract violations the kernels must contain (both kernels):
+    # a sequence whose rows run past num_q_rows is skipped, rows past
+    # max_q_len are not computed, rows at a negative position (n > L) get
+    # zeros; the other sequences' rows equal those of a valid call
+    w = pi.make_workload(3, S=3, seq_lens=[500, 300, 200], q_lens=[3, 4, 2])
+    announce(f"broken row ranges, partition_tokens={P}")
+    m = pkv()
+    q, kc, vc, bt, sl = dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_tables), dev(w.seq_lens)
+    qs_ok = dev(w.q_start)  # [0, 3, 7, 9]
+    ref = m.paged_multi_token_attention(q, qs_ok, w.max_q_len, kc, vc, bt, sl, w.scale, partition_tokens=P)
+    sentinel = 7.0
+
+    def run(q_start, max_q_len, lens):
+        out = torch.full_like(q, sentinel)
+        return m.paged_multi_token_attention(q, dev(np.array(q_start, np.int32)), max_q_len, kc, vc, bt,
+                                             dev(np.array(lens, np.int32)), w.scale, out=out, partition_tokens=P)
+
+    lens = [int(x) for x in w.seq_lens]
+    # sequence 2's rows end past num_q_rows = 9: skipped
+    a = run([0, 3, 7, 12], w.max_q_len, lens)
+    # max_q_len 3 < sequence 1's 4 rows: its 4th row is not computed
+    b = run([0, 3, 7, 9], 3, lens)
+    # sequence 1 holds 2 tokens for its 4 rows: rows at positions -2, -1 get zeros
+    c = run([0, 3, 7, 9], w.max_q_len, [lens[0], 2, lens[2]])
+    torch.cuda.synchronize()
+    eq = lambda x, y: torch.equal(x.view(torch.int16), y.view(torch.int16))
+    assert eq(a[:7], ref[:7]) and torch.all(a[7:].float() == sentinel)
+    assert eq(b[:3], ref[:3]) and eq(b[7:], ref[7:]) and torch.all(b[6].float() == sentinel)
+    assert eq(c[:3], ref[:3]) and eq(c[7:], ref[7:]) and torch.all(c[3:5].float() == 0)
+    assert torch.isfinite(c[5:7].float()).all()
