@@ -301,6 +301,22 @@ def bench_copy_blocks(args, w, torch, pkv) -> dict:
     ms = np.array([a.elapsed_time(b) for a, b in evs])
     t = float(ms.mean()) / 1e3
     gbps = moved / t / 1e9
+    # ceiling: a plain device-to-device copy of the same bytes (half read, half written) in the same run
+    half = moved // 2
+    csrc = torch.empty(half, dtype=torch.uint8, device="cuda")
+    cdst = torch.empty_like(csrc)
+    csrc.fill_(1)
+    for _ in range(3):
+        cdst.copy_(csrc)
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    torch.cuda.synchronize()
+    for a, b in cev:
+        a.record(stream)
+        cdst.copy_(csrc)
+        b.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = moved / (float(np.mean([a.elapsed_time(b) for a, b in cev])) / 1e3) / 1e9
+    del csrc, cdst
     return {"metric": "block copy GB/s (bytes read + written by pkv_copy_blocks)", "value": round(gbps, 1),
             "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": round(t * 1e3, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -309,6 +325,7 @@ def bench_copy_blocks(args, w, torch, pkv) -> dict:
                        "block_bytes_per_pool": block_bytes},
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                          "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "device_copy": round(copy_gbps, 1), "frac_of_device_copy": round(gbps / copy_gbps, 4),
                          "kernel": "copy_blocks_kernel", "algorithmic_bytes_per_launch": moved,
                          "launch_us": {"mean": round(t * 1e6, 2), "median": round(float(np.median(ms)) * 1e3, 2)}},
             "cpu_baseline": None}
