@@ -36,7 +36,8 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0
 
 # counter records (rocprofv3 FETCH_SIZE / WRITE_SIZE of the attention launch) per configuration
-TRAFFIC_RECORDS = {2: "traffic_paged_decode_attention_mha_bf16.txt",
+TRAFFIC_RECORDS = {(2, "fp8"): "traffic_paged_decode_attention_mha_fp8.txt",
+                   2: "traffic_paged_decode_attention_mha_bf16.txt",
                    3: "traffic_paged_decode_attention_gqa_bf16.txt",
                    4: "traffic_paged_decode_attention_long_context_bf16.txt"}
 
@@ -420,15 +421,17 @@ def kernel_sources_sha256(paths) -> str:
     return h.hexdigest()
 
 
-def measured_traffic(path, config: int, partition_tokens: int, contiguous: bool):
+def measured_traffic(path, config: int, partition_tokens: int, contiguous: bool, kv_dtype: str = "native"):
     """HBM bytes per attention launch from a counter record, or None when the
-    record is missing or was taken on another workload or another version of
-    the kernel sources."""
+    record is missing or was taken on another workload (configuration, pool
+    dtype, partition length) or another version of the kernel sources."""
     if not path or not os.path.isfile(path) or contiguous:
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("config") != config or rec.get("partition_tokens") != partition_tokens:
+        return None
+    if rec.get("kv_dtype", "native") != kv_dtype:
         return None
     if rec.get("kernel_sources_sha256") != kernel_sources_sha256(rec.get("kernel_sources", [])):
         return None
@@ -620,9 +623,10 @@ def main() -> int:
     kv_bytes = w.kv_read_bytes()
     attn_avg_s = float(attn_ms.mean()) / 1e3
     achieved = kv_bytes / attn_avg_s / 1e9
-    traffic_path = args.traffic or os.path.join(ROOT, "profiles", TRAFFIC_RECORDS.get(args.config, ""))
-    traffic = None if (w.dtype == "fp8" or args.block_size) else measured_traffic(traffic_path, args.config, P_used,
-                                                                                      args.contiguous)
+    record = TRAFFIC_RECORDS.get((args.config, "fp8") if w.dtype == "fp8" else args.config, "")
+    traffic_path = args.traffic or os.path.join(ROOT, "profiles", record)
+    traffic = None if args.block_size else measured_traffic(traffic_path, args.config, P_used, args.contiguous,
+                                                            "fp8" if w.dtype == "fp8" else "native")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                 "kernel": ("paged_decode_attention with the step's longest-first schedule: "
