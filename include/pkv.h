@@ -37,7 +37,8 @@
  *   value: ((b*Hkv + h)*hs + d)*B + t
  * Each (block, KV head) tile is B*hs contiguous elements in both pools.
  *
- *   q, out        [num_seqs][num_q_heads][head_size], element type T (bf16 with FP8 pools)
+ *   q, out        [num_seqs][num_q_heads][head_size], element type T (bf16 with FP8 pools;
+ *                 out is fp32 when the descriptor's out_f32 is set)
  *   k, v (append) [num_tokens][num_kv_heads][head_size], element type T (bf16 with FP8 pools)
  *   block_tables  int32 [num_seqs][max_blocks_per_seq]
  *   seq_lens      int32 [num_seqs]
@@ -121,6 +122,13 @@ typedef struct {
                            /* which are bf16 when the pools are FP8)           */
     float k_scale;         /* FP8 pools: key value = code * k_scale (> 0);     */
     float v_scale;         /* value = code * v_scale.  Ignored otherwise.      */
+    int32_t out_f32;       /* element type of the attention output `out`:      */
+                           /* 0 = the type of q (bf16 with bf16 and FP8 pools, */
+                           /* rounded to nearest even); 1 = fp32, the value    */
+                           /* that rounding would take.  With fp32 pools both  */
+                           /* mean fp32.  Values other than 0 and 1 are       */
+                           /* PKV_ERR_INVALID_ARG in every call; calls that    */
+                           /* write no attention output otherwise ignore it.   */
 } pkv_cache_desc;
 
 /* Layout contract version; changes whenever the pool layout above changes. */
@@ -234,12 +242,14 @@ PKV_API size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *   out[s][h] = sum_t softmax_t(scale * q[s][h] . K[t]) * V[t],  t < L,
  * where K[t] and V[t] are slot t % B of block block_tables[s][t / B], KV
  * head kvh.  Accumulation is fp32; a bf16 output is rounded to nearest
- * even; L == 0 gives a zero output.
+ * even (cache->out_f32 = 1 writes the fp32 value instead, and then the bf16
+ * output of the same call is exactly that value rounded to nearest even);
+ * L == 0 gives a zero output.
  *   q             device T [num_seqs][num_q_heads][head_size]
  *   k_cache, v_cache  device pools (layout above)
  *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
  *   seq_lens      device int32 [num_seqs]
- *   out           device T [num_seqs][num_q_heads][head_size], written
+ *   out           device T (fp32 with cache->out_f32) [num_seqs][num_q_heads][head_size], written
  *   workspace     device scratch of workspace_bytes >= pkv_decode_workspace_bytes(...)
  *                 (may be NULL when that size is 0); contents are overwritten
  *   partition_tokens  0 = library's choice, else as in pkv_decode_partition_tokens
@@ -537,6 +547,63 @@ PKV_API int32_t pkv_pool_block_table(const pkv_block_pool* pool, int64_t seq, in
 PKV_API pkv_status pkv_pool_export(const pkv_block_pool* pool, const int64_t* seqs, int32_t num_seqs,
                                    int32_t max_blocks_per_seq, int32_t pad_block, int32_t* block_tables,
                                    int32_t* seq_lens);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Contract check (debugging aid)
+ * ---------------------------------------------------------------------------
+ *
+ * The kernels contain a broken device-side contract (they skip an
+ * out-of-pool block or slot and clamp a length) but do not report it.
+ * pkv_validate reports it.  The rules checked, from the pages:
+ *   - a used table entry (index < ceil(L / B)) names a block inside the pool
+ *     and 0 <= L <= max_blocks_per_seq * B (the table walk of the cache-
+ *     structure page, "软件地址翻译" / "Block Table");
+ *   - the slots of one append are distinct and inside the pool (the cache-
+ *     structure page, "写入新 K/V": each new token has its own slot);
+ *   - no slot lies in a block that more than one sequence references
+ *     ("PagedAttention 笔记", "写时复制是正确性的边界": a shared block is only
+ *     read; a writer copies it first, pkv_copy_blocks).
+ * Counts are exact; each "first" field is the smallest offending index, or
+ * -1 when there is none.
+ */
+typedef struct {
+    int64_t bad_seq_lens;         /* sequences with seq_len < 0 or > max_blocks_per_seq * B        */
+    int64_t bad_block_ids;        /* used table entries outside [0, num_blocks)                    */
+    int64_t bad_slots;            /* slots >= num_blocks * B (negative slots are skips, not errors) */
+    int64_t duplicate_slots;      /* tokens whose slot (>= 0) equals an earlier token's slot       */
+    int64_t shared_block_writes;  /* tokens whose slot lies in a block with ref_counts > 1         */
+    int64_t first_bad_seq_len;    /* sequence index                                                */
+    int64_t first_bad_block_id;   /* s * max_blocks_per_seq + i of table entry i of sequence s      */
+    int64_t first_bad_slot;       /* token index                                                   */
+    int64_t first_duplicate_slot; /* token index (the later token of a repeated slot)              */
+    int64_t first_shared_block_write; /* token index                                               */
+} pkv_validate_report;
+
+/*
+ * Checks the inputs of an attention call, an append or a decode step:
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
+ *   seq_lens      device int32 [num_seqs]
+ *   slot_mapping  device int64 [num_tokens]: the slots of an append; or NULL
+ *                 (num_tokens ignored): the decode step's slots, one per
+ *                 sequence, by the rule of pkv_decode_slot_mapping (token
+ *                 index = sequence index)
+ *   ref_counts    device int32 [cache->num_blocks], each block's number of
+ *                 referencing sequences (pkv_pool_ref_count), or NULL to skip
+ *                 the shared-block rule
+ *   report        device pkv_validate_report, 8-byte aligned, written
+ * Only the tables, lengths, slots and counts are read, never the pools.
+ * Asynchronous on `stream` (three launches; the report is complete when the
+ * stream reaches it); a duplicate check compares every pair of slots, so the
+ * cost grows with num_tokens squared (a debugging aid, not for the hot path).
+ * Errors: PKV_ERR_INVALID_ARG (null report, a null array that the sizes
+ * need, negative sizes, misaligned report, bad descriptor),
+ * PKV_ERR_UNSUPPORTED (as for the descriptor), PKV_ERR_HIP.
+ */
+PKV_API pkv_status pkv_validate(const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                                int32_t max_blocks_per_seq, const int64_t* slot_mapping, int32_t num_tokens,
+                                const int32_t* ref_counts, const pkv_cache_desc* cache, pkv_validate_report* report,
+                                void* stream);
 
 /*
  * ---------------------------------------------------------------------------

@@ -46,7 +46,7 @@ class PkvError(RuntimeError):
 class CacheDesc(ctypes.Structure):
     _fields_ = [("num_blocks", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("block_size", ctypes.c_int32), ("head_size", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float)]
+                ("k_scale", ctypes.c_float), ("v_scale", ctypes.c_float), ("out_f32", ctypes.c_int32)]
 
 
 _lib = None
@@ -105,6 +105,8 @@ def library():
         L.pkv_copy_blocks.argtypes = [P, i32, ctypes.POINTER(CacheDesc), P, P, P]
         L.pkv_multi_token_kernel.restype = i32
         L.pkv_multi_token_kernel.argtypes = [i32, i32, i32, ctypes.POINTER(CacheDesc), i32]
+        L.pkv_validate.restype = i32
+        L.pkv_validate.argtypes = [P, P, i32, i32, P, i32, P, ctypes.POINTER(CacheDesc), P, P]
         L.pkv_probe_stream_read.restype = i32
         L.pkv_probe_stream_read.argtypes = [P, sz, P, i32, P]
         L.pkv_pool_create.restype = P
@@ -172,12 +174,25 @@ def cache_desc(k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: float = 1.
     x = 16 // k_cache.element_size()
     if tuple(k_cache.shape) != (nb, hkv, hs // x, B, x) or hs % x:
         raise ValueError(f"k_cache shape {tuple(k_cache.shape)} does not match v_cache {tuple(v_cache.shape)}")
-    return CacheDesc(nb, hkv, B, hs, _DTYPES[k_cache.dtype], float(k_scale), float(v_scale))
+    return CacheDesc(nb, hkv, B, hs, _DTYPES[k_cache.dtype], float(k_scale), float(v_scale), 0)
 
 
 def io_dtype(k_cache: torch.Tensor) -> torch.dtype:
     """Element type of q, out and the appended k, v for these pools."""
     return torch.bfloat16 if _DTYPES.get(k_cache.dtype) == PKV_FP8_E4M3 else k_cache.dtype
+
+
+def _out_tensor(q: torch.Tensor, out: Optional[torch.Tensor], out_dtype: Optional[torch.dtype],
+                desc: CacheDesc) -> torch.Tensor:
+    """The attention output: q's shape, and q's dtype or float32 (with bf16
+    queries a float32 output receives the values before bf16 rounding; the
+    descriptor's out_f32 is set for it)."""
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if out.shape != q.shape or out.dtype not in (q.dtype, torch.float32):
+        raise ValueError("out must have q's shape and q's dtype (or float32)")
+    desc.out_f32 = 1 if out.dtype == torch.float32 else 0
+    return out
 
 
 def layout_version() -> int:
@@ -303,11 +318,13 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
                            block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
                            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                            partition_tokens: int = 0, schedule: Optional[torch.Tensor] = None,
-                           stream=None, k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+                           stream=None, k_scale: float = 1.0, v_scale: float = 1.0,
+                           out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
     """out[s, h] = softmax(scale * q[s, h] K^T) V over the L = seq_lens[s]
     tokens of sequence s, K/V found through block_tables.  `schedule`: the
     longest-first schedule decode_append wrote for these tables and lengths
-    (optional; results are the same without it)."""
+    (optional; results are the same without it).  `out` (or out_dtype) may
+    be float32 with bf16 queries: the values before bf16 rounding."""
     desc = cache_desc(k_cache, v_cache, k_scale, v_scale)
     if q.dtype != io_dtype(k_cache):
         raise ValueError("q must have the pools' dtype")
@@ -319,10 +336,7 @@ def paged_decode_attention(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torc
     if block_tables.shape[0] != S or seq_lens.shape != (S,):
         raise ValueError("block_tables must be [S, M] and seq_lens [S]")
     M = block_tables.shape[1]
-    if out is None:
-        out = torch.empty_like(q)
-    if out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("out must match q")
+    out = _out_tensor(q, out, out_dtype, desc)
     if workspace is None:
         workspace = alloc_workspace(q, k_cache, v_cache, block_tables, partition_tokens)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
@@ -338,7 +352,8 @@ def paged_decode_step(q: torch.Tensor, new_k: torch.Tensor, new_v: torch.Tensor,
                       v_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
                       out: Optional[torch.Tensor] = None, slot_mapping: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, partition_tokens: int = 0,
-                      stream=None, k_scale: float = 1.0, v_scale: float = 1.0) -> torch.Tensor:
+                      stream=None, k_scale: float = 1.0, v_scale: float = 1.0,
+                      out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
     """A whole decode step in one call: store new_k[s], new_v[s] at position
     seq_lens[s] - 1, then attend over all seq_lens[s] tokens.  The append
     launch also writes the batch's longest-first schedule into the workspace
@@ -361,10 +376,7 @@ def paged_decode_step(q: torch.Tensor, new_k: torch.Tensor, new_v: torch.Tensor,
     if slot_mapping is not None and (slot_mapping.dtype != torch.int64 or slot_mapping.shape != (S,)):
         raise ValueError("slot_mapping must be int64 [S]")
     M = block_tables.shape[1]
-    if out is None:
-        out = torch.empty_like(q)
-    if out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("out must match q")
+    out = _out_tensor(q, out, out_dtype, desc)
     if workspace is None:
         workspace = alloc_step_workspace(q, k_cache, v_cache, block_tables, partition_tokens)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
@@ -378,11 +390,12 @@ def paged_decode_step(q: torch.Tensor, new_k: torch.Tensor, new_v: torch.Tensor,
 
 
 def decode_step(q, k_cache, v_cache, block_tables, seq_lens, new_k, new_v, scale, out=None, workspace=None,
-                slot_mapping=None, partition_tokens=0, stream=None, k_scale=1.0, v_scale=1.0) -> torch.Tensor:
+                slot_mapping=None, partition_tokens=0, stream=None, k_scale=1.0, v_scale=1.0,
+                out_dtype=None) -> torch.Tensor:
     """One decode step: append of the new tokens, then attention (two launches on one stream)."""
     return paged_decode_step(q, new_k, new_v, k_cache, v_cache, block_tables, seq_lens, scale, out=out,
                              slot_mapping=slot_mapping, workspace=workspace, partition_tokens=partition_tokens,
-                             stream=stream, k_scale=k_scale, v_scale=v_scale)
+                             stream=stream, k_scale=k_scale, v_scale=v_scale, out_dtype=out_dtype)
 
 
 # ---- several query tokens per sequence -------------------------------------
@@ -499,7 +512,7 @@ def paged_multi_token_attention(q: torch.Tensor, q_start: torch.Tensor, max_q_le
                                 scale: float, out: Optional[torch.Tensor] = None,
                                 workspace: Optional[torch.Tensor] = None, partition_tokens: int = 0,
                                 schedule: Optional[torch.Tensor] = None, stream=None, k_scale: float = 1.0,
-                                v_scale: float = 1.0) -> torch.Tensor:
+                                v_scale: float = 1.0, out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
     """Causal paged attention of every query row over its sequence's cached
     tokens (the rows' own tokens must already be in the cache).  `schedule`:
     the one multi_token_slot_mapping wrote for these tables and lengths, or
@@ -507,10 +520,7 @@ def paged_multi_token_attention(q: torch.Tensor, q_start: torch.Tensor, max_q_le
     desc = cache_desc(k_cache, v_cache, k_scale, v_scale)
     S = _check_rows(q, q_start, block_tables, seq_lens, desc, k_cache)
     rows, Hq, _ = q.shape
-    if out is None:
-        out = torch.empty_like(q)
-    if out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("out must match q")
+    out = _out_tensor(q, out, out_dtype, desc)
     if workspace is None:
         workspace = alloc_multi_token_workspace(q, k_cache, v_cache, block_tables, max_q_len, partition_tokens)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
@@ -528,7 +538,7 @@ def paged_multi_token_step(q: torch.Tensor, new_k: torch.Tensor, new_v: torch.Te
                            seq_lens: torch.Tensor, scale: float, out: Optional[torch.Tensor] = None,
                            slot_mapping: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                            partition_tokens: int = 0, stream=None, k_scale: float = 1.0,
-                           v_scale: float = 1.0) -> torch.Tensor:
+                           v_scale: float = 1.0, out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
     """Slot mapping of the rows, append of every row's new_k / new_v, then
     paged_multi_token_attention (three launches on one stream)."""
     desc = cache_desc(k_cache, v_cache, k_scale, v_scale)
@@ -542,10 +552,7 @@ def paged_multi_token_step(q: torch.Tensor, new_k: torch.Tensor, new_v: torch.Te
         slot_mapping = torch.empty(rows, dtype=torch.int64, device=q.device)
     if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (rows,):
         raise ValueError("slot_mapping must be int64 [rows]")
-    if out is None:
-        out = torch.empty_like(q)
-    if out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("out must match q")
+    out = _out_tensor(q, out, out_dtype, desc)
     if workspace is None:
         workspace = alloc_multi_token_step_workspace(q, k_cache, v_cache, block_tables, max_q_len,
                                                      partition_tokens)
@@ -557,6 +564,42 @@ def paged_multi_token_step(q: torch.Tensor, new_k: torch.Tensor, new_v: torch.Te
         S, Hq, block_tables.shape[1], ctypes.byref(desc), float(scale), _dev(out, "out"),
         _dev(slot_mapping, "slot_mapping"), ws_ptr, ws_bytes, int(partition_tokens), _stream(stream)))
     return out
+
+
+# Fields of pkv_validate_report, in order (int64 each).
+VALIDATE_FIELDS = ("bad_seq_lens", "bad_block_ids", "bad_slots", "duplicate_slots", "shared_block_writes",
+                   "first_bad_seq_len", "first_bad_block_id", "first_bad_slot", "first_duplicate_slot",
+                   "first_shared_block_write")
+
+
+def validate(block_tables: torch.Tensor, seq_lens: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+             slot_mapping: Optional[torch.Tensor] = None, ref_counts: Optional[torch.Tensor] = None,
+             stream=None) -> dict:
+    """Checks tables, lengths and slots against the kernels' device-side
+    contract (block IDs in the pool, lengths within the table, distinct slots
+    inside the pool, no slot in a block with ref_counts > 1) and returns the
+    report as a dict of VALIDATE_FIELDS (first_* = -1 when none).  Without
+    slot_mapping the decode step's slots are checked.  Reads no pool data;
+    waits for the GPU to return the report."""
+    desc = cache_desc(k_cache, v_cache)
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_tables and seq_lens must be int32")
+    S, M = block_tables.shape
+    if seq_lens.shape != (S,):
+        raise ValueError("seq_lens must be [S]")
+    if slot_mapping is not None and (slot_mapping.dtype != torch.int64 or slot_mapping.dim() != 1):
+        raise ValueError("slot_mapping must be int64 [T]")
+    if ref_counts is not None and (ref_counts.dtype != torch.int32 or ref_counts.shape != (desc.num_blocks,)):
+        raise ValueError("ref_counts must be int32 [num_blocks]")
+    report = torch.empty(len(VALIDATE_FIELDS), dtype=torch.int64, device=block_tables.device)
+    _check("pkv_validate", library().pkv_validate(
+        _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), S, M,
+        _dev(slot_mapping, "slot_mapping") if slot_mapping is not None else None,
+        slot_mapping.shape[0] if slot_mapping is not None else 0,
+        _dev(ref_counts, "ref_counts") if ref_counts is not None else None, ctypes.byref(desc),
+        _dev(report, "report"), _stream(stream)))
+    torch.cuda.synchronize(report.device)
+    return dict(zip(VALIDATE_FIELDS, report.cpu().tolist()))
 
 
 def probe_stream_read(buf: torch.Tensor, out: torch.Tensor, work_groups: int, stream=None) -> None:

@@ -19,7 +19,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "append.hip", "decode.hip", "copy.hip", "prefill.hip", "probe.hip", "pool.cpp"]
+SOURCES = ["api.hip", "append.hip", "decode.hip", "copy.hip", "prefill.hip", "probe.hip", "validate.hip", "pool.cpp"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",

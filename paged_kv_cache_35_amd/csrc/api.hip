@@ -85,6 +85,8 @@ pkv_status check_cache(const pkv_cache_desc* c)
         return PKV_ERR_UNSUPPORTED;
     if (c->dtype == PKV_FP8_E4M3 && B < 16)
         return PKV_ERR_UNSUPPORTED;
+    if (c->out_f32 != 0 && c->out_f32 != 1)
+        return PKV_ERR_INVALID_ARG;
     return PKV_OK;
 }
 
@@ -357,6 +359,7 @@ pkv_status attention_args(const void* q, const void* k_cache, const void* v_cach
     a.block_tables = block_tables;
     a.seq_lens = seq_lens;
     a.out = out;
+    a.out_f32 = cache->out_f32;
     const size_t units = (size_t)num_seqs * num_q_heads * parts;
     a.ws_o = need > 0 ? (float*)workspace : nullptr;
     a.ws_ml = need > 0 ? (float*)workspace + units * cache->head_size : nullptr;
@@ -725,6 +728,25 @@ pkv_status pkv_copy_blocks(const int32_t* pairs, int32_t num_pairs, const pkv_ca
         (int64_t)cache->num_kv_heads * cache->block_size * cache->head_size * elem_bytes(cache->dtype);
     return hip_status(pkv::launch_copy_blocks(pairs, num_pairs, cache->num_blocks, block_bytes, k_cache, v_cache,
                                               (hipStream_t)stream));
+}
+
+pkv_status pkv_validate(const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                        int32_t max_blocks_per_seq, const int64_t* slot_mapping, int32_t num_tokens,
+                        const int32_t* ref_counts, const pkv_cache_desc* cache, pkv_validate_report* report,
+                        void* stream)
+{
+    if (!report || ((uintptr_t)report & 7u) != 0 || num_seqs < 0 || max_blocks_per_seq <= 0)
+        return PKV_ERR_INVALID_ARG;
+    const pkv_status st = check_cache(cache);
+    if (st != PKV_OK)
+        return st;
+    if (num_seqs > 0 && (!block_tables || !seq_lens))
+        return PKV_ERR_INVALID_ARG;
+    if (slot_mapping && num_tokens < 0)
+        return PKV_ERR_INVALID_ARG;
+    return hip_status(pkv::launch_validate(block_tables, seq_lens, num_seqs, max_blocks_per_seq, slot_mapping,
+                                           slot_mapping ? num_tokens : 0, ref_counts, cache->block_size,
+                                           cache->num_blocks, report, (hipStream_t)stream));
 }
 
 pkv_status pkv_probe_stream_read(const void* buf, size_t bytes, void* out, int32_t work_groups, void* stream)

@@ -62,8 +62,33 @@ __device__ __forceinline__ float max_over_lane_groups(float x)
     return __builtin_elementwise_maximum(c, d);
 }
 
-__device__ __forceinline__ void store_elem(__bf16* p, float x) { *p = (__bf16)x; }
-__device__ __forceinline__ void store_elem(float* p, float x) { *p = x; }
+// Output elements.  With bf16 queries the output is bf16, rounded to
+// nearest even, or, when out_f32 is set, the fp32 value that rounding would
+// take (so that the kernel's own error can be seen apart from the output
+// rounding).  fp32 queries always give fp32.  i indexes elements of the
+// output's own type; store_out4 needs i to be a multiple of 4.
+template <typename T>
+__device__ __forceinline__ void store_out(void* out, int64_t i, float x, bool out_f32)
+{
+    if (sizeof(T) == 4 || out_f32)
+        static_cast<float*>(out)[i] = x;
+    else
+        static_cast<__bf16*>(out)[i] = (__bf16)x;
+}
+
+template <typename T>
+__device__ __forceinline__ void store_out4(void* out, int64_t i, f32x4 x, bool out_f32)
+{
+    if (sizeof(T) == 4 || out_f32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(out) + i) = x;
+    } else {
+        bf16x4 v;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            v[k] = (__bf16)x[k];
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out) + i) = v;
+    }
+}
 
 // Four E4M3 codes (one dword) to four bf16: v_cvt_pk_f32_fp8 gives the exact
 // values in fp32, and an E4M3 value has at most 4 significant bits, so its

@@ -417,7 +417,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     const int32_t* __restrict__ seq_lens, int32_t Hq, int32_t Hkv,
     int32_t M, int32_t num_blocks, int32_t PB, int32_t max_parts, int32_t interleave, int32_t lpt, float qscale,
     const int32_t* __restrict__ sched_order, const int32_t* __restrict__ sched_lens,
-    const int32_t* __restrict__ sched_tables, float oscale, T* __restrict__ out,
+    const int32_t* __restrict__ sched_tables, float oscale, void* __restrict__ out, int32_t out_f32,
     float* __restrict__ ws_o, float* __restrict__ ws_ml, const int32_t* __restrict__ q_start, int32_t num_q_rows,
     int32_t max_q_len, int32_t RT, const int32_t* __restrict__ sched_count, const uint32_t* __restrict__ sched_items,
     int32_t rank_in_z)
@@ -446,7 +446,8 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     // heads (and row tiles) and y, z the ranks and chunks: rank in z (chunks
     // of one sequence consecutive) for small batches, where few work-groups
     // find themselves past their sequence's end, rank in y otherwise.
-    int kvh, rt = 0, yr, chunk, s_listed = 0;
+    // S_grid: the sequences of this launch.
+    int kvh, rt = 0, yr, chunk, s_listed = 0, S_grid;
     if (sched_items) {
         const int HR = MQ ? Hkv * RT : Hkv;  // (KV head, row tile) pairs
         const int item = blockIdx.x / HR;
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
         s_listed = (int)it.y;  // the sequence of rank yr, without another dependent load
         // a list that does not belong to this launch (caller error) must not
         // send a work-group outside its sequences or chunks
-        const int S_grid = (int)(gridDim.x / ((unsigned)HR * max_parts));
+        S_grid = (int)(gridDim.x / ((unsigned)HR * max_parts));
         if (yr >= S_grid || chunk >= max_parts || (unsigned)s_listed >= (unsigned)S_grid)
             return;
     } else {
@@ -469,6 +470,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
         rt = MQ ? blockIdx.x - kvh * RT : 0;  // row tile
         yr = rank_in_z ? blockIdx.z : blockIdx.y;
         chunk = rank_in_z ? blockIdx.y : blockIdx.z;
+        S_grid = (int)(rank_in_z ? gridDim.z : gridDim.y);
     }
     const int lane = threadIdx.x & 63;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, kept scalar
@@ -494,10 +496,14 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     int s = yr;
     if (sched_order) {
         // schedule given (decode step): rank y's sequence, length and table
-        // row are read below from y alone
+        // row are read below from y alone.  An order that does not belong
+        // to this batch (caller error) must not send the work-group to a
+        // sequence outside it: q, q_start and out are indexed by s.
         s = sched_items ? s_listed : sched_order[yr];
+        if ((unsigned)s >= (unsigned)S_grid)
+            return;  // uniform (one index per work-group), before any barrier
     } else if (lpt && chunk == 0) {
-        const int S = rank_in_z ? gridDim.z : gridDim.y;  // <= kLptMaxSeqs = 256, M < 2^23 (checked on the host)
+        const int S = S_grid;  // <= kLptMaxSeqs = 64, M < 2^23 (checked on the host)
         unsigned* sm_key = reinterpret_cast<unsigned*>(&sm_out[0][0]);
         const int cap = M * BS;
         for (int i = threadIdx.x; i < S; i += NW * 64) {
@@ -576,10 +582,10 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
         if (chunk == 0 && w == 0) {
             if constexpr (MQ) {
                 for (int idx = lane; idx < tile_rows * HS; idx += 64)
-                    store_elem(out + out_row(16 * rt + idx / HS) + idx % HS, 0.f);
+                    store_out<T>(out, out_row(16 * rt + idx / HS) + idx % HS, 0.f, out_f32);
             } else {
                 for (int idx = lane; idx < G * HS; idx += 64)
-                    store_elem(out + ((int64_t)s * Hq + (int64_t)kvh * G) * HS + idx, 0.f);
+                    store_out<T>(out, ((int64_t)s * Hq + (int64_t)kvh * G) * HS + idx, 0.f, out_f32);
             }
         }
         return;
@@ -886,17 +892,9 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
         acc *= inv;
         if (nchunks == 1) {
             // without MQ the group's G heads are adjacent rows of out
-            T* dst = out + (MQ ? out_row(16 * rt + g) + (4 * e) % HS
-                               : ((int64_t)s * Hq + (int64_t)kvh * G) * HS + 4 * e);
-            if constexpr (sizeof(T) == 2) {
-                bf16x4 v;
-#pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    v[k] = (__bf16)acc[k];
-                *(bf16x4*)dst = v;
-            } else {
-                *(f32x4*)dst = acc;
-            }
+            store_out4<T>(out,
+                          MQ ? out_row(16 * rt + g) + (4 * e) % HS : ((int64_t)s * Hq + (int64_t)kvh * G) * HS + 4 * e,
+                          acc, out_f32);
         } else {
             *(f32x4*)(ws_o + blk * RPB * HS + 4 * e) = acc;
             if ((4 * e) % HS == 0) {
@@ -964,7 +962,8 @@ template <typename T, int HS>
 __global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sched_order,
     const int32_t* __restrict__ sched_lens, int32_t S, int32_t M, int32_t BS, int32_t CB, int32_t Hq, int32_t Hkv,
-    int32_t max_parts, const float* __restrict__ ws_o, const float* __restrict__ ws_ml, T* __restrict__ out)
+    int32_t max_parts, const float* __restrict__ ws_o, const float* __restrict__ ws_ml, void* __restrict__ out,
+    int32_t out_f32)
 {
     constexpr int R = kMergeThreads / HS;  // partition groups
     __shared__ float sm_w[kMergeChunk];
@@ -976,6 +975,8 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
         const int y = (int)(pr / Hq);
         const int h = (int)(pr - (int64_t)y * Hq);
         const int s = sched_order ? sched_order[y] : y;
+        if ((unsigned)s >= (unsigned)S)
+            continue;  // an order that does not belong to this batch: uniform, before any barrier
         int L = sched_order ? sched_lens[y] : seq_lens[s];
         L = L < 0 ? 0 : (L > M * BS ? M * BS : L);
         const int nblk = (L + BS - 1) / BS;
@@ -1030,7 +1031,7 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
 #pragma unroll
             for (int k = 0; k < R; ++k)
                 tot += sm_acc[k][threadIdx.x];
-            store_elem(out + ((int64_t)s * Hq + h) * HS + threadIdx.x, wsum > 0.f ? tot / wsum : 0.f);
+            store_out<T>(out, ((int64_t)s * Hq + h) * HS + threadIdx.x, wsum > 0.f ? tot / wsum : 0.f, out_f32);
         }
         __syncthreads();  // sm_acc and sm_w are reused by the next pair
     }
@@ -1048,7 +1049,8 @@ template <typename T, int HS>
 __global__ __launch_bounds__(64) void paged_decode_reduce_few_kernel(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sched_order,
     const int32_t* __restrict__ sched_lens, int32_t S, int32_t M, int32_t BS, int32_t CB, int32_t Hq, int32_t Hkv,
-    int32_t max_parts, const float* __restrict__ ws_o, const float* __restrict__ ws_ml, T* __restrict__ out)
+    int32_t max_parts, const float* __restrict__ ws_o, const float* __restrict__ ws_ml, void* __restrict__ out,
+    int32_t out_f32)
 {
     constexpr int Q = HS / 4;  // lanes with work: 4 head dims each
     const int G = Hq / Hkv;
@@ -1057,6 +1059,8 @@ __global__ __launch_bounds__(64) void paged_decode_reduce_few_kernel(
         const int y = (int)(pr / Hq);
         const int h = (int)(pr - (int64_t)y * Hq);
         const int s = sched_order ? sched_order[y] : y;
+        if ((unsigned)s >= (unsigned)S)
+            continue;  // an order that does not belong to this batch
         int L = sched_order ? sched_lens[y] : seq_lens[s];
         L = L < 0 ? 0 : (L > M * BS ? M * BS : L);
         const int nblk = (L + BS - 1) / BS;
@@ -1081,10 +1085,11 @@ __global__ __launch_bounds__(64) void paged_decode_reduce_few_kernel(
             wsum += wgt;
             acc += wgt * *(const f32x4*)(ws_o + ((u0 + p) * G + g) * HS + d);
         }
-        T* dst = out + ((int64_t)s * Hq + h) * HS + d;
+        f32x4 res;
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-            store_elem(dst + k, wsum > 0.f ? acc[k] / wsum : 0.f);
+            res[k] = wsum > 0.f ? acc[k] / wsum : 0.f;
+        store_out4<T>(out, ((int64_t)s * Hq + h) * HS + d, res, out_f32);
     }
 }
 
@@ -1096,8 +1101,8 @@ __global__ __launch_bounds__(64) void paged_decode_reduce_few_kernel(
 template <typename T, int HS>
 __global__ __launch_bounds__(256) void paged_multi_token_reduce_kernel(
     const int32_t* __restrict__ seq_lens, int32_t M, int32_t BS, int32_t CB, int32_t Hq, int32_t Hkv,
-    int32_t max_parts, const float* __restrict__ ws_o, const float* __restrict__ ws_ml, T* __restrict__ out,
-    const int32_t* __restrict__ q_start, int32_t num_q_rows, int32_t max_q_len, int32_t RT)
+    int32_t max_parts, const float* __restrict__ ws_o, const float* __restrict__ ws_ml, void* __restrict__ out,
+    int32_t out_f32, const int32_t* __restrict__ q_start, int32_t num_q_rows, int32_t max_q_len, int32_t RT)
 {
     static_assert(HS % 16 == 0 && HS / 16 <= 8, "16 threads per row, at most 8 dims each");
     constexpr int DPT = HS / 16;  // head dims per thread
@@ -1151,10 +1156,11 @@ __global__ __launch_bounds__(256) void paged_multi_token_reduce_kernel(
         return;
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     const int i = rho / G;
-    T* dst = out + ((int64_t)(qs0 + i) * Hq + (int64_t)kvh * G + (rho - i * G)) * HS + q * DPT;
+    const int64_t dst = ((int64_t)(qs0 + i) * Hq + (int64_t)kvh * G + (rho - i * G)) * HS + q * DPT;
 #pragma unroll
-    for (int k = 0; k < DPT; ++k)
-        store_elem(dst + k, acc[k] * inv);
+    for (int k = 0; k < DPT; k += 4)
+        store_out4<T>(out, dst + k, (f32x4){acc[k] * inv, acc[k + 1] * inv, acc[k + 2] * inv, acc[k + 3] * inv},
+                      out_f32);
 }
 
 template <typename T, int HS, int BS, bool F8, bool MQ>
@@ -1174,7 +1180,7 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
                        a.num_q_heads, a.num_kv_heads, a.max_blocks_per_seq, a.num_blocks, a.partition_blocks,
                        a.max_parts, a.interleave,
                        (a.num_seqs <= kLptMaxSeqs && a.max_blocks_per_seq < (1 << 23)) ? 1 : 0, qscale,
-                       a.sched_order, a.sched_lens, a.sched_tables, F8 ? a.v_scale : 1.0f, (T*)a.out, a.ws_o,
+                       a.sched_order, a.sched_lens, a.sched_tables, F8 ? a.v_scale : 1.0f, a.out, a.out_f32, a.ws_o,
                        a.ws_ml, a.q_start, a.num_q_rows, a.max_q_len, a.row_tiles, a.sched_count, a.sched_items,
                        rank_in_z);
     hipError_t e = hipGetLastError();
@@ -1183,20 +1189,20 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
     if constexpr (MQ)
         hipLaunchKernelGGL((paged_multi_token_reduce_kernel<T, HS>), dim3(a.row_tiles, a.num_kv_heads, a.num_seqs),
                            dim3(256), 0, stream, a.seq_lens, a.max_blocks_per_seq, BS, a.partition_blocks * NW,
-                           a.num_q_heads, a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, (T*)a.out, a.q_start,
+                           a.num_q_heads, a.num_kv_heads, a.max_parts, a.ws_o, a.ws_ml, a.out, a.out_f32, a.q_start,
                            a.num_q_rows, a.max_q_len, a.row_tiles);
     else if (a.max_parts <= kFewChunks)
         hipLaunchKernelGGL((paged_decode_reduce_few_kernel<T, HS>),
                            dim3((unsigned)std::min<int64_t>((int64_t)a.num_q_heads * a.num_seqs, kFewMergeWaves)),
                            dim3(64), 0, stream, a.seq_lens, a.sched_order, a.sched_lens, a.num_seqs,
                            a.max_blocks_per_seq, BS, a.partition_blocks * NW, a.num_q_heads, a.num_kv_heads,
-                           a.max_parts, a.ws_o, a.ws_ml, (T*)a.out);
+                           a.max_parts, a.ws_o, a.ws_ml, a.out, a.out_f32);
     else
         hipLaunchKernelGGL((paged_decode_reduce_kernel<T, HS>),
                            dim3((unsigned)std::min<int64_t>((int64_t)a.num_q_heads * a.num_seqs, kMergeGroups)),
                            dim3(kMergeThreads), 0, stream, a.seq_lens, a.sched_order, a.sched_lens, a.num_seqs,
                            a.max_blocks_per_seq, BS, a.partition_blocks * NW, a.num_q_heads, a.num_kv_heads,
-                           a.max_parts, a.ws_o, a.ws_ml, (T*)a.out);
+                           a.max_parts, a.ws_o, a.ws_ml, a.out, a.out_f32);
     return hipGetLastError();
 }
 

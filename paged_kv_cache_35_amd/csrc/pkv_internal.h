@@ -31,6 +31,7 @@ struct DecodeArgs {
     const int32_t* block_tables;
     const int32_t* seq_lens;
     void* out;
+    int32_t out_f32;  // bf16 queries: 1 = out holds fp32 (the value before rounding to bf16)
     // Longest-first schedule written by the decode step's append launch (all
     // null otherwise): work-group row y attends sequence order[y], whose
     // length and table row are lens[y] and tables[y].
@@ -137,6 +138,12 @@ hipError_t launch_multi_token_slot_mapping(const int32_t* block_tables, const in
                                            int32_t max_q_len, int32_t max_blocks_per_seq, int32_t block_size,
                                            int64_t* slot_mapping, const AppendArgs::Schedule& sched,
                                            hipStream_t stream);
+
+// Contract check (validate.hip): fills the pkv_validate_report at report_buf.
+hipError_t launch_validate(const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
+                           int32_t max_blocks_per_seq, const int64_t* slot_mapping, int32_t num_tokens,
+                           const int32_t* ref_counts, int32_t block_size, int32_t num_blocks, void* report_buf,
+                           hipStream_t stream);
 
 hipError_t launch_slot_mapping(const int32_t* block_tables, const int32_t* seq_lens, int32_t num_seqs,
                                int32_t max_blocks_per_seq, int32_t block_size, int64_t* slot_mapping,

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     const typename std::conditional<F8, uint8_t, __bf16>::type* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ q_start, int32_t num_q_rows, int32_t max_q_len, int32_t Hq, int32_t Hkv, int32_t M,
-    int32_t num_blocks, int32_t RB, float qscale, float oscale, __bf16* __restrict__ out)
+    int32_t num_blocks, int32_t RB, float qscale, float oscale, void* __restrict__ out, int32_t out_f32)
 {
     static_assert(BS >= 16 && (BS % 16) == 0, "blocks of 16, 32 or 64 tokens");
     constexpr int TILE = HS * BS;  // elements of one (block, KV head) tile
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     const int last_row = (row0 + kPfRows < nrows ? row0 + kPfRows : nrows) - 1;
     if (L == 0) {
         for (int idx = tid; idx < (last_row - row0 + 1) * HS; idx += kPfThreads)
-            out[out_row(row0 + idx / HS) + idx % HS] = (__bf16)0.f;
+            store_out<__bf16>(out, out_row(row0 + idx / HS) + idx % HS, 0.f, out_f32);
         return;
     }
     // row rho sees the tokens below L - n + rho / G + 1 (at least 0)
@@ -544,10 +544,10 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
             const float l_g = __shfl(l_tot, g);
             const float inv = l_g > 0.f ? oscale / l_g : 0.f;
             if (tb + g < nrows) {
-                __bf16* dst = out + out_row(tb + g);
+                const int64_t dst = out_row(tb + g);
 #pragma unroll
                 for (int i = 0; i < HS / 16; ++i)
-                    dst[16 * i + c] = (__bf16)(O[kt][i][jj] * inv);
+                    store_out<__bf16>(out, dst + 16 * i + c, O[kt][i][jj] * inv, out_f32);
             }
         }
     }
@@ -564,7 +564,7 @@ static hipError_t launch_prefill_typed(const DecodeArgs& a, hipStream_t stream)
     hipLaunchKernelGGL((paged_prefill_kernel<HS, BS, F8>), dim3((unsigned)groups), dim3(kPfThreads), 0,
                        stream, (const __bf16*)a.q, (const C*)a.k_cache, (const C*)a.v_cache, a.block_tables,
                        a.seq_lens, a.q_start, a.num_q_rows, a.max_q_len, a.num_q_heads, a.num_kv_heads,
-                       a.max_blocks_per_seq, a.num_blocks, RB, qscale, F8 ? a.v_scale : 1.0f, (__bf16*)a.out);
+                       a.max_blocks_per_seq, a.num_blocks, RB, qscale, F8 ? a.v_scale : 1.0f, a.out, a.out_f32);
     return hipGetLastError();
 }
 

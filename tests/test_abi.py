@@ -329,3 +329,36 @@ def test_unpartitioned_multi_token_kernel_support(lib):
     assert lib.paged_multi_token_attention(FAKE, None, 8, 2, FAKE, FAKE, FAKE, FAKE, 4, 8, 4096,
                                            ctypes.byref(desc(dtype=1)), 0.125, FAKE, None, 0, -1, None, 0,
                                            None) == INVALID
+
+
+def test_output_type_flag_is_checked(lib):
+    d = desc(dtype=1)
+    d.out_f32 = 2
+    assert attn(lib, d=d) == INVALID
+    d.out_f32 = 1
+    assert attn(lib, d=d, S=0) == OK
+
+
+def validate(lib, *, bt=FAKE, sl=FAKE, S=4, M=4, slots=None, T=0, rc=None, d=None, report=FAKE):
+    d = d or desc()
+    return lib.pkv_validate(bt, sl, S, M, slots, T, rc, ctypes.byref(d), report, None)
+
+
+def test_validate_rejects_bad_arguments(lib):
+    # every check happens on the host, before the report is touched
+    assert validate(lib, report=None) == INVALID
+    assert validate(lib, report=ctypes.c_void_p(0x10004)) == INVALID  # report not 8-byte aligned
+    assert validate(lib, S=-1) == INVALID
+    assert validate(lib, M=0) == INVALID
+    assert validate(lib, bt=None) == INVALID
+    assert validate(lib, sl=None) == INVALID
+    assert validate(lib, slots=FAKE, T=-1) == INVALID
+    assert validate(lib, d=desc(hs=96)) == UNSUPPORTED
+    assert validate(lib, d=desc(nb=0)) == INVALID
+
+
+def test_validate_report_layout():
+    # the binding's field list follows the header's struct, in order
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{([^}]*)\} pkv_validate_report;", text).group(1)
+    assert tuple(re.findall(r"int64_t\s+(\w+);", body)) == pkv.VALIDATE_FIELDS

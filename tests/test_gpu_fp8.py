@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 import pkv_inputs as pi
-from tests.test_gpu_parity import SMALL, announce, check_attention, dev, host_bits, host_f64, same_bytes
+from tests.test_gpu_parity import (SMALL, announce, check_attention, check_rounding, dev, host_bits, host_f64,
+                                   same_bytes)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -127,8 +128,8 @@ def test_partition_lengths_fp8(P):
     check_step(w, *run_fp8(w, partition_tokens=P))
 
 
-@pytest.mark.parametrize("cfg", [2, 4])
-def test_full_config_fp8_sampled(cfg):
+@pytest.mark.parametrize("cfg", [2, 3, 4, 5])
+def test_full_config_fp8(cfg):
     w = pi.make_workload(cfg, dtype="fp8")
     announce(f"fp8 full config {cfg}")
     out, kc, vc, slots = run_fp8(w, step=True)
@@ -138,8 +139,14 @@ def test_full_config_fp8_sampled(cfg):
     oracle.kv_append_fp8(w.new_k, w.new_v, ref_slots, kp, vp, oracle.fp8_inv_scale(w.k_scale),
                          oracle.fp8_inv_scale(w.v_scale))
     assert same_bytes(host_bits(kc), kp) and same_bytes(host_bits(vc), vp)
-    rng = np.random.default_rng(200 + cfg)
-    units = rng.choice(w.S * w.Hq, size=96 if cfg == 4 else 192, replace=False)
-    ref = oracle.paged_attention_fp8(w.q, kp, vp, w.block_tables, w.seq_lens, w.scale, w.k_scale, w.v_scale,
-                                     units=units)
-    check_attention(w, host_f64(out).reshape(-1, w.hs)[units], ref)
+    # every (sequence, query head) row against the oracle's full pass
+    ref = oracle.paged_attention_fp8(w.q, kp, vp, w.block_tables, w.seq_lens, w.scale, w.k_scale, w.v_scale)
+    check_attention(w, host_f64(out), ref)
+    # the same attention with an fp32 output: the fp32 bar, and the bf16
+    # output is its exact rounding
+    out32 = pkv().paged_decode_attention(dev(w.q), kc, vc, dev(w.block_tables), dev(w.seq_lens), w.scale,
+                                         partition_tokens=w.partition_tokens, k_scale=w.k_scale,
+                                         v_scale=w.v_scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_attention(w, host_f64(out32), ref, out_f32=True)
+    check_rounding(out, out32)
