@@ -312,6 +312,33 @@ PKV_API pkv_status paged_decode_step(const void* q, const void* new_k, const voi
                                      int32_t partition_tokens, void* stream);
 
 /*
+ * The decode step of paged_decode_step for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same two launches and the same
+ * results, bit for bit, with the workspace taken from a device array inside
+ * the library instead of a caller buffer.  The array holds
+ * PKV_STATIC_SCRATCH_BYTES on every GPU the library runs on, until the
+ * process ends; the call uses the current device's copy (stream must belong
+ * to the current device) and allocates nothing (no hipMalloc, no allocating
+ * library routine).  All calls on one GPU share that array and each leaves
+ * its contents behind: calls that may overlap on one GPU (different streams,
+ * or different host threads without ordering) race and must not be issued;
+ * calls ordered on one stream are safe.  Nothing in it needs clearing
+ * between calls.
+ *   arguments as paged_decode_step, without workspace / workspace_bytes
+ * Errors: as paged_decode_step; PKV_ERR_WORKSPACE when
+ * pkv_decode_step_workspace_bytes(...) for these sizes exceeds
+ * PKV_STATIC_SCRATCH_BYTES; PKV_ERR_UNSUPPORTED on a device index >= 64.
+ */
+#define PKV_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+
+PKV_API pkv_status paged_decode_step_static(const void* q, const void* new_k, const void* new_v, void* k_cache,
+                                            void* v_cache, const int32_t* block_tables, const int32_t* seq_lens,
+                                            int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                            const pkv_cache_desc* cache, float scale, void* out,
+                                            int64_t* slot_mapping, int32_t partition_tokens, void* stream);
+
+/*
  * ---------------------------------------------------------------------------
  * Several query tokens per sequence: chunked prefill, prefill of the tokens a
  * prefix-cache lookup missed, and the draft tokens of speculative decoding

@@ -87,6 +87,9 @@ def library():
         L.paged_decode_step.restype = i32
         L.paged_decode_step.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, ctypes.POINTER(CacheDesc), f32, P, P, P,
                                         sz, i32, P]
+        L.paged_decode_step_static.restype = i32
+        L.paged_decode_step_static.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, ctypes.POINTER(CacheDesc), f32, P,
+                                               P, i32, P]
         L.pkv_copy_blocks.restype = i32
         L.pkv_multi_token_workspace_bytes.restype = sz
         L.pkv_multi_token_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
@@ -386,6 +389,48 @@ def paged_decode_step(q: torch.Tensor, new_k: torch.Tensor, new_v: torch.Tensor,
         _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), S, Hq, M, ctypes.byref(desc), float(scale),
         _dev(out, "out"), _dev(slot_mapping, "slot_mapping") if slot_mapping is not None else None, ws_ptr, ws_bytes,
         int(partition_tokens), _stream(stream)))
+    return out
+
+
+# Workspace size of the library's own device array (paged_decode_step_static).
+STATIC_SCRATCH_BYTES = 32 << 20
+
+
+def paged_decode_step_static(q: torch.Tensor, new_k: torch.Tensor, new_v: torch.Tensor, k_cache: torch.Tensor,
+                             v_cache: torch.Tensor, block_tables: torch.Tensor, seq_lens: torch.Tensor, scale: float,
+                             out: torch.Tensor, slot_mapping: Optional[torch.Tensor] = None,
+                             partition_tokens: int = 0, stream=None, k_scale: float = 1.0,
+                             v_scale: float = 1.0) -> torch.Tensor:
+    """paged_decode_step without a workspace argument and without any
+    allocation: the library takes the workspace from its own device array
+    (STATIC_SCRATCH_BYTES per GPU).  `out` must be given (it may be float32
+    with bf16 queries).  Calls that could overlap on one GPU must not be
+    issued: they share the array."""
+    desc = cache_desc(k_cache, v_cache, k_scale, v_scale)
+    if q.dtype != io_dtype(k_cache):
+        raise ValueError("q must have the pools' dtype")
+    S, Hq, hs = q.shape
+    if hs != desc.head_size:
+        raise ValueError("q head size does not match the pools")
+    if new_k.shape != new_v.shape or tuple(new_k.shape) != (S, desc.num_kv_heads, desc.head_size):
+        raise ValueError("new_k and new_v must be [S, Hkv, head_size]")
+    if new_k.dtype != io_dtype(k_cache) or new_v.dtype != io_dtype(k_cache):
+        raise ValueError("new_k, new_v and the pools must share a dtype")
+    if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_tables and seq_lens must be int32")
+    if block_tables.shape[0] != S or seq_lens.shape != (S,):
+        raise ValueError("block_tables must be [S, M] and seq_lens [S]")
+    if slot_mapping is not None and (slot_mapping.dtype != torch.int64 or slot_mapping.shape != (S,)):
+        raise ValueError("slot_mapping must be int64 [S]")
+    if out is None:
+        raise ValueError("out must be given (this call allocates nothing)")
+    out = _out_tensor(q, out, None, desc)
+    _check("paged_decode_step_static", library().paged_decode_step_static(
+        _dev(q, "q"), _dev(new_k, "new_k"), _dev(new_v, "new_v"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_tables, "block_tables"), _dev(seq_lens, "seq_lens"), S, Hq, block_tables.shape[1],
+        ctypes.byref(desc), float(scale), _dev(out, "out"),
+        _dev(slot_mapping, "slot_mapping") if slot_mapping is not None else None, int(partition_tokens),
+        _stream(stream)))
     return out
 
 

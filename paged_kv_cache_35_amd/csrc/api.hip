@@ -3,7 +3,9 @@
 // include/pkv.h.
 #include <string.h>
 
+#include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/pkv.h"
 #include "pkv_internal.h"
@@ -706,6 +708,84 @@ pkv_status paged_decode_step(const void* q, const void* new_k, const void* new_v
     if (st != PKV_OK)
         return st;
     return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+// Workspace of paged_decode_step_static: a file-scope device array, one copy
+// per GPU (each at its own address), held until the process ends.  In host
+// code the name `scratch` is only a stand-in for the symbol: its device
+// address comes from hipGetSymbolAddress, called once per device with that
+// device current, and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[PKV_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// The current device's copy of `scratch` (looked up on the first call on
+// each device).
+pkv_status device_scratch(void** ptr)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_status(e);
+    if (dev < 0 || dev >= kMaxDevices)
+        return PKV_ERR_UNSUPPORTED;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess)
+                return hip_status(e);
+            if (!p)
+                return PKV_ERR_HIP;
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pkv_status paged_decode_step_static(const void* q, const void* new_k, const void* new_v, void* k_cache,
+                                    void* v_cache, const int32_t* block_tables, const int32_t* seq_lens,
+                                    int32_t num_seqs, int32_t num_q_heads, int32_t max_blocks_per_seq,
+                                    const pkv_cache_desc* cache, float scale, void* out, int64_t* slot_mapping,
+                                    int32_t partition_tokens, void* stream)
+{
+    // the sizes are checked here only as far as the workspace needs them;
+    // paged_decode_step checks everything else before its first launch
+    if (num_seqs < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0)
+        return PKV_ERR_INVALID_ARG;
+    const pkv_status st = check_cache(cache);
+    if (st != PKV_OK)
+        return st;
+    const size_t need = pkv_decode_step_workspace_bytes(num_seqs, num_q_heads, cache->num_kv_heads,
+                                                        cache->head_size, max_blocks_per_seq, cache->block_size,
+                                                        partition_tokens);
+    if (need > PKV_STATIC_SCRATCH_BYTES)
+        return PKV_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0) {
+        const pkv_status ss = device_scratch(&ws);
+        if (ss != PKV_OK)
+            return ss;
+    }
+    // nothing in the step needs the workspace cleared: the append launch
+    // writes the whole schedule and each chunk partial is written before the
+    // merge reads it
+    return paged_decode_step(q, new_k, new_v, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_q_heads,
+                             max_blocks_per_seq, cache, scale, out, slot_mapping, ws, need > 0 ? need : 0,
+                             partition_tokens, stream);
 }
 
 pkv_status pkv_copy_blocks(const int32_t* pairs, int32_t num_pairs, const pkv_cache_desc* cache, void* k_cache,

@@ -339,6 +339,29 @@ def test_output_type_flag_is_checked(lib):
     assert attn(lib, d=d, S=0) == OK
 
 
+def step_static(lib, *, S=4, Hq=8, M=4, d=None, P=0):
+    d = d or desc()
+    return lib.paged_decode_step_static(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, S, Hq, M, ctypes.byref(d), 0.125,
+                                        FAKE, None, P, None)
+
+
+def test_static_step_checks_arguments_before_anything_else(lib):
+    # sizes whose workspace exceeds the library's device array, bad sizes and
+    # descriptors: rejected on the host, nothing touched
+    big = desc(nb=1, hkv=8, B=32, hs=128, dtype=1)
+    assert pkv.step_workspace_bytes(512, 64, 8, 128, 4096, 32) > pkv.STATIC_SCRATCH_BYTES
+    assert step_static(lib, S=512, Hq=64, M=4096, d=big) == WORKSPACE
+    assert step_static(lib, S=-1) == INVALID
+    assert step_static(lib, d=desc(hs=96)) == UNSUPPORTED
+    assert step_static(lib, S=0) == OK
+
+
+def test_static_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define PKV_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pkv.STATIC_SCRATCH_BYTES
+
+
 def validate(lib, *, bt=FAKE, sl=FAKE, S=4, M=4, slots=None, T=0, rc=None, d=None, report=FAKE):
     d = d or desc()
     return lib.pkv_validate(bt, sl, S, M, slots, T, rc, ctypes.byref(d), report, None)
