@@ -617,16 +617,18 @@ VALIDATE_FIELDS = ("bad_seq_lens", "bad_block_ids", "bad_slots", "duplicate_slot
                    "first_shared_block_write")
 
 
-def validate(block_tables: torch.Tensor, seq_lens: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+def validate(block_tables: torch.Tensor, seq_lens: torch.Tensor, num_blocks: int, block_size: int,
              slot_mapping: Optional[torch.Tensor] = None, ref_counts: Optional[torch.Tensor] = None,
              stream=None) -> dict:
     """Checks tables, lengths and slots against the kernels' device-side
-    contract (block IDs in the pool, lengths within the table, distinct slots
-    inside the pool, no slot in a block with ref_counts > 1) and returns the
-    report as a dict of VALIDATE_FIELDS (first_* = -1 when none).  Without
-    slot_mapping the decode step's slots are checked.  Reads no pool data;
-    waits for the GPU to return the report."""
-    desc = cache_desc(k_cache, v_cache)
+    contract for a pool of num_blocks blocks of block_size tokens (block IDs
+    in the pool, lengths within the table, distinct slots inside the pool, no
+    slot in a block with ref_counts > 1) and returns the report as a dict of
+    VALIDATE_FIELDS (first_* = -1 when none).  Without slot_mapping the
+    decode step's slots are checked.  Reads no pool data; waits for the GPU
+    to return the report."""
+    # only the pool's block count and block size matter to the check
+    desc = CacheDesc(int(num_blocks), 1, int(block_size), 128, PKV_BF16, 1.0, 1.0, 0)
     if block_tables.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise ValueError("block_tables and seq_lens must be int32")
     S, M = block_tables.shape
