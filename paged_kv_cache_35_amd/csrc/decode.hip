@@ -109,27 +109,41 @@ __device__ __forceinline__ V load_stream(const V* p)
     return __builtin_nontemporal_load(p);
 }
 
+// Address of one lane's operand: a wave-uniform base (the tile pointer plus
+// the offset that does not depend on the lane, which stays in scalar
+// registers) plus the lane's own unsigned byte offset.  Written this way the
+// loads take the scalar-base + 32-bit vector-offset form, so a unit's loads
+// share one or two offset registers instead of a 64-bit address each.
+template <typename E>
+__device__ __forceinline__ const E* lane_at(const E* base, int uniform_elems, uint32_t lane_bytes)
+{
+    return reinterpret_cast<const E*>(reinterpret_cast<const char*>(base + uniform_elems) + lane_bytes);
+}
+
 // Issue the loads of 16-token sub-tile m of one (block, KV head) tile.
 // `tile_k`/`tile_v` point at the tile's first element; lane = 16*r + c.
 template <typename T, int HS, int BS>
 __device__ __forceinline__ void load_tile(TileRegs<T, HS>& t, const T* __restrict__ tile_k,
                                           const T* __restrict__ tile_v, int m, int r, int c)
 {
+    // (bf16 keeps plain element offsets here: the scalar-base form saves
+    // nothing at 16 tokens and costs the head-size-64 variants a wave)
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int i = 0; i < HS / 32; ++i)  // chunk 4i + r of token 16m + c
             t.k.v[i] = load_stream((const bf16x8*)(tile_k + ((4 * i + r) * BS + 16 * m + c) * 8));
+#pragma unroll
+        for (int i = 0; i < HS / 16; ++i)  // head dim 16i + c, tokens 16m + 4r .. +3
+            t.v.v[i] = load_stream((const bf16x4*)(tile_v + (16 * i + c) * BS + 16 * m + 4 * r));
     } else {
+        const uint32_t k_lane = (uint32_t)(r * BS + c) * 16u;
+        const uint32_t v_lane = (uint32_t)(c * BS + 4 * r) * 4u;
 #pragma unroll
         for (int i = 0; i < HS / 16; ++i)
-            t.k.v[i] = load_stream((const f32x4*)(tile_k + ((4 * i + r) * BS + 16 * m + c) * 4));
-    }
+            t.k.v[i] = load_stream((const f32x4*)lane_at(tile_k, (4 * i * BS + 16 * m) * 4, k_lane));
 #pragma unroll
-    for (int i = 0; i < HS / 16; ++i) {  // head dim 16i + c, tokens 16m + 4r .. +3
-        if constexpr (sizeof(T) == 2)
-            t.v.v[i] = load_stream((const bf16x4*)(tile_v + (16 * i + c) * BS + 16 * m + 4 * r));
-        else
-            t.v.v[i] = load_stream((const f32x4*)(tile_v + (16 * i + c) * BS + 16 * m + 4 * r));
+        for (int i = 0; i < HS / 16; ++i)
+            t.v.v[i] = load_stream((const f32x4*)lane_at(tile_v, 16 * i * BS + 16 * m, v_lane));
     }
 }
 
@@ -199,14 +213,18 @@ template <int HS, int BS>
 __device__ __forceinline__ void load_wide(WideRegs<HS>& t, const __bf16* __restrict__ tile_k,
                                           const __bf16* __restrict__ tile_v, int m, int r, int c)
 {
+    // key chunk 4i + r of token 32m + 16mp + c; value head dim 16i + c,
+    // tokens 32m + 8r .. +7 (lane parts in bytes)
+    const uint32_t k_lane = (uint32_t)(r * BS + c) * 16u;
+    const uint32_t v_lane = (uint32_t)(c * BS + 8 * r) * 2u;
 #pragma unroll
     for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
         for (int i = 0; i < HS / 32; ++i)
-            t.k[mp].v[i] = load_stream((const bf16x8*)(tile_k + ((4 * i + r) * BS + 32 * m + 16 * mp + c) * 8));
+            t.k[mp].v[i] = load_stream((const bf16x8*)lane_at(tile_k, (4 * i * BS + 32 * m + 16 * mp) * 8, k_lane));
 #pragma unroll
-    for (int i = 0; i < HS / 16; ++i)  // head dim 16i + c, tokens 32m + 8r .. +7
-        t.v[i] = load_value_part((const bf16x8*)(tile_v + (16 * i + c) * BS + 32 * m + 8 * r), BS == 32);
+    for (int i = 0; i < HS / 16; ++i)
+        t.v[i] = load_value_part((const bf16x8*)lane_at(tile_v, 16 * i * BS + 32 * m, v_lane), BS == 32);
 }
 
 // FP8 (E4M3) caches, bf16 queries: one 16-token sub-tile as raw codes.
@@ -228,12 +246,14 @@ template <int HS, int BS>
 __device__ __forceinline__ void load_fp8(Fp8Regs<HS>& t, const uint8_t* __restrict__ tile_k,
                                          const uint8_t* __restrict__ tile_v, int m, int r, int c)
 {
+    const uint32_t k_lane = (uint32_t)(r * BS + c) * 16u;
+    const uint32_t v_lane = (uint32_t)(c * BS + 4 * r);
 #pragma unroll
     for (int i = 0; i < HS / 64; ++i)
-        t.k[i] = load_stream((const u32x4*)(tile_k + ((4 * i + r) * BS + 16 * m + c) * 16));
+        t.k[i] = load_stream((const u32x4*)lane_at(tile_k, (4 * i * BS + 16 * m) * 16, k_lane));
 #pragma unroll
     for (int i = 0; i < HS / 16; ++i)
-        t.v[i] = load_stream((const unsigned*)(tile_v + (16 * i + c) * BS + 16 * m + 4 * r));
+        t.v[i] = load_stream((const unsigned*)lane_at(tile_v, 16 * i * BS + 16 * m, v_lane));
 }
 
 template <int HS>
@@ -275,14 +295,16 @@ __device__ __forceinline__ void load_fp8_wide(Fp8WideRegs<HS>& t, const uint8_t*
                                               const uint8_t* __restrict__ tile_v, int m, int r, int c)
 {
     typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const uint32_t k_lane = (uint32_t)(r * BS + c) * 16u;
+    const uint32_t v_lane = (uint32_t)(c * BS + 8 * r);
 #pragma unroll
     for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
         for (int i = 0; i < HS / 64; ++i)
-            t.k[mp][i] = load_stream((const u32x4*)(tile_k + ((4 * i + r) * BS + 32 * m + 16 * mp + c) * 16));
+            t.k[mp][i] = load_stream((const u32x4*)lane_at(tile_k, (4 * i * BS + 32 * m + 16 * mp) * 16, k_lane));
 #pragma unroll
     for (int i = 0; i < HS / 16; ++i) {
-        const u32x2 w = load_value_part((const u32x2*)(tile_v + (16 * i + c) * BS + 32 * m + 8 * r), BS == 32);
+        const u32x2 w = load_value_part((const u32x2*)lane_at(tile_v, 16 * i * BS + 32 * m, v_lane), BS == 32);
         t.v[i][0] = w[0];
         t.v[i][1] = w[1];
     }
@@ -388,8 +410,6 @@ constexpr int decode_waves_per_eu(int elem, int HS, int BS, bool F8, bool MQ)
     if (elem != 2)
         return 1;
     int w = BS == 1 ? 2 : (BS <= 16 ? 3 : 2);
-    if (BS == 64 && HS == 128 && !F8)
-        w = 1;
     if (F8 && MQ)
         w -= 1;
     return w < 1 ? 1 : w;
@@ -494,14 +514,19 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     //   chunk learns that its sequence has no such chunk from one length
     //   load.
     int s = yr;
+    bool s_ok = true;  // false: a schedule entry outside the batch
     if (sched_order) {
         // schedule given (decode step): rank y's sequence, length and table
         // row are read below from y alone.  An order that does not belong
         // to this batch (caller error) must not send the work-group to a
-        // sequence outside it: q, q_start and out are indexed by s.
+        // sequence outside it: q and q_start are read at sequence 0 instead
+        // and the work-group takes the empty-sequence exit below without
+        // storing anything.  (A return of its own here costs the FP8
+        // variants registers: the compiler then holds the prologue's loads
+        // back.)
         s = sched_items ? s_listed : sched_order[yr];
-        if ((unsigned)s >= (unsigned)S_grid)
-            return;  // uniform (one index per work-group), before any barrier
+        s_ok = (unsigned)s < (unsigned)S_grid;
+        s = s_ok ? s : 0;
     } else if (lpt && chunk == 0) {
         const int S = S_grid;  // <= kLptMaxSeqs = 64, M < 2^23 (checked on the host)
         unsigned* sm_key = reinterpret_cast<unsigned*>(&sm_out[0][0]);
@@ -572,14 +597,14 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
             return;  // uniform: before any barrier
     }
 
-    const int L = L_in < 0 ? 0 : (L_in > M * BS ? M * BS : L_in);
+    const int L = (L_in < 0 || !s_ok) ? 0 : (L_in > M * BS ? M * BS : L_in);
     // row rho of the tile, as (query row, head) of out
     auto out_row = [&](int rho) __attribute__((always_inline)) -> int64_t {
         const int i = rho / G;
         return ((int64_t)(qs0 + i) * Hq + (int64_t)kvh * G + (rho - i * G)) * HS;
     };
     if (L == 0) {
-        if (chunk == 0 && w == 0) {
+        if (chunk == 0 && w == 0 && s_ok) {
             if constexpr (MQ) {
                 for (int idx = lane; idx < tile_rows * HS; idx += 64)
                     store_out<T>(out, out_row(16 * rt + idx / HS) + idx % HS, 0.f, out_f32);
