@@ -545,13 +545,15 @@ def contiguous_tables(w) -> np.ndarray:
     """The workload's block tables with each sequence's blocks renumbered to
     adjacent IDs (sequence after sequence from block 0): the same kernel and
     sizes on contiguous storage, for the paged-vs-contiguous diagnostic (the
-    timing does not depend on the values the blocks hold)."""
+    timing does not depend on the values the blocks hold).  None when the
+    pool cannot hold every sequence's blocks apart (shared blocks)."""
     nblk = -(-np.clip(w.seq_lens.astype(np.int64), 0, None) // w.B)
+    if int(nblk.sum()) > w.num_blocks:
+        return None
     base = np.concatenate([[0], np.cumsum(nblk)[:-1]])
     t = np.full_like(w.block_tables, w.block_tables[0, 0])
     for s in range(w.S):
         t[s, :nblk[s]] = base[s] + np.arange(nblk[s])
-    assert int(nblk.sum()) <= w.num_blocks
     return t.astype(np.int32)
 
 
@@ -694,8 +696,11 @@ def bench_decode(args, config: int, torch, pkv, pi, sr: dict, seed: int) -> dict
     # sequence's blocks renumbered adjacent (after the parity check, since
     # the appends through these tables write other slots)
     contig = None
-    if not args.contiguous and not args.no_contiguous_diag:
-        ct = torch.from_numpy(contiguous_tables(w)).cuda()
+    ct_host = None if (args.contiguous or args.no_contiguous_diag) else contiguous_tables(w)
+    if ct_host is None and not (args.contiguous or args.no_contiguous_diag):
+        contig = {"skipped": "the tables share blocks: their blocks cannot all be laid out apart in this pool"}
+    if ct_host is not None:
+        ct = torch.from_numpy(ct_host).cuda()
         cevs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
         for _ in range(max(2, args.warmup)):
             step_timed(tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)), ct)

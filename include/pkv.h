@@ -399,9 +399,9 @@ PKV_API size_t pkv_multi_token_workspace_bytes(int32_t num_seqs, int32_t num_q_h
 /*
  * Bytes of device workspace of paged_multi_token_step with the batch's
  * longest-first schedule: the attention partials
- * (pkv_multi_token_workspace_bytes), rounded up to 256, plus the schedule
- * (pkv_decode_schedule_bytes); just the partials when no schedule applies
- * (PKV_PARTITION_NONE, or num_seqs outside 2 .. 4096).
+ * (pkv_multi_token_workspace_bytes; none with PKV_PARTITION_NONE), rounded
+ * up to 256, plus the schedule (pkv_decode_schedule_bytes); just the
+ * partials when no schedule applies (num_seqs outside 2 .. 4096).
  */
 PKV_API size_t pkv_multi_token_step_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                                     int32_t head_size, int32_t max_q_len,
@@ -450,8 +450,8 @@ PKV_API pkv_status pkv_multi_token_append(const void* k, const void* v, const in
  * pkv_multi_token_slot_mapping, or paged_multi_token_step).  schedule:
  * the longest-first schedule pkv_multi_token_slot_mapping (or
  * pkv_decode_append) wrote for these same block_tables and seq_lens, or
- * NULL, as in paged_decode_attention (the partitioned kernel reads it; the
- * results are bit-identical either way).
+ * NULL, as in paged_decode_attention (both kernels start the longest
+ * sequences first with it; the results are bit-identical either way).
  * PKV_ERR_UNSUPPORTED for max_q_len > 65535 or num_seqs > 65535.
  */
 PKV_API pkv_status paged_multi_token_attention(const void* q, const int32_t* q_start, int32_t num_q_rows,

@@ -614,7 +614,7 @@ size_t pkv_multi_token_step_workspace_bytes(int32_t num_seqs, int32_t num_q_head
         return 0;
     const size_t attn = pkv_multi_token_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_size, max_q_len,
                                                         max_blocks_per_seq, block_size, partition_tokens);
-    if (partition_tokens == PKV_PARTITION_NONE ||
+    if (partition_tokens != PKV_PARTITION_NONE &&
         pkv_decode_partition_tokens(num_seqs, num_q_heads, num_kv_heads, head_size, max_blocks_per_seq, block_size,
                                     partition_tokens) <= 0)
         return attn;
@@ -644,15 +644,17 @@ pkv_status paged_multi_token_step(const void* q, const void* new_k, const void* 
         return PKV_ERR_UNSUPPORTED;
     // With room for it (pkv_multi_token_step_workspace_bytes), the slot
     // mapping launch writes the longest-first schedule after the attention
-    // partials and the attention launch reads it; a workspace of
-    // pkv_multi_token_workspace_bytes runs the same step without it.
-    // (Not written when the unpartitioned kernel runs: it does not use it.)
+    // partials and the attention launch reads it (either kernel); a
+    // workspace of pkv_multi_token_workspace_bytes runs the same step
+    // without it.
     pkv::AppendArgs::Schedule sched = {};
-    const size_t attn = pkv_multi_token_workspace_bytes(num_seqs, num_q_heads, cache->num_kv_heads,
-                                                        cache->head_size, max_q_len, max_blocks_per_seq,
-                                                        cache->block_size, partition_tokens);
+    const size_t attn = partition_tokens == PKV_PARTITION_NONE
+                            ? 0
+                            : pkv_multi_token_workspace_bytes(num_seqs, num_q_heads, cache->num_kv_heads,
+                                                              cache->head_size, max_q_len, max_blocks_per_seq,
+                                                              cache->block_size, partition_tokens);
     const size_t sb = pkv_decode_schedule_bytes(num_seqs, max_blocks_per_seq);
-    if (!picks_prefill(a, partition_tokens) && sb > 0 && workspace && workspace_bytes >= round_up(attn, 256) + sb) {
+    if (sb > 0 && workspace && workspace_bytes >= round_up(attn, 256) + sb) {
         sched = schedule_parts((char*)workspace + round_up(attn, 256), num_seqs, max_blocks_per_seq,
                                cache->block_size);
         use_schedule(a, sched, partition_tokens);

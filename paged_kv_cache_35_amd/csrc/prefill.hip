@@ -104,7 +104,8 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     const typename std::conditional<F8, uint8_t, __bf16>::type* __restrict__ v_cache,
     const int32_t* __restrict__ block_tables, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ q_start, int32_t num_q_rows, int32_t max_q_len, int32_t Hq, int32_t Hkv, int32_t M,
-    int32_t num_blocks, int32_t RB, float qscale, float oscale, void* __restrict__ out, int32_t out_f32)
+    int32_t num_blocks, int32_t RB, float qscale, float oscale, void* __restrict__ out, int32_t out_f32,
+    int32_t num_seqs, const int32_t* __restrict__ sched_order)
 {
     static_assert(BS >= 16 && (BS % 16) == 0, "blocks of 16, 32 or 64 tokens");
     constexpr int TILE = HS * BS;  // elements of one (block, KV head) tile
@@ -114,19 +115,31 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     constexpr int KSLOTS = HS * 4;
     __shared__ bf16x8 lds[NST * STAGE_SLOTS];
 
-    // XCD-aware order: work-groups are dealt to the 8 XCDs round-robin by
-    // their linear index, and each XCD has its own L2.  The row blocks of one
-    // (sequence, KV head) read the same keys and values, so consecutive
-    // logical indices are mapped to one XCD: physical index p runs on XCD
-    // p % 8, and XCD x takes the x-th contiguous share of the logical range.
-    const int64_t N = (int64_t)gridDim.x;
+    // Work order.  Work-groups are dealt to the 8 XCDs round-robin by their
+    // linear index p (XCD p % 8), each XCD has its own L2, and on an XCD
+    // they start in increasing p.  The RB row blocks of one (sequence, KV
+    // head) pair read the same keys and values, so they go to one XCD: pair
+    // g = rank * Hkv + kvh runs on XCD g % 8, its row blocks at consecutive
+    // slots p / 8 there.  Pairs are taken in rank order, the sequence of
+    // rank y being sched_order[y] (longest first, from the longest-first
+    // schedule) or sequence y without one, and a pair's row blocks last row
+    // block first (it sees the most tokens): so the longest work starts
+    // first on every XCD and no long sequence is left running alone at the
+    // end.  The grid is rounded up to whole rounds of 8 pairs; work-groups
+    // past the last pair exit at once.
     const int64_t p = blockIdx.x;
     const int64_t xcd = p % kXcds, slot = p / kXcds;
-    const int64_t q8 = N / kXcds, rem = N % kXcds;
-    const int64_t logical = (xcd < rem ? xcd * (q8 + 1) : rem * (q8 + 1) + (xcd - rem) * q8) + slot;
-    const int rb = (int)(logical % RB);
-    const int kvh = (int)((logical / RB) % Hkv);
-    const int s = (int)(logical / ((int64_t)RB * Hkv));
+    const int64_t pair = (slot / RB) * kXcds + xcd;
+    if (pair >= (int64_t)num_seqs * Hkv)
+        return;  // uniform, before any barrier
+    const int rb = RB - 1 - (int)(slot % RB);
+    const int kvh = (int)(pair % Hkv);
+    const int rank = (int)(pair / Hkv);
+    int s = sched_order ? sched_order[rank] : rank;
+    // an order that does not belong to this batch (caller error) names a
+    // sequence outside it: that work-group writes nothing
+    const bool s_ok = (unsigned)s < (unsigned)num_seqs;
+    s = s_ok ? s : 0;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -137,7 +150,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     int qs0 = q_start[s];
     const int qs1 = q_start[s + 1];
     int n = qs1 - qs0;
-    if (qs0 < 0 || n < 0 || qs1 > num_q_rows)
+    if (qs0 < 0 || n < 0 || qs1 > num_q_rows || !s_ok)
         n = 0;
     n = n < max_q_len ? n : max_q_len;
     const int nrows = n * G;
@@ -560,11 +573,14 @@ static hipError_t launch_prefill_typed(const DecodeArgs& a, hipStream_t stream)
     const int G = a.num_q_heads / a.num_kv_heads;
     const int RB = (a.max_q_len * G + kPfRows - 1) / kPfRows;
     const float qscale = a.scale * kLog2e * (F8 ? a.k_scale : 1.0f);
-    const int64_t groups = (int64_t)a.num_seqs * a.num_kv_heads * RB;  // < 2^31: checked on the host
+    // whole rounds of kXcds (sequence, KV head) pairs (see the work order in the kernel)
+    const int64_t pairs = (int64_t)a.num_seqs * a.num_kv_heads;
+    const int64_t groups = (pairs + kXcds - 1) / kXcds * kXcds * RB;  // < 2^31: checked on the host
     hipLaunchKernelGGL((paged_prefill_kernel<HS, BS, F8>), dim3((unsigned)groups), dim3(kPfThreads), 0,
                        stream, (const __bf16*)a.q, (const C*)a.k_cache, (const C*)a.v_cache, a.block_tables,
                        a.seq_lens, a.q_start, a.num_q_rows, a.max_q_len, a.num_q_heads, a.num_kv_heads,
-                       a.max_blocks_per_seq, a.num_blocks, RB, qscale, F8 ? a.v_scale : 1.0f, a.out, a.out_f32);
+                       a.max_blocks_per_seq, a.num_blocks, RB, qscale, F8 ? a.v_scale : 1.0f, a.out, a.out_f32,
+                       a.num_seqs, a.sched_order);
     return hipGetLastError();
 }
 
@@ -586,7 +602,7 @@ bool prefill_shape_supported(int32_t dtype, int32_t block_size, int32_t head_siz
 int64_t prefill_work_groups(int64_t num_seqs, int64_t num_q_heads, int64_t num_kv_heads, int64_t max_q_len)
 {
     const int64_t G = num_q_heads / num_kv_heads;
-    return num_seqs * num_kv_heads * ((max_q_len * G + kPfRows - 1) / kPfRows);
+    return (num_seqs * num_kv_heads + kXcds - 1) / kXcds * kXcds * ((max_q_len * G + kPfRows - 1) / kPfRows);
 }
 
 bool prefill_supported(const DecodeArgs& a)

@@ -206,10 +206,11 @@ def test_multi_token_step_workspace_sizes(lib):
     # no partials (one chunk covers the table): the schedule alone
     assert attn(64, 32, 32, 128, 8, 128, 16, 0) == 0
     assert f(64, 32, 32, 128, 8, 128, 16, 0) == sched(64, 128)
-    # no schedule: one sequence, more than 4096, or the unpartitioned kernel
+    # no schedule: one sequence or more than 4096
     assert f(1, 32, 8, 128, 4, 1024, 16, 0) == attn(1, 32, 8, 128, 4, 1024, 16, 0)
     assert f(4097, 32, 8, 128, 4, 8, 16, 0) == attn(4097, 32, 8, 128, 4, 8, 16, 0)
-    assert f(16, 32, 8, 128, 512, 1024, 16, -1) == 0
+    # the unpartitioned kernel: no partials, the schedule alone
+    assert f(16, 32, 8, 128, 512, 1024, 16, -1) == sched(16, 1024)
     # invalid shapes: 0
     assert f(16, 30, 8, 128, 4, 1024, 16, 0) == 0
     assert f(16, 32, 8, 128, 0, 1024, 16, 0) == 0

@@ -355,6 +355,52 @@ def test_attention_with_a_caller_schedule(S):
     assert torch.equal(sched, dsched)
 
 
+@pytest.mark.parametrize("S,q_lens,B", [(20, 40, 16), (13, 70, 32), (9, [200, 3, 64, 17, 90, 1, 33, 129, 8], 64)])
+def test_unpartitioned_kernel_with_the_schedule(S, q_lens, B):
+    # the unpartitioned kernel takes (sequence, KV head) pairs longest first
+    # when given the schedule (13 sequences x 8 KV heads is not a whole round
+    # of 8 pairs per XCD): the step with its schedule, the attention with a
+    # caller schedule and the attention without one give the same bits, and
+    # match the oracle
+    w = pi.make_workload(3, S=S, len_lo=16, len_hi=2000, B=B, seed=40 + S, q_lens=q_lens)
+    announce(f"unpartitioned kernel with schedule: S={S} B={B} rows={w.rows} lens {list(w.seq_lens)}")
+    m = pkv()
+    NONE = m.PARTITION_NONE
+    r = MRun(w, partition_tokens=NONE)
+    full_check(w, r)
+    ws = m.alloc_multi_token_step_workspace(r.q, r.kc, r.vc, r.bt, w.max_q_len, NONE)
+    assert ws is not None
+    kc, vc = dev(w.k_cache), dev(w.v_cache)
+    slots = torch.empty(w.rows, dtype=torch.int64, device="cuda")
+    out = m.paged_multi_token_step(r.q, r.nk, r.nv, kc, vc, r.qs, w.max_q_len, r.bt, r.sl, w.scale,
+                                   slot_mapping=slots, workspace=ws, partition_tokens=NONE)
+    sched = m.alloc_schedule(r.bt)
+    m.multi_token_slot_mapping(r.bt, r.sl, r.qs, w.rows, w.max_q_len, w.B, schedule=sched)
+    out2 = m.paged_multi_token_attention(r.q, r.qs, w.max_q_len, r.kc, r.vc, r.bt, r.sl, w.scale,
+                                         partition_tokens=NONE, schedule=sched)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), r.out.view(torch.int16))
+    assert torch.equal(out2.view(torch.int16), r.out.view(torch.int16))
+
+
+def test_unpartitioned_kernel_contains_a_foreign_schedule():
+    # a schedule never written for this batch (every word outside it): no
+    # work-group writes outside out (guard rows around it keep their bits)
+    w = pi.make_workload(3, S=10, len_lo=100, len_hi=900, seed=50, q_lens=70)
+    announce("unpartitioned kernel, foreign schedule")
+    m = pkv()
+    q, kc, vc = dev(w.q), dev(w.k_cache), dev(w.v_cache)
+    bt, sl, qs = dev(w.block_tables), dev(w.seq_lens), dev(w.q_start)
+    sched = m.alloc_schedule(bt)
+    sched.view(torch.int32).fill_(0x7FFF7FFF)
+    guard = torch.full((w.rows + 2, w.Hq, w.hs), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = guard[1:w.rows + 1]
+    m.paged_multi_token_attention(q, qs, w.max_q_len, kc, vc, bt, sl, w.scale, out=out,
+                                  partition_tokens=m.PARTITION_NONE, schedule=sched)
+    torch.cuda.synchronize()
+    assert torch.all(guard[0] == 7.0).item() and torch.all(guard[w.rows + 1] == 7.0).item()
+
+
 @pytest.mark.parametrize("P", [0, 64, -1])
 def test_broken_row_ranges_are_contained(P):
     # caller contract violations the kernels must contain (both kernels):
