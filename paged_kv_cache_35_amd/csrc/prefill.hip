@@ -360,28 +360,43 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                             (t0 + tt < Lq[kt] && ((tmask >> tt) & 1)) ? sc[kt][4 * mp + jj] : -INFINITY;
                     }
         }
-        // Online softmax of tile kt up to the bf16 hi / lo probability
-        // operands.  The running maximum is raised only when a score exceeds
-        // it by more than kRescaleSlack; the accumulators are rescaled by the
-        // caller (rescale_tile) before the next value sum into them.
-        auto softmax = [&](int kt, bf16x8& hi, bf16x8& lo, float& alpha) __attribute__((always_inline)) -> bool {
+        // Online softmax of tile kt, in two parts.  raise_max: the running
+        // maximum is raised only when a score exceeds it by more than
+        // kRescaleSlack, and then alpha (the factor the accumulators are
+        // rescaled by, in rescale_tile, before the next value sum into them)
+        // is formed; probs: the exponentials and the bf16 hi / lo probability
+        // operands.  The split lets tile 1's rare branch sit before tile 0's
+        // value sum, so that tile 1's exponentials can be issued between
+        // tile 0's matrix instructions.
+        auto raise_max = [&](int kt, float& alpha) __attribute__((always_inline)) -> bool {
             // IEEE maximum (NaN-propagating): three-operand instructions
             // that need no canonicalization of the matrix results, unlike fmaxf
-            float mx = __builtin_elementwise_maximum(
+            const float mx = __builtin_elementwise_maximum(
                 __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[kt][0], sc[kt][1]),
                                               __builtin_elementwise_maximum(sc[kt][2], sc[kt][3])),
                 __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[kt][4], sc[kt][5]),
                                               __builtin_elementwise_maximum(sc[kt][6], sc[kt][7])));
-            mx = max_over_lane_groups(mx) * qscale;
-            const bool raise = __ballot(mx > m_run[kt] + kRescaleSlack) != 0;  // uniform
-            const float m_new = raise ? fmaxf(m_run[kt], mx) : m_run[kt];
-            alpha = __builtin_amdgcn_exp2f(m_run[kt] - m_new);  // 1 unless raised
-            m_run[kt] = m_new;
-            l_part[kt] *= alpha;
+            // A row's maximum exceeds the running maximum by the slack exactly
+            // when one of its lanes' own maxima does (the running maximum is
+            // the same in the row's four lane groups, and scaling by qscale > 0
+            // keeps the order), so the ballot needs no exchange between lane
+            // groups; the row maximum is formed only when the maximum rises.
+            const bool raise = __ballot(mx * qscale > m_run[kt] + kRescaleSlack) != 0;  // uniform
+            alpha = 1.f;
+            if (raise) {
+                const float m_new = fmaxf(m_run[kt], max_over_lane_groups(mx) * qscale);
+                alpha = __builtin_amdgcn_exp2f(m_run[kt] - m_new);
+                m_run[kt] = m_new;
+                l_part[kt] *= alpha;
+            }
+            return raise;
+        };
+        auto probs = [&](int kt, bf16x8& hi, bf16x8& lo) __attribute__((always_inline)) {
+            const float m_cur = m_run[kt];
             float pv[8];  // pv[e]: token 8r + e (key_token order)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][e], qscale, -m_new));
+                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kt][e], qscale, -m_cur));
                 l_part[kt] += pv[e];
             }
             // hi = bf16(p) two at a time; lo = bf16(p - hi), with hi read back
@@ -398,7 +413,6 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
             }
             hi = __builtin_bit_cast(bf16x8, hw);
             lo = __builtin_bit_cast(bf16x8, lw);
-            return raise;
         };
         auto rescale_tile = [&](int kt, float alpha) __attribute__((always_inline)) {
             float a_row[4];
@@ -418,29 +432,31 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                 O[kt][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, vop[i], O[kt][i], 0, 0, 0);
             }
         };
-        // tile 0, then tile 1's softmax (vector work) written next to tile
-        // 0's value sum (matrix work) so the two can be issued interleaved;
-        // tile 1's rescale waits until after that
-        // The value sums (and tile 1's softmax between them) run at raised
-        // wave priority: of the two waves sharing a SIMD, the one with
+        // Both tiles' rare branches (raise and rescale) come first, so that
+        // what follows is one straight run: tile 0's value sum (matrix work)
+        // with tile 1's exponentials (vector work) written next to it, to be
+        // issued interleaved, then tile 1's value sum.
+        // The value sums (and tile 1's exponentials between them) run at
+        // raised wave priority: of the two waves sharing a SIMD, the one with
         // matrix work ready issues it first while the other computes its
         // scores and softmax, which keeps the matrix pipe busier (measured
         // 3 to 5 % faster on 512-token chunks; priority over the scores as
         // well, or over tile 0's value sum only, was not faster).
         bf16x8 hi0, lo0, hi1, lo1;
         float a0, a1;
-        if (softmax(0, hi0, lo0, a0))
+        if (raise_max(0, a0))
             rescale_tile(0, a0);
+        probs(0, hi0, lo0);
+        if (raise_max(1, a1))
+            rescale_tile(1, a1);
         __builtin_amdgcn_s_setprio(1);
         value_sum(0, hi0, lo0);
-        const bool raise1 = softmax(1, hi1, lo1, a1);
+        probs(1, hi1, lo1);
 #pragma unroll
         for (int k = 0; k < 2 * (HS / 16); ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four vector instructions
         }
-        if (raise1)
-            rescale_tile(1, a1);
         value_sum(1, hi1, lo1);
         __builtin_amdgcn_s_setprio(0);
     };
