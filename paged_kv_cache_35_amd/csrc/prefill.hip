@@ -25,10 +25,9 @@
 //    + m % 4: the scores of M-tiles mp = 0, 1 then give lane group r the
 //    tokens 8r .. 8r+7 in order, which is the token order of the value MFMA's
 //    operands, so the probabilities need no exchange between lanes.  Values sit
-//    as [hs][32 tokens] in four 16-byte slots per row; for the 16-byte reads
-//    of 16 consecutive head dims to hit distinct banks, the slots of row d
-//    are permuted (slot q holds tokens 8 (q ^ ((d / 4) % 4)) ..) in the bf16
-//    path, and the rows are padded by 8 elements in the FP8 path.
+//    as [hs][32 tokens] in four 16-byte slots per row, the slots of row d
+//    permuted (vslot) so that the value-operand reads are free of bank
+//    conflicts.
 //  * Each wave reads one unit's key and value operands once from LDS and
 //    uses them for both of its row tiles (scores, then the value sum with
 //    hi + lo bf16 probability parts as in decode).
@@ -58,13 +57,24 @@ __device__ __forceinline__ int key_token(int pos)
 {
     return 8 * ((pos & 15) >> 2) + 4 * (pos >> 4) + (pos & 3);
 }
-constexpr int kPfVRow = kPfUnit + 8;              // LDS value row (elements), padded
+// LDS slot (16 bytes) of tokens 8q .. 8q+7 of value row d: four slots per
+// row, permuted by (d / 4) % 4 through 0, 3, 2, 1.  A value-operand read has
+// lane group r = lane / 16 read slot r of row 16 i + lane % 16.  gfx950 serves
+// a 128-bit LDS read in four cycles when no two lanes of a cycle share a
+// 16-byte bank group; measured with the bank-conflict counter, this
+// permutation keeps the value-operand read at that rate, while the plain
+// layout, or the permutations q ^ ((d / 4) % 4) and 0, 3, 1, 2, cost four
+// extra cycles per read.
+__device__ __forceinline__ int vslot(int d, int q)
+{
+    return 4 * d + (q ^ ((0x6C >> (2 * ((d >> 2) & 3))) & 3));
+}
 constexpr int kXcds = 8;                          // MI355X: 8 XCDs of 32 compute units
 
 template <int HS>
 struct PfStage {
     bf16x8 k[HS / 8][kPfUnit];        // chunk f (head dims 8f .. 8f+7) of token t
-    __bf16 v[HS][kPfVRow];            // head dim d, token t
+    bf16x8 v[HS * 4];                 // slot vslot(d, q): head dim d, tokens 8q .. 8q+7
 };
 
 // s_waitcnt with vmcnt(n) and the other counters left alone (gfx9
@@ -76,12 +86,11 @@ __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Global reads of one unit: 4 * HS key and 4 * HS value pieces of 16 bytes
-// (bf16: 8 elements), or 2 * HS of each (FP8: 16 codes); a thread takes
-// pieces tid, tid + 256, ...
-template <int HS, bool F8>
+// Global reads of one unit from FP8 pools: 2 * HS key and 2 * HS value
+// pieces of 16 codes; a thread takes pieces tid, tid + 256, ...
+template <int HS>
 struct PfPieces {
-    static constexpr int P = F8 ? 2 * HS : 4 * HS;  // pieces of each kind
+    static constexpr int P = 2 * HS;  // pieces of each kind
     static constexpr int N = (P + kPfThreads - 1) / kPfThreads;
     u32x4 k[N];
     u32x4 v[N];
@@ -226,66 +235,52 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         return ((uint32_t)id < (uint32_t)num_blocks ? id : 0) * block_stride + head_off;
     };
 
-    // ---- staging: this thread's pieces of unit u ----
-    PfPieces<HS, F8> pc;
+    // ---- FP8 staging: this thread's pieces of unit u ----
+    PfPieces<HS> pc;
+    // Key piece p: chunk f16 = p / 32 (16 head dims) at LDS position p % 32.
+    // Value piece p: head dim d = p % HS, tokens 16 h .. 16 h + 15 with
+    // h = p / HS, so that the lanes of a wave deposit consecutive rows (the
+    // deposits then hit distinct bank groups in every pass, as the reads do).
     auto fetch = [&](int u) __attribute__((always_inline)) {
-        const int t0 = u * kPfUnit;
-        if (t0 / BS >= win + 64) {  // uniform: the unit's first block left the window
-            win += 64;
-            ids = ids_next;
-            ids_next = win + 64 + lane < M ? trow[win + 64 + lane] : 0;
-        }
+        if constexpr (F8) {
+            const int t0 = u * kPfUnit;
+            if (t0 / BS >= win + 64) {  // uniform: the unit's first block left the window
+                win += 64;
+                ids = ids_next;
+                ids_next = win + 64 + lane < M ? trow[win + 64 + lane] : 0;
+            }
 #pragma unroll
-        for (int k = 0; k < PfPieces<HS, F8>::N; ++k) {
-            const int p = tid + k * kPfThreads;
-            if (PfPieces<HS, F8>::P % kPfThreads != 0 && p >= PfPieces<HS, F8>::P)
-                break;
-            if constexpr (F8) {
-                // key chunk f16 (16 head dims) of token t; value codes of head
-                // dim d, tokens 16h .. 16h+15
+            for (int k = 0; k < PfPieces<HS>::N; ++k) {
+                const int p = tid + k * kPfThreads;
+                if (PfPieces<HS>::P % kPfThreads != 0 && p >= PfPieces<HS>::P)
+                    break;
                 const int f16 = p / kPfUnit, t = p % kPfUnit;  // LDS position t
                 const int T = t0 + key_token(t);
                 pc.k[k] = *(
                     (const u32x4*)(k_cache + block_at(T / BS) + ((int64_t)f16 * BS + T % BS) * 16));
-                const int d = p / 2, h = p % 2;
+                const int d = p % HS, h = p / HS;
                 const int Tv = t0 + 16 * h;
-                pc.v[k] = *(
-                    (const u32x4*)(v_cache + block_at(Tv / BS) + (int64_t)d * BS + Tv % BS));
-            } else {
-                // key chunk f (8 head dims) of token t; value head dim d,
-                // tokens 8 q8 .. 8 q8 + 7
-                const int f = p / kPfUnit, t = p % kPfUnit;  // LDS position t
-                const int T = t0 + key_token(t);
-                pc.k[k] = *(
-                    (const u32x4*)(k_cache + block_at(T / BS) + ((int64_t)f * BS + T % BS) * 8));
-                const int d = p / 4, q8 = p % 4;
-                const int Tv = t0 + 8 * q8;
                 pc.v[k] = *(
                     (const u32x4*)(v_cache + block_at(Tv / BS) + (int64_t)d * BS + Tv % BS));
             }
         }
     };
     auto deposit = [&](PfStage<HS>& st) __attribute__((always_inline)) {
+        if constexpr (F8) {
 #pragma unroll
-        for (int k = 0; k < PfPieces<HS, F8>::N; ++k) {
-            const int p = tid + k * kPfThreads;
-            if (PfPieces<HS, F8>::P % kPfThreads != 0 && p >= PfPieces<HS, F8>::P)
-                break;
-            if constexpr (F8) {
+            for (int k = 0; k < PfPieces<HS>::N; ++k) {
+                const int p = tid + k * kPfThreads;
+                if (PfPieces<HS>::P % kPfThreads != 0 && p >= PfPieces<HS>::P)
+                    break;
                 const int f16 = p / kPfUnit, t = p % kPfUnit;
                 u32x4 lo, hi;
                 fp8x16_to_bf16(pc.k[k], lo, hi);
                 st.k[2 * f16][t] = __builtin_bit_cast(bf16x8, lo);
                 st.k[2 * f16 + 1][t] = __builtin_bit_cast(bf16x8, hi);
-                const int d = p / 2, h = p % 2;
+                const int d = p % HS, h = p / HS;
                 fp8x16_to_bf16(pc.v[k], lo, hi);
-                *(u32x4*)&st.v[d][16 * h] = lo;
-                *(u32x4*)&st.v[d][16 * h + 8] = hi;
-            } else {
-                const int f = p / kPfUnit, t = p % kPfUnit;
-                st.k[f][t] = __builtin_bit_cast(bf16x8, pc.k[k]);
-                const int d = p / 4, q8 = p % 4;
-                *(u32x4*)&st.v[d][8 * q8] = pc.v[k];
+                st.v[vslot(d, 2 * h)] = __builtin_bit_cast(bf16x8, lo);
+                st.v[vslot(d, 2 * h + 1)] = __builtin_bit_cast(bf16x8, hi);
             }
         }
     };
@@ -322,7 +317,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
         for (int i = 0; i < HS / 16; ++i) {
             const int d = 16 * i + c;
-            vop[i] = F8 ? vst[d * (kPfVRow / 8) + r] : vst[d * 4 + (r ^ ((d >> 2) & 3))];
+            vop[i] = vst[vslot(d, r)];
         }
         const bool all_valid = tmask == 0xFFFFFFFFu;
         if (t0 + kPfUnit > L || !all_valid) {
@@ -485,13 +480,14 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     } else {
         // ---- direct global-to-LDS loads, two units ahead, three stages ----
         // This thread's slots: key slot p = tid + 256 k is chunk p / 32 at
-        // position p % 32 = tid % 32, token key_token(tid % 32); value slot p is row d = p / 4, holding
-        // tokens 8 q8 .. 8 q8 + 7 with q8 = (p % 4) ^ ((d / 4) % 4), the same
-        // q8 for every k.
+        // position p % 32 = tid % 32, token key_token(tid % 32); value slot p
+        // = vslot(d, q8) is row d = p / 4, holding tokens 8 q8 .. 8 q8 + 7,
+        // where q8 depends on p % 4 and (d / 4) % 4 = (tid / 16) % 4 only: the
+        // same q8 for every k.
         constexpr int NP = (4 * HS) / kPfThreads;  // slots of each kind per thread
         constexpr int NDMA = 2 * NP;               // load instructions per wave per unit
         const int tK = key_token(tid % kPfUnit);
-        const int q8 = (tid & 3) ^ ((tid >> 4) & 3);
+        const int q8 = (tid & 3) ^ ((0x6C >> (2 * ((tid >> 4) & 3))) & 3);  // vslot(tid / 4, q8) = tid
         // Block IDs: a unit spans at most two table entries, j0 = 32 v / BS
         // and j0 + 1 (B = 16), read with scalar loads (uniform addresses) one
         // unit before the unit's loads are issued; each lane takes the entry
