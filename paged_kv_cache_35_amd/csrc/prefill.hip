@@ -13,11 +13,13 @@
 //  * Work-group (KV head, row block, sequence), 4 waves, 32 rows per wave as
 //    two 16-row MFMA tiles; a row is a (query token, group member) pair.
 //  * The keys and values are walked in 32-token units staged in LDS, one
-//    barrier per unit.  bf16 pools: three stages, filled by direct
+//    barrier per unit.  bf16 pools: four stages, filled by direct
 //    global-to-LDS loads (global_load_lds_dwordx4: lane i of a wave
-//    instruction lands at base + 16 i) issued two units ahead, so no
-//    registers hold data in flight.  FP8 pools: two stages, the next unit's
-//    codes loaded into registers and converted to bf16 on the way into LDS.
+//    instruction lands at base + 16 i) issued three units ahead, so no
+//    registers hold data in flight; the loop is software-pipelined, the
+//    scores of unit u + 1 formed while unit u's softmax runs.  FP8 pools: two
+//    stages, the next unit's codes loaded into registers and converted to
+//    bf16 on the way into LDS.
 //    Keys sit in LDS as [hs/8][32 positions] 16-byte chunks, so a lane's
 //    16-byte read is the A operand of v_mfma_f32_16x16x32_bf16 (position
 //    row c, 8 head dims) and a lane group reads 256 contiguous bytes.
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     static_assert(BS >= 16 && (BS % 16) == 0, "blocks of 16, 32 or 64 tokens");
     constexpr int TILE = HS * BS;  // elements of one (block, KV head) tile
     // LDS stages of 16-byte slots: keys [hs/8][32] first, then values
-    constexpr int NST = F8 ? 2 : 3;
+    constexpr int NST = F8 ? 2 : 4;
     constexpr int STAGE_SLOTS = F8 ? (int)(sizeof(PfStage<HS>) / 16) : HS * 8;
     constexpr int KSLOTS = HS * 4;
     __shared__ bf16x8 lds[NST * STAGE_SLOTS];
@@ -295,10 +297,9 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         }
     };
 
-    auto compute = [&](const bf16x8* kst, const bf16x8* vst, int u, unsigned tmask) __attribute__((always_inline)) {
-        const int t0 = u * kPfUnit;
-        // scores of both row tiles, one key M-tile (16 tokens) at a time
-        f32x4 S[kPfTiles][2];
+    // Scores of both row tiles for the unit whose keys are staged at kst, one
+    // key M-tile (16 tokens) at a time.
+    auto scores = [&](const bf16x8* kst, f32x4 (&S)[kPfTiles][2]) __attribute__((always_inline)) {
 #pragma unroll
         for (int mp = 0; mp < 2; ++mp) {
             bf16x8 kop[HS / 32];
@@ -313,25 +314,32 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                     S[kt][mp] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[i], qr[kt][i], S[kt][mp], 0, 0, 0);
             }
         }
+    };
+
+    // Softmax and value sum of unit u from its scores S and the values staged
+    // at vst.  With next_tag true it also forms the next unit's scores Sn
+    // from the keys at kst_next: those matrix instructions do not depend on
+    // this unit's vector work, and are written next to the exponentials so
+    // that the two are issued interleaved.
+    auto finish = [&](auto next_tag, const bf16x8* vst, const bf16x8* kst_next, int u, unsigned tmask,
+                      const f32x4 (&S)[kPfTiles][2], f32x4 (&Sn)[kPfTiles][2]) __attribute__((always_inline)) {
+        constexpr bool NEXT = decltype(next_tag)::value;
+        const int t0 = u * kPfUnit;
         bf16x8 vop[HS / 16];
 #pragma unroll
         for (int i = 0; i < HS / 16; ++i) {
             const int d = 16 * i + c;
             vop[i] = vst[vslot(d, r)];
         }
-        const bool all_valid = tmask == 0xFFFFFFFFu;
-        if (t0 + kPfUnit > L || !all_valid) {
-            // value slots past the sequence or in a skipped block may hold
-            // anything: zero them so that 0 * NaN never reaches the sum
+        bf16x8 kop[2][HS / 32];
+        if constexpr (NEXT) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int tt = 8 * r + e;
-                const bool keep = t0 + tt < L && ((tmask >> tt) & 1);
+            for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
-                for (int i = 0; i < HS / 16; ++i)
-                    vop[i][e] = keep ? vop[i][e] : (__bf16)0.f;
-            }
+                for (int i = 0; i < HS / 32; ++i)
+                    kop[mp][i] = kst_next[(4 * i + r) * kPfUnit + 16 * mp + c];
         }
+        const bool all_valid = tmask == 0xFFFFFFFFu;
         // raw scores; the scale is applied inside the exponent (qscale > 0
         // keeps the maximum where it is)
         float sc[kPfTiles][8];
@@ -360,9 +368,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         // kRescaleSlack, and then alpha (the factor the accumulators are
         // rescaled by, in rescale_tile, before the next value sum into them)
         // is formed; probs: the exponentials and the bf16 hi / lo probability
-        // operands.  The split lets tile 1's rare branch sit before tile 0's
-        // value sum, so that tile 1's exponentials can be issued between
-        // tile 0's matrix instructions.
+        // operands.
         auto raise_max = [&](int kt, float& alpha) __attribute__((always_inline)) -> bool {
             // IEEE maximum (NaN-propagating): three-operand instructions
             // that need no canonicalization of the matrix results, unlike fmaxf
@@ -422,38 +428,78 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         };
         auto value_sum = [&](int kt, const bf16x8& hi, const bf16x8& lo) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < HS / 16; ++i) {
+            for (int i = 0; i < HS / 16; ++i)
                 O[kt][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, vop[i], O[kt][i], 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < HS / 16; ++i)
                 O[kt][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, vop[i], O[kt][i], 0, 0, 0);
-            }
         };
-        // Both tiles' rare branches (raise and rescale) come first, so that
-        // what follows is one straight run: tile 0's value sum (matrix work)
-        // with tile 1's exponentials (vector work) written next to it, to be
-        // issued interleaved, then tile 1's value sum.
-        // The value sums (and tile 1's exponentials between them) run at
-        // raised wave priority: of the two waves sharing a SIMD, the one with
-        // matrix work ready issues it first while the other computes its
-        // scores and softmax, which keeps the matrix pipe busier (measured
-        // 3 to 5 % faster on 512-token chunks; priority over the scores as
-        // well, or over tile 0's value sum only, was not faster).
-        bf16x8 hi0, lo0, hi1, lo1;
+        // Every rare branch (raise and rescale of both tiles, value masking)
+        // comes first, so that what follows is one straight run.
         float a0, a1;
         if (raise_max(0, a0))
             rescale_tile(0, a0);
-        probs(0, hi0, lo0);
         if (raise_max(1, a1))
             rescale_tile(1, a1);
-        __builtin_amdgcn_s_setprio(1);
-        value_sum(0, hi0, lo0);
-        probs(1, hi1, lo1);
+        if (t0 + kPfUnit > L || !all_valid) {
+            // value slots past the sequence or in a skipped block may hold
+            // anything: zero them so that 0 * NaN never reaches the sum
 #pragma unroll
-        for (int k = 0; k < 2 * (HS / 16); ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four vector instructions
+            for (int e = 0; e < 8; ++e) {
+                const int tt = 8 * r + e;
+                const bool keep = t0 + tt < L && ((tmask >> tt) & 1);
+#pragma unroll
+                for (int i = 0; i < HS / 16; ++i)
+                    vop[i][e] = keep ? vop[i][e] : (__bf16)0.f;
+            }
         }
-        value_sum(1, hi1, lo1);
-        __builtin_amdgcn_s_setprio(0);
+        bf16x8 hi0, lo0, hi1, lo1;
+        if constexpr (NEXT) {
+            // the next unit's scores, one matrix instruction between every
+            // five vector instructions of the exponentials
+#pragma unroll
+            for (int mp = 0; mp < 2; ++mp)
+#pragma unroll
+                for (int kt = 0; kt < kPfTiles; ++kt) {
+                    Sn[kt][mp] = (f32x4)0.f;
+#pragma unroll
+                    for (int i = 0; i < HS / 32; ++i)
+                        Sn[kt][mp] =
+                            __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[mp][i], qr[kt][i], Sn[kt][mp], 0, 0, 0);
+                }
+            probs(0, hi0, lo0);
+            probs(1, hi1, lo1);
+#pragma unroll
+            for (int k = 0; k < 2 * kPfTiles * (HS / 32); ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five vector instructions
+            }
+            // The value sums run at raised wave priority: of the two waves
+            // sharing a SIMD, the one with matrix work ready issues it first
+            // while the other computes its softmax.
+            __builtin_amdgcn_s_setprio(1);
+            value_sum(0, hi0, lo0);
+            value_sum(1, hi1, lo1);
+            __builtin_amdgcn_s_setprio(0);
+        } else {
+            // tile 0's value sum with tile 1's exponentials written next to it
+            probs(0, hi0, lo0);
+            __builtin_amdgcn_s_setprio(1);
+            value_sum(0, hi0, lo0);
+            probs(1, hi1, lo1);
+#pragma unroll
+            for (int k = 0; k < 2 * (HS / 16); ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four vector instructions
+            }
+            value_sum(1, hi1, lo1);
+            __builtin_amdgcn_s_setprio(0);
+        }
+    };
+    auto compute = [&](const bf16x8* kst, const bf16x8* vst, int u, unsigned tmask) __attribute__((always_inline)) {
+        f32x4 S[kPfTiles][2];
+        scores(kst, S);
+        finish(std::false_type(), vst, nullptr, u, tmask, S, S);
     };
 
     // ---- the unit loop: fetch u+1 while computing u, one barrier per unit ----
@@ -478,7 +524,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
             __syncthreads();
         }
     } else {
-        // ---- direct global-to-LDS loads, two units ahead, three stages ----
+        // ---- direct global-to-LDS loads, three units ahead, four stages ----
         // This thread's slots: key slot p = tid + 256 k is chunk p / 32 at
         // position p % 32 = tid % 32, token key_token(tid % 32); value slot p
         // = vslot(d, q8) is row d = p / 4, holding tokens 8 q8 .. 8 q8 + 7,
@@ -527,32 +573,54 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                                                  16, 0, 0);
             }
         };
-        // entries of units u (a), u+1 (b), u+2 (c)
-        int32_t a0, a1, b0, b1, c0, c1;
+        // Software pipeline over units: in iteration u, unit u + 1 has landed
+        // and its scores are formed while unit u's softmax and value sum run
+        // (finish), so the loads run three units ahead into four stages.
+        // Entries of units u (a), u+1 (b), u+2 (c), u+3 (d).
+        int32_t a0, a1, b0, b1, c0, c1, d0, d1;
         entries(0, a0, a1);
         entries(1, b0, b1);
         entries(2, c0, c1);
+        entries(3, d0, d1);
         issue(0, a0, a1);
         issue(1, b0, b1);
+        issue(2, c0, c1);
+        // the units this wave computes (its rows see tokens below L_w)
+        const int nu_w = (L_w + kPfUnit - 1) / kPfUnit < nunits ? (L_w + kPfUnit - 1) / kPfUnit : nunits;
+        f32x4 S[kPfTiles][2];
+        wait_vmcnt<2 * NDMA>();  // loads(0) landed; loads(1), loads(2) may be outstanding
+        __syncthreads();
+        if (nu_w > 0)
+            scores(lds, S);
         for (int u = 0; u < nunits; ++u) {
-            // issued before this point, in order: ..., loads(u), loads(u+1).
-            // This wave's loads of unit u have landed once at most NDMA are
+            // issued before this point, in order: ..., loads(u+1), loads(u+2).
+            // This wave's loads of unit u+1 have landed once at most NDMA are
             // outstanding; the barrier makes every wave's part visible and
             // frees the stage of unit u-1
             wait_vmcnt<NDMA>();
             __syncthreads();
-            int32_t d0, d1;
-            entries(u + 3, d0, d1);
-            issue(u + 2, c0, c1);
+            int32_t e0, e1;
+            entries(u + 4, e0, e1);
+            issue(u + 3, d0, d1);
             // tokens of unit u whose block ID is inside the pool
             const bool ok0 = (uint32_t)a0 < (uint32_t)num_blocks, ok1 = (uint32_t)a1 < (uint32_t)num_blocks;
             const unsigned tmask = BS >= kPfUnit ? (ok0 ? 0xFFFFFFFFu : 0u)
                                                  : ((ok0 ? 0x0000FFFFu : 0u) | (ok1 ? 0xFFFF0000u : 0u));
-            if (u * kPfUnit < L_w)  // uniform per wave: this wave's rows see some of the unit
-                compute(lds + (u % NST) * STAGE_SLOTS, lds + (u % NST) * STAGE_SLOTS + KSLOTS, u, tmask);
-            a0 = b0; a1 = b1; b0 = c0; b1 = c1; c0 = d0; c1 = d1;
+            if (u < nu_w) {  // uniform per wave
+                // the next unit's keys have landed (also past this wave's
+                // last unit or the work-group's, where the scores go unused)
+                f32x4 Sn[kPfTiles][2];
+                finish(std::true_type(), lds + (u % NST) * STAGE_SLOTS + KSLOTS,
+                       lds + ((u + 1) % NST) * STAGE_SLOTS, u, tmask, S, Sn);
+#pragma unroll
+                for (int kt = 0; kt < kPfTiles; ++kt)
+#pragma unroll
+                    for (int mp = 0; mp < 2; ++mp)
+                        S[kt][mp] = Sn[kt][mp];
+            }
+            a0 = b0; a1 = b1; b0 = c0; b1 = c1; c0 = d0; c1 = d1; d0 = e0; d1 = e1;
         }
-        // the last two iterations' loads still write LDS: wait before the
+        // the last three iterations' loads still write LDS: wait before the
         // work-group's LDS can be handed to another
         wait_vmcnt<0>();
     }
