@@ -324,6 +324,36 @@ def test_repeat_runs_bit_identical():
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
+@pytest.mark.parametrize("S", [12, 80, 300])
+def test_schedule_reused_by_repeated_attention_calls(S):
+    # A schedule is read, never consumed, by the attention launch: calls
+    # that reuse one schedule without a new append, and calls of two batches
+    # with their own schedules in between, all give the same bits as the
+    # first call, and the oracle's result.  S = 12 walks the ranked grid,
+    # S = 80 and 300 the chunk list (lengths up to 3000: two chunks for the
+    # long sequences, so the chunk merge runs too).
+    m = pkv()
+    runs = []
+    for k, n in enumerate((S, S + 7)):
+        w = pi.make_workload(3, S=n, len_lo=1, len_hi=3000, seed=100 + k)
+        q, kc, vc = dev(w.q), dev(w.k_cache), dev(w.v_cache)
+        bt, sl = dev(w.block_tables), dev(w.seq_lens)
+        sched = m.alloc_schedule(bt)
+        m.decode_append(dev(w.new_k), dev(w.new_v), bt, sl, kc, vc, schedule=sched)
+        runs.append((w, q, kc, vc, bt, sl, sched))
+    announce(f"schedule reused: batches of {S} and {S + 7}, three calls each, interleaved")
+    firsts = []
+    for rep in range(3):
+        for i, (w, q, kc, vc, bt, sl, sched) in enumerate(runs):
+            out = m.paged_decode_attention(q, kc, vc, bt, sl, w.scale, schedule=sched)
+            torch.cuda.synchronize()
+            if rep == 0:
+                firsts.append(out.clone())
+                check_attention(w, host_f64(out), oracle.decode_step(w)[3])
+            else:
+                assert torch.equal(out.view(torch.int16), firsts[i].view(torch.int16)), (rep, i)
+
+
 def test_block_relabelling_bit_identical():
     w = pi.make_workload(3, S=9, len_lo=16, len_hi=2500)
     announce("determinism: relabelled physical blocks")
