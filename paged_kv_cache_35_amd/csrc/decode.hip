@@ -715,13 +715,17 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
         float sc[4];
         float mx = -INFINITY;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            float v = S[jj] * qscale;
-            if (partial)
-                v = (tok0 + 4 * r + jj < Lt && ((tmask >> (4 * r + jj)) & 1)) ? v : -INFINITY;
-            sc[jj] = v;
-            mx = fmaxf(mx, v);
+        for (int jj = 0; jj < 4; ++jj)
+            sc[jj] = S[jj] * qscale;
+        if (partial) {
+            asm volatile("");  // a real branch: most tiles need no masking
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                sc[jj] = (tok0 + 4 * r + jj < Lt && ((tmask >> (4 * r + jj)) & 1)) ? sc[jj] : -INFINITY;
         }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            mx = fmaxf(mx, sc[jj]);
         if (partial)
             zero_masked_values<T, HS>(t, tok0, Lv, r, tmask);
         update_max(mx);
@@ -748,14 +752,20 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
             for (int mp = 0; mp < 2; ++mp) {
                 const f32x4 S = tile_scores<__bf16, HS>(t.k[mp], qr);
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    float v = S[jj] * qscale;
-                    if (partial)
-                        v = (tok0 + 16 * mp + 4 * r + jj < Lt) ? v : -INFINITY;
-                    sc[4 * mp + jj] = v;
-                    mx = fmaxf(mx, v);
-                }
+                for (int jj = 0; jj < 4; ++jj)
+                    sc[4 * mp + jj] = S[jj] * qscale;
             }
+            if (partial) {
+                asm volatile("");  // a real branch: most units need no masking
+#pragma unroll
+                for (int mp = 0; mp < 2; ++mp)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+                        sc[4 * mp + jj] = (tok0 + 16 * mp + 4 * r + jj < Lt) ? sc[4 * mp + jj] : -INFINITY;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+                mx = fmaxf(mx, sc[k]);
             if (partial) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
