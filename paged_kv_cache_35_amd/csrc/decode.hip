@@ -559,22 +559,30 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     // This wave's blocks: base, base + stride, ... (nb_w of them, <= PB).
     // Contiguous mode: partition `part` = PB consecutive blocks.  Interleaved
     // mode: the chunk's blocks dealt round-robin to the NW waves, which keeps
-    // the waves balanced when a sequence ends inside the chunk.  A wave with
-    // no blocks still joins the work-group merge below.
+    // the waves balanced when a sequence ends inside the chunk.  With several
+    // units per block (B = 64) the units are dealt instead, so that a short
+    // sequence's few blocks still spread over all waves: unit k of the chunk
+    // goes to wave k % NW, which then holds part w % PER of every
+    // (NW / PER)-th block (its list has up to PER * PB blocks, at most 64).
+    // A wave with no blocks still joins the work-group merge below.
     // (Blocks smaller than a unit always use contiguous partitions: a unit's
     // tokens are then consecutive.)
     const int cb0 = chunk * NW * PB;
     const bool ilv = !kSmall && interleave;
-    const int base = ilv ? cb0 + w : part * PB;
-    const int stride = ilv ? NW : 1;
-    // Physical block IDs of this wave's blocks, one per lane (<= PB <= 64);
-    // the tile loop broadcasts them with readlane.  Loaded for all PB lanes
+    constexpr bool kUnitDeal = !kSmall && PER > 1 && NW % PER == 0;
+    const bool deal = kUnitDeal && ilv && PB * PER <= 64;  // uniform
+    const int base = deal ? cb0 + w / PER : (ilv ? cb0 + w : part * PB);
+    const int stride = deal ? NW / PER : (ilv ? NW : 1);
+    const int wpart = deal ? w % PER : 0;  // the part of each block this wave takes (unit dealing)
+    const int nlist = deal ? PB * PER : PB;  // entries of this wave's block list
+    // Physical block IDs of this wave's blocks, one per lane (nlist <= 64);
+    // the tile loop broadcasts them with readlane.  Loaded for all nlist lanes
     // within the table row, without waiting for the sequence length, so
     // that this load and the length load are in flight together; entries
     // past the sequence's blocks are never used.
     const int tb = base + lane * stride;
     const int32_t* trow = sched_order ? sched_tables + (int64_t)yr * M : block_tables + (int64_t)s * M;
-    const int32_t id_lane = (lane < PB && tb < M) ? trow[tb] : 0;
+    const int32_t id_lane = (lane < nlist && tb < M) ? trow[tb] : 0;
     // The length is loaded next, before anything waits (the query-row bounds
     // below may end the work-group), so that both loads are in flight at once.
     const int L_in = sched_order ? sched_lens[yr] : seq_lens[s];
@@ -620,8 +628,9 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
         return;  // the whole work-group is past the end (uniform: before any barrier)
     const int nchunks = (nblk + NW * PB - 1) / (NW * PB);
     const int cnb = (nblk - cb0 < NW * PB) ? nblk - cb0 : NW * PB;
-    const int nb_w = ilv ? (cnb > w ? (cnb - w + NW - 1) / NW : 0)
-                                : (base >= nblk ? 0 : ((nblk - base < PB) ? nblk - base : PB));
+    const int nb_w = deal ? (cnb > w / PER ? (cnb - w / PER + stride - 1) / stride : 0)
+                     : ilv ? (cnb > w ? (cnb - w + NW - 1) / NW : 0)
+                           : (base >= nblk ? 0 : ((nblk - base < PB) ? nblk - base : PB));
 
     // query operand: row c of the tile.  Rows past the tile's real rows are
     // padding: they repeat a real row (head c % G without MQ), and their
@@ -801,7 +810,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     };
 
     // Software pipeline over the partition's units (UT tokens each): unit u
-    // is part m = u % PER of block j = u / PER.  The next unit's
+    // is part part_of(u) of list block j_of(u).  The next unit's
     // loads are in flight while the current one is computed.  The
     // steady-state loop always prefetches and the last one or two units are
     // peeled, so every compute is preceded by exactly one batch of loads and
@@ -810,7 +819,10 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
         F8, typename std::conditional<kWide, Fp8WideRegs<HS>, Fp8Regs<HS>>::type,
         typename std::conditional<kWide, WideRegs<HS>, TileRegs<T, HS>>::type>::type;
     // 0 for a wave past the end
-    const int nunits = kSmall ? (nb_w * BS + UT - 1) / UT : nb_w * PER;
+    const int nunits = kSmall ? (nb_w * BS + UT - 1) / UT : (deal ? nb_w : nb_w * PER);
+    // unit u: block j_of(u) of this wave's list, part part_of(u) of it
+    auto j_of = [&](int u) __attribute__((always_inline)) { return deal ? u : u / PER; };
+    auto part_of = [&](int u) __attribute__((always_inline)) { return deal ? wpart : u % PER; };
     // small blocks: bit j set when this wave's block ID j is inside the pool
     const uint64_t valid_blocks = kSmall ? __ballot((uint32_t)id_lane < (uint32_t)num_blocks) : 0;
     // returns the unit's token mask (all 16 bits when every block is valid,
@@ -820,23 +832,24 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
             return load_small<T, HS, BS>(t, k_cache, v_cache, (int64_t)Hkv * TILE, (int64_t)kvh * TILE, id_lane,
                                          valid_blocks, num_blocks, u, r, c);
         } else {
-            const int j = u / PER;
+            const int j = j_of(u);
+            const int m = part_of(u);
             const C* tk;
             const C* tv;
             const bool ok = tile_ptr_ok(j, tk, tv);
             if constexpr (F8 && kWide)
-                load_fp8_wide<HS, BS>(t, tk, tv, u % PER, r, c);
+                load_fp8_wide<HS, BS>(t, tk, tv, m, r, c);
             else if constexpr (F8)
-                load_fp8<HS, BS>(t, tk, tv, u % PER, r, c);
+                load_fp8<HS, BS>(t, tk, tv, m, r, c);
             else if constexpr (kWide)
-                load_wide<HS, BS>(t, tk, tv, u % PER, r, c);
+                load_wide<HS, BS>(t, tk, tv, m, r, c);
             else
-                load_tile<T, HS, BS>(t, tk, tv, u % PER, r, c);
+                load_tile<T, HS, BS>(t, tk, tv, m, r, c);
             return ok ? 0xFFFF : 0;
         }
     };
     auto first_token = [&](int u) __attribute__((always_inline)) {
-        return kSmall ? base * BS + UT * u : (base + (u / PER) * stride) * BS + UT * (u % PER);
+        return kSmall ? base * BS + UT * u : (base + j_of(u) * stride) * BS + UT * part_of(u);
     };
     auto run = [&](Regs& t, int u, int tmask) __attribute__((always_inline)) {
         const int tok0 = first_token(u);

@@ -58,6 +58,33 @@ def test_multi_token_parity(B):
     full_check(w, MRun(w))
 
 
+# Lengths at unit and block edges.  With the library's partition length the
+# kernel deals a chunk's units (32 tokens for bf16 and FP8 at B = 64, 16 for
+# fp32 at B = 32 and 64) to its four waves, so a short sequence can leave a
+# wave nothing but units past the sequence's end, or nothing at all.
+EDGE_LENS = [1, 16, 17, 31, 32, 33, 48, 63, 64, 65, 96, 97, 128, 129, 160, 191, 192, 193, 255, 256, 257,
+             300, 511, 512, 513, 2047, 2049]
+
+
+@pytest.mark.parametrize("B,dtype", [(64, "bf16"), (64, "fp8"), (32, "f32"), (64, "f32")])
+def test_units_dealt_at_edge_lengths(B, dtype):
+    w = pi.make_workload(3, seq_lens=EDGE_LENS, dtype=dtype, B=B, seed=25)
+    announce(f"decode B={B} {dtype} edge lengths {list(w.seq_lens)}")
+    if dtype == "fp8":
+        check_step(w, *run_fp8(w))
+        return
+    r = Run(w)
+    check_attention(w, host_f64(r.out), oracle.decode_step(w)[3])
+
+
+@pytest.mark.parametrize("B,dtype", [(64, "bf16"), (64, "fp8")])
+def test_units_dealt_at_edge_lengths_multi_token(B, dtype):
+    q_lens = [min(n, k) for n, k in zip(EDGE_LENS, [1, 2, 5, 16, 33, 3, 64] * 4)]
+    w = pi.make_workload(3, seq_lens=EDGE_LENS, dtype=dtype, B=B, seed=26, q_lens=q_lens)
+    announce(f"multi-token B={B} {dtype} edge lengths {list(w.seq_lens)} q_start={list(w.q_start)}")
+    full_check(w, MRun(w))
+
+
 @pytest.mark.parametrize("mq", [False, True])
 def test_fp8_pools_with_64_token_blocks(mq):
     kw = dict(S=6, len_lo=30, len_hi=1500, B=64, dtype="fp8", seed=24)
