@@ -16,8 +16,10 @@
 //    barrier per unit.  bf16 pools: four stages, filled by direct
 //    global-to-LDS loads (global_load_lds_dwordx4: lane i of a wave
 //    instruction lands at base + 16 i) issued three units ahead, so no
-//    registers hold data in flight; the loop is software-pipelined, the
-//    scores of unit u + 1 formed while unit u's softmax runs.  FP8 pools: two
+//    registers hold data in flight; the loop is software-pipelined: a
+//    unit's softmax (vector work) comes first, then one run of matrix work,
+//    its value sums and the scores of the next unit, which the other wave on
+//    the SIMD overlaps with its own softmax.  FP8 pools: two
 //    stages, the next unit's codes loaded into registers and converted to
 //    bf16 on the way into LDS.
 //    Keys sit in LDS as [hs/8][32 positions] 16-byte chunks, so a lane's
@@ -319,8 +321,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     // Softmax and value sum of unit u from its scores S and the values staged
     // at vst.  With next_tag true it also forms the next unit's scores Sn
     // from the keys at kst_next: those matrix instructions do not depend on
-    // this unit's vector work, and are written next to the exponentials so
-    // that the two are issued interleaved.
+    // this unit's vector work, and are issued with the value sums, after it.
     auto finish = [&](auto next_tag, const bf16x8* vst, const bf16x8* kst_next, int u, unsigned tmask,
                       const f32x4 (&S)[kPfTiles][2], f32x4 (&Sn)[kPfTiles][2]) __attribute__((always_inline)) {
         constexpr bool NEXT = decltype(next_tag)::value;
@@ -455,8 +456,17 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         }
         bf16x8 hi0, lo0, hi1, lo1;
         if constexpr (NEXT) {
-            // the next unit's scores, one matrix instruction between every
-            // five vector instructions of the exponentials
+            // Two phases: every exponential of the unit first, then every
+            // matrix instruction (the next unit's scores and this unit's value
+            // sums) at raised wave priority.  A wave issues an MFMA and the
+            // vector instructions after it almost one after the other, so the
+            // overlap comes from the other wave on the SIMD: the one with
+            // matrix work ready issues it first while the other computes its
+            // softmax.
+            probs(0, hi0, lo0);
+            probs(1, hi1, lo1);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int mp = 0; mp < 2; ++mp)
 #pragma unroll
@@ -467,17 +477,6 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                         Sn[kt][mp] =
                             __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[mp][i], qr[kt][i], Sn[kt][mp], 0, 0, 0);
                 }
-            probs(0, hi0, lo0);
-            probs(1, hi1, lo1);
-#pragma unroll
-            for (int k = 0; k < 2 * kPfTiles * (HS / 32); ++k) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // five vector instructions
-            }
-            // The value sums run at raised wave priority: of the two waves
-            // sharing a SIMD, the one with matrix work ready issues it first
-            // while the other computes its softmax.
-            __builtin_amdgcn_s_setprio(1);
             value_sum(0, hi0, lo0);
             value_sum(1, hi1, lo1);
             __builtin_amdgcn_s_setprio(0);
