@@ -66,10 +66,11 @@ EDGE_LENS = [1, 16, 17, 31, 32, 33, 48, 63, 64, 65, 96, 97, 128, 129, 160, 191, 
              300, 511, 512, 513, 2047, 2049]
 
 
-@pytest.mark.parametrize("B,dtype", [(64, "bf16"), (64, "fp8"), (32, "f32"), (64, "f32")])
-def test_units_dealt_at_edge_lengths(B, dtype):
-    w = pi.make_workload(3, seq_lens=EDGE_LENS, dtype=dtype, B=B, seed=25)
-    announce(f"decode B={B} {dtype} edge lengths {list(w.seq_lens)}")
+@pytest.mark.parametrize("B,dtype,hs", [(64, "bf16", 128), (64, "bf16", 64), (64, "fp8", 128), (32, "f32", 128),
+                                        (64, "f32", 128), (64, "f32", 64)])
+def test_units_dealt_at_edge_lengths(B, dtype, hs):
+    w = pi.make_workload(3, seq_lens=EDGE_LENS, dtype=dtype, B=B, hs=hs, seed=25)
+    announce(f"decode B={B} {dtype} hs={hs} edge lengths {list(w.seq_lens)}")
     if dtype == "fp8":
         check_step(w, *run_fp8(w))
         return
