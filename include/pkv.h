@@ -361,7 +361,10 @@ PKV_API pkv_status paged_decode_step_static(const void* q, const void* new_k, co
  * 0 .. num_q_rows - 1 is skipped, rows past max_q_len are not computed, and
  * a row whose position is negative (n_s > L_s) attends to nothing and gets
  * zeros.  q and out: [num_q_rows][num_q_heads][head_size] in the query
- * type; new k/v: [num_q_rows][num_kv_heads][head_size].
+ * type; new k/v: [num_q_rows][num_kv_heads][head_size].  A call with no
+ * query rows (num_q_rows or max_q_len 0: every sequence sits the step out)
+ * launches nothing and returns PKV_OK after the shape checks; q, out and
+ * the new rows may then be null.
  */
 
 /*

@@ -525,6 +525,13 @@ pkv_status multi_token_args(const void* q, const int32_t* q_start, int32_t num_q
 {
     if (num_q_rows < 0 || max_q_len < 0)
         return PKV_ERR_INVALID_ARG;
+    // No query rows (every sequence sits this step out): nothing to compute
+    // or append, and q, out and the new rows may be empty (null).  The
+    // shapes and the pool descriptor are still checked, as for an empty
+    // batch.
+    if (num_q_rows == 0 || max_q_len == 0)
+        return attention_args(q, k_cache, v_cache, block_tables, seq_lens, 0, num_q_heads, max_blocks_per_seq, cache,
+                              scale, out, workspace, workspace_bytes, 0, a, nothing_to_do, false);
     // PKV_PARTITION_NONE: the unpartitioned (prefill) kernel, no workspace
     const bool unpartitioned = partition_tokens == PKV_PARTITION_NONE;
     const int32_t P = unpartitioned ? 0 : partition_tokens;
@@ -540,10 +547,6 @@ pkv_status multi_token_args(const void* q, const int32_t* q_start, int32_t num_q
                                    need > workspace_bytes ? 0 : workspace_bytes, P, a, nothing_to_do, !unpartitioned);
     if (st != PKV_OK || nothing_to_do)
         return st;
-    if (num_q_rows == 0 || max_q_len == 0) {
-        nothing_to_do = true;
-        return PKV_OK;
-    }
     if (!q_start)
         return PKV_ERR_INVALID_ARG;
     const int64_t G = num_q_heads / cache->num_kv_heads;

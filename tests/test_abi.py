@@ -287,6 +287,18 @@ def test_multi_token_attention_rejects_bad_arguments(lib):
                                            0.125, None, None, 0, 0, None, 0, None) == OK
 
 
+def test_multi_token_calls_without_rows_do_nothing(lib):
+    # sequences that all sit this step out: no rows, so q, out and the new
+    # rows are empty (null); the shapes are still checked
+    for rows, mql in ((0, 0), (0, 4), (8, 0)):
+        assert mq(lib, q=None, out=None, rows=rows, mql=mql) == OK
+        assert mq(lib, q=None, out=None, rows=rows, mql=mql, Hq=12) == INVALID
+        assert lib.paged_multi_token_step(None, None, None, FAKE, FAKE, FAKE, rows, mql, FAKE, FAKE, 4, 8, 4,
+                                          ctypes.byref(desc()), 0.125, None, None, None, 0, 0, None) == OK
+        assert lib.paged_multi_token_step(None, None, None, FAKE, FAKE, FAKE, rows, mql, FAKE, FAKE, 4, 8, 4,
+                                          ctypes.byref(desc(hs=96)), 0.125, None, None, None, 0, 0, None) != OK
+
+
 def test_multi_token_step_and_slot_mapping_reject_bad_arguments(lib):
     d = desc()
     f = lib.paged_multi_token_step

@@ -119,6 +119,26 @@ def test_sequences_without_rows_and_a_larger_max_q_len():
     full_check(w, r)
 
 
+@pytest.mark.parametrize("lens", [[0], [0, 12, 300]])
+def test_a_batch_without_any_rows_does_nothing(lens):
+    # every sequence sits the step out: q, out and the new rows are empty,
+    # the pools are left as they are
+    w = pi.make_workload(2, seq_lens=lens, q_lens=[0] * len(lens))
+    announce(f"no rows at all, lengths {lens}")
+    assert w.rows == 0
+    m = pkv()
+    q, kc, vc, bt, sl, qs = dev(w.q), dev(w.k_cache), dev(w.v_cache), dev(w.block_tables), dev(w.seq_lens), \
+        dev(w.q_start)
+    kc0, vc0 = kc.clone(), vc.clone()
+    for mql in (0, 4):
+        out = m.paged_multi_token_step(q, dev(w.new_k), dev(w.new_v), kc, vc, qs, mql, bt, sl, w.scale)
+        out2 = m.paged_multi_token_attention(q, qs, mql, kc, vc, bt, sl, w.scale)
+        torch.cuda.synchronize()
+        assert out.numel() == 0 and out2.numel() == 0
+    assert torch.equal(kc.view(torch.uint8), kc0.view(torch.uint8))
+    assert torch.equal(vc.view(torch.uint8), vc0.view(torch.uint8))
+
+
 def test_step_matches_the_separate_calls():
     w = pi.make_workload(3, S=6, len_lo=300, len_hi=2500, q_lens=[64, 5, 1, 37, 128, 16])
     announce("multi-token step vs slot mapping + append + attention")

@@ -3,6 +3,8 @@ multi-token step, against the oracle: element type, head size, block size,
 group size, batch size, lengths (with empty sequences, one-token ones and
 full tables) and partition length drawn from a fixed seed, so the cases are
 the same on every run.  Appends bit-exact, outputs within the bars."""
+import os
+
 import numpy as np
 import pytest
 
@@ -53,9 +55,30 @@ def draw_case(rng, multi, unpartitioned=False):
     return dict(dtype=dtype, hs=hs, B=B, Hkv=Hkv, Hq=Hkv * G, seq_lens=[int(x) for x in lens], q_lens=q_lens, P=P)
 
 
+def draw_long_rows(rng):
+    """A case for the unpartitioned kernel with many rows per sequence."""
+    dtype = ["bf16", "fp8"][rng.integers(2)]
+    hs = [64, 128][rng.integers(2)]
+    B = [16, 32, 64][rng.integers(3)]
+    Hkv = [1, 2, 4][rng.integers(3)]
+    G = [1, 2, 4][rng.integers(3)]
+    lens = rng.integers(64, 2000, int(rng.integers(1, 7)))
+    q_lens = [int(min(L, rng.integers(16, 200))) for L in lens]
+    return dict(dtype=dtype, hs=hs, B=B, Hkv=Hkv, Hq=Hkv * G, seq_lens=[int(x) for x in lens], q_lens=q_lens, P=-1)
+
+
 _rng = np.random.default_rng(20260211)
 DECODE = [draw_case(_rng, False) for _ in range(24)]
 MULTI = [draw_case(_rng, True) for _ in range(12)] + [draw_case(_rng, True, unpartitioned=True) for _ in range(4)]
+# More cases on request: PKV_RANDOM_CASES="seed:decode:multi:long" draws that
+# many decode-step, multi-token-step and long-row cases from the given seed
+# (for example "4242:1500:600:200", a few minutes on one GPU).
+_extra = os.environ.get("PKV_RANDOM_CASES")
+if _extra:
+    _seed, _nd, _nm, _nl = (int(x) for x in _extra.split(":"))
+    _erng = np.random.default_rng(_seed)
+    DECODE += [draw_case(_erng, False) for _ in range(_nd)]
+    MULTI += [draw_case(_erng, True) for _ in range(_nm)] + [draw_long_rows(_erng) for _ in range(_nl)]
 
 
 def case_id(c):
