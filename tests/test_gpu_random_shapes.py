@@ -67,6 +67,27 @@ def draw_long_rows(rng):
     return dict(dtype=dtype, hs=hs, B=B, Hkv=Hkv, Hq=Hkv * G, seq_lens=[int(x) for x in lens], q_lens=q_lens, P=-1)
 
 
+def draw_wide(rng, multi):
+    """A case on the paths draw_case leaves rare: half of them batches of
+    65-300 sequences (the schedule's chunk list), each through either the
+    whole step or the stand-alone attention on the appended pools without a
+    schedule, and half of the bf16 / FP8 ones with an fp32 output."""
+    c = draw_case(rng, multi)
+    if rng.random() < 0.5:
+        S = int(rng.integers(65, 301))
+        lens = rng.integers(1, 800 if c["B"] == 1 else 2500, S)
+        for k in range(S):
+            u = rng.random()
+            lens[k] = 0 if u < 0.05 else (1 if u < 0.1 else lens[k])
+        c["seq_lens"] = [int(x) for x in lens]
+        c["Hq"] = c["Hkv"] * min(c["Hq"] // c["Hkv"], 4)
+        if multi:
+            c["q_lens"] = [int(min(L, rng.integers(1, 12))) if L > 0 else 0 for L in lens]
+    c["mode"] = ["step", "attn"][rng.integers(2)]
+    c["f32out"] = c["dtype"] != "f32" and bool(rng.random() < 0.5)
+    return c
+
+
 _rng = np.random.default_rng(20260211)
 DECODE = [draw_case(_rng, False) for _ in range(24)]
 MULTI = [draw_case(_rng, True) for _ in range(12)] + [draw_case(_rng, True, unpartitioned=True) for _ in range(4)]
@@ -79,6 +100,14 @@ if _extra:
     _erng = np.random.default_rng(_seed)
     DECODE += [draw_case(_erng, False) for _ in range(_nd)]
     MULTI += [draw_case(_erng, True) for _ in range(_nm)] + [draw_long_rows(_erng) for _ in range(_nl)]
+# PKV_RANDOM_WIDE="seed:decode:multi": cases from draw_wide (large batches,
+# stand-alone attention without a schedule, fp32 outputs)
+WIDE = []
+_wide = os.environ.get("PKV_RANDOM_WIDE")
+if _wide:
+    _seed, _nd, _nm = (int(x) for x in _wide.split(":"))
+    _wrng = np.random.default_rng(_seed)
+    WIDE = [draw_wide(_wrng, False) for _ in range(_nd)] + [draw_wide(_wrng, True) for _ in range(_nm)]
 
 
 def case_id(c):
@@ -124,3 +153,41 @@ def test_random_multi_token_step(c):
     assert np.array_equal(slots.cpu().numpy(), ref_slots)
     assert same_bytes(host_bits(kc), kp) and same_bytes(host_bits(vc), vp)
     check_attention(w, host_f64(out), ref)
+
+
+def check_wide(c):
+    multi = c["q_lens"] is not None
+    w = workload(c)
+    announce(f"random {'multi-token' if multi else 'decode'} {c['mode']} {case_id(c)} f32out={c['f32out']}")
+    m = pkv()
+    sc = dict(k_scale=w.k_scale, v_scale=w.v_scale, partition_tokens=c["P"],
+              out_dtype=torch.float32 if c["f32out"] else None)
+    ref_slots, kp, vp, ref = oracle.multi_token_step(w) if multi else oracle.decode_step(w)
+    bt, sl = dev(w.block_tables), dev(w.seq_lens)
+    if c["mode"] == "step":
+        kc, vc = dev(w.k_cache), dev(w.v_cache)
+        slots = torch.empty(w.rows if multi else w.S, dtype=torch.int64, device="cuda")
+        if multi:
+            out = m.paged_multi_token_step(dev(w.q), dev(w.new_k), dev(w.new_v), kc, vc, dev(w.q_start), w.max_q_len,
+                                           bt, sl, w.scale, slot_mapping=slots, **sc)
+        else:
+            out = m.paged_decode_step(dev(w.q), dev(w.new_k), dev(w.new_v), kc, vc, bt, sl, w.scale,
+                                      slot_mapping=slots, **sc)
+        torch.cuda.synchronize()
+        assert np.array_equal(slots.cpu().numpy(), ref_slots)
+        assert same_bytes(host_bits(kc), kp) and same_bytes(host_bits(vc), vp)
+    else:  # the attention alone on the appended pools, no schedule
+        if multi:
+            out = m.paged_multi_token_attention(dev(w.q), dev(w.q_start), w.max_q_len, dev(kp), dev(vp), bt, sl,
+                                                w.scale, **sc)
+        else:
+            out = m.paged_decode_attention(dev(w.q), dev(kp), dev(vp), bt, sl, w.scale, **sc)
+        torch.cuda.synchronize()
+    check_attention(w, host_f64(out), ref, out_f32=c["f32out"])
+
+
+if WIDE:  # defined only on request, so a default run has no empty parameter set
+    @pytest.mark.parametrize("c", WIDE, ids=[f"{c['mode']}{'-f32out' if c['f32out'] else ''}-{case_id(c)}"
+                                             for c in WIDE])
+    def test_random_wide(c):
+        check_wide(c)
