@@ -217,9 +217,9 @@ PKV_API pkv_status pkv_decode_append(const void* k, const void* v, const int32_t
  * Context-partition length, in tokens, that paged_decode_attention will use
  * for these sizes.  partition_tokens > 0 requests that length (it must be a
  * multiple of block_size and at most 64 * block_size, and for blocks of
- * fewer than 16 tokens a multiple of 16); 0 lets the library choose
- * (min(512, 64 * block_size), or the whole table when shorter).  Returns 0
- * for invalid sizes.
+ * fewer than 16 tokens a multiple of 16 and at most 512); 0 lets the
+ * library choose (512, or the whole table when shorter).  Returns 0 for
+ * invalid sizes.
  */
 PKV_API int32_t pkv_decode_partition_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t head_size, int32_t max_blocks_per_seq,

@@ -30,21 +30,27 @@ size_t round_up(size_t n, size_t a) { return (n + a - 1) / a * a; }
 
 // Library choice of the context-partition length: kDefaultPartitionTokens
 // (512: 32 blocks at B = 16, 16 at B = 32), at most 64 blocks (one block ID
-// per lane of the wave), or one partition when the table is shorter.  Blocks
-// of fewer than 16 tokens are read in 16-token units that must not straddle
-// two partitions: the length is then a multiple of 16.
+// per lane of the wave; blocks of fewer than 16 tokens: 512 tokens, the
+// IDs in windows of 64), or one partition when the table is shorter.
+// Blocks of fewer than 16 tokens are read in 16-token units that must not
+// straddle two partitions: the length is then a multiple of 16.
 constexpr int64_t kDefaultPartitionTokens = 512;
 int32_t resolve_partition_tokens(int32_t max_blocks_per_seq, int32_t block_size, int32_t requested)
 {
     if (requested < 0 || max_blocks_per_seq <= 0 || block_size <= 0)
         return 0;
+    // a wave's list holds at most 64 blocks, or 512 tokens' worth of blocks
+    // of fewer than 16 tokens (kept in windows of 64 by the kernel)
+    const int64_t max_blocks = block_size < 16 ? 512 / block_size : 64;
     if (requested > 0) {
-        if (requested % block_size != 0 || requested / block_size > 64 || (block_size < 16 && requested % 16 != 0))
+        if (requested % block_size != 0 || requested / block_size > max_blocks ||
+            (block_size < 16 && requested % 16 != 0))
             return 0;
         return requested;
     }
     const int64_t whole = (int64_t)max_blocks_per_seq * block_size;
-    const int64_t dflt = kDefaultPartitionTokens < 64 * block_size ? kDefaultPartitionTokens : 64 * block_size;
+    const int64_t dflt =
+        kDefaultPartitionTokens < max_blocks * block_size ? kDefaultPartitionTokens : max_blocks * block_size;
     return (int32_t)(whole < dflt ? whole : dflt);
 }
 

@@ -575,14 +575,27 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     const int stride = deal ? NW / PER : (ilv ? NW : 1);
     const int wpart = deal ? w % PER : 0;  // the part of each block this wave takes (unit dealing)
     const int nlist = deal ? PB * PER : PB;  // entries of this wave's block list
-    // Physical block IDs of this wave's blocks, one per lane (nlist <= 64);
-    // the tile loop broadcasts them with readlane.  Loaded for all nlist lanes
+    // Physical block IDs of this wave's blocks, one per lane (the first 64;
+    // small blocks keep the rest in windows, below); the tile loop
+    // broadcasts them with readlane.  Loaded for all nlist lanes
     // within the table row, without waiting for the sequence length, so
     // that this load and the length load are in flight together; entries
     // past the sequence's blocks are never used.
     const int tb = base + lane * stride;
     const int32_t* trow = sched_order ? sched_tables + (int64_t)yr * M : block_tables + (int64_t)s * M;
     const int32_t id_lane = (lane < nlist && tb < M) ? trow[tb] : 0;
+    // Blocks of fewer than 16 tokens: a partition of up to 512 tokens holds
+    // more than 64 blocks (B = 1), so its list is kept in windows of 64
+    // entries, window k in idw[k] (idw[0] = id_lane), all loaded here; the
+    // tile loop moves to the next window by shifting them down.
+    constexpr int NWIN = kSmall ? 512 / (64 * BS) : 1;
+    int32_t idw[NWIN];
+    idw[0] = id_lane;
+#pragma unroll
+    for (int k = 1; k < NWIN; ++k) {
+        const int e = 64 * k + lane;  // list entry
+        idw[k] = (e < nlist && base + e < M) ? trow[base + e] : 0;
+    }
     // The length is loaded next, before anything waits (the query-row bounds
     // below may end the work-group), so that both loads are in flight at once.
     const int L_in = sched_order ? sched_lens[yr] : seq_lens[s];
@@ -823,14 +836,25 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     // unit u: block j_of(u) of this wave's list, part part_of(u) of it
     auto j_of = [&](int u) __attribute__((always_inline)) { return deal ? u : u / PER; };
     auto part_of = [&](int u) __attribute__((always_inline)) { return deal ? wpart : u % PER; };
-    // small blocks: bit j set when this wave's block ID j is inside the pool
-    const uint64_t valid_blocks = kSmall ? __ballot((uint32_t)id_lane < (uint32_t)num_blocks) : 0;
+    // small blocks: bit j set when block j of the current window is inside the pool
+    uint64_t valid_blocks = kSmall ? __ballot((uint32_t)id_lane < (uint32_t)num_blocks) : 0;
+    int cur_win = 0;  // the window idw[0] holds (small blocks)
     // returns the unit's token mask (all 16 bits when every block is valid,
     // 0 for an invalid block of B >= 16)
     auto issue = [&](Regs& t, int u) __attribute__((always_inline)) -> int {
         if constexpr (kSmall) {
-            return load_small<T, HS, BS>(t, k_cache, v_cache, (int64_t)Hkv * TILE, (int64_t)kvh * TILE, id_lane,
-                                         valid_blocks, num_blocks, u, r, c);
+            // a window is 64 blocks, 4 * BS units; units are issued in
+            // increasing order, so the next window is at most one step away
+            constexpr int UPW = 4 * BS;
+            if (NWIN > 1 && u / UPW != cur_win) {  // uniform
+#pragma unroll
+                for (int k = 0; k + 1 < NWIN; ++k)
+                    idw[k] = idw[k + 1];
+                ++cur_win;
+                valid_blocks = __ballot((uint32_t)idw[0] < (uint32_t)num_blocks);
+            }
+            return load_small<T, HS, BS>(t, k_cache, v_cache, (int64_t)Hkv * TILE, (int64_t)kvh * TILE, idw[0],
+                                         valid_blocks, num_blocks, u - cur_win * UPW, r, c);
         } else {
             const int j = j_of(u);
             const int m = part_of(u);

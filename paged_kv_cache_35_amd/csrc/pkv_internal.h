@@ -61,7 +61,7 @@ struct DecodeArgs {
     int32_t max_blocks_per_seq;
     int32_t num_blocks;
     int32_t dtype;            // pkv_dtype
-    int32_t partition_blocks; // blocks per context partition (<= 64), one wave each
+    int32_t partition_blocks; // blocks per context partition (<= 64, or <= 512 tokens of B < 16), one wave each
     int32_t max_parts;        // chunks per sequence: ceil(max_blocks_per_seq / (partition_blocks * kDecodeWaves))
     int32_t interleave;       // 1: a chunk's blocks dealt round-robin to its waves;
                               // 0: one contiguous partition per wave

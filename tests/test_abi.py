@@ -321,8 +321,9 @@ def test_multi_token_step_and_slot_mapping_reject_bad_arguments(lib):
 
 def test_partition_lengths_for_every_block_size(lib):
     f = lib.pkv_decode_partition_tokens
-    # default: 512 tokens, at most 64 blocks of the wave's list
-    assert f(4, 8, 8, 64, 1024, 1, 0) == 64
+    # default: 512 tokens, at most 64 blocks of the wave's list (blocks of
+    # fewer than 16 tokens: 512 tokens, the list kept in windows of 64)
+    assert f(4, 8, 8, 64, 1024, 1, 0) == 512
     assert f(4, 8, 8, 64, 1024, 8, 0) == 512
     assert f(4, 8, 8, 64, 1024, 64, 0) == 512
     assert f(4, 8, 8, 64, 3, 8, 0) == 24          # a short table: one partition
@@ -330,7 +331,10 @@ def test_partition_lengths_for_every_block_size(lib):
     assert f(4, 8, 8, 64, 1024, 8, 24) == 0
     assert f(4, 8, 8, 64, 1024, 8, 32) == 32
     assert f(4, 8, 8, 64, 1024, 1, 48) == 48
-    assert f(4, 8, 8, 64, 1024, 1, 80) == 0       # 80 blocks of one token
+    assert f(4, 8, 8, 64, 1024, 1, 80) == 80      # 80 blocks of one token: two windows
+    assert f(4, 8, 8, 64, 1024, 1, 512) == 512
+    assert f(4, 8, 8, 64, 1024, 1, 528) == 0      # beyond 512 tokens
+    assert f(4, 8, 8, 64, 1024, 8, 576) == 0      # beyond 64 blocks
     assert f(4, 8, 8, 64, 1024, 64, 4096) == 4096
 
 

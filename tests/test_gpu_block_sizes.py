@@ -41,7 +41,8 @@ def test_decode_parity(B, dtype, hs, Hq, Hkv):
     check_attention(w, host_f64(r.out), ref)
 
 
-@pytest.mark.parametrize("B,P", [(1, 16), (1, 48), (8, 16), (8, 128), (64, 64), (64, 1024)])
+@pytest.mark.parametrize("B,P", [(1, 16), (1, 48), (1, 80), (1, 208), (1, 512), (8, 16), (8, 128), (64, 64),
+                                 (64, 1024)])
 def test_partition_lengths(B, P):
     w = pi.make_workload(3, S=5, len_lo=100, len_hi=2000, B=B, seed=22)
     announce(f"decode B={B} P={P} lens={list(w.seq_lens)}")
@@ -98,6 +99,47 @@ def test_fp8_pools_with_64_token_blocks(mq):
     else:
         check_step(w, *run_fp8(w))
         check_step(w, *run_fp8(w, step=True))
+
+
+@pytest.mark.parametrize("multi", [False, True])
+def test_one_token_blocks_in_windows(multi):
+    # B = 1 with 512-token partitions: each wave's block IDs sit in windows of
+    # 64; IDs outside the pool at window edges (entries 63, 64, 127 of the
+    # first partition, 200, 511) and at the next partition's first entry
+    # (512) skip exactly those tokens
+    lens = [1100, 700, 90]
+    kw = dict(seq_lens=lens, B=1, seed=28)
+    if multi:
+        kw["q_lens"] = [5, 3, 1]
+    w = pi.make_workload(3, **kw)
+    bad_at = [63, 64, 127, 200, 511, 512]
+    announce(f"B=1 windows: lengths {lens}, out-of-pool IDs at {bad_at}{' (multi-token)' if multi else ''}")
+    r = MRun(w) if multi else Run(w)
+    m = pkv()
+    bt = r.bt.clone()
+    for j in bad_at:
+        bt[0, j] = -1 - j
+    if multi:
+        out = m.paged_multi_token_attention(r.q, r.qs, w.max_q_len, r.kc, r.vc, bt, r.sl, w.scale)
+    else:
+        out = m.paged_decode_attention(r.q, r.kc, r.vc, bt, r.sl, w.scale)
+    torch.cuda.synchronize()
+    assert m.decode_partition_tokens(w.S, w.Hq, w.Hkv, w.hs, w.M, 1, 0) == 512
+    kp, vp = host_bits(r.kc), host_bits(r.vc)
+    keep = [j for j in range(w.M) if j not in bad_at]
+    tables = np.full_like(w.block_tables, w.block_tables[0, -1])
+    tables[0, :len(keep)] = w.block_tables[0, keep]
+    tables[1:] = w.block_tables[1:]
+    lens2 = w.seq_lens.copy()
+    lens2[0] -= len(bad_at)
+    if multi:
+        # every hole lies below the rows, so on the compacted table each row
+        # attends the same tokens as on the original one
+        assert max(bad_at) < w.seq_lens[0] - 5
+        ref = oracle.paged_multi_token_attention(w.q, w.q_start, kp, vp, tables, lens2, w.scale)
+    else:
+        ref = oracle.paged_attention(w.q, kp, vp, tables, lens2, w.scale)
+    check_attention(w, host_f64(out), ref)
 
 
 def test_fp8_pools_refuse_small_blocks():
