@@ -2,10 +2,13 @@
 """Decode-step benchmark for the paged KV-cache library on one MI355X.
 
 A step is one pass of the whole decode hot path over one batch, one
-`paged_decode_step` call: slot mapping of the new tokens, their KV append
-and the batch's longest-first schedule (one launch), then paged decode
-attention (context partitions, merged by log-sum-exp inside each
-work-group and, for sequences longer than one chunk, by a merge kernel).
+`paged_decode_step` call: slot mapping of the new tokens, their KV append,
+and paged decode attention (context partitions, merged by log-sum-exp
+inside each work-group and, for sequences longer than one chunk, by a
+merge kernel).  Batches of up to 64 sequences run it as one launch (the
+attention takes the new tokens from the step's input while work-groups of
+the same launch store them); larger ones as an append launch that also
+writes the batch's longest-first schedule, then the attention launch.
 Inputs are synthetic and
 resident in HBM before timing starts.
 
@@ -20,7 +23,8 @@ must read / the sum of the three step times), and `per_config` holds each
 layer's own record (step time and its spread, append and attention times,
 graph replay, roofline with its counter record, CPU oracle baseline with a
 full-size parity check, paged-vs-contiguous diagnostic).  The top-level
-`roofline` is the dominant kernel's: the attention call that takes longest.
+`roofline` is the dominant kernel's: the attention launch that takes
+longest (the one-launch step where the step is one launch).
 `--config N` runs one configuration alone and prints its record.
 
 Prints one JSON line.  `roofline` times the attention call with HIP events
@@ -42,6 +46,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# paged_decode_step is one launch for batches of up to this many sequences
+ONE_LAUNCH_MAX_SEQS = 64
 
 # counter records (rocprofv3 FETCH_SIZE / WRITE_SIZE of the attention launch) per configuration
 TRAFFIC_RECORDS = {(2, "fp8"): "traffic_paged_decode_attention_mha_fp8.txt",
@@ -582,21 +588,36 @@ def bench_decode(args, config: int, torch, pkv, pi, sr: dict, seed: int) -> dict
     P_used = pkv.decode_partition_tokens(w.S, w.Hq, w.Hkv, w.hs, w.M, w.B, P)
     turn = [0]
 
+    # batches of up to ONE_LAUNCH_MAX_SEQS sequences: the step is one launch
+    # (attention plus the stores of the new tokens; a chunk merge launch
+    # where the sequences are split)
+    one_launch = w.S <= ONE_LAUNCH_MAX_SEQS
+
     def step():
         # one decode step: slot of each sequence's new token (from its block
-        # table), append of its K/V and the longest-first schedule (one
-        # launch), then the attention (plus the chunk merge where needed)
+        # table) and the append of its K/V, and the attention (plus the chunk
+        # merge where needed); larger batches: the append launch also writes
+        # the longest-first schedule, then the attention launch
         d = copies[turn[0] % len(copies)]
         turn[0] += 1
         pkv.paged_decode_step(d["q"], d["nk"], d["nv"], d["kc"], d["vc"], d["bt"], d["sl"], w.scale, out=out,
                               slot_mapping=slots, workspace=ws_step, partition_tokens=P, stream=stream, **sc)
 
     def step_timed(ev, tables=None):
-        # the same step through the two entry points it is made of, with
-        # events around the append launch and around the attention launch
+        # the same step with events around its launches: a one-launch step
+        # whole (ev[0] .. ev[1], no separate append), else through the two
+        # entry points it is made of, with events around the append launch
+        # and around the attention launch
         d = copies[turn[0] % len(copies)]
         turn[0] += 1
         bt = d["bt"] if tables is None else tables
+        if one_launch:
+            ev[2].record(stream)
+            ev[0].record(stream)
+            pkv.paged_decode_step(d["q"], d["nk"], d["nv"], d["kc"], d["vc"], bt, d["sl"], w.scale, out=out,
+                                  slot_mapping=slots, workspace=ws_step, partition_tokens=P, stream=stream, **sc)
+            ev[1].record(stream)
+            return
         ev[2].record(stream)
         pkv.decode_append(d["nk"], d["nv"], bt, d["sl"], d["kc"], d["vc"], slot_mapping=slots, schedule=sched,
                           stream=stream, **sc)
@@ -671,7 +692,11 @@ def bench_decode(args, config: int, torch, pkv, pi, sr: dict, seed: int) -> dict
         traffic_path, config, P_used, args.contiguous, "fp8" if w.dtype == "fp8" else "native")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                "kernel": ("paged_decode_attention with the step's longest-first schedule: "
+                "kernel": (("paged_decode_step in one launch: paged_decode_partition_kernel with the new tokens' "
+                            "stores" + (" (one chunk per sequence, no merge launch)" if ws is None else
+                                        " + chunk merge kernel"))
+                           if one_launch else
+                           "paged_decode_attention with the step's longest-first schedule: "
                            "paged_decode_partition_kernel alone (one chunk per sequence, no merge launch)"
                            if ws is None else
                            "paged_decode_attention with the step's longest-first schedule: partition kernel + "
@@ -730,8 +755,9 @@ def bench_decode(args, config: int, torch, pkv, pi, sr: dict, seed: int) -> dict
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "decode_tokens_per_s": round(w.S / (ms_step / 1e3), 1),
         "attention_calls_per_s": round(1.0 / attn_avg_s, 1),
-        "append_us": {"mean": round(float(append_ms.mean()) * 1e3, 2),
-                      "median": round(float(np.median(append_ms)) * 1e3, 2)},
+        "append_us": ("inside the attention launch" if one_launch else
+                      {"mean": round(float(append_ms.mean()) * 1e3, 2),
+                       "median": round(float(np.median(append_ms)) * 1e3, 2)}),
         "graph_replay": graph_info,
         "paged_vs_contiguous": contig,
         "roofline": roofline,

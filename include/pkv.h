@@ -285,17 +285,20 @@ PKV_API size_t pkv_decode_step_workspace_bytes(int32_t num_seqs, int32_t num_q_h
 /*
  * One whole decode step in one call: for each sequence s, the new token
  * new_k[s], new_v[s] is stored in the slot of position seq_lens[s] - 1
- * (pkv_decode_append), then the attention of paged_decode_attention is
- * computed over all seq_lens[s] tokens, the new one included.  Two kernels
- * are launched in order on `stream`; the result, the pools and slot_mapping
- * are bit-identical to calling those two functions.  Every argument is
- * validated before anything is launched, so a rejected call changes nothing.
- * The append launch also writes the batch's longest-first schedule into the
- * workspace, and the attention launch reads it (see
- * pkv_decode_schedule_bytes).  (A single-launch variant, where the wave
- * reading the last block also stores the new token, was measured slower on
- * MI355X: stores issued while the pools are being streamed cost more than a
- * separate append launch.)
+ * (pkv_decode_append), and the attention of paged_decode_attention is
+ * computed over all seq_lens[s] tokens, the new one included.  The result,
+ * the pools and slot_mapping are bit-identical to calling those two
+ * functions in that order.  Every argument is validated before anything is
+ * launched, so a rejected call changes nothing.
+ *   - Batches of up to 64 sequences: one launch (plus the chunk merge where
+ *     sequences span several chunks).  The attention ranks the batch longest
+ *     first itself and takes each new token from new_k / new_v; work-groups
+ *     of the same launch, after the attention's, store the new tokens.
+ *   - Larger batches: the append launch, which also writes the batch's
+ *     longest-first schedule into the workspace (see
+ *     pkv_decode_schedule_bytes), then the attention launch, which reads it.
+ * new_k / new_v must not overlap the pools (they are read while the pools
+ * are written).
  *   new_k, new_v  device T [num_seqs][num_kv_heads][head_size]
  *   slot_mapping  device int64 [num_seqs] receiving the slots, or NULL
  *   workspace     device scratch of workspace_bytes >=
@@ -314,7 +317,7 @@ PKV_API pkv_status paged_decode_step(const void* q, const void* new_k, const voi
 /*
  * The decode step of paged_decode_step for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
- * harnesses that forbid allocation): the same two launches and the same
+ * harnesses that forbid allocation): the same launches and the same
  * results, bit for bit, with the workspace taken from a device array inside
  * the library instead of a caller buffer.  The array holds
  * PKV_STATIC_SCRATCH_BYTES on every GPU the library runs on, until the

@@ -352,6 +352,7 @@ pkv_status attention_args(const void* q, const void* k_cache, const void* v_cach
     if (check_workspace && need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
         return PKV_ERR_WORKSPACE;
 
+    a.step_append = {};
     a.sched_order = nullptr;
     a.sched_lens = nullptr;
     a.sched_tables = nullptr;
@@ -703,6 +704,17 @@ pkv_status paged_decode_step(const void* q, const void* new_k, const void* new_v
                                                         partition_tokens);
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
         return PKV_ERR_WORKSPACE;
+    if (num_seqs <= pkv::kLptMaxSeqs) {
+        // one launch: the attention ranks the batch itself and takes the new
+        // tokens from new_k / new_v, and work-groups after its own store them
+        // (plus the chunk merge launch, where there is one)
+        const pkv::AppendArgs ap = append_args(new_k, new_v, slot_mapping, block_tables, seq_lens, max_blocks_per_seq,
+                                               num_seqs, cache, k_cache, v_cache);
+        const int32_t chunks = cache->num_kv_heads * cache->head_size / (16 / ap.elem_bytes);  // 16-byte key chunks
+        a.step_append = {new_k, new_v, k_cache, v_cache, slot_mapping,
+                         (chunks + pkv::kStoreThreads - 1) / pkv::kStoreThreads, ap.k_inv_scale, ap.v_inv_scale};
+        return hip_status(pkv::launch_decode(a, (hipStream_t)stream));
+    }
     // the append launch writes the longest-first schedule after the
     // attention partials; the attention launch reads it
     pkv::AppendArgs::Schedule sched = {};

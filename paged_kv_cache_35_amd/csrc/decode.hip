@@ -40,6 +40,7 @@
 #include <type_traits>
 
 #include "attn_common.h"
+#include "kv_store.h"
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -335,6 +336,119 @@ __device__ __forceinline__ void fp8_wide_to_operands(const Fp8WideRegs<HS>& raw,
     }
 }
 
+// Decode step in one launch: the unit's token p (the sequence's new token)
+// is replaced by its K/V as the step's input holds them (sk, sv: head_size
+// elements each, the input type), in the operand layout of each unit
+// shape.  For FP8 pools the codes are formed as the store forms them
+// (quantize16, quantize1 with the same inverse scales), so the attention
+// reads the same bytes it would read from the pools after the store.
+// Sets element (or byte) j of a value operand where j is wave-uniform.
+template <int N, typename V, typename E>
+__device__ __forceinline__ void set_elem(V& v, int j, E x)
+{
+#pragma unroll
+    for (int e = 0; e < N; ++e)
+        if (e == j)
+            v[e] = x;
+}
+
+__device__ __forceinline__ unsigned set_byte(unsigned w, int j, unsigned code)
+{
+    return (w & ~(0xFFu << (8 * j))) | (code << (8 * j));
+}
+
+// 16-token unit, bf16 or fp32 (TileRegs): key chunk 4i + r of token c,
+// value tokens 4r .. 4r + 3 of head dim 16i + c.
+template <typename T, int HS>
+__device__ __forceinline__ void patch_token(TileRegs<T, HS>& t, const T* sk, const T* sv, int p, int r, int c,
+                                            float, float)
+{
+    constexpr int X = 16 / (int)sizeof(T);
+    using KV = typename std::conditional<sizeof(T) == 2, bf16x8, f32x4>::type;
+    if (c == p) {
+#pragma unroll
+        for (int i = 0; i < HS / (4 * X); ++i)
+            t.k.v[i] = *(const KV*)(sk + (4 * i + r) * X);
+    }
+    if (r == p / 4) {
+#pragma unroll
+        for (int i = 0; i < HS / 16; ++i)
+            set_elem<4>(t.v.v[i], p & 3, sv[16 * i + c]);
+    }
+}
+
+// 32-token unit, bf16 (WideRegs): key chunk 4i + r of token 16mp + c, value
+// tokens 8r .. 8r + 7 of head dim 16i + c.
+template <int HS>
+__device__ __forceinline__ void patch_token(WideRegs<HS>& t, const __bf16* sk, const __bf16* sv, int p, int r,
+                                            int c, float, float)
+{
+    if (c == (p & 15)) {
+#pragma unroll
+        for (int i = 0; i < HS / 32; ++i) {
+            const bf16x8 x = *(const bf16x8*)(sk + (4 * i + r) * 8);
+            if (p < 16)
+                t.k[0].v[i] = x;
+            else
+                t.k[1].v[i] = x;
+        }
+    }
+    if (r == (p >> 3)) {
+#pragma unroll
+        for (int i = 0; i < HS / 16; ++i)
+            set_elem<8>(t.v[i], p & 7, sv[16 * i + c]);
+    }
+}
+
+// 16-token unit of FP8 codes (Fp8Regs): key chunk 4i + r (16 dims) of token
+// c, value codes of tokens 4r .. 4r + 3 of head dim 16i + c.
+template <int HS>
+__device__ __forceinline__ void patch_token(Fp8Regs<HS>& t, const __bf16* sk, const __bf16* sv, int p, int r,
+                                            int c, float k_inv, float v_inv)
+{
+    if (c == p) {
+#pragma unroll
+        for (int i = 0; i < HS / 64; ++i) {
+            const u32x4 in[2] = {*(const u32x4*)(sk + (4 * i + r) * 16), *(const u32x4*)(sk + (4 * i + r) * 16 + 8)};
+            t.k[i] = quantize16(in, k_inv);
+        }
+    }
+    if (r == p / 4) {
+#pragma unroll
+        for (int i = 0; i < HS / 16; ++i)
+            t.v[i] = set_byte(t.v[i], p & 3, quantize1(__builtin_bit_cast(uint16_t, sv[16 * i + c]), v_inv));
+    }
+}
+
+// 32-token unit of FP8 codes (Fp8WideRegs): key chunk 4i + r of token
+// 16mp + c, value codes of tokens 8r .. 8r + 7 of head dim 16i + c.
+template <int HS>
+__device__ __forceinline__ void patch_token(Fp8WideRegs<HS>& t, const __bf16* sk, const __bf16* sv, int p, int r,
+                                            int c, float k_inv, float v_inv)
+{
+    if (c == (p & 15)) {
+#pragma unroll
+        for (int i = 0; i < HS / 64; ++i) {
+            const u32x4 in[2] = {*(const u32x4*)(sk + (4 * i + r) * 16), *(const u32x4*)(sk + (4 * i + r) * 16 + 8)};
+            const u32x4 code = quantize16(in, k_inv);
+            if (p < 16)
+                t.k[0][i] = code;
+            else
+                t.k[1][i] = code;
+        }
+    }
+    if (r == (p >> 3)) {
+#pragma unroll
+        for (int i = 0; i < HS / 16; ++i) {
+            const unsigned code = quantize1(__builtin_bit_cast(uint16_t, sv[16 * i + c]), v_inv);
+            if ((p & 7) < 4)
+                t.v[i][0] = set_byte(t.v[i][0], p & 3, code);
+            else
+                t.v[i][1] = set_byte(t.v[i][1], p & 3, code);
+        }
+    }
+}
+
 // Scores S^T for one 16-token sub-tile: element j of the result is token
 // 4r + j of the sub-tile, query head c.
 template <typename T, int HS>
@@ -440,7 +554,7 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     const int32_t* __restrict__ sched_tables, float oscale, void* __restrict__ out, int32_t out_f32,
     float* __restrict__ ws_o, float* __restrict__ ws_ml, const int32_t* __restrict__ q_start, int32_t num_q_rows,
     int32_t max_q_len, int32_t RT, const int32_t* __restrict__ sched_count, const uint32_t* __restrict__ sched_items,
-    int32_t rank_in_z)
+    int32_t rank_in_z, DecodeArgs::StepAppend sa)
 {
     using C = typename std::conditional<F8, uint8_t, T>::type;  // pool element type
     static_assert(!F8 || sizeof(T) == 2, "FP8 pools are read with bf16 queries");
@@ -466,9 +580,33 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     // heads (and row tiles) and y, z the ranks and chunks: rank in z (chunks
     // of one sequence consecutive) for small batches, where few work-groups
     // find themselves past their sequence's end, rank in y otherwise.
+    // Decode step in one launch (sa.k set): a 1-D grid whose first
+    // S * Hkv * max_parts work-groups are the attention's, in the order of
+    // the 3-D grid (KV head, then chunk, then rank), followed by sa.groups
+    // work-groups per sequence that store its new token.  Placed last, the
+    // stores fill the slots the attention's tail leaves free (placed first,
+    // they delayed the attention's first work-groups).
     // S_grid: the sequences of this launch.
     int kvh, rt = 0, yr, chunk, s_listed = 0, S_grid;
-    if (sched_items) {
+    if (!MQ && sa.k) {
+        static_assert(NW * 64 == kStoreThreads, "a store work-group is one attention work-group");
+        const int per_seq = Hkv * max_parts;
+        S_grid = (int)(gridDim.x / (unsigned)(per_seq + sa.groups));
+        const int bx = blockIdx.x;
+        if (bx >= S_grid * per_seq) {  // uniform: before any barrier
+            using E = typename std::conditional<F8, uint8_t,
+                                                typename std::conditional<sizeof(T) == 2, uint16_t, uint32_t>::type>::type;
+            const int t = bx - S_grid * per_seq;
+            store_token<E, true>(t / sa.groups, t % sa.groups, (const u32x4*)sa.k, (const u32x4*)sa.v,
+                                 sa.slot_mapping, block_tables, seq_lens, M, (u32x4*)sa.k_cache, (E*)sa.v_cache, Hkv,
+                                 HS, BS, num_blocks, sa.k_inv_scale, sa.v_inv_scale);
+            return;
+        }
+        kvh = bx % Hkv;
+        const int rest = bx / Hkv;
+        chunk = rest % max_parts;
+        yr = rest / max_parts;
+    } else if (sched_items) {
         const int HR = MQ ? Hkv * RT : Hkv;  // (KV head, row tile) pairs
         const int item = blockIdx.x / HR;
         const int xr = blockIdx.x - item * HR;
@@ -676,6 +814,30 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
         }
     }
 
+    // Decode step in one launch: the new token (position L - 1) comes from
+    // sa.k / sa.v.  It is patched in only where the store writes it: the
+    // length inside the table row (L == L_in) and the unit's block inside the
+    // pool (checked with the unit).  Each wave of the chunk holding it copies
+    // it to the end of the wave's own slice of the merge buffer, which only
+    // the merge uses again, after the tile loop; no other wave reads the
+    // copy, so it needs no barrier.
+    const bool patch = !MQ && sa.k != nullptr && L == L_in;
+    const int tokp = L - 1;
+    const bool stash = patch && tokp / BS >= cb0 && tokp / BS < cb0 + NW * PB;
+    T* const st = reinterpret_cast<T*>(&sm_out[w][16 * HS]) - 2 * HS;  // key, then value
+    constexpr int kStashWords = 2 * HS * (int)sizeof(T) / 4;           // 64, 128 or 256
+    uint32_t stw[kStashWords / 64];
+    if (stash) {
+        const int64_t row = ((int64_t)s * Hkv + kvh) * HS;
+        const uint32_t* srck = reinterpret_cast<const uint32_t*>(static_cast<const T*>(sa.k) + row);
+        const uint32_t* srcv = reinterpret_cast<const uint32_t*>(static_cast<const T*>(sa.v) + row);
+#pragma unroll
+        for (int k = 0; k < kStashWords / 64; ++k) {
+            const int idx = lane + 64 * k;
+            stw[k] = idx < kStashWords / 2 ? srck[idx] : srcv[idx - kStashWords / 2];
+        }
+    }
+
     f32x4 O[HS / 16];
 #pragma unroll
     for (int i = 0; i < HS / 16; ++i)
@@ -877,6 +1039,11 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     };
     auto run = [&](Regs& t, int u, int tmask) __attribute__((always_inline)) {
         const int tok0 = first_token(u);
+        if constexpr (!MQ) {
+            const int p = tokp - tok0;  // the new token's place in the unit
+            if (patch && p >= 0 && p < UT && ((tmask >> (kSmall ? p : 0)) & 1))  // uniform
+                patch_token(t, st, st + HS, p, r, c, sa.k_inv_scale, sa.v_inv_scale);
+        }
         const bool ok = tmask == 0xFFFF;
         if constexpr (F8 && kWide) {
             WideRegs<HS> op;  // the raw codes as bf16 operands
@@ -895,6 +1062,13 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
     if (nunits > 0) {
         Regs ta, tb;
         int ok_a = issue(ta, 0);
+        if (stash) {  // after the first unit's loads, so that they are not held back
+            uint32_t* sw = reinterpret_cast<uint32_t*>(st);
+#pragma unroll
+            for (int k = 0; k < kStashWords / 64; ++k)
+                sw[lane + 64 * k] = stw[k];
+            __builtin_amdgcn_wave_barrier();
+        }
         int ok_b = 0;
         int u = 0;
         for (; u + 2 < nunits; u += 2) {
@@ -1243,7 +1417,9 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
     const bool listed = a.sched_items != nullptr;
     const int rank_in_z = a.num_seqs <= kLptMaxSeqs ? 1 : 0;
     const int64_t HR = (int64_t)a.num_kv_heads * (MQ ? a.row_tiles : 1);  // (KV head, row tile) pairs
-    const dim3 grid = listed      ? dim3((unsigned)(HR * a.num_seqs * a.max_parts))
+    const bool fused = !MQ && a.step_append.k != nullptr;
+    const dim3 grid = fused ? dim3((unsigned)(a.num_seqs * (HR * a.max_parts + a.step_append.groups)))
+                      : listed      ? dim3((unsigned)(HR * a.num_seqs * a.max_parts))
                       : rank_in_z ? dim3((unsigned)HR, a.max_parts, a.num_seqs)
                                   : dim3((unsigned)HR, a.num_seqs, a.max_parts);
     const float qscale = a.scale * kLog2e * (F8 ? a.k_scale : 1.0f);
@@ -1254,7 +1430,7 @@ static hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream)
                        (a.num_seqs <= kLptMaxSeqs && a.max_blocks_per_seq < (1 << 23)) ? 1 : 0, qscale,
                        a.sched_order, a.sched_lens, a.sched_tables, F8 ? a.v_scale : 1.0f, a.out, a.out_f32, a.ws_o,
                        a.ws_ml, a.q_start, a.num_q_rows, a.max_q_len, a.row_tiles, a.sched_count, a.sched_items,
-                       rank_in_z);
+                       rank_in_z, a.step_append);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_parts <= 1)
         return e;  // one chunk per sequence: the partition kernel wrote the output

@@ -17,6 +17,7 @@ constexpr int kDecodeWaves = 4;
 // longest first by the attention kernel itself (each work-group ranks all
 // lengths: O(S^2 / threads) work, which outweighs the gain on larger batches).
 constexpr int kLptMaxSeqs = 64;
+constexpr int kStoreThreads = 256;  // threads of a work-group that stores new tokens (kv_store.h)
 // The decode step's append launch writes a longest-first schedule for
 // batches of up to this many sequences (each of its work-groups reads all
 // lengths once).
@@ -67,6 +68,21 @@ struct DecodeArgs {
                               // 0: one contiguous partition per wave
     float scale;
     float k_scale, v_scale;   // FP8 pools: stored code * scale (1 otherwise)
+    // Decode step in one launch (k null otherwise; one query row per
+    // sequence): after the attention's work-groups come `groups` work-groups
+    // per sequence that store its new token k[s], v[s] in the slot of
+    // position seq_lens[s] - 1 (store_token in kv_store.h), and the attention
+    // takes that token from k / v instead of the pools, which those
+    // work-groups may not have written yet.
+    struct StepAppend {
+        const void* k;
+        const void* v;
+        void* k_cache;          // the pools (written)
+        void* v_cache;
+        int64_t* slot_mapping;  // receives the slots, or null
+        int32_t groups;         // store work-groups per token
+        float k_inv_scale, v_inv_scale;  // FP8 pools: code = E4M3(fp32(x * inv_scale))
+    } step_append;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

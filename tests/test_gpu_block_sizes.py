@@ -175,3 +175,51 @@ def test_block_id_outside_the_pool_skips_its_tokens(B, bad):
     lens[0] -= B
     ref = oracle.paged_attention(w.q, kp, vp, tables, lens, w.scale)
     check_attention(w, host_f64(out), ref)
+
+
+# The decode step of up to 64 sequences is one launch: the attention takes
+# each new token from the step's input while work-groups of the same launch
+# store it.  Its output, pools and slots must be those of the separate
+# slot-mapping, append and attention calls, bit for bit, in every unit
+# shape (16-token tiles, 32-token units, FP8 codes, blocks under 16 tokens)
+# and wherever the new token falls in its unit.  Planted: a sequence whose
+# last block ID is negative and one whose last block is past the pool (the
+# token is neither stored nor attended), and a length past the table row
+# (the step attends the row's tokens and stores nothing).
+ONE_LAUNCH_CASES = [(1, "bf16", 128), (1, "f32", 64), (8, "bf16", 128), (8, "f32", 128), (8, "bf16", 64),
+                    (16, "bf16", 128), (16, "bf16", 64), (16, "f32", 128), (16, "fp8", 128), (16, "fp8", 64),
+                    (32, "bf16", 128), (32, "f32", 64), (32, "fp8", 128), (64, "bf16", 128), (64, "bf16", 64),
+                    (64, "f32", 128), (64, "fp8", 128), (64, "fp8", 64)]
+
+
+@pytest.mark.parametrize("P", [None, 64])
+@pytest.mark.parametrize("B,dtype,hs", ONE_LAUNCH_CASES)
+def test_one_launch_step_bit_identical_to_separate_calls(B, dtype, hs, P):
+    lens = EDGE_LENS + [0, 5, 700, 40]
+    w = pi.make_workload(3, seq_lens=lens, dtype=dtype, B=B, hs=hs, Hq=8, Hkv=2, seed=27)
+    assert w.S <= 64
+    bt = w.block_tables.copy()
+    sl = w.seq_lens.copy()
+    nb = w.k_cache.shape[0]
+    bt[28, 4 // B] = -1                     # length 5: last block ID negative
+    bt[29, 699 // B] = nb + 3               # length 700: last block past the pool
+    sl[30] = w.M * B + 9                    # length past the table row
+    part = w.partition_tokens if P is None else P
+    announce(f"one-launch decode step B={B} {dtype} hs={hs} P={part} lens={list(sl)}")
+    m = pkv()
+    sc = dict(k_scale=w.k_scale, v_scale=w.v_scale)
+    q, nk, nv, bt_d, sl_d = dev(w.q), dev(w.new_k), dev(w.new_v), dev(bt), dev(sl)
+    kc, vc = dev(w.k_cache), dev(w.v_cache)
+    slots = torch.full((w.S,), -7, dtype=torch.int64, device="cuda")
+    out = m.paged_decode_step(q, nk, nv, kc, vc, bt_d, sl_d, w.scale, slot_mapping=slots, partition_tokens=part, **sc)
+    kc2, vc2 = dev(w.k_cache), dev(w.v_cache)
+    slots2 = m.decode_slot_mapping(bt_d, sl_d, B)
+    m.kv_cache_append(nk, nv, slots2, kc2, vc2, **sc)
+    out2 = m.paged_decode_attention(q, kc2, vc2, bt_d, sl_d, w.scale, partition_tokens=part, **sc)
+    torch.cuda.synchronize()
+    assert torch.equal(slots, slots2)
+    assert list(slots2[28:31].cpu().numpy()) == [-1, (nb + 3) * B + 699 % B, -1]
+    assert same_bytes(host_bits(kc), host_bits(kc2))
+    assert same_bytes(host_bits(vc), host_bits(vc2))
+    bits = torch.int16 if out.dtype == torch.bfloat16 else torch.int32
+    assert torch.equal(out.view(bits), out2.view(bits))
