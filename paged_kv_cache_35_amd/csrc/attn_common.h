@@ -90,21 +90,15 @@ __device__ __forceinline__ void store_out4(void* out, int64_t i, f32x4 x, bool o
     }
 }
 
-// Four E4M3 codes (one dword) to four bf16: v_cvt_pk_f32_fp8 gives the exact
-// values in fp32, and an E4M3 value has at most 4 significant bits, so its
-// fp32 pattern's upper half is the same value in bf16.  Element e of the
-// result is code e (byte e of w).
-__device__ __forceinline__ unsigned upper_halves(float x0, float x1)
-{
-    return (__builtin_bit_cast(unsigned, x0) >> 16) | (__builtin_bit_cast(unsigned, x1) & 0xFFFF0000u);
-}
-
+// Four E4M3 codes (one dword) to four bf16.  Every E4M3 value (at most 4
+// significant bits, exponents 2^-9 .. 2^8) is exact in bf16, and gfx950
+// converts two codes to two packed bf16 in one instruction
+// (v_cvt_scalef32_pk_bf16_fp8; a scale of 1.0 leaves the values as they
+// are).  Element e of the result is code e (byte e of w).
 __device__ __forceinline__ void fp8x4_to_bf16(unsigned w, unsigned& lo, unsigned& hi)
 {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);  // codes 0, 1
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);   // codes 2, 3
-    lo = upper_halves(a[0], a[1]);
-    hi = upper_halves(b[0], b[1]);
+    lo = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));  // codes 0, 1
+    hi = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));   // codes 2, 3
 }
 
 }  // namespace pkv

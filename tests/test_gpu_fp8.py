@@ -150,3 +150,41 @@ def test_full_config_fp8(cfg):
     torch.cuda.synchronize()
     check_attention(w, host_f64(out32), ref, out_f32=True)
     check_rounding(out, out32)
+
+
+@pytest.mark.parametrize("path", ["decode", "multi_token", "multi_token_unpartitioned"])
+def test_every_finite_code_reads_back_exactly(path):
+    # One cached token per sequence: its softmax weight is exactly 1, so with
+    # an fp32 output each head dim returns that token's value code times
+    # v_scale, with no rounding.  The two KV heads' 256 value dims hold every
+    # finite E4M3 code (the two NaN codes replaced by zeros); the other slots
+    # of the block hold NaN codes, which must stay masked.
+    Hkv, hs, B, nb, blk = 2, 128, 16, 4, 2
+    codes = np.arange(256, dtype=np.uint8).reshape(Hkv, hs)
+    codes[codes == 0x7F] = 0x00
+    codes[codes == 0xFF] = 0x80
+    kp = np.full((nb, Hkv, hs // 16, B, 16), 0x7F, np.uint8)
+    kp[blk, :, :, 0, :] = 0  # the token's key: zeros
+    vp = np.full((nb, Hkv, hs, B), 0x7F, np.uint8)
+    vp[blk, :, :, 0] = codes
+    v_scale = 2.0
+    expect = np.array([[oracle.fp8_decode(c) for c in row] for row in codes]) * v_scale
+    rng = np.random.default_rng(11)
+    q = dev(pi.bf16_bits_from_f32(rng.standard_normal((1, Hkv, hs)).astype(np.float32)))
+    bt, sl = dev(np.array([[blk, 1]], np.int32)), dev(np.array([1], np.int32))
+    kc, vc = dev(kp), dev(vp)
+    announce(f"fp8 exact codes through {path}")
+    m = pkv()
+    if path == "decode":
+        out = m.paged_decode_attention(q, kc, vc, bt, sl, 0.125, k_scale=1.0, v_scale=v_scale,
+                                       out_dtype=torch.float32)
+    else:
+        P = m.PARTITION_NONE if path == "multi_token_unpartitioned" else 0
+        qs = dev(np.array([0, 1], np.int32))
+        out = m.paged_multi_token_attention(q, qs, 1, kc, vc, bt, sl, 0.125, partition_tokens=P, k_scale=1.0,
+                                            v_scale=v_scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)[0]
+    bad = np.argwhere(got != expect)
+    assert bad.size == 0, f"{len(bad)} codes differ, first head {bad[0][0]} dim {bad[0][1]}: " \
+                          f"code {codes[tuple(bad[0])]:#04x} got {got[tuple(bad[0])]} want {expect[tuple(bad[0])]}"
