@@ -211,10 +211,14 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     }
 
     f32x4 O[kPfTiles][HS / 16];
-    float m_run[kPfTiles], l_part[kPfTiles];
+    // m_thr: the raw score above which the running maximum is raised,
+    // (m_run + kRescaleSlack) / qscale, kept beside m_run so that the test
+    // per unit is one compare
+    float m_run[kPfTiles], m_thr[kPfTiles], l_part[kPfTiles];
 #pragma unroll
     for (int kt = 0; kt < kPfTiles; ++kt) {
         m_run[kt] = -1e30f;
+        m_thr[kt] = (-1e30f + kRescaleSlack) / qscale;
         l_part[kt] = 0.f;
 #pragma unroll
         for (int i = 0; i < HS / 16; ++i)
@@ -352,17 +356,20 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                 for (int jj = 0; jj < 4; ++jj)
                     sc[kt][4 * mp + jj] = S[kt][mp][jj];
         if (t0 + kPfUnit > Lmin[0] || t0 + kPfUnit > Lmin[1] || !all_valid) {
-            asm volatile("" ::: "memory");  // a real branch: most units need no masking
+            // a real branch: most units need no masking.  Token tt = 8r + e
+            // of the unit (e = 4mp + jj, key_token order) is kept when e is
+            // below lim = Lq - t0 - 8r and bit e of tm = tmask >> 8r is set;
+            // the asm keeps lim and tm from being formed before the branch
+            int tm = (int)(tmask >> (8 * r));
+            asm volatile("" : "+v"(tm));
 #pragma unroll
-            for (int kt = 0; kt < kPfTiles; ++kt)
+            for (int kt = 0; kt < kPfTiles; ++kt) {
+                int lim = Lq[kt] - t0 - 8 * r;
+                asm volatile("" : "+v"(lim));
 #pragma unroll
-                for (int mp = 0; mp < 2; ++mp)
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        const int tt = key_token(16 * mp + 4 * r + jj);  // = 8r + 4mp + jj
-                        sc[kt][4 * mp + jj] =
-                            (t0 + tt < Lq[kt] && ((tmask >> tt) & 1)) ? sc[kt][4 * mp + jj] : -INFINITY;
-                    }
+                for (int e = 0; e < 8; ++e)
+                    sc[kt][e] = (e < lim && ((tm >> e) & 1)) ? sc[kt][e] : -INFINITY;
+            }
         }
         // Online softmax of tile kt, in two parts.  raise_max: the running
         // maximum is raised only when a score exceeds it by more than
@@ -373,22 +380,27 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         auto raise_max = [&](int kt, float& alpha) __attribute__((always_inline)) -> bool {
             // IEEE maximum (NaN-propagating): three-operand instructions
             // that need no canonicalization of the matrix results, unlike fmaxf
-            const float mx = __builtin_elementwise_maximum(
-                __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[kt][0], sc[kt][1]),
-                                              __builtin_elementwise_maximum(sc[kt][2], sc[kt][3])),
-                __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[kt][4], sc[kt][5]),
-                                              __builtin_elementwise_maximum(sc[kt][6], sc[kt][7])));
+            // (grouped so that it forms four instructions: three of three
+            // operands and one of two)
+            const float m1 = __builtin_elementwise_maximum(
+                __builtin_elementwise_maximum(sc[kt][0], sc[kt][1]), sc[kt][2]);
+            const float m2 = __builtin_elementwise_maximum(
+                __builtin_elementwise_maximum(sc[kt][3], sc[kt][4]), sc[kt][5]);
+            const float m3 = __builtin_elementwise_maximum(
+                __builtin_elementwise_maximum(sc[kt][6], sc[kt][7]), m1);
+            const float mx = __builtin_elementwise_maximum(m2, m3);
             // A row's maximum exceeds the running maximum by the slack exactly
             // when one of its lanes' own maxima does (the running maximum is
             // the same in the row's four lane groups, and scaling by qscale > 0
             // keeps the order), so the ballot needs no exchange between lane
             // groups; the row maximum is formed only when the maximum rises.
-            const bool raise = __ballot(mx * qscale > m_run[kt] + kRescaleSlack) != 0;  // uniform
+            const bool raise = __ballot(mx > m_thr[kt]) != 0;  // uniform
             alpha = 1.f;
             if (raise) {
                 const float m_new = fmaxf(m_run[kt], max_over_lane_groups(mx) * qscale);
                 alpha = __builtin_amdgcn_exp2f(m_run[kt] - m_new);
                 m_run[kt] = m_new;
+                m_thr[kt] = (m_new + kRescaleSlack) / qscale;
                 l_part[kt] *= alpha;
             }
             return raise;
