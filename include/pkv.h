@@ -249,6 +249,8 @@ PKV_API size_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *   k_cache, v_cache  device pools (layout above)
  *   block_tables  device int32 [num_seqs][max_blocks_per_seq]
  *   seq_lens      device int32 [num_seqs]
+ *   scale         softmax scale, positive and finite (else PKV_ERR_INVALID_ARG;
+ *                 the same rule holds for every attention entry point below)
  *   out           device T (fp32 with cache->out_f32) [num_seqs][num_q_heads][head_size], written
  *   workspace     device scratch of workspace_bytes >= pkv_decode_workspace_bytes(...)
  *                 (may be NULL when that size is 0); contents are overwritten

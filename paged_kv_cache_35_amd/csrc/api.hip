@@ -324,6 +324,10 @@ pkv_status attention_args(const void* q, const void* k_cache, const void* v_cach
     pkv_status st = check_cache(cache);
     if (st != PKV_OK)
         return st;
+    // the kernels keep the running maximum of raw scores, which needs a
+    // positive scale
+    if (!(scale > 0.f) || !std::isfinite(scale))
+        return PKV_ERR_INVALID_ARG;
     const int32_t Hkv = cache->num_kv_heads;
     if (num_q_heads % Hkv != 0)
         return PKV_ERR_INVALID_ARG;

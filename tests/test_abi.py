@@ -58,9 +58,9 @@ FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: validation fails
 
 
 def attn(lib, *, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, S=4, Hq=8, M=4, d=None, out=FAKE, ws=None,
-         ws_bytes=0, P=0, sched=None, sched_bytes=0):
+         ws_bytes=0, P=0, sched=None, sched_bytes=0, scale=0.125):
     d = d or desc()
-    return lib.paged_decode_attention(q, kc, vc, bt, sl, S, Hq, M, ctypes.byref(d), 0.125, out, ws, ws_bytes, P,
+    return lib.paged_decode_attention(q, kc, vc, bt, sl, S, Hq, M, ctypes.byref(d), scale, out, ws, ws_bytes, P,
                                       sched, sched_bytes, None)
 
 
@@ -78,6 +78,10 @@ def test_attention_rejects_bad_arguments(lib):
     assert attn(lib, d=desc(dtype=2, k_scale=0.0)) == INVALID
     assert attn(lib, d=desc(dtype=2, v_scale=float("inf"))) == INVALID
     assert attn(lib, d=desc(dtype=2), S=0) == OK
+    # the softmax scale must be positive and finite
+    for bad in (0.0, -0.125, float("inf"), float("nan")):
+        assert attn(lib, scale=bad) == INVALID
+        assert attn(lib, scale=bad, S=0) == INVALID
     assert attn(lib, d=desc(nb=0)) == INVALID
     assert attn(lib, M=0) == INVALID
     assert attn(lib, S=-1) == INVALID
@@ -262,10 +266,11 @@ def test_multi_token_workspace_sizes(lib):
     assert f(16, 30, 8, 128, 4, 1024, 16, 0) == 0
 
 
-def mq(lib, *, q=FAKE, qs=FAKE, rows=8, mql=2, S=4, Hq=8, M=4, d=None, out=FAKE, ws=None, ws_bytes=0, P=0):
+def mq(lib, *, q=FAKE, qs=FAKE, rows=8, mql=2, S=4, Hq=8, M=4, d=None, out=FAKE, ws=None, ws_bytes=0, P=0,
+       scale=0.125):
     d = d or desc()
     return lib.paged_multi_token_attention(q, qs, rows, mql, FAKE, FAKE, FAKE, FAKE, S, Hq, M, ctypes.byref(d),
-                                           0.125, out, ws, ws_bytes, P, None, 0, None)
+                                           scale, out, ws, ws_bytes, P, None, 0, None)
 
 
 def test_multi_token_attention_rejects_bad_arguments(lib):
@@ -275,6 +280,9 @@ def test_multi_token_attention_rejects_bad_arguments(lib):
     assert mq(lib, mql=65536) == UNSUPPORTED
     assert mq(lib, q=ctypes.c_void_p(0x10008)) == INVALID
     assert mq(lib, Hq=12) == INVALID
+    for bad in (0.0, -1.0, float("nan")):
+        assert mq(lib, scale=bad) == INVALID
+        assert mq(lib, scale=bad, P=-1) == INVALID
     need = lib.pkv_multi_token_workspace_bytes(4, 8, 8, 64, 2, 4096, 16, 0)
     assert need > 0
     assert mq(lib, M=4096, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
