@@ -150,6 +150,50 @@ def stream_read_ceiling(torch, pkv, nbytes: int = 2 << 30, reps: int = 20) -> di
     return {"gbps": round(best[0], 1), "work_groups": best[1], "bytes": nbytes}
 
 
+def gather_read_ceiling(torch, pkv, w, copies, reps: int = 20):
+    """The rate of the workload's paged access pattern on its own: the
+    library's gather-read probe over the key and value tiles that the
+    attention reads (every (sequence, KV head, block) tile of each
+    sequence's first ceil(L / B) table entries, keys and values in turn, in
+    batch order), every address known in advance, alternating between the
+    input copies as the timed steps do (best of four grid sizes).  None when
+    a tile is not a multiple of 1 KiB (B = 1)."""
+    esz = {"f32": 4, "bf16": 2, "fp8": 1}[w.dtype]
+    tile = w.B * w.hs * esz
+    if tile % 1024:
+        return None
+    nblk = (w.seq_lens.astype(np.int64) + w.B - 1) // w.B
+    ids, heads = [], []
+    for s in range(w.S):
+        row = w.block_tables[s, :nblk[s]].astype(np.int64)
+        ids.append(np.tile(row, w.Hkv))
+        heads.append(np.repeat(np.arange(w.Hkv, dtype=np.int64), nblk[s]))
+    base = (np.concatenate(ids) * w.Hkv + np.concatenate(heads)) * tile
+    offs = np.repeat(base, 2)  # key tile, then the value tile at the same place of the other pool
+    t_offs = torch.from_numpy(offs).cuda()
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    nbytes = len(offs) * tile
+    best = (0.0, 0)
+    for wg in (512, 1024, 2048, 4096):
+        for i in range(3):
+            d = copies[i % len(copies)]
+            pkv.probe_gather_read(d["kc"], d["vc"], t_offs, tile, out, wg, stream=stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(reps):
+            d = copies[i % len(copies)]
+            pkv.probe_gather_read(d["kc"], d["vc"], t_offs, tile, out, wg, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / reps
+        best = max(best, (nbytes / us / 1e3, wg, us))
+    del t_offs, out
+    return {"gbps": round(best[0], 1), "work_groups": best[1], "us": round(best[2], 2), "bytes": int(nbytes),
+            "tiles": int(len(offs)), "tile_bytes": int(tile),
+            "gbps_algorithmic": round(w.kv_read_bytes() / best[2] / 1e3, 1)}
+
+
 def multi_token_counts(w):
     """(KV bytes, attention flops) one multi-token step must move and do: each
     sequence's L cached tokens once per KV head (keys and values), plus the
@@ -711,6 +755,14 @@ def bench_decode(args, config: int, torch, pkv, pi, sr: dict, seed: int) -> dict
         roofline.update({"unique_bytes_per_launch": unique,
                          "achieved_unique_gbps": round(unique / attn_avg_s / 1e9, 1)})
     roofline.update({"stream_read": sr, "frac_of_stream_read": round(achieved / sr["gbps"], 4)})
+    # the same tiles read by the gather-read probe alone: the ceiling of this
+    # access pattern (frac = the probe's time over the launch's time).  Not
+    # for shared blocks: the probe reads each branch's copy of the prefix at
+    # another time, so it gets less from the caches than the attention does
+    gr = None if (args.contiguous or unique < kv_bytes) else gather_read_ceiling(torch, pkv, w, copies)
+    if gr is not None:
+        roofline.update({"gather_read": gr, "frac_of_gather_read": round(achieved / gr["gbps_algorithmic"], 4)})
+        log(f"config {config}: gather-read probe {gr['gbps']} GB/s over {gr['tiles']} tiles ({gr['us']} us)")
     cpu = None
     if not args.no_cpu_baseline:
         log(f"config {config}: timing the CPU oracle sample")

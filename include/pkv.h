@@ -661,6 +661,31 @@ PKV_API pkv_status pkv_validate(const int32_t* block_tables, const int32_t* seq_
 PKV_API pkv_status pkv_probe_stream_read(const void* buf, size_t bytes, void* out, int32_t work_groups,
                                          void* stream);
 
+/*
+ * Gather-read probe: reads num_tiles whole tiles of tile_bytes each, tile t
+ * from buf0 (t even) or buf1 (t odd) at byte offset tile_offsets[t], with
+ * `work_groups` work-groups of 256 threads (each wave the next contiguous
+ * share of the list, eight 16-byte non-temporal loads in flight per thread).
+ * With the key and value tiles of a pool's blocks listed in turn (one
+ * (block, KV head) tile of each per entry pair, as block_tables and
+ * seq_lens select them: the cache-structure page's block-table translation)
+ * it gives the rate of the paged access pattern on its own, every address
+ * known in advance: the ceiling of decode attention on that pool, below the
+ * streaming probe's.  Not part of the attention method.
+ *   buf0, buf1     device buffers of bytes0, bytes1 bytes, 16-byte aligned
+ *   tile_offsets   device int64 [num_tiles]; a tile at a negative offset, an
+ *                  offset that is not a multiple of 16, or reaching past its
+ *                  buffer is skipped (never read)
+ *   tile_bytes     a multiple of 1024, 1024 .. 1048576
+ *   out            device buffer of 4 bytes, written as by pkv_probe_stream_read
+ *   work_groups    1 .. 1048576
+ * Asynchronous on `stream`.  PKV_ERR_INVALID_ARG for a null or misaligned
+ * buffer, tile_bytes or work_groups out of range, or a negative num_tiles.
+ */
+PKV_API pkv_status pkv_probe_gather_read(const void* buf0, size_t bytes0, const void* buf1, size_t bytes1,
+                                         const int64_t* tile_offsets, int64_t num_tiles, int32_t tile_bytes,
+                                         void* out, int32_t work_groups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

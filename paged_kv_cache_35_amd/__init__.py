@@ -112,6 +112,8 @@ def library():
         L.pkv_validate.argtypes = [P, P, i32, i32, P, i32, P, ctypes.POINTER(CacheDesc), P, P]
         L.pkv_probe_stream_read.restype = i32
         L.pkv_probe_stream_read.argtypes = [P, sz, P, i32, P]
+        L.pkv_probe_gather_read.restype = i32
+        L.pkv_probe_gather_read.argtypes = [P, sz, P, sz, P, i64, i32, P, i32, P]
         L.pkv_pool_create.restype = P
         L.pkv_pool_create.argtypes = [i32, i32]
         L.pkv_pool_create_with_free_list.restype = P
@@ -658,6 +660,25 @@ def probe_stream_read(buf: torch.Tensor, out: torch.Tensor, work_groups: int, st
         raise ValueError("out must hold 4 bytes")
     _check("pkv_probe_stream_read", library().pkv_probe_stream_read(
         _dev(buf, "buf"), buf.numel() * buf.element_size(), _dev(out, "out"), int(work_groups), _stream(stream)))
+
+
+def probe_gather_read(buf0: torch.Tensor, buf1: torch.Tensor, tile_offsets: torch.Tensor, tile_bytes: int,
+                      out: torch.Tensor, work_groups: int, stream=None) -> None:
+    """One read of the tiles listed in tile_offsets (int64 byte offsets; even
+    entries in buf0, odd ones in buf1), a measurement aid: time it to get
+    the rate of a paged access pattern; `out` is a 4-byte device buffer."""
+    for name, b in (("buf0", buf0), ("buf1", buf1)):
+        if not b.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if tile_offsets.dtype != torch.int64 or not tile_offsets.is_contiguous():
+        raise ValueError("tile_offsets must be a contiguous int64 tensor")
+    if out.numel() * out.element_size() < 4:
+        raise ValueError("out must hold 4 bytes")
+    n = tile_offsets.numel()
+    _check("pkv_probe_gather_read", library().pkv_probe_gather_read(
+        _dev(buf0, "buf0"), buf0.numel() * buf0.element_size(), _dev(buf1, "buf1"),
+        buf1.numel() * buf1.element_size(), _dev(tile_offsets, "tile_offsets") if n else None, n, int(tile_bytes),
+        _dev(out, "out"), int(work_groups), _stream(stream)))
 
 
 def copy_blocks(pairs: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:

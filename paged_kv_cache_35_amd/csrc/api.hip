@@ -865,4 +865,18 @@ pkv_status pkv_probe_stream_read(const void* buf, size_t bytes, void* out, int32
     return hip_status(pkv::launch_stream_read(buf, bytes, out, work_groups, (hipStream_t)stream));
 }
 
+pkv_status pkv_probe_gather_read(const void* buf0, size_t bytes0, const void* buf1, size_t bytes1,
+                                 const int64_t* tile_offsets, int64_t num_tiles, int32_t tile_bytes, void* out,
+                                 int32_t work_groups, void* stream)
+{
+    if (!buf0 || !buf1 || !out || !aligned16(buf0) || !aligned16(buf1) || num_tiles < 0 ||
+        work_groups < 1 || work_groups > (1 << 20) || tile_bytes < 1024 || tile_bytes > (1 << 20) ||
+        tile_bytes % 1024 != 0 || (num_tiles > 0 && !tile_offsets))
+        return PKV_ERR_INVALID_ARG;
+    if (num_tiles == 0)
+        return PKV_OK;
+    return hip_status(pkv::launch_gather_read(buf0, bytes0, buf1, bytes1, tile_offsets, num_tiles, tile_bytes, out,
+                                              work_groups, (hipStream_t)stream));
+}
+
 }  // extern "C"

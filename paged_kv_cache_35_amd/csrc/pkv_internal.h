@@ -90,6 +90,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 // Streaming-read probe (probe.hip): reads bytes (a multiple of 16) of buf
 // with work_groups work-groups; out receives at most one 4-byte marker.
 hipError_t launch_stream_read(const void* buf, size_t bytes, void* out, int32_t work_groups, hipStream_t stream);
+hipError_t launch_gather_read(const void* buf0, size_t bytes0, const void* buf1, size_t bytes1,
+                              const int64_t* tile_offsets, int64_t num_tiles, int32_t tile_bytes, void* out,
+                              int32_t work_groups, hipStream_t stream);
 
 // Multi-token attention with many rows per (sequence, KV head): the
 // prefill kernel (prefill.hip) takes 128 rows per work-group over the whole

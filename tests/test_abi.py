@@ -253,6 +253,21 @@ def test_stream_probe_rejects_bad_arguments(lib):
     assert f(FAKE, 0, FAKE, 64, None) == OK  # nothing to read
 
 
+def test_gather_probe_rejects_bad_arguments(lib):
+    f = lib.pkv_probe_gather_read
+    assert f(None, 4096, FAKE, 4096, FAKE, 4, 1024, FAKE, 8, None) == INVALID
+    assert f(FAKE, 4096, None, 4096, FAKE, 4, 1024, FAKE, 8, None) == INVALID
+    assert f(FAKE, 4096, FAKE, 4096, FAKE, 4, 1024, None, 8, None) == INVALID
+    assert f(ctypes.c_void_p(0x10008), 4096, FAKE, 4096, FAKE, 4, 1024, FAKE, 8, None) == INVALID
+    assert f(FAKE, 4096, FAKE, 4096, None, 4, 1024, FAKE, 8, None) == INVALID   # tiles without a list
+    assert f(FAKE, 4096, FAKE, 4096, FAKE, -1, 1024, FAKE, 8, None) == INVALID
+    for tb in (0, 512, 1536, (1 << 20) + 1024):
+        assert f(FAKE, 4096, FAKE, 4096, FAKE, 4, tb, FAKE, 8, None) == INVALID
+    assert f(FAKE, 4096, FAKE, 4096, FAKE, 4, 1024, FAKE, 0, None) == INVALID
+    assert f(FAKE, 4096, FAKE, 4096, FAKE, 4, 1024, FAKE, (1 << 20) + 1, None) == INVALID
+    assert f(FAKE, 4096, FAKE, 4096, None, 0, 1024, FAKE, 8, None) == OK  # nothing to read
+
+
 def test_multi_token_workspace_sizes(lib):
     f = lib.pkv_multi_token_workspace_bytes
     # one chunk covers the table: none

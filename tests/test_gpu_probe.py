@@ -44,3 +44,41 @@ def test_probe_reads_every_word(work_groups):
     m.probe_stream_read(buf, out, work_groups)
     torch.cuda.synchronize()
     assert int(out[0]) == 0
+
+
+@pytest.mark.parametrize("tile_bytes,work_groups", [(1024, 1), (1024, 64), (4096, 3), (16384, 1000)])
+def test_gather_probe_reads_every_listed_tile(tile_bytes, work_groups):
+    # Tiles at shuffled, non-overlapping places of two buffers (even list
+    # entries in the first, odd in the second), plus entries the probe must
+    # skip (negative, misaligned, reaching past the end): a marker at the
+    # first or last word of any listed tile must come back.
+    import numpy as np
+
+    m = pkv()
+    words = (1 << 20) // 4  # 1 MiB per buffer
+    slots = (words * 4) // tile_bytes
+    rng = np.random.default_rng(tile_bytes + work_groups)
+    n_each = min(slots, 96)
+    offs0 = rng.permutation(slots)[:n_each] * tile_bytes
+    offs1 = rng.permutation(slots)[:n_each] * tile_bytes
+    offs = np.empty(2 * n_each, np.int64)
+    offs[0::2], offs[1::2] = offs0, offs1
+    bad = np.array([-tile_bytes, 8, words * 4, words * 4 - 16], np.int64)  # skipped
+    listed = np.concatenate([offs, bad])
+    announce(f"gather probe: {len(listed)} tiles of {tile_bytes} B, {work_groups} work-groups")
+    bufs = [torch.zeros(words, dtype=torch.int32, device="cuda") for _ in range(2)]
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+    t_offs = torch.from_numpy(listed).cuda()
+    for t in range(len(offs)):
+        for pos in (offs[t] // 4, (offs[t] + tile_bytes) // 4 - 1):
+            b = bufs[t % 2]
+            b[pos] = MARKER
+            out.zero_()
+            m.probe_gather_read(bufs[0], bufs[1], t_offs, tile_bytes, out, work_groups)
+            torch.cuda.synchronize()
+            assert int(out[0]) == MARKER, f"tile {t} word {pos} not read"
+            b[pos] = 0
+    out.zero_()
+    m.probe_gather_read(bufs[0], bufs[1], t_offs, tile_bytes, out, work_groups)
+    torch.cuda.synchronize()
+    assert int(out[0]) == 0
