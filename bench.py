@@ -175,7 +175,7 @@ def gather_read_ceiling(torch, pkv, w, copies, reps: int = 20):
     stream = torch.cuda.current_stream()
     nbytes = len(offs) * tile
     best = (0.0, 0)
-    for wg in (512, 1024, 2048, 4096):
+    for wg in (4096, 8192, 16384, 32768):
         for i in range(3):
             d = copies[i % len(copies)]
             pkv.probe_gather_read(d["kc"], d["vc"], t_offs, tile, out, wg, stream=stream)
