@@ -1,12 +1,14 @@
+// Read probes: measurement aids, not part of the attention method.
+//
 // Streaming-read probe: the rate at which the GPU reads a large buffer that
 // no kernel has touched recently, the practical ceiling of the library's
 // bandwidth-bound kernels (decode attention reads each key and value byte
-// once).  It is a measurement aid, not part of the attention method.
+// once).  Work-group b reads the b-th contiguous share of the buffer; each
+// thread keeps eight independent 16-byte non-temporal loads in flight and
+// folds the words it read into one value by XOR, which it stores only when
+// it equals a marker, so that no load can be dropped.
 //
-// Streaming-read probe: work-group b reads the b-th contiguous share of the
-// buffer; each thread keeps eight independent 16-byte non-temporal loads in
-// flight and folds the words it read into one value by XOR, which it stores
-// only when it equals a marker, so that no load can be dropped.
+// Gather-read probe: see gather_read_kernel below.
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -53,7 +55,8 @@ __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const u32x4v
 // exchange; each lane keeps kProbeDepth 16-byte non-temporal loads in
 // flight, lane l reading words l, l + 64, ... of each tile (tile_words is a
 // multiple of 64).  A tile outside its buffer, or at a negative offset or
-// one that is not a multiple of 16, is skipped.  The words read are folded by XOR as in the streaming probe.
+// one that is not a multiple of 16, is skipped.  The words read are folded
+// by XOR as in the streaming probe.
 __global__ __launch_bounds__(kProbeThreads) void gather_read_kernel(
     const char* __restrict__ b0, const char* __restrict__ b1, size_t n0, size_t n1,
     const int64_t* __restrict__ offs, int64_t ntiles, int32_t tile_words, unsigned* __restrict__ out)
