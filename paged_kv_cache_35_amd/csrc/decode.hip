@@ -1159,44 +1159,18 @@ __global__ __launch_bounds__(NW * 64) PKV_OCCUPANCY void paged_decode_partition_
 // carry l_p = 0 and get weight 0).  Sequences with one partition were
 // written by the partition kernel and are skipped here.
 //
-// A long context has hundreds of partitions per head, so the work is spread
-// over the work-group: the weights are computed once per partition into LDS
-// (in chunks of kMergeChunk partitions), and each thread then accumulates
-// one head dim over a strided subset of partitions with a batch of
-// independent loads in flight; the subsets are combined through LDS.
+// A long context has dozens to hundreds of partitions per head, so the work
+// is spread over the work-group in one pass: thread t takes head dims
+// 4 (t % (HS/4)) .. + 3 of partitions t / (HS/4), + R, + 2R, ... (R groups of
+// HS/4 threads), loading kMergeBatch partitions' (m, l) and 16-byte o at a
+// time with no load waiting on another, and keeps its own running maximum
+// (acc and the weight sum rescaled when it rises, as in the online softmax).
+// The R groups' (m, weight sum, acc) are then combined by the same rule
+// through LDS.  The result equals the formula above up to the order of the
+// fp32 sums.
 constexpr int kMergeThreads = 256;
-constexpr int kMergeChunk = 2048;
+constexpr int kMergeBatch = 4;
 
-__device__ __forceinline__ float block_reduce_max(float v, float* red)
-{
-    for (int o = 32; o > 0; o >>= 1)
-        v = fmaxf(v, __shfl_xor(v, o));
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0)
-        red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    float r = red[0];
-    for (int i = 1; i < kMergeThreads / 64; ++i)
-        r = fmaxf(r, red[i]);
-    return r;
-}
-
-__device__ __forceinline__ float block_reduce_sum(float v, float* red)
-{
-    for (int o = 32; o > 0; o >>= 1)
-        v += __shfl_xor(v, o);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0)
-        red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    float r = red[0];
-    for (int i = 1; i < kMergeThreads / 64; ++i)
-        r += red[i];
-    return r;
-}
-
-// MQ: one work-group per (query head, sequence, query row i = blockIdx.z);
-// the partials of row rho = i * G + g sit in row tile rho / 16, row rho % 16.
 // Persistent over (sequence rank, query head) pairs: work-group b takes
 // pairs b, b + gridDim.x, ...  Rank y is the y-th sequence of the
 // longest-first schedule when one is given (the sequences that span several
@@ -1211,11 +1185,13 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
     int32_t max_parts, const float* __restrict__ ws_o, const float* __restrict__ ws_ml, void* __restrict__ out,
     int32_t out_f32)
 {
-    constexpr int R = kMergeThreads / HS;  // partition groups
-    __shared__ float sm_w[kMergeChunk];
-    __shared__ float sm_red[kMergeThreads / 64];
-    __shared__ float sm_acc[R][HS];
+    constexpr int Q = HS / 4;               // threads per partition row (4 head dims each)
+    constexpr int R = kMergeThreads / Q;    // partition groups
+    __shared__ float sm_m[R][Q], sm_l[R][Q];
+    __shared__ f32x4 sm_acc[R][Q];
     const int G = Hq / Hkv;
+    const int q4 = threadIdx.x % Q;
+    const int grp = threadIdx.x / Q;
     const int64_t pairs = (int64_t)S * Hq;
     for (int64_t pr = blockIdx.x; pr < pairs; pr += gridDim.x) {
         const int y = (int)(pr / Hq);
@@ -1233,53 +1209,61 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
         const int kvh = h / G;
         const int g = h - kvh * G;
         const int64_t u0 = ((int64_t)s * Hkv + kvh) * max_parts;
-        auto row = [&](int p) __attribute__((always_inline)) { return (u0 + p) * G + g; };
 
-        float mx = -INFINITY;
-        for (int p = threadIdx.x; p < nparts; p += kMergeThreads)
-            if (ws_ml[2 * row(p) + 1] > 0.f)
-                mx = fmaxf(mx, ws_ml[2 * row(p)]);
-        mx = block_reduce_max(mx, sm_red);
-
-        const int d = threadIdx.x % HS;
-        const int grp = threadIdx.x / HS;
-        float acc = 0.f, wpart = 0.f;
-        for (int c0 = 0; c0 < nparts; c0 += kMergeChunk) {
-            const int cn = nparts - c0 < kMergeChunk ? nparts - c0 : kMergeChunk;
-            __syncthreads();  // previous chunk's weights fully consumed
-            for (int i = threadIdx.x; i < cn; i += kMergeThreads) {
-                const float l = ws_ml[2 * row(c0 + i) + 1];
-                const float wgt = l > 0.f ? l * __builtin_amdgcn_exp2f(ws_ml[2 * row(c0 + i)] - mx) : 0.f;
-                sm_w[i] = wgt;
-                wpart += wgt;
-            }
-            __syncthreads();
-            const float* base = ws_o + row(c0) * HS + d;
-            const int64_t pstride = (int64_t)G * HS;  // between consecutive partitions
-            int i = grp;
-            for (; i + 7 * R < cn; i += 8 * R) {
-                float v[8];
+        float m_t = -INFINITY, l_t = 0.f;
+        f32x4 acc = (f32x4)0.f;
+        for (int p0 = grp; p0 < nparts; p0 += kMergeBatch * R) {
+            float2 ml[kMergeBatch];
+            f32x4 o[kMergeBatch];
 #pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    v[k] = base[(int64_t)(i + k * R) * pstride];
-#pragma unroll
-                for (int k = 0; k < 8; ++k)
-                    acc += sm_w[i + k * R] * v[k];
+            for (int k = 0; k < kMergeBatch; ++k) {
+                const int p = p0 + k * R;
+                ml[k] = make_float2(0.f, 0.f);
+                o[k] = (f32x4)0.f;
+                if (p < nparts) {
+                    const int64_t row = (u0 + p) * G + g;
+                    ml[k] = *reinterpret_cast<const float2*>(ws_ml + 2 * row);
+                    o[k] = *reinterpret_cast<const f32x4*>(ws_o + row * HS + 4 * q4);
+                }
             }
-            for (; i < cn; i += R)
-                acc += sm_w[i] * base[(int64_t)i * pstride];
+#pragma unroll
+            for (int k = 0; k < kMergeBatch; ++k) {
+                if (ml[k].y > 0.f) {  // l_p > 0 (never true past nparts)
+                    if (ml[k].x > m_t) {  // the running maximum rises: rescale what was summed
+                        const float f = __builtin_amdgcn_exp2f(m_t - ml[k].x);  // 0 while m_t is -inf
+                        acc *= f;
+                        l_t *= f;
+                        m_t = ml[k].x;
+                    }
+                    const float wgt = ml[k].y * __builtin_amdgcn_exp2f(ml[k].x - m_t);
+                    acc += wgt * o[k];
+                    l_t += wgt;
+                }
+            }
         }
-        const float wsum = block_reduce_sum(wpart, sm_red);
-        sm_acc[grp][d] = acc;
+        sm_m[grp][q4] = m_t;
+        sm_l[grp][q4] = l_t;
+        sm_acc[grp][q4] = acc;
         __syncthreads();
-        if (threadIdx.x < HS) {
-            float tot = 0.f;
+        if (threadIdx.x < Q) {
+            float mx = -INFINITY;
 #pragma unroll
             for (int k = 0; k < R; ++k)
-                tot += sm_acc[k][threadIdx.x];
-            store_out<T>(out, ((int64_t)s * Hq + h) * HS + threadIdx.x, wsum > 0.f ? tot / wsum : 0.f, out_f32);
+                if (sm_l[k][q4] > 0.f)
+                    mx = fmaxf(mx, sm_m[k][q4]);
+            float wsum = 0.f;
+            f32x4 tot = (f32x4)0.f;
+#pragma unroll
+            for (int k = 0; k < R; ++k)
+                if (sm_l[k][q4] > 0.f) {
+                    const float f = __builtin_amdgcn_exp2f(sm_m[k][q4] - mx);
+                    wsum += sm_l[k][q4] * f;
+                    tot += f * sm_acc[k][q4];
+                }
+            const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+            store_out4<T>(out, ((int64_t)s * Hq + h) * HS + 4 * q4, tot * inv, out_f32);
         }
-        __syncthreads();  // sm_acc and sm_w are reused by the next pair
+        __syncthreads();  // the LDS slots are reused by the next pair
     }
 }
 
