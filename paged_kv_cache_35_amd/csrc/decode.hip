@@ -1269,8 +1269,9 @@ __global__ __launch_bounds__(kMergeThreads) void paged_decode_reduce_kernel(
 
 // Chunk merge for launches with few chunks per sequence (at most
 // kFewChunks): one wave per (sequence rank, query head) pair, persistent over
-// the pairs, each lane taking 4 consecutive head dims and summing the chunks
-// in increasing order; no LDS, no barrier.  (With many chunks, the work-group
+// the pairs, each lane taking 4 consecutive head dims, loading every chunk's
+// (m, l) and partial at once and summing the chunks in increasing order; no
+// LDS, no barrier.  (With many chunks, the work-group
 // of the kernel above spreads a pair's chunks over its threads instead.)
 constexpr int kFewChunks = 8;
 constexpr int kFewMergeWaves = 8192;
@@ -1301,19 +1302,31 @@ __global__ __launch_bounds__(64) void paged_decode_reduce_few_kernel(
         const int g = h - kvh * G;
         const int d = 4 * threadIdx.x;
         const int64_t u0 = ((int64_t)s * Hkv + kvh) * max_parts;
-        float mx = -INFINITY;
-        for (int p = 0; p < nparts; ++p) {
-            const float2 ml = *(const float2*)(ws_ml + 2 * ((u0 + p) * G + g));
-            if (ml.y > 0.f)
-                mx = fmaxf(mx, ml.x);
+        // every chunk's (m, l) and 16-byte partial in flight at once
+        float2 ml[kFewChunks];
+        f32x4 o[kFewChunks];
+#pragma unroll
+        for (int p = 0; p < kFewChunks; ++p) {
+            ml[p] = make_float2(0.f, 0.f);
+            o[p] = (f32x4)0.f;
+            if (p < nparts) {
+                const int64_t row = (u0 + p) * G + g;
+                ml[p] = *(const float2*)(ws_ml + 2 * row);
+                o[p] = *(const f32x4*)(ws_o + row * HS + d);
+            }
         }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int p = 0; p < kFewChunks; ++p)
+            if (ml[p].y > 0.f)
+                mx = fmaxf(mx, ml[p].x);
         float wsum = 0.f;
         f32x4 acc = (f32x4)0.f;
-        for (int p = 0; p < nparts; ++p) {
-            const float2 ml = *(const float2*)(ws_ml + 2 * ((u0 + p) * G + g));
-            const float wgt = ml.y > 0.f ? ml.y * __builtin_amdgcn_exp2f(ml.x - mx) : 0.f;
+#pragma unroll
+        for (int p = 0; p < kFewChunks; ++p) {  // in increasing chunk order
+            const float wgt = ml[p].y > 0.f ? ml[p].y * __builtin_amdgcn_exp2f(ml[p].x - mx) : 0.f;
             wsum += wgt;
-            acc += wgt * *(const f32x4*)(ws_o + ((u0 + p) * G + g) * HS + d);
+            acc += wgt * o[p];
         }
         f32x4 res;
 #pragma unroll
